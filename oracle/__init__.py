@@ -1,0 +1,191 @@
+"""ctypes wrapper for the CPU oracle (TEST INFRASTRUCTURE ONLY).
+
+Only tests/, __graft_entry__.smoke() and bench.py's CPU-baseline leg may
+import this package.  It works on numpy arrays on the host and never touches
+a GPU.  Arrays holding 16-bit values are numpy uint16 (raw bit patterns).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle_zero.so")
+
+BF16, FP16 = 0, 1
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built: run oracle/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        vp = ctypes.c_void_p
+        L.ora_flatten_layout.argtypes = [i64p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int64, i64p, i64p]
+        L.ora_flatten_layout.restype = ctypes.c_int
+        L.ora_shard_segments.argtypes = [i64p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int64, ctypes.c_int32, i64p,
+                                         ctypes.c_int64]
+        L.ora_shard_segments.restype = ctypes.c_int64
+        L.ora_array_split_start.argtypes = [ctypes.c_int64] * 3
+        L.ora_array_split_start.restype = ctypes.c_int64
+        for name in ("ora_f32_to_bf16_n", "ora_f32_to_f16_n",
+                     "ora_bf16_to_f32_n", "ora_f16_to_f32_n"):
+            getattr(L, name).argtypes = [vp, vp, ctypes.c_int64]
+            getattr(L, name).restype = None
+        L.ora_adamw_scalars.argtypes = [vp, ctypes.c_int64, vp]
+        L.ora_adamw_scalars.restype = None
+        L.ora_reduce.argtypes = [vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_int64, vp, ctypes.c_int, vp, vp]
+        L.ora_reduce.restype = None
+        L.ora_adamw.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int64,
+                                vp, ctypes.c_int64, vp]
+        L.ora_adamw.restype = None
+        L.ora_step.argtypes = [vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int64,
+                               ctypes.c_int64, vp, vp, vp, vp, ctypes.c_int, vp,
+                               ctypes.c_int64, vp, vp]
+        L.ora_step.restype = None
+        L.ora_model_state_bytes.argtypes = [ctypes.c_double, ctypes.c_double,
+                                            ctypes.c_int, ctypes.c_double]
+        L.ora_model_state_bytes.restype = ctypes.c_double
+        L.ora_comm_bytes.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                     ctypes.c_double, ctypes.c_double]
+        L.ora_comm_bytes.restype = ctypes.c_double
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _need(a, dtype, name):
+    if not (isinstance(a, np.ndarray) and a.dtype == dtype and a.flags.c_contiguous):
+        raise TypeError(f"{name}: need a C-contiguous numpy {np.dtype(dtype).name} array")
+
+
+def flatten_layout(numels, n_dp, align=1):
+    """-> (offsets, N, N_pad, S) or raises ValueError."""
+    nums = np.ascontiguousarray(numels, dtype=np.int64)
+    offs = np.zeros(len(nums), dtype=np.int64)
+    out = np.zeros(3, dtype=np.int64)
+    rc = lib().ora_flatten_layout(
+        nums.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(nums), n_dp, align,
+        offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    if rc != 0:
+        raise ValueError("invalid layout arguments")
+    return offs, int(out[0]), int(out[1]), int(out[2])
+
+
+def shard_segments(numels, n_dp, rank, align=1):
+    """-> list of (tensor, tensor_off, shard_off, len); tensor -1 is padding."""
+    nums = np.ascontiguousarray(numels, dtype=np.int64)
+    p = nums.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    cnt = lib().ora_shard_segments(p, len(nums), n_dp, align, rank, None, 0)
+    if cnt < 0:
+        raise ValueError("invalid segment arguments")
+    q = np.zeros(4 * max(cnt, 1), dtype=np.int64)
+    lib().ora_shard_segments(p, len(nums), n_dp, align, rank,
+                             q.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), cnt)
+    return [tuple(int(x) for x in q[4 * i:4 * i + 4]) for i in range(cnt)]
+
+
+def array_split_start(n, parts, i):
+    return lib().ora_array_split_start(n, parts, i)
+
+
+def f32_to_bf16(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    lib().ora_f32_to_bf16_n(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def f32_to_f16(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    lib().ora_f32_to_f16_n(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def bf16_to_f32(h):
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    y = np.empty(h.shape, dtype=np.float32)
+    lib().ora_bf16_to_f32_n(_ptr(h), _ptr(y), h.size)
+    return y
+
+
+def f16_to_f32(h):
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    y = np.empty(h.shape, dtype=np.float32)
+    lib().ora_f16_to_f32_n(_ptr(h), _ptr(y), h.size)
+    return y
+
+
+def _hp(lr, beta1, beta2, eps, weight_decay, grad_scale):
+    return np.array([lr, beta1, beta2, eps, weight_decay, grad_scale], dtype=np.float64)
+
+
+def adamw_scalars(step, lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1,
+                  grad_scale=1.0):
+    """-> dict of the fp32 scalars s, b1, c1, b2, c2, bc1, bc2, lr, eps, d."""
+    hp = _hp(lr, beta1, beta2, eps, weight_decay, grad_scale)
+    out = np.zeros(10, dtype=np.float32)
+    lib().ora_adamw_scalars(_ptr(hp), step, _ptr(out))
+    keys = ("s", "b1", "c1", "b2", "c2", "bc1", "bc2", "lr", "eps", "d")
+    return dict(zip(keys, (np.float32(v) for v in out)))
+
+
+def reduce(grads, gdt, n_contrib, ld, length, acc, accumulate, overflow=None, sumsq=None):
+    """In place on acc (float32[length]); overflow uint32[1]; sumsq float64[1]."""
+    _need(grads, np.uint16, "grads")
+    _need(acc, np.float32, "acc")
+    if length > 0 and grads.size < (n_contrib - 1) * ld + length:
+        raise ValueError("grads too small")
+    lib().ora_reduce(_ptr(grads), gdt, n_contrib, ld, length, _ptr(acc),
+                     int(bool(accumulate)), _ptr(overflow), _ptr(sumsq))
+
+
+def adamw(acc, w, m, v, wout, wdt, length, step, lr=1e-4, beta1=0.9, beta2=0.999,
+          eps=1e-8, weight_decay=0.1, grad_scale=1.0, skip=None):
+    """In place on w, m, v (float32) and wout (uint16)."""
+    for a, n in ((acc, "acc"), (w, "w"), (m, "m"), (v, "v")):
+        _need(a, np.float32, n)
+    _need(wout, np.uint16, "wout")
+    hp = _hp(lr, beta1, beta2, eps, weight_decay, grad_scale)
+    lib().ora_adamw(_ptr(acc), _ptr(w), _ptr(m), _ptr(v), _ptr(wout), wdt, length,
+                    _ptr(hp), step, _ptr(skip))
+
+
+def step(grads, gdt, n_dp, ld, length, w, m, v, wout, wdt, step, lr=1e-4, beta1=0.9,
+         beta2=0.999, eps=1e-8, weight_decay=0.1, grad_scale=None, overflow=None,
+         sumsq=None):
+    """Fused reduce + AdamW + cast, in place on w, m, v, wout.
+
+    grad_scale defaults to 1/n_dp, the average over ranks."""
+    _need(grads, np.uint16, "grads")
+    for a, n in ((w, "w"), (m, "m"), (v, "v")):
+        _need(a, np.float32, n)
+    _need(wout, np.uint16, "wout")
+    if length > 0 and grads.size < (n_dp - 1) * ld + length:
+        raise ValueError("grads too small")
+    if grad_scale is None:
+        grad_scale = 1.0 / n_dp
+    hp = _hp(lr, beta1, beta2, eps, weight_decay, grad_scale)
+    lib().ora_step(_ptr(grads), gdt, n_dp, ld, length, _ptr(w), _ptr(m), _ptr(v),
+                   _ptr(wout), wdt, _ptr(hp), step, _ptr(overflow), _ptr(sumsq))
+
+
+def model_state_bytes(n, n_dp, stage, k=12):
+    return lib().ora_model_state_bytes(float(n), float(n_dp), stage, float(k))
+
+
+def comm_bytes(n, n_dp, stage, param_bytes=2, grad_bytes=2):
+    return lib().ora_comm_bytes(float(n), float(n_dp), stage, float(param_bytes),
+                                float(grad_bytes))

@@ -1,0 +1,345 @@
+/*
+ * oracle_zero.c -- plain CPU oracle (TEST INFRASTRUCTURE ONLY; see the
+ * header).  Single-threaded, one element at a time, IEEE binary32 with
+ * round-to-nearest-even for the optimizer arithmetic, built with
+ * -ffp-contract=off and without any fast-math option.
+ *
+ * What pins each function (tests/test_oracle_*.py):
+ *  - ora_flatten_layout / ora_shard_segments: the tiny workload's printed
+ *    sizes (10,000 elements, 4 ranks, shard 2,500), numpy.array_split
+ *    boundaries when n_dp divides N, brute-force tiling on tiny lists, the
+ *    7B and GPT-2-XL totals.
+ *  - converters: exhaustive against torch / numpy library conversions.
+ *  - ora_reduce: exact sums (fractions) within the recursive-summation bound,
+ *    numpy float64 sums, the sum-of-shards identity (reduce-scatter followed
+ *    by all-gather equals all-reduce).
+ *  - ora_adamw / ora_step: torch.optim.AdamW on the CPU (a library routine),
+ *    the step-1 closed form (update ~ -lr*sign(g) - lr*wd*w), the constant-
+ *    gradient closed form, a high-precision brute force on tiny inputs, and
+ *    sharded == unsharded.
+ *  - ora_model_state_bytes / ora_comm_bytes: the numbers the pages print.
+ * ora_step's sumsq output is order dependent and checked only against a
+ * float64 sum within a bound (parity unpinned bitwise by design).
+ */
+#include "oracle_zero.h"
+
+#include <math.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Layout.  "ZeRO and FSDP", "The idea, one stage at a time": one flat vector
+ * of N numbers cut into n_dp equal contiguous shards; rank r owns shard r.
+ * Equal shards need N_pad = n_dp * S >= N; the tail is zero padding. */
+
+int ora_flatten_layout(const int64_t *numels, int64_t n_tensors, int32_t n_dp,
+                       int64_t align, int64_t *offsets, int64_t out3[3]) {
+    if (n_tensors < 0 || n_dp < 1 || align < 1 || out3 == 0) return -1;
+    if (n_tensors > 0 && numels == 0) return -1;
+    int64_t n = 0;
+    for (int64_t i = 0; i < n_tensors; ++i) {
+        if (numels[i] < 0) return -1;
+        if (offsets) offsets[i] = n;
+        n += numels[i];
+    }
+    int64_t unit = (int64_t)n_dp * align;
+    int64_t units = (n + unit - 1) / unit;
+    int64_t shard = units * align;
+    out3[0] = n;
+    out3[1] = shard * n_dp;
+    out3[2] = shard;
+    return 0;
+}
+
+int64_t ora_shard_segments(const int64_t *numels, int64_t n_tensors,
+                           int32_t n_dp, int64_t align, int32_t rank,
+                           int64_t *quads, int64_t cap) {
+    int64_t lay[3];
+    if (ora_flatten_layout(numels, n_tensors, n_dp, align, 0, lay) != 0)
+        return -1;
+    if (rank < 0 || rank >= n_dp) return -1;
+    int64_t n = lay[0], shard = lay[2];
+    int64_t lo = (int64_t)rank * shard, hi = lo + shard;
+    int64_t count = 0, start = 0;
+    for (int64_t t = 0; t < n_tensors; ++t) {
+        int64_t a = start, b = start + numels[t];
+        start = b;
+        int64_t s = a > lo ? a : lo;
+        int64_t e = b < hi ? b : hi;
+        if (e > s) {
+            if (count < cap) {
+                quads[4 * count + 0] = t;
+                quads[4 * count + 1] = s - a;
+                quads[4 * count + 2] = s - lo;
+                quads[4 * count + 3] = e - s;
+            }
+            ++count;
+        }
+    }
+    /* the zero padding [N, N_pad) */
+    int64_t s = n > lo ? n : lo;
+    if (hi > s) {
+        if (count < cap) {
+            quads[4 * count + 0] = -1;
+            quads[4 * count + 1] = s - n;
+            quads[4 * count + 2] = s - lo;
+            quads[4 * count + 3] = hi - s;
+        }
+        ++count;
+    }
+    return count;
+}
+
+/* "A sharded Adam step": the shards are the pieces of numpy.array_split,
+ * whose first (n mod parts) pieces are one element longer. */
+int64_t ora_array_split_start(int64_t n, int64_t parts, int64_t i) {
+    int64_t each = n / parts, extra = n % parts;
+    return i * each + (i < extra ? i : extra);
+}
+
+/* ------------------------------------------------------------------------ */
+/* 16-bit formats.  bf16 is the top half of an fp32; fp16 is IEEE binary16. */
+
+static float bits_to_f32(uint32_t u) {
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static uint32_t f32_to_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return u;
+}
+
+float ora_bf16_to_f32(uint16_t h) { return bits_to_f32((uint32_t)h << 16); }
+
+float ora_f16_to_f32(uint16_t h) {
+    uint32_t sign = (uint32_t)(h >> 15) << 31;
+    uint32_t e = (h >> 10) & 0x1F;
+    uint32_t mant = h & 0x3FF;
+    if (e == 0x1F) /* Inf / NaN: keep the payload */
+        return bits_to_f32(sign | 0x7F800000u | (mant << 13));
+    if (e != 0) /* normal: rebias 15 -> 127 */
+        return bits_to_f32(sign | ((e + 112u) << 23) | (mant << 13));
+    /* zero or subnormal: value = mant * 2^-24, exact in fp32 */
+    float mag = (float)mant * 0x1p-24f;
+    return sign ? -mag : mag;
+}
+
+uint16_t ora_f32_to_bf16(float f) {
+    uint32_t u = f32_to_bits(f);
+    uint32_t sign = u & 0x80000000u;
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) /* NaN */
+        return (uint16_t)((sign >> 16) | 0x7FC0u);
+    /* keep the top 16 bits, rounding the dropped 16 to nearest, ties to
+     * even.  A carry out of the mantissa moves to the exponent, which turns
+     * the largest finite values into Inf as rounding requires. */
+    uint32_t hi = u >> 16, lo = u & 0xFFFFu;
+    if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) hi += 1;
+    return (uint16_t)hi;
+}
+
+uint16_t ora_f32_to_f16(float f) {
+    uint32_t u = f32_to_bits(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t mag = u & 0x7FFFFFFFu;
+    if (mag > 0x7F800000u) return (uint16_t)(sign | 0x7E00u); /* NaN */
+    if (mag == 0x7F800000u) return (uint16_t)(sign | 0x7C00u); /* Inf */
+    int32_t e = (int32_t)(mag >> 23) - 127; /* unbiased exponent */
+    uint32_t m = mag & 0x7FFFFFu;
+    if (e > 15) return (uint16_t)(sign | 0x7C00u); /* overflow */
+    uint32_t full;  /* significand with implicit bit, 24 bits */
+    int32_t shift;  /* right shift that lands it on the fp16 grid */
+    uint32_t ebits; /* fp16 biased exponent before rounding */
+    if (mag >= 0x38800000u) { /* |f| >= 2^-14: fp16 normal range */
+        full = m | 0x800000u;
+        shift = 13;
+        ebits = (uint32_t)(e + 15);
+    } else {
+        /* at most half of 2^-24 (a tie goes to the even 0) -> signed zero;
+         * this also covers every fp32 subnormal */
+        if (mag <= 0x33000000u) return sign;
+        /* subnormal target: value = q * 2^-24 with
+         * q = round(full * 2^(e - 23 + 24)), a right shift by -e-1 in
+         * [14, 24] because -25 <= e <= -15 here */
+        full = m | 0x800000u;
+        shift = -e - 1;
+        ebits = 0;
+    }
+    uint32_t q = full >> shift;
+    uint32_t rem = full & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u))) q += 1;
+    uint32_t out;
+    if (ebits == 0) {
+        out = q; /* q <= 0x400; 0x400 is the smallest normal, correctly */
+    } else {
+        /* q in [0x400, 0x800]; 0x800 means the mantissa overflowed */
+        out = (ebits << 10) + (q - 0x400u);
+        if (out >= 0x7C00u) out = 0x7C00u;
+    }
+    return (uint16_t)(sign | out);
+}
+
+void ora_f32_to_bf16_n(const float *x, uint16_t *y, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) y[i] = ora_f32_to_bf16(x[i]);
+}
+void ora_f32_to_f16_n(const float *x, uint16_t *y, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) y[i] = ora_f32_to_f16(x[i]);
+}
+void ora_bf16_to_f32_n(const uint16_t *x, float *y, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) y[i] = ora_bf16_to_f32(x[i]);
+}
+void ora_f16_to_f32_n(const uint16_t *x, float *y, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) y[i] = ora_f16_to_f32(x[i]);
+}
+
+static float widen(uint16_t h, int dt) {
+    return dt == ORA_FP16 ? ora_f16_to_f32(h) : ora_bf16_to_f32(h);
+}
+
+static uint16_t narrow(float f, int dt) {
+    return dt == ORA_FP16 ? ora_f32_to_f16(f) : ora_f32_to_bf16(f);
+}
+
+static int nonfinite(float f) { return isnan(f) || isinf(f); }
+
+/* ------------------------------------------------------------------------ */
+/* AdamW.  "ZeRO and FSDP", "A sharded Adam step":
+ *   m <- b1 m + (1 - b1) g,  v <- b2 v + (1 - b2) g^2,
+ *   w <- w - lr * mhat / (sqrt(vhat) + eps),
+ *   mhat = m / (1 - b1^t), vhat = v / (1 - b2^t), t counted from 1.
+ * The configs on "DeepSpeed ZeRO" ("A worked example") and "ZeRO Optimizer,
+ * in depth" ("Running it with DeepSpeed") name AdamW with a weight decay; its
+ * decay is the decoupled one (Loshchilov & Hutter): the master weight is
+ * first multiplied by (1 - lr * wd), then the Adam step is subtracted.
+ * Every scalar below is formed in double and rounded once to fp32. */
+
+void ora_adamw_scalars(const double hp6[6], int64_t step, float out10[10]) {
+    double lr = hp6[0], beta1 = hp6[1], beta2 = hp6[2], eps = hp6[3];
+    double wd = hp6[4], grad_scale = hp6[5];
+    out10[0] = (float)grad_scale;                       /* s   */
+    out10[1] = (float)beta1;                            /* b1  */
+    out10[2] = (float)(1.0 - beta1);                    /* c1  */
+    out10[3] = (float)beta2;                            /* b2  */
+    out10[4] = (float)(1.0 - beta2);                    /* c2  */
+    out10[5] = (float)(1.0 - pow(beta1, (double)step)); /* bc1 */
+    out10[6] = (float)(1.0 - pow(beta2, (double)step)); /* bc2 */
+    out10[7] = (float)lr;                               /* lr  */
+    out10[8] = (float)eps;                              /* eps */
+    out10[9] = (float)(1.0 - lr * wd);                  /* d   */
+}
+
+/* one element of the update; g is the averaged fp32 gradient */
+static void adamw_element(float g, float *w, float *m, float *v,
+                          const float c[10]) {
+    float b1 = c[1], c1 = c[2], b2 = c[3], c2 = c[4];
+    float bc1 = c[5], bc2 = c[6], lr = c[7], eps = c[8], d = c[9];
+    float mt = b1 * *m + c1 * g;
+    float vt = b2 * *v + c2 * (g * g);
+    float mhat = mt / bc1;
+    float vhat = vt / bc2;
+    float den = sqrtf(vhat) + eps;
+    float u = mhat / den;
+    float wt = *w * d - lr * u;
+    *m = mt;
+    *v = vt;
+    *w = wt;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The reduce.  "ZeRO and FSDP", "The idea, one stage at a time": the reduce-
+ * scatter hands rank r the averaged gradient of shard r.  Here the n ranks'
+ * 16-bit rows for that shard are widened and summed left to right (the
+ * average's scale is applied with the update). */
+
+static float row_sum(const uint16_t *grads, int gdt, int32_t n, int64_t ld,
+                     int64_t j, int *bad) {
+    float a = 0.0f;
+    for (int32_t k = 0; k < n; ++k) {
+        float x = widen(grads[(int64_t)k * ld + j], gdt);
+        if (nonfinite(x)) *bad = 1;
+        a = (k == 0) ? x : a + x;
+    }
+    return a;
+}
+
+void ora_reduce(const uint16_t *grads, int gdt, int32_t n_contrib, int64_t ld,
+                int64_t len, float *acc, int accumulate, uint32_t *overflow,
+                double *sumsq) {
+    int bad = 0;
+    double ss = 0.0;
+    for (int64_t j = 0; j < len; ++j) {
+        float a = row_sum(grads, gdt, n_contrib, ld, j, &bad);
+        float r = accumulate ? acc[j] + a : a;
+        acc[j] = r;
+        ss += (double)r * (double)r;
+    }
+    if (overflow && bad) *overflow = 1u;
+    if (sumsq) *sumsq += ss;
+}
+
+void ora_adamw(const float *acc, float *w, float *m, float *v, uint16_t *wout,
+               int wdt, int64_t len, const double hp6[6], int64_t step,
+               const uint32_t *skip) {
+    if (skip && *skip) return;
+    float c[10];
+    ora_adamw_scalars(hp6, step, c);
+    for (int64_t j = 0; j < len; ++j) {
+        float g = acc[j] * c[0];
+        adamw_element(g, &w[j], &m[j], &v[j], c);
+        wout[j] = narrow(w[j], wdt);
+    }
+}
+
+void ora_step(const uint16_t *grads, int gdt, int32_t n_dp, int64_t ld,
+              int64_t len, float *w, float *m, float *v, uint16_t *wout,
+              int wdt, const double hp6[6], int64_t step, uint32_t *overflow,
+              double *sumsq) {
+    float c[10];
+    ora_adamw_scalars(hp6, step, c);
+    int bad = 0;
+    double ss = 0.0;
+    for (int64_t j = 0; j < len; ++j) {
+        float a = row_sum(grads, gdt, n_dp, ld, j, &bad);
+        float g = a * c[0];
+        ss += (double)g * (double)g;
+        adamw_element(g, &w[j], &m[j], &v[j], c);
+        wout[j] = narrow(w[j], wdt);
+    }
+    if (overflow && bad) *overflow = 1u;
+    if (sumsq) *sumsq += ss;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Accounting.  "ZeRO and FSDP", "Memory per GPU": weights 2N, gradients 2N,
+ * optimizer K N; stage 1 divides the optimizer term by n_dp, stage 2 also
+ * the gradients, stage 3 also the weights. */
+
+double ora_model_state_bytes(double n, double n_dp, int stage, double k) {
+    double w = 2.0 * n, g = 2.0 * n, o = k * n;
+    switch (stage) {
+    case 0: return w + g + o;
+    case 1: return w + g + o / n_dp;
+    case 2: return w + g / n_dp + o / n_dp;
+    case 3: return w / n_dp + g / n_dp + o / n_dp;
+    default: return -1.0;
+    }
+}
+
+/* "ZeRO and FSDP", "Communication volume": a ring reduce-scatter or all-
+ * gather of N elements sends (n_dp - 1) N / n_dp per GPU, an all-reduce
+ * twice that.  Stage 0 all-reduces gradients; stages 1 and 2 reduce-scatter
+ * gradients and all-gather weights; stage 3 all-gathers weights twice and
+ * reduce-scatters gradients. */
+double ora_comm_bytes(double n, double n_dp, int stage, double param_bytes,
+                      double grad_bytes) {
+    double f = (n_dp - 1.0) / n_dp * n;
+    switch (stage) {
+    case 0: return 2.0 * f * grad_bytes;
+    case 1:
+    case 2: return f * grad_bytes + f * param_bytes;
+    case 3: return 2.0 * f * param_bytes + f * grad_bytes;
+    default: return -1.0;
+    }
+}

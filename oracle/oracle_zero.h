@@ -1,0 +1,113 @@
+/*
+ * oracle_zero.h -- the CPU oracle for one rank's sharded mixed-precision
+ * optimizer step (flatten + shard, gradient reduce, fp32 AdamW, 16-bit cast).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this code: it exists so that tests, the smoke check and the
+ * benchmark's CPU-baseline leg have an independent, plainly written reference.
+ * It shares no source with the HIP library (its own header, its own
+ * converters, its own constant set-up).
+ *
+ * Everything here is single-threaded, element by element, in IEEE binary32
+ * with round-to-nearest-even (fp32 is the precision the pages fix for the
+ * master weights and both Adam moments), every operation written out, built
+ * with -ffp-contract=off so that no multiply-add is fused.
+ *
+ * Sources (page title, then section):
+ *  - "ZeRO and FSDP" (Zero to Frontier, section 10.3), "The idea, one stage
+ *    at a time": flatten all parameters into one vector of N, cut it into
+ *    n_dp equal contiguous shards, rank r owns shard r; stage 1 reduce-
+ *    scatters the averaged gradient, updates the fp32 master shard, casts it
+ *    to bfloat16, and all-gathers.  Same page, "A sharded Adam step": the
+ *    average over ranks, Adam with bias correction from t = 1.  Same page,
+ *    "Memory per GPU" and "Communication volume": the accounting formulas.
+ *  - "ZeRO Optimizer, in depth ..." (aicassindra), "Where the 16 bytes per
+ *    parameter go": 2 + 2 + 12 bytes per parameter.
+ *  - "DeepSpeed ZeRO" (ozercemkelahmet), "Mixed precision": fp16 needs loss
+ *    scaling; the configs there name AdamW.
+ *
+ * Parity status per function is listed in oracle_zero.c's header.
+ */
+#ifndef ORACLE_ZERO_H
+#define ORACLE_ZERO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* 16-bit storage formats of gradients and weights. */
+enum { ORA_BF16 = 0, ORA_FP16 = 1 };
+
+/* ---- layout: flatten + equal contiguous shards ---------------------------
+ * numels[n_tensors] -> offsets[n_tensors] (prefix sums, nullable),
+ * out3 = {N, N_pad, S} with S = align * ceil(N / (n_dp * align)),
+ * N_pad = n_dp * S.  Returns 0, or -1 on invalid arguments. */
+int ora_flatten_layout(const int64_t *numels, int64_t n_tensors, int32_t n_dp,
+                       int64_t align, int64_t *offsets, int64_t out3[3]);
+
+/* The pieces of shard `rank`: quads {tensor, tensor_off, shard_off, len},
+ * tensor = -1 for padding.  Writes at most cap quads, returns the total
+ * count (or -1 on invalid arguments). */
+int64_t ora_shard_segments(const int64_t *numels, int64_t n_tensors,
+                           int32_t n_dp, int64_t align, int32_t rank,
+                           int64_t *quads, int64_t cap);
+
+/* Boundaries of numpy.array_split(range(n), parts): start of piece i. */
+int64_t ora_array_split_start(int64_t n, int64_t parts, int64_t i);
+
+/* ---- 16-bit <-> fp32 conversions ------------------------------------------ */
+float ora_bf16_to_f32(uint16_t h);
+float ora_f16_to_f32(uint16_t h);
+uint16_t ora_f32_to_bf16(float f); /* RNE; NaN -> sign | 0x7FC0 */
+uint16_t ora_f32_to_f16(float f);  /* RNE; NaN -> sign | 0x7E00 */
+void ora_f32_to_bf16_n(const float *x, uint16_t *y, int64_t n);
+void ora_f32_to_f16_n(const float *x, uint16_t *y, int64_t n);
+void ora_bf16_to_f32_n(const uint16_t *x, float *y, int64_t n);
+void ora_f16_to_f32_n(const uint16_t *x, float *y, int64_t n);
+
+/* ---- AdamW scalars --------------------------------------------------------
+ * hp6 = {lr, beta1, beta2, eps, weight_decay, grad_scale} as doubles, step
+ * t >= 1.  out10 = {s, b1, c1, b2, c2, bc1, bc2, lr, eps, d} in fp32, each
+ * computed in double and rounded once. */
+void ora_adamw_scalars(const double hp6[6], int64_t step, float out10[10]);
+
+/* ---- the reduce (the reduce-scatter's arithmetic for one shard) -----------
+ * a_j = G_0[j] + G_1[j] + ... + G_{n-1}[j], widened to fp32, left to right.
+ * accumulate == 0: acc[j] = a_j; else acc[j] = acc[j] + a_j.
+ * overflow (nullable): set to 1 if any widened input is +-Inf or NaN.
+ * sumsq (nullable): += sum over j of acc[j]^2 (after the update), in double. */
+void ora_reduce(const uint16_t *grads, int gdt, int32_t n_contrib, int64_t ld,
+                int64_t len, float *acc, int accumulate, uint32_t *overflow,
+                double *sumsq);
+
+/* ---- AdamW from an fp32 gradient buffer ------------------------------------
+ * g = acc[j] * s, then the AdamW element update of w/m/v, and
+ * wout[j] = 16-bit cast of the new w (wdt).  skip (nullable): if *skip != 0
+ * nothing at all is written. */
+void ora_adamw(const float *acc, float *w, float *m, float *v, uint16_t *wout,
+               int wdt, int64_t len, const double hp6[6], int64_t step,
+               const uint32_t *skip);
+
+/* ---- fused: reduce n_dp rows, then AdamW, then cast -----------------------
+ * Equal, element by element, to ora_reduce(accumulate = 0) into a temporary
+ * followed by ora_adamw.  overflow reports non-finite inputs (the update is
+ * still applied); sumsq (nullable) += sum of g_j^2 with g_j = a_j * s. */
+void ora_step(const uint16_t *grads, int gdt, int32_t n_dp, int64_t ld,
+              int64_t len, float *w, float *m, float *v, uint16_t *wout,
+              int wdt, const double hp6[6], int64_t step, uint32_t *overflow,
+              double *sumsq);
+
+/* ---- accounting ----------------------------------------------------------
+ * Model-state bytes per GPU for stage 0..3 with 2-byte weights and grads and
+ * K bytes of optimizer state per parameter; -1 for any other stage. */
+double ora_model_state_bytes(double n, double n_dp, int stage, double k);
+/* Bytes each GPU sends per optimizer step under ring collectives. */
+double ora_comm_bytes(double n, double n_dp, int stage, double param_bytes,
+                      double grad_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
