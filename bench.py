@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark: one data-parallel rank's sharded optimizer step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+reduce the n_dp ranks' 16-bit gradient rows for the owned shard, AdamW on
+the fp32 master/m/v shard, cast into the shard's slot of the full 16-bit
+weight buffer.  Default workload: the Llama-shaped 7B parameter list
+(6,738,415,616 parameters) flattened over n_dp = 8 ranks, rank 1's shard of
+842,301,952 parameters, bf16 gradients ~N(0, 1e-3) with 1% outliers x100,
+fp32 master ~N(0, 0.02), AdamW lr 1e-4, betas (0.9, 0.999), eps 1e-8,
+weight decay 0.1.  Inputs are drawn on the device and resident in HBM
+before the timed region.
+
+Prints one JSON line:
+  value = params/s of the owned shard, with the algorithmic HBM GB/s and its
+  fraction of 8 TB/s (bytes per parameter: 2 n_dp + 26 for the fused step),
+  roofline = the dominant kernel's achieved GB/s from HIP events on the
+  stream it runs on, traffic = counter-measured HBM bytes per launch when a
+  counter summary for the current kernel source is committed under profiles/,
+  cpu_baseline = the CPU oracle timed on a bounded sample on this host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "zero_sharded_mixed_flatten_amd", "csrc", "zero_shard.hip")
+COUNTERS_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=2,
+                   help="workload: 1 GPT-2-XL n_dp=1, 2 7B n_dp=8 (default), "
+                        "3 7B n_dp=64, 4 7B n_dp=8 fp16 with 4 micro-batches")
+    p.add_argument("--cpu-sample-log2", type=int, default=25,
+                   help="CPU baseline sample: 2^k parameters of the shard")
+    p.add_argument("--cpu-steps", type=int, default=8)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def source_digest():
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+
+
+def committed_traffic(workload_name, launches_per_step):
+    """Counter-measured HBM bytes per launch of the dominant kernel, from the
+    committed counter summary -- only if it was taken on this kernel source."""
+    path = os.path.join(COUNTERS_DIR, f"{workload_name}.counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the sharded step is emulated with all n_dp "
+              "ranks' gradient rows in one GPU's HBM, and no multi-GPU path is built. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import zero_sharded_mixed_flatten_amd as zs
+    from synth import F32
+    from synth.synth_const import BUF_GRAD, BUF_MASTER
+    from synth.workloads import workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    wl = workload(args.config)
+    lay, _ = zs.zero_flatten_layout(wl.numels, wl.n_dp)
+    S, n_dp, rank = lay.shard, wl.n_dp, wl.rank
+    draw = wl.grad
+    gdt = zs.ZERO_BF16 if draw.kind == synth.BF16 else zs.ZERO_FP16
+    tdt = torch.bfloat16 if gdt == zs.ZERO_BF16 else torch.float16
+    micro = wl.micro_batches
+    hp_kw = dict(wl.hp)
+
+    # ---- inputs, resident in HBM -------------------------------------------
+    slab = torch.empty((n_dp, S), dtype=tdt, device=dev)
+    for k in range(n_dp):
+        synth.fill_device(slab[k], draw.kind, wl.seed,
+                          synth.tag(BUF_GRAD, wl.cid, 1, 0, k), rank * S,
+                          draw.eff_sigma, draw.thr, draw.outlier_mul)
+    master = torch.empty(S, dtype=torch.float32, device=dev)
+    synth.fill_device(master, F32, wl.seed, synth.tag(BUF_MASTER, wl.cid), rank * S,
+                      wl.master_sigma)
+    m = torch.zeros(S, dtype=torch.float32, device=dev)
+    v = torch.zeros(S, dtype=torch.float32, device=dev)
+    wfull = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device=dev)
+    acc = torch.empty(S, dtype=torch.float32, device=dev) if micro > 1 else None
+    flag = torch.zeros(1, dtype=torch.int32, device=dev) if micro > 1 else None
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    # ---- one step of the hot path ------------------------------------------
+    events = []
+
+    def step(t, timed):
+        if micro == 1:
+            hp = zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **hp_kw)
+            e0 = torch.cuda.Event(enable_timing=True) if timed else None
+            e1 = torch.cuda.Event(enable_timing=True) if timed else None
+            if timed:
+                e0.record(stream)
+            zs.zero_shard_step(slab, S, S, master, m, v, wfull, lay, rank, hp, stream=stream)
+            if timed:
+                e1.record(stream)
+                events.append((e0, e1))
+        else:
+            # stage-2 accumulation: one reduce per micro-batch (the same
+            # resident slab stands in for each micro-batch's rows), then
+            # AdamW gated on the overflow flag
+            flag.zero_()
+            for mb in range(micro):
+                zs.zero_shard_reduce(slab, n_dp, S, S, acc, accumulate=mb > 0, overflow=flag,
+                                     stream=stream)
+            hp = zs.AdamWHParams(step=t, grad_scale=1.0 / (n_dp * wl.loss_scale * micro),
+                                 **hp_kw)
+            e0 = torch.cuda.Event(enable_timing=True) if timed else None
+            e1 = torch.cuda.Event(enable_timing=True) if timed else None
+            if timed:
+                e0.record(stream)
+            zs.zero_shard_adamw(acc, master, m, v, wfull, lay, rank, hp, skip=flag,
+                                stream=stream)
+            if timed:
+                e1.record(stream)
+                events.append((e0, e1))
+
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        step(t, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        t += 1
+        step(t, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_per_step = wall * 1e3 / args.steps
+    if micro == 1:
+        bytes_per_param = 2 * n_dp + 26
+        kernel = "step_vec_kernel (fused reduce + AdamW + cast)"
+    else:
+        # 4 B written by the first reduce, 2 n_dp + 8 by each later one,
+        # 30 by the gated AdamW (acc 4 + state 12 read, state 12 + weight 2 written)
+        bytes_per_param = (2 * n_dp + 4) + (micro - 1) * (2 * n_dp + 8) + 30
+        kernel = "adamw_vec_kernel (gated AdamW + cast; timed launch)"
+    step_bytes = bytes_per_param * S
+    kms = [a.elapsed_time(b) for a, b in events]
+    k_avg = statistics.fmean(kms)
+    if micro == 1:
+        launch_bytes = step_bytes
+    else:
+        launch_bytes = 30 * S
+    achieved = launch_bytes / (k_avg * 1e-3) / 1e9
+    traffic = committed_traffic(wl.name, 1 if micro == 1 else micro + 1)
+
+    line = {
+        "metric": "sharded AdamW step params/s and HBM GB/s (% of 8 TB/s), 7B n_dp=8 shard",
+        "value": S * args.steps / wall,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "hbm_gbps": step_bytes / wall * args.steps / 1e9,
+        "hbm_frac": step_bytes / wall * args.steps / 1e9 / HBM_PEAK_GBPS,
+        "config": {"workload": wl.name, "n_params": lay.n, "n_dp": n_dp, "rank": rank,
+                   "shard": S, "grad_dtype": "bf16" if gdt == zs.ZERO_BF16 else "fp16",
+                   "state_dtype": "fp32", "weight_dtype": "bf16",
+                   "micro_batches": micro, "bytes_per_param": bytes_per_param,
+                   "launches_per_step": 1 if micro == 1 else micro + 1},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "launch_ms_avg": k_avg, "launch_ms_min": min(kms),
+                     "launch_ms_median": statistics.median(kms),
+                     "algorithmic_bytes_per_launch": launch_bytes},
+        "cpu_baseline": None,
+    }
+
+    # ---- the oracle on the host: a reported baseline, never the target ------
+    if not args.no_cpu_baseline:
+        del slab, master, m, v, wfull, acc
+        torch.cuda.empty_cache()
+        line["cpu_baseline"] = cpu_baseline(wl, S, rank, args.cpu_sample_log2, args.cpu_steps)
+
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, S, rank, log2n, steps):
+    import numpy as np
+
+    import oracle
+    import synth
+    from synth import F32
+    from synth.synth_const import BUF_GRAD, BUF_MASTER
+
+    n = min(1 << log2n, S)
+    draw = wl.grad
+    rows = np.stack([synth.fill_host(draw.kind, wl.seed, synth.tag(BUF_GRAD, wl.cid, 1, 0, k),
+                                     rank * S, n, draw.eff_sigma, draw.thr, draw.outlier_mul)
+                     for k in range(wl.n_dp)])
+    w = synth.fill_host(F32, wl.seed, synth.tag(BUF_MASTER, wl.cid), rank * S, n, wl.master_sigma)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    wout = np.zeros(n, np.uint16)
+    acc = np.zeros(n, np.float32)
+    gdt = oracle.BF16 if draw.kind == synth.BF16 else oracle.FP16
+    t0 = time.perf_counter()
+    for t in range(1, steps + 1):
+        if wl.micro_batches == 1:
+            oracle.step(rows, gdt, wl.n_dp, n, n, w, m, v, wout, oracle.BF16, t,
+                        grad_scale=1.0 / wl.n_dp, **wl.hp)
+        else:
+            flag = np.zeros(1, np.uint32)
+            for mb in range(wl.micro_batches):
+                oracle.reduce(rows, gdt, wl.n_dp, n, n, acc, mb > 0, overflow=flag)
+            oracle.adamw(acc, w, m, v, wout, oracle.BF16, n, t,
+                         grad_scale=1.0 / (wl.n_dp * wl.loss_scale * wl.micro_batches),
+                         skip=flag, **wl.hp)
+    dt = time.perf_counter() - t0
+    return {"value": n * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} parameters of rank {rank}'s shard, {wl.n_dp} gradient rows, "
+                      f"{steps} optimizer steps, single-threaded C oracle ({dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,245 @@
+/*
+ * zero_shard.h -- C ABI of the MI355X (gfx950) library for one data-parallel
+ * rank's sharded mixed-precision optimizer step.
+ *
+ * The path, as the pages describe it:
+ *  1. Flatten every parameter into one vector of N numbers and cut it into
+ *     n_dp equal contiguous shards; rank r owns shard r ("ZeRO and FSDP",
+ *     Zero to Frontier 10.3, "The idea, one stage at a time").
+ *  2. Reduce-scatter the 16-bit gradients so rank r holds the average over
+ *     ranks of shard r (same section; "ZeRO Optimizer, in depth", "What each
+ *     stage changes inside one step").  On one GPU the n_dp ranks' rows for
+ *     the owned shard sit in HBM and this library performs the collective's
+ *     arithmetic: widen to fp32, sum, scale.
+ *  3. With gradient accumulation at stage 2, reduce after every micro-batch
+ *     into an fp32 shard buffer ("ZeRO and FSDP", the catch described under
+ *     "The idea, one stage at a time").
+ *  4. Run AdamW on the fp32 master weights and the two fp32 moments of the
+ *     shard ("ZeRO and FSDP", "A sharded Adam step": Adam with bias
+ *     correction from t = 1; the configs of "DeepSpeed ZeRO", "A worked
+ *     example", name AdamW, applied with decoupled weight decay).
+ *  5. Cast the updated master to 16 bits into the shard's slot of the full
+ *     weight buffer, which is where the all-gather delivers it ("ZeRO and
+ *     FSDP", "The idea, one stage at a time").
+ * The state is the 2 + 2 + 12 bytes per parameter of "ZeRO Optimizer, in
+ * depth", "Where the 16 bytes per parameter go".
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are plain HIP device addresses the caller allocated
+ *    (e.g. torch.empty(..., device="cuda")).  The library allocates and
+ *    frees nothing, on the device or the host, and keeps no global state;
+ *    the caller owns every buffer before, during and after a call.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *    and runs asynchronously: a call returns once its kernels are launched.
+ *    Buffers must stay valid until the stream has passed them.
+ *  - Arguments are validated on the host before anything is launched; on any
+ *    error status nothing is launched and nothing is written.
+ *  - Element counts and offsets are in elements, never bytes.
+ *  - Element j of the processed range is independent of every other element:
+ *    any range can be processed by one call or split over several calls
+ *    (buckets) with identical results.
+ *  - Arithmetic is IEEE binary32 with round-to-nearest-even, no fused
+ *    multiply-add, correctly rounded division and square root, and no
+ *    flushing of denormals; the scalars are formed on the host in double
+ *    and rounded once to fp32 (see zero_adamw_hparams).
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_SHARD_ABI_VERSION 1
+
+/* every entry point is exported from the shared library */
+#if defined(__GNUC__) || defined(__clang__)
+#define ZERO_API __attribute__((visibility("default")))
+#else
+#define ZERO_API
+#endif
+
+typedef enum zero_status {
+    ZERO_OK = 0,
+    ZERO_EINVAL = 1,  /* a required pointer is NULL, or a size, count, rank,
+                         dtype, stage or hyperparameter is out of its domain */
+    ZERO_EALIAS = 2,  /* two buffers that must be disjoint overlap */
+    ZERO_ERANGE = 3,  /* the range to process does not fit in the shard or
+                         in the full weight buffer */
+    ZERO_EDEVICE = 4  /* the HIP runtime refused a kernel launch; faults
+                         inside kernels surface at the caller's next
+                         synchronisation instead */
+} zero_status;
+
+/* 16-bit storage formats for gradients and weights. */
+typedef enum zero_dtype { ZERO_BF16 = 0, ZERO_FP16 = 1 } zero_dtype;
+
+/* Flat layout: N parameters, n_dp shards of `shard` elements each,
+ * n_pad = n_dp * shard >= n; elements [n, n_pad) are zero padding.
+ * shard is the smallest multiple of `align` with n_dp * shard >= n. */
+typedef struct zero_layout {
+    int64_t n;
+    int64_t n_pad;
+    int64_t shard;
+    int64_t align;
+    int32_t n_dp;
+    int32_t reserved; /* zero */
+} zero_layout;
+
+/* AdamW hyperparameters.  Doubles on purpose: each fp32 constant of the
+ * update is formed in double and rounded once, so that (1 - beta1) is the
+ * float nearest 0.1 and not 1 - (float)0.9.  The constants are
+ *   s = fl(grad_scale), b1 = fl(beta1), c1 = fl(1 - beta1),
+ *   b2 = fl(beta2), c2 = fl(1 - beta2),
+ *   bc1 = fl(1 - pow(beta1, step)), bc2 = fl(1 - pow(beta2, step)),
+ *   lr = fl(lr), eps = fl(eps), d = fl(1 - lr * weight_decay)
+ * with pow from the C library and fl() the round-to-nearest conversion to
+ * float.  Per element j, with a_j the fp32 sum of the contributions:
+ *   g = a_j * s
+ *   m = b1 * m + c1 * g
+ *   v = b2 * v + c2 * (g * g)
+ *   w = w * d - lr * ((m / bc1) / (sqrt(v / bc2) + eps))
+ *   out = 16-bit round-to-nearest-even of w
+ * (each operation rounded to fp32 in this order). */
+typedef struct zero_adamw_hparams {
+    double lr;
+    double beta1;        /* in [0, 1) */
+    double beta2;        /* in [0, 1) */
+    double eps;          /* finite, > 0 */
+    double weight_decay; /* finite, >= 0 */
+    double grad_scale;   /* finite, > 0: 1 / (n_dp * loss_scale * micro_batches)
+                            averages over ranks and micro-batches and undoes a
+                            static fp16 loss scale */
+    int64_t step;        /* t >= 1, counted from 1 */
+} zero_adamw_hparams;
+
+/* One contiguous piece of a shard: elements [shard_off, shard_off + len) of
+ * the shard are elements [tensor_off, tensor_off + len) of parameter
+ * `tensor`, or of the zero padding when tensor == -1. */
+typedef struct zero_segment {
+    int64_t tensor;
+    int64_t tensor_off;
+    int64_t shard_off;
+    int64_t len;
+} zero_segment;
+
+/* ZERO_SHARD_ABI_VERSION of the loaded library. */
+ZERO_API int32_t zero_abi_version(void);
+
+/* A static, human-readable name for a status code (never NULL). */
+ZERO_API const char *zero_status_string(zero_status status);
+
+/* ---- layout (host only) ------------------------------------------------
+ * Flatten n_tensors parameters of numels[i] elements, in that order, into
+ * one vector and cut it into n_dp equal contiguous shards ("ZeRO and FSDP",
+ * "The idea, one stage at a time").  offsets (nullable, n_tensors entries)
+ * receives each parameter's first flat index.  align >= 1 rounds the shard
+ * up to a multiple of align (8 makes every shard slot 16-byte aligned for
+ * 16-bit data); align = 1 gives the plain ceil(N / n_dp).
+ * EINVAL: out NULL, numels NULL with n_tensors > 0, n_tensors < 0, a numel
+ * < 0, n_dp < 1, align < 1, or N_pad overflowing int64. */
+ZERO_API zero_status zero_flatten_layout(const int64_t *numels, int64_t n_tensors,
+                                int32_t n_dp, int64_t align,
+                                int64_t *offsets, zero_layout *out);
+
+/* The pieces of shard `rank` in shard order: the parameters it overlaps,
+ * then the padding.  Writes min(count, cap) entries to out (nullable when
+ * cap == 0) and the total number to *count.  The layout must be the one
+ * zero_flatten_layout returns for the same numels.
+ * EINVAL: NULL layout/count, numels NULL with n_tensors > 0, cap < 0,
+ * rank outside [0, n_dp), or numels inconsistent with the layout. */
+ZERO_API zero_status zero_shard_segments(const zero_layout *layout,
+                                const int64_t *numels, int64_t n_tensors,
+                                int32_t rank, zero_segment *out, int64_t cap,
+                                int64_t *count);
+
+/* ---- the reduce (device) ------------------------------------------------
+ * The reduce-scatter's arithmetic for one shard range, with optional
+ * micro-batch accumulation (stage 2 reduces after every micro-batch).
+ *   grads: device, dtype gdt, n_contrib rows; row k starts at element
+ *          k * ld and holds that rank's gradient for elements [0, len) of
+ *          the range.  ld = len is a packed [n_contrib][len] slab; ld =
+ *          N_pad with grads already offset to the shard start reads each
+ *          rank's full flat gradient in place.  Read only.
+ *   acc:   device fp32[len].  accumulate == 0: acc[j] = a_j; otherwise
+ *          acc[j] = acc[j] + a_j, where a_j = G_0[j] + ... + G_{n-1}[j]
+ *          summed left to right in fp32.  No scale is applied here.
+ *   overflow: device uint32 or NULL; set to 1 (never cleared) when some
+ *          acc[j] after the update is +-Inf or NaN.
+ *   sumsq: device double or NULL; the sum over j of acc[j]^2 is ADDED to
+ *          it (order unspecified).  The caller zeroes both before a pass.
+ * EINVAL: n_contrib < 1, len < 0, ld < len, bad gdt, or a NULL grads/acc
+ * with len > 0.  EALIAS: acc, overflow, sumsq overlap each other or a row.
+ * len == 0 is a no-op. */
+ZERO_API zero_status zero_shard_reduce(const void *grads, zero_dtype gdt,
+                              int32_t n_contrib, int64_t ld, int64_t len,
+                              float *acc, int32_t accumulate,
+                              uint32_t *overflow, double *sumsq, void *stream);
+
+/* ---- AdamW from an fp32 gradient buffer (device) -------------------------
+ * For j in [0, len): g = acc[j] * s, the AdamW update of master[j], m[j],
+ * v[j] in place (see zero_adamw_hparams), and the 16-bit cast of the new
+ * master written to weight_full[rank * shard + shard_off + j].
+ *   acc, master, m, v: device fp32[len], pointing at shard element
+ *          shard_off.  Nothing else of weight_full is touched.
+ *   skip:  device uint32 or NULL; when *skip != 0 at run time the kernel
+ *          writes nothing (a step skipped after an overflow).
+ * EINVAL: bad layout, rank, dtype, hyperparameters, shard_off < 0, len < 0,
+ * or a NULL required pointer with len > 0.  ERANGE: shard_off + len >
+ * shard.  EALIAS: any two of acc, master, m, v, the weight slot, skip
+ * overlap. */
+ZERO_API zero_status zero_shard_adamw(const float *acc, float *master, float *m,
+                             float *v, void *weight_full, zero_dtype wdt,
+                             const zero_layout *layout, int32_t rank,
+                             int64_t shard_off, int64_t len,
+                             const zero_adamw_hparams *hp,
+                             const uint32_t *skip, void *stream);
+
+/* ---- fused step (device) ---------------------------------------------------
+ * One pass over the range: reduce layout->n_dp rows in fp32 (as
+ * zero_shard_reduce with accumulate = 0), scale by s, AdamW, cast into the
+ * slot -- bit-identical to zero_shard_reduce followed by zero_shard_adamw,
+ * but each element's bytes cross HBM once: 2 * n_dp bytes of gradients and
+ * 12 of state read, 12 of state and 2 of weight written.
+ *   grads: device, dtype gdt, layout->n_dp rows of stride ld (elements), as
+ *          for zero_shard_reduce.
+ *   master, m, v: device fp32[len] at shard element shard_off.
+ *   weight_full: device 16-bit buffer of layout->n_pad elements; elements
+ *          [rank * shard + shard_off, ... + len) are written, nothing else.
+ *   overflow: device uint32 or NULL; set to 1 when some a_j is non-finite.
+ *          The update is applied regardless (a single pass cannot wait for
+ *          the whole shard's verdict); use reduce + adamw with skip to gate.
+ *   sumsq: device double or NULL; the sum over j of g^2 is ADDED to it.
+ * Errors as for zero_shard_reduce and zero_shard_adamw. */
+ZERO_API zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_t ld,
+                            int64_t len, float *master, float *m, float *v,
+                            void *weight_full, zero_dtype wdt,
+                            const zero_layout *layout, int32_t rank,
+                            int64_t shard_off, const zero_adamw_hparams *hp,
+                            uint32_t *overflow, double *sumsq, void *stream);
+
+/* ---- accounting (host only) ----------------------------------------------
+ * Model-state bytes per GPU at ZeRO stage 0..3 for n parameters on n_dp
+ * ranks with 2-byte weights and gradients and k bytes of optimizer state
+ * per parameter ("ZeRO and FSDP", "Memory per GPU": 16N, 4N + 12N/n_dp,
+ * 2N + 14N/n_dp, 16N/n_dp for k = 12).  EINVAL: out NULL, stage outside
+ * 0..3, n < 0, n_dp < 1, k < 0. */
+ZERO_API zero_status zero_model_state_bytes(double n, double n_dp, int32_t stage,
+                                   double k, double *out);
+
+/* Bytes each GPU sends per optimizer step with ring collectives ("ZeRO and
+ * FSDP", "Communication volume"): a reduce-scatter or all-gather of N
+ * elements sends (n_dp - 1) / n_dp * N per GPU, an all-reduce twice that.
+ * Stage 0 all-reduces gradients; stages 1 and 2 reduce-scatter gradients
+ * and all-gather weights; stage 3 all-gathers weights twice and
+ * reduce-scatters gradients.  EINVAL as above, or element sizes <= 0. */
+ZERO_API zero_status zero_comm_bytes(double n, double n_dp, int32_t stage,
+                            double param_bytes, double grad_bytes,
+                            double *out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZERO_SHARD_H */

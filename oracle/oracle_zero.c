@@ -251,14 +251,18 @@ static void adamw_element(float g, float *w, float *m, float *v,
 /* The reduce.  "ZeRO and FSDP", "The idea, one stage at a time": the reduce-
  * scatter hands rank r the averaged gradient of shard r.  Here the n ranks'
  * 16-bit rows for that shard are widened and summed left to right (the
- * average's scale is applied with the update). */
+ * average's scale is applied with the update).
+ * Overflow flag: "DeepSpeed ZeRO", "Mixed precision" says fp16 training
+ * needs loss scaling; what scaling guards against is a gradient that is no
+ * longer finite.  The flag is raised when a reduced (and, for the reduce,
+ * accumulated) fp32 gradient element is +-Inf or NaN, which covers every
+ * non-finite input row and a sum that overflows. */
 
 static float row_sum(const uint16_t *grads, int gdt, int32_t n, int64_t ld,
-                     int64_t j, int *bad) {
+                     int64_t j) {
     float a = 0.0f;
     for (int32_t k = 0; k < n; ++k) {
         float x = widen(grads[(int64_t)k * ld + j], gdt);
-        if (nonfinite(x)) *bad = 1;
         a = (k == 0) ? x : a + x;
     }
     return a;
@@ -270,8 +274,9 @@ void ora_reduce(const uint16_t *grads, int gdt, int32_t n_contrib, int64_t ld,
     int bad = 0;
     double ss = 0.0;
     for (int64_t j = 0; j < len; ++j) {
-        float a = row_sum(grads, gdt, n_contrib, ld, j, &bad);
+        float a = row_sum(grads, gdt, n_contrib, ld, j);
         float r = accumulate ? acc[j] + a : a;
+        if (nonfinite(r)) bad = 1;
         acc[j] = r;
         ss += (double)r * (double)r;
     }
@@ -301,7 +306,8 @@ void ora_step(const uint16_t *grads, int gdt, int32_t n_dp, int64_t ld,
     int bad = 0;
     double ss = 0.0;
     for (int64_t j = 0; j < len; ++j) {
-        float a = row_sum(grads, gdt, n_dp, ld, j, &bad);
+        float a = row_sum(grads, gdt, n_dp, ld, j);
+        if (nonfinite(a)) bad = 1;
         float g = a * c[0];
         ss += (double)g * (double)g;
         adamw_element(g, &w[j], &m[j], &v[j], c);

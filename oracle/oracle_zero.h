@@ -76,7 +76,8 @@ void ora_adamw_scalars(const double hp6[6], int64_t step, float out10[10]);
 /* ---- the reduce (the reduce-scatter's arithmetic for one shard) -----------
  * a_j = G_0[j] + G_1[j] + ... + G_{n-1}[j], widened to fp32, left to right.
  * accumulate == 0: acc[j] = a_j; else acc[j] = acc[j] + a_j.
- * overflow (nullable): set to 1 if any widened input is +-Inf or NaN.
+ * overflow (nullable): set to 1 if any acc[j] after the update is +-Inf or
+ * NaN (so any non-finite input, or a sum that overflowed).
  * sumsq (nullable): += sum over j of acc[j]^2 (after the update), in double. */
 void ora_reduce(const uint16_t *grads, int gdt, int32_t n_contrib, int64_t ld,
                 int64_t len, float *acc, int accumulate, uint32_t *overflow,
@@ -92,8 +93,9 @@ void ora_adamw(const float *acc, float *w, float *m, float *v, uint16_t *wout,
 
 /* ---- fused: reduce n_dp rows, then AdamW, then cast -----------------------
  * Equal, element by element, to ora_reduce(accumulate = 0) into a temporary
- * followed by ora_adamw.  overflow reports non-finite inputs (the update is
- * still applied); sumsq (nullable) += sum of g_j^2 with g_j = a_j * s. */
+ * followed by ora_adamw.  overflow is set when a reduced a_j is non-finite
+ * (the update is still applied); sumsq (nullable) += sum of g_j^2 with
+ * g_j = a_j * s. */
 void ora_step(const uint16_t *grads, int gdt, int32_t n_dp, int64_t ld,
               int64_t len, float *w, float *m, float *v, uint16_t *wout,
               int wdt, const double hp6[6], int64_t step, uint32_t *overflow,

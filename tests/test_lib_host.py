@@ -1,0 +1,202 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the
+header declares, and its host-only parts (layout, segments, accounting,
+argument validation) agree with the oracle.  No kernel is launched here."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import zero_sharded_mixed_flatten_amd as zs
+from synth.workloads import gpt2xl_numels, llama7b_numels
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zero_shard.h")
+GOLD = os.path.join(ROOT, "tests", "golden")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return re.findall(r"^ZERO_API\s+[\w\s\*]*?\b(zero_\w+)\s*\(", src, flags=re.M)
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 9, names
+    lib = ctypes.CDLL(zs.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.zero_abi_version() == zs.ABI_VERSION
+
+
+def test_status_strings():
+    lib = ctypes.CDLL(zs.library_path())
+    lib.zero_status_string.restype = ctypes.c_char_p
+    for code in range(5):
+        assert lib.zero_status_string(code).startswith(b"ZERO_")
+    assert lib.zero_status_string(99) == b"unknown zero_status"
+
+
+def test_tiny_layout_golden():
+    g = json.load(open(os.path.join(GOLD, "tiny_layout.json")))
+    lay, offs = zs.zero_flatten_layout(g["numels"], g["n_dp"], g["align"])
+    assert (lay.n, lay.n_pad, lay.shard, lay.n_dp) == (g["n"], g["n_pad"], g["shard"], g["n_dp"])
+    assert zs.zero_shard_segments(lay, g["numels"], g["rank"]) == \
+        [(0, g["slot_begin"], 0, g["slot_end"] - g["slot_begin"])]
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_layout_and_segments_match_oracle(seed):
+    rng = np.random.default_rng(seed)
+    numels = [int(x) for x in rng.integers(0, 300, size=int(rng.integers(0, 12)))]
+    n_dp = int(rng.integers(1, 70))
+    align = int(rng.choice([1, 2, 8, 64]))
+    lay, offs = zs.zero_flatten_layout(numels, n_dp, align)
+    o_offs, n, n_pad, s = oracle.flatten_layout(numels, n_dp, align)
+    assert (lay.n, lay.n_pad, lay.shard) == (n, n_pad, s)
+    assert np.array_equal(offs, o_offs)
+    for r in sorted({0, n_dp - 1, int(rng.integers(0, n_dp))}):
+        assert zs.zero_shard_segments(lay, numels, r) == oracle.shard_segments(numels, n_dp, r, align)
+
+
+@pytest.mark.parametrize("numels,n_dp", [(llama7b_numels(), 8), (llama7b_numels(), 64),
+                                         (gpt2xl_numels(), 1)])
+def test_model_layouts_match_oracle(numels, n_dp):
+    lay, offs = zs.zero_flatten_layout(numels, n_dp)
+    o = oracle.flatten_layout(numels, n_dp)
+    assert (lay.n, lay.n_pad, lay.shard) == o[1:] and np.array_equal(offs, o[0])
+    for r in sorted({0, min(1, n_dp - 1), n_dp - 1}):
+        assert zs.zero_shard_segments(lay, numels, r) == oracle.shard_segments(numels, n_dp, r)
+
+
+@pytest.mark.parametrize("args", [([4], 0, 1), ([4], 2, 0), ([-1], 2, 1),
+                                  ([2 ** 62, 2 ** 62], 1, 1), ([2 ** 62 + 1], 2, 2 ** 61)])
+def test_layout_rejects_invalid(args):
+    with pytest.raises(zs.ZeroError) as e:
+        zs.zero_flatten_layout(*args)
+    assert e.value.status == zs.ZERO_EINVAL
+
+
+def test_segments_reject_inconsistent_numels():
+    lay, _ = zs.zero_flatten_layout([10, 20], 4)
+    with pytest.raises(zs.ZeroError):
+        zs.zero_shard_segments(lay, [10, 21], 0)
+    with pytest.raises(zs.ZeroError):
+        zs.zero_shard_segments(lay, [10, 20], 4)
+
+
+def test_accounting_matches_oracle_and_pages():
+    g = json.load(open(os.path.join(GOLD, "accounting.json")))
+    for e in g["state_memory"]:
+        got = zs.zero_model_state_bytes(e["n"], e["n_dp"], e["stage"], 12)
+        assert got == oracle.model_state_bytes(e["n"], e["n_dp"], e["stage"], 12)
+        assert abs(got / 1e9 - e["gb"]) <= e["abs_tol_gb"]
+    for e in g["comm"]:
+        got = zs.zero_comm_bytes(e["n"], e["n_dp"], e["stage"], e["param_bytes"], e["grad_bytes"])
+        assert abs(got / 1e9 - e["gb"]) <= e["abs_tol_gb"]
+    for stage in range(4):
+        for n_dp in (1, 3, 8, 64):
+            assert zs.zero_comm_bytes(1e9, n_dp, stage) == pytest.approx(
+                oracle.comm_bytes(1e9, n_dp, stage), rel=1e-15)
+    with pytest.raises(zs.ZeroError):
+        zs.zero_model_state_bytes(1e9, 8, 4)
+
+
+# ---------------------------------------------------------------------------
+# argument validation of the device entry points: every case here must be
+# rejected on the host before any launch, so it is exercised with made-up
+# addresses -- and therefore only where no GPU is visible.
+
+def _no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+cpu_only = pytest.mark.skipif(not _no_gpu(), reason="uses made-up device addresses")
+
+L = zs._lib
+P = ctypes.c_void_p
+BASE = 1 << 40
+
+
+def _hp(**kw):
+    h = zs.AdamWHParams(**kw)
+    return h._c()
+
+
+def _step(grads=BASE, ld=1024, length=1024, master=BASE + (1 << 30), m=BASE + (2 << 30),
+          v=BASE + (3 << 30), wfull=BASE + (4 << 30), lay=None, rank=1, shard_off=0,
+          hp=None, ovf=None, ssq=None, gdt=0, wdt=0):
+    if lay is None:
+        lay = zs.zero_flatten_layout([4096], 4)[0]
+    hp = hp or _hp()
+    return L.zero_shard_step(P(grads), gdt, ld, length, P(master), P(m), P(v), P(wfull), wdt,
+                             ctypes.byref(lay), rank, shard_off, ctypes.byref(hp),
+                             P(ovf) if ovf else None, P(ssq) if ssq else None, None)
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(rank=4), zs.ZERO_EINVAL), (dict(rank=-1), zs.ZERO_EINVAL),
+    (dict(ld=1000), zs.ZERO_EINVAL), (dict(length=-1), zs.ZERO_EINVAL),
+    (dict(gdt=2), zs.ZERO_EINVAL), (dict(wdt=5), zs.ZERO_EINVAL),
+    (dict(grads=0), zs.ZERO_EINVAL), (dict(master=0), zs.ZERO_EINVAL),
+    (dict(hp=_hp(step=0)), zs.ZERO_EINVAL), (dict(hp=_hp(beta1=1.0)), zs.ZERO_EINVAL),
+    (dict(hp=_hp(beta2=-0.1)), zs.ZERO_EINVAL), (dict(hp=_hp(eps=0.0)), zs.ZERO_EINVAL),
+    (dict(hp=_hp(grad_scale=float("inf"))), zs.ZERO_EINVAL),
+    (dict(hp=_hp(lr=float("nan"))), zs.ZERO_EINVAL),
+    (dict(hp=_hp(weight_decay=-1.0)), zs.ZERO_EINVAL),
+    (dict(shard_off=1, length=1024), zs.ZERO_ERANGE),
+    (dict(shard_off=-1), zs.ZERO_EINVAL),
+    (dict(length=1025, ld=1025), zs.ZERO_ERANGE),
+    (dict(m=BASE + (1 << 30) + 4092), zs.ZERO_EALIAS),       # m overlaps master's tail
+    (dict(v=BASE + 2046), zs.ZERO_EALIAS),                    # v inside row 0
+    (dict(master=BASE + 3 * 1024 * 2), zs.ZERO_EALIAS),       # master on the last row
+    (dict(wfull=BASE + (3 << 30) - 2 * 1024), zs.ZERO_EALIAS),  # slot over v
+    (dict(ovf=BASE + 100), zs.ZERO_EALIAS),
+    (dict(ssq=BASE + (2 << 30) + 8), zs.ZERO_EALIAS),
+])
+def test_step_rejects_bad_arguments(kw, status):
+    assert _step(**kw) == status
+
+
+@cpu_only
+def test_step_bad_layout_and_empty_range():
+    lay = zs.zero_flatten_layout([4096], 4)[0]
+    bad = zs.ZeroLayout(lay.n, lay.n_pad + 1, lay.shard, lay.align, lay.n_dp, 0)
+    assert _step(lay=bad) == zs.ZERO_EINVAL
+    # an empty range is a no-op that needs no buffers at all
+    assert _step(length=0, grads=0, master=0, m=0, v=0, wfull=0) == zs.ZERO_OK
+
+
+@cpu_only
+def test_reduce_and_adamw_reject_bad_arguments():
+    R = L.zero_shard_reduce
+    assert R(P(BASE), 0, 0, 16, 16, P(BASE + 4096), 0, None, None, None) == zs.ZERO_EINVAL
+    assert R(P(BASE), 0, 2, 8, 16, P(BASE + 4096), 0, None, None, None) == zs.ZERO_EINVAL
+    assert R(P(BASE), 3, 2, 16, 16, P(BASE + 4096), 0, None, None, None) == zs.ZERO_EINVAL
+    assert R(P(BASE), 0, 2, 16, 16, P(BASE + 40), 0, None, None, None) == zs.ZERO_EALIAS
+    assert R(P(BASE), 0, 2, 16, 16, P(BASE + 4096), 0, P(BASE + 4096 + 60), None,
+             None) == zs.ZERO_EALIAS
+    assert R(None, 0, 2, 16, 0, None, 0, None, None, None) == zs.ZERO_OK
+    A = L.zero_shard_adamw
+    lay = zs.zero_flatten_layout([4096], 4)[0]
+    hp = _hp()
+    args = [P(BASE), P(BASE + (1 << 30)), P(BASE + (2 << 30)), P(BASE + (3 << 30)),
+            P(BASE + (4 << 30)), 0, ctypes.byref(lay), 1, 0, 1024, ctypes.byref(hp),
+            None, None]
+    bad = list(args)
+    bad[8], bad[9] = 512, 1024
+    assert A(*bad) == zs.ZERO_ERANGE
+    bad = list(args)
+    bad[11] = P(BASE + (1 << 30) + 16)  # skip flag inside master
+    assert A(*bad) == zs.ZERO_EALIAS
+    bad = list(args)
+    bad[1] = P(BASE + 4000)  # master over acc
+    assert A(*bad) == zs.ZERO_EALIAS

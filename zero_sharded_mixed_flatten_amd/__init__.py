@@ -1,0 +1,239 @@
+"""zero_sharded_mixed_flatten_amd -- one data-parallel rank's sharded,
+mixed-precision optimizer step on MI355X (gfx950).
+
+A thin ctypes binding over libzero_shard.so (include/zero_shard.h).  Every
+function here has the name of the C entry point it calls and only marshals
+arguments: torch tensors become device pointers and dtype codes, the current
+torch stream becomes the HIP stream.  All work runs in the library's HIP
+kernels; there is no fallback of any kind -- importing this package without
+the built library raises ImportError.
+
+    layout, offsets = zero_flatten_layout(numels, n_dp)
+    hp = AdamWHParams(lr=1e-4, step=1, grad_scale=1 / n_dp)
+    zero_shard_step(grads, ld, S, master, m, v, weight_full, layout, rank, hp)
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libzero_shard.so")
+
+ZERO_OK, ZERO_EINVAL, ZERO_EALIAS, ZERO_ERANGE, ZERO_EDEVICE = range(5)
+ZERO_BF16, ZERO_FP16 = 0, 1
+ABI_VERSION = 1
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_lib.zero_status_string(status).decode()}")
+
+
+class ZeroLayout(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("n_pad", ctypes.c_int64), ("shard", ctypes.c_int64),
+                ("align", ctypes.c_int64), ("n_dp", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"ZeroLayout(n={self.n}, n_pad={self.n_pad}, shard={self.shard}, "
+                f"align={self.align}, n_dp={self.n_dp})")
+
+
+class _HParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double), ("grad_scale", ctypes.c_double),
+                ("step", ctypes.c_int64)]
+
+
+class _Segment(ctypes.Structure):
+    _fields_ = [("tensor", ctypes.c_int64), ("tensor_off", ctypes.c_int64),
+                ("shard_off", ctypes.c_int64), ("len", ctypes.c_int64)]
+
+
+@dataclass
+class AdamWHParams:
+    """AdamW hyperparameters as the C struct takes them (doubles)."""
+    lr: float = 1e-4
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.1
+    grad_scale: float = 1.0
+    step: int = 1
+
+    def _c(self) -> _HParams:
+        return _HParams(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay,
+                        self.grad_scale, int(self.step))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950) first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+    lay_p = ctypes.POINTER(ZeroLayout)
+    hp_p = ctypes.POINTER(_HParams)
+    L.zero_abi_version.argtypes = []
+    L.zero_abi_version.restype = i32
+    L.zero_status_string.argtypes = [ctypes.c_int]
+    L.zero_status_string.restype = ctypes.c_char_p
+    L.zero_flatten_layout.argtypes = [vp, i64, i32, i64, vp, lay_p]
+    L.zero_flatten_layout.restype = ctypes.c_int
+    L.zero_shard_segments.argtypes = [lay_p, vp, i64, i32, vp, i64, ctypes.POINTER(i64)]
+    L.zero_shard_segments.restype = ctypes.c_int
+    L.zero_shard_reduce.argtypes = [vp, ctypes.c_int, i32, i64, i64, vp, i32, vp, vp, vp]
+    L.zero_shard_reduce.restype = ctypes.c_int
+    L.zero_shard_adamw.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, lay_p, i32, i64, i64,
+                                   hp_p, vp, vp]
+    L.zero_shard_adamw.restype = ctypes.c_int
+    L.zero_shard_step.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, ctypes.c_int,
+                                  lay_p, i32, i64, hp_p, vp, vp, vp]
+    L.zero_shard_step.restype = ctypes.c_int
+    L.zero_model_state_bytes.argtypes = [dbl, dbl, i32, dbl, ctypes.POINTER(dbl)]
+    L.zero_model_state_bytes.restype = ctypes.c_int
+    L.zero_comm_bytes.argtypes = [dbl, dbl, i32, dbl, dbl, ctypes.POINTER(dbl)]
+    L.zero_comm_bytes.restype = ctypes.c_int
+    if L.zero_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH}: ABI version {L.zero_abi_version()} != {ABI_VERSION}")
+    return L
+
+
+_lib = _load()
+
+
+def _check(status: int, what: str):
+    if status != ZERO_OK:
+        raise ZeroError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# argument marshalling
+
+
+def _dtype_code(t, what: str) -> int:
+    import torch
+    if t.dtype in (torch.bfloat16,):
+        return ZERO_BF16
+    if t.dtype in (torch.float16,):
+        return ZERO_FP16
+    raise TypeError(f"{what}: 16-bit tensor (bfloat16 or float16) expected, got {t.dtype}")
+
+
+def _dev_ptr(t, what: str, dtype=None):
+    """Device address of a CUDA tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not getattr(t, "is_cuda", False):
+        raise TypeError(f"{what}: a GPU tensor is required")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what}: {dtype} expected, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, like):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(like.device)
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+# ---------------------------------------------------------------------------
+# entry points
+
+
+def zero_flatten_layout(numels: Sequence[int], n_dp: int, align: int = 1
+                        ) -> Tuple[ZeroLayout, np.ndarray]:
+    """Flat layout of the parameter list and each parameter's flat offset."""
+    nums = np.ascontiguousarray(numels, dtype=np.int64)
+    offs = np.zeros(len(nums), dtype=np.int64)
+    lay = ZeroLayout()
+    _check(_lib.zero_flatten_layout(nums.ctypes.data_as(ctypes.c_void_p), len(nums), n_dp,
+                                    align, offs.ctypes.data_as(ctypes.c_void_p),
+                                    ctypes.byref(lay)), "zero_flatten_layout")
+    return lay, offs
+
+
+def zero_shard_segments(layout: ZeroLayout, numels: Sequence[int], rank: int
+                        ) -> List[Tuple[int, int, int, int]]:
+    """(tensor, tensor_off, shard_off, len) pieces of shard `rank`; tensor -1 is padding."""
+    nums = np.ascontiguousarray(numels, dtype=np.int64)
+    cnt = ctypes.c_int64(0)
+    p = nums.ctypes.data_as(ctypes.c_void_p)
+    _check(_lib.zero_shard_segments(ctypes.byref(layout), p, len(nums), rank, None, 0,
+                                    ctypes.byref(cnt)), "zero_shard_segments")
+    segs = (_Segment * max(cnt.value, 1))()
+    _check(_lib.zero_shard_segments(ctypes.byref(layout), p, len(nums), rank, segs, cnt.value,
+                                    ctypes.byref(cnt)), "zero_shard_segments")
+    return [(s.tensor, s.tensor_off, s.shard_off, s.len) for s in segs[:cnt.value]]
+
+
+def zero_shard_reduce(grads, n_contrib: int, ld: int, length: int, acc,
+                      accumulate: bool = False, overflow=None, sumsq=None, stream=None):
+    """acc[:length] (+)= sum of n_contrib 16-bit rows of stride ld starting at grads."""
+    import torch
+    _check(_lib.zero_shard_reduce(
+        _dev_ptr(grads, "grads"), _dtype_code(grads, "grads"), n_contrib, ld, length,
+        _dev_ptr(acc, "acc", torch.float32), int(bool(accumulate)),
+        _dev_ptr(overflow, "overflow", torch.int32), _dev_ptr(sumsq, "sumsq", torch.float64),
+        _stream(stream, acc)), "zero_shard_reduce")
+
+
+def zero_shard_adamw(acc, master, m, v, weight_full, layout: ZeroLayout, rank: int,
+                     hp: AdamWHParams, shard_off: int = 0, length: Optional[int] = None,
+                     skip=None, stream=None):
+    """AdamW on master/m/v[:length] from the fp32 gradient acc, cast into the slot."""
+    import torch
+    if length is None:
+        length = master.numel()
+    hpc = hp._c()
+    _check(_lib.zero_shard_adamw(
+        _dev_ptr(acc, "acc", torch.float32), _dev_ptr(master, "master", torch.float32),
+        _dev_ptr(m, "m", torch.float32), _dev_ptr(v, "v", torch.float32),
+        _dev_ptr(weight_full, "weight_full"), _dtype_code(weight_full, "weight_full"),
+        ctypes.byref(layout), rank, shard_off, length, ctypes.byref(hpc),
+        _dev_ptr(skip, "skip", torch.int32), _stream(stream, master)), "zero_shard_adamw")
+
+
+def zero_shard_step(grads, ld: int, length: int, master, m, v, weight_full,
+                    layout: ZeroLayout, rank: int, hp: AdamWHParams, shard_off: int = 0,
+                    overflow=None, sumsq=None, stream=None):
+    """Fused reduce of layout.n_dp rows + AdamW + cast into the weight slot."""
+    import torch
+    hpc = hp._c()
+    _check(_lib.zero_shard_step(
+        _dev_ptr(grads, "grads"), _dtype_code(grads, "grads"), ld, length,
+        _dev_ptr(master, "master", torch.float32), _dev_ptr(m, "m", torch.float32),
+        _dev_ptr(v, "v", torch.float32), _dev_ptr(weight_full, "weight_full"),
+        _dtype_code(weight_full, "weight_full"), ctypes.byref(layout), rank, shard_off,
+        ctypes.byref(hpc), _dev_ptr(overflow, "overflow", torch.int32),
+        _dev_ptr(sumsq, "sumsq", torch.float64), _stream(stream, master)), "zero_shard_step")
+
+
+def zero_model_state_bytes(n: float, n_dp: float, stage: int, k: float = 12) -> float:
+    out = ctypes.c_double()
+    _check(_lib.zero_model_state_bytes(n, n_dp, stage, k, ctypes.byref(out)),
+           "zero_model_state_bytes")
+    return out.value
+
+
+def zero_comm_bytes(n: float, n_dp: float, stage: int, param_bytes: float = 2,
+                    grad_bytes: float = 2) -> float:
+    out = ctypes.c_double()
+    _check(_lib.zero_comm_bytes(n, n_dp, stage, param_bytes, grad_bytes, ctypes.byref(out)),
+           "zero_comm_bytes")
+    return out.value
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+__all__ = ["zero_flatten_layout", "zero_shard_segments", "zero_shard_reduce",
+           "zero_shard_adamw", "zero_shard_step", "zero_model_state_bytes", "zero_comm_bytes",
+           "AdamWHParams", "ZeroLayout", "ZeroError", "ZERO_BF16", "ZERO_FP16", "library_path"]

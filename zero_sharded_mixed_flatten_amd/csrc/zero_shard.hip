@@ -1,0 +1,635 @@
+// zero_shard.hip -- gfx950 kernels and device entry points of libzero_shard.
+//
+// One data-parallel rank's sharded optimizer step, as "ZeRO and FSDP" (Zero
+// to Frontier 10.3) lays it out under "The idea, one stage at a time" and "A
+// sharded Adam step": the ranks' 16-bit gradient rows for the owned shard
+// are averaged (the reduce-scatter's arithmetic), AdamW updates the fp32
+// master and moments of the shard, and the new master is cast to 16 bits
+// into the shard's slot of the full weight buffer (the all-gather's
+// destination).
+//
+// Nothing here is a contraction: the work is a stream over HBM of
+// 2 * n_dp + 26 bytes per element (fused step), so the kernels are built for
+// bandwidth.  Each thread owns 8-element chunks: every gradient row and the
+// master/m/v shard are read with 16-byte loads, all of a chunk's loads are
+// issued before any arithmetic, sums stay in registers, and results leave
+// with 16-byte non-temporal stores (nothing is re-read, so nothing should
+// stay in the caches).  LDS and wave reductions appear only in the optional
+// overflow flag and sum of squares.
+//
+// Arithmetic is IEEE binary32, round-to-nearest-even, in a fixed order: the
+// build uses -ffp-contract=off (no fused multiply-add), HIP's correctly
+// rounded fp32 division and square root, and keeps denormals.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "zero_shard.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 256;  // threads per workgroup: 4 wave64s
+constexpr int kVec = 8;      // elements per chunk: 16 bytes of 16-bit data
+constexpr int kRowBatch = 8; // gradient rows loaded together per chunk
+// Grid caps.  A plain step launches one thread per chunk up to kMaxBlocks
+// workgroups; with a flag or sum requested the grid stays small so that
+// each workgroup's single atomic does not pile up on one address.
+constexpr int64_t kMaxBlocks = 1 << 20;
+constexpr int64_t kMaxBlocksWithFlags = 2048;
+
+// fp32 constants of the update, formed on the host (see zero_adamw_hparams)
+struct Consts {
+    float s, b1, c1, b2, c2, bc1, bc2, lr, eps, d;
+};
+
+// ---------------------------------------------------------------------------
+// 16-bit <-> fp32.  Widening is exact.  Narrowing uses gfx950's packed
+// converts (v_cvt_pk_bf16_f32, v_cvt_pk_f16_f32): round to nearest even.
+
+template <int DT>
+__device__ __forceinline__ f32x2 widen2(uint32_t w) {
+    if constexpr (DT == ZERO_BF16) {
+        return f32x2{__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
+    } else {
+        return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t narrow2(float lo, float hi) {
+    const f32x2 x{lo, hi};
+    if constexpr (DT == ZERO_BF16) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+    } else {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float widen1(uint16_t h) {
+    return widen2<DT>(static_cast<uint32_t>(h))[0];
+}
+
+template <int DT>
+__device__ __forceinline__ uint16_t narrow1(float f) {
+    return static_cast<uint16_t>(narrow2<DT>(f, 0.0f) & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// memory helpers: 16-byte loads/stores marked non-temporal (streamed once)
+
+__device__ __forceinline__ u32x4 load16(const uint16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ f32x4 load16(const float *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+}
+__device__ __forceinline__ void store16(uint16_t *p, u32x4 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(p));
+}
+__device__ __forceinline__ void store16(float *p, f32x4 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
+}
+
+// ---------------------------------------------------------------------------
+// the arithmetic of one element
+
+// AdamW ("ZeRO and FSDP", "A sharded Adam step", with decoupled decay):
+// m = b1 m + c1 g; v = b2 v + c2 g^2; w = w d - lr (m / bc1) / (sqrt(v / bc2) + eps)
+__device__ __forceinline__ void adamw_element(float g, float &w, float &m, float &v,
+                                              const Consts &c) {
+    const float mt = c.b1 * m + c.c1 * g;
+    const float vt = c.b2 * v + c.c2 * (g * g);
+    const float mhat = mt / c.bc1;
+    const float vhat = vt / c.bc2;
+    const float den = sqrtf(vhat) + c.eps;
+    const float upd = mhat / den;
+    w = w * c.d - c.lr * upd;
+    m = mt;
+    v = vt;
+}
+
+// Sum of the rows for one 8-element chunk: a[e] = G_0[e] + G_1[e] + ...,
+// left to right in fp32.  Rows are fetched kRowBatch at a time, all loads of
+// a batch issued before the first add.  NDP > 0 fixes the row count at
+// compile time; NDP == 0 reads it from n.
+template <int GDT, int NDP>
+__device__ __forceinline__ void reduce_chunk(const uint16_t *__restrict__ p, int64_t ld, int n,
+                                             float a[kVec]) {
+    const int rows = NDP > 0 ? NDP : n;
+    u32x4 x[kRowBatch];
+#pragma unroll
+    for (int b = 0; b < kRowBatch; ++b)
+        if (b < rows) x[b] = load16(p + static_cast<int64_t>(b) * ld);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x2 t = widen2<GDT>(x[0][q]);
+        a[2 * q] = t[0];
+        a[2 * q + 1] = t[1];
+    }
+#pragma unroll
+    for (int b = 1; b < kRowBatch; ++b) {
+        if (b < rows) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x2 t = widen2<GDT>(x[b][q]);
+                a[2 * q] = a[2 * q] + t[0];
+                a[2 * q + 1] = a[2 * q + 1] + t[1];
+            }
+        }
+    }
+    for (int k = kRowBatch; k < rows; k += kRowBatch) {
+#pragma unroll
+        for (int b = 0; b < kRowBatch; ++b)
+            if (k + b < rows) x[b] = load16(p + static_cast<int64_t>(k + b) * ld);
+#pragma unroll
+        for (int b = 0; b < kRowBatch; ++b) {
+            if (k + b < rows) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x2 t = widen2<GDT>(x[b][q]);
+                    a[2 * q] = a[2 * q] + t[0];
+                    a[2 * q + 1] = a[2 * q + 1] + t[1];
+                }
+            }
+        }
+    }
+}
+
+// The optional shard-wide outputs: one atomic per wave for the flag, a wave
+// then workgroup reduction and one atomic per workgroup for the sum.  Every
+// thread of the workgroup must reach this point.
+template <bool OVF, bool SSQ>
+__device__ __forceinline__ void flags_epilogue(bool bad, double ss, uint32_t *ovf, double *ssq) {
+    if constexpr (OVF) {
+        if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) atomicOr(ovf, 1u);
+    }
+    if constexpr (SSQ) {
+        __shared__ double part[kBlock / 64];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double t = 0.0;
+#pragma unroll
+            for (int wv = 0; wv < kBlock / 64; ++wv) t += part[wv];
+            atomicAdd(ssq, t);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fused step: reduce -> scale -> AdamW -> cast, one pass
+
+template <int GDT, int WDT, int NDP, bool OVF, bool SSQ>
+__global__ void __launch_bounds__(kBlock)
+step_vec_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int64_t nvec,
+                float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
+                uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
+                double *__restrict__ ssq) {
+    bool bad = false;
+    double ss = 0.0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec;
+         i += stride) {
+        const int64_t e0 = i * kVec;
+        const f32x4 w0 = load16(W + e0), w1 = load16(W + e0 + 4);
+        const f32x4 m0 = load16(M + e0), m1 = load16(M + e0 + 4);
+        const f32x4 v0 = load16(V + e0), v1 = load16(V + e0 + 4);
+        float a[kVec];
+        reduce_chunk<GDT, NDP>(grads + e0, ld, n_dp, a);
+        float w[kVec] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        float m[kVec] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+        float v[kVec] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            if constexpr (OVF) bad |= !__builtin_isfinite(a[e]);
+            const float g = a[e] * c.s;
+            if constexpr (SSQ) ss += static_cast<double>(g) * static_cast<double>(g);
+            adamw_element(g, w[e], m[e], v[e], c);
+        }
+        store16(W + e0, f32x4{w[0], w[1], w[2], w[3]});
+        store16(W + e0 + 4, f32x4{w[4], w[5], w[6], w[7]});
+        store16(M + e0, f32x4{m[0], m[1], m[2], m[3]});
+        store16(M + e0 + 4, f32x4{m[4], m[5], m[6], m[7]});
+        store16(V + e0, f32x4{v[0], v[1], v[2], v[3]});
+        store16(V + e0 + 4, f32x4{v[4], v[5], v[6], v[7]});
+        store16(out + e0, u32x4{narrow2<WDT>(w[0], w[1]), narrow2<WDT>(w[2], w[3]),
+                                narrow2<WDT>(w[4], w[5]), narrow2<WDT>(w[6], w[7])});
+    }
+    flags_epilogue<OVF, SSQ>(bad, ss, ovf, ssq);
+}
+
+// element-per-thread variant for unaligned buffers and ragged tails
+template <int GDT, int WDT, bool OVF, bool SSQ>
+__global__ void __launch_bounds__(kBlock)
+step_scalar_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int64_t len,
+                   float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
+                   uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
+                   double *__restrict__ ssq) {
+    bool bad = false;
+    double ss = 0.0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < len;
+         j += stride) {
+        float a = widen1<GDT>(grads[j]);
+        for (int k = 1; k < n_dp; ++k) a = a + widen1<GDT>(grads[static_cast<int64_t>(k) * ld + j]);
+        if constexpr (OVF) bad |= !__builtin_isfinite(a);
+        const float g = a * c.s;
+        if constexpr (SSQ) ss += static_cast<double>(g) * static_cast<double>(g);
+        float w = W[j], m = M[j], v = V[j];
+        adamw_element(g, w, m, v, c);
+        W[j] = w;
+        M[j] = m;
+        V[j] = v;
+        out[j] = narrow1<WDT>(w);
+    }
+    flags_epilogue<OVF, SSQ>(bad, ss, ovf, ssq);
+}
+
+// ---------------------------------------------------------------------------
+// reduce into an fp32 buffer (optionally accumulating across micro-batches)
+
+template <int GDT, int NDP, bool ACC, bool OVF, bool SSQ>
+__global__ void __launch_bounds__(kBlock)
+reduce_vec_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int64_t nvec,
+                  float *__restrict__ acc, uint32_t *__restrict__ ovf, double *__restrict__ ssq) {
+    bool bad = false;
+    double ss = 0.0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec;
+         i += stride) {
+        const int64_t e0 = i * kVec;
+        f32x4 p0 = {}, p1 = {};
+        if constexpr (ACC) {
+            p0 = load16(acc + e0);
+            p1 = load16(acc + e0 + 4);
+        }
+        float a[kVec];
+        reduce_chunk<GDT, NDP>(grads + e0, ld, n, a);
+        if constexpr (ACC) {
+            const float prev[kVec] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) a[e] = prev[e] + a[e];
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            if constexpr (OVF) bad |= !__builtin_isfinite(a[e]);
+            if constexpr (SSQ) ss += static_cast<double>(a[e]) * static_cast<double>(a[e]);
+        }
+        store16(acc + e0, f32x4{a[0], a[1], a[2], a[3]});
+        store16(acc + e0 + 4, f32x4{a[4], a[5], a[6], a[7]});
+    }
+    flags_epilogue<OVF, SSQ>(bad, ss, ovf, ssq);
+}
+
+template <int GDT, bool ACC, bool OVF, bool SSQ>
+__global__ void __launch_bounds__(kBlock)
+reduce_scalar_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int64_t len,
+                     float *__restrict__ acc, uint32_t *__restrict__ ovf,
+                     double *__restrict__ ssq) {
+    bool bad = false;
+    double ss = 0.0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < len;
+         j += stride) {
+        float a = widen1<GDT>(grads[j]);
+        for (int k = 1; k < n; ++k) a = a + widen1<GDT>(grads[static_cast<int64_t>(k) * ld + j]);
+        if constexpr (ACC) a = acc[j] + a;
+        if constexpr (OVF) bad |= !__builtin_isfinite(a);
+        if constexpr (SSQ) ss += static_cast<double>(a) * static_cast<double>(a);
+        acc[j] = a;
+    }
+    flags_epilogue<OVF, SSQ>(bad, ss, ovf, ssq);
+}
+
+// ---------------------------------------------------------------------------
+// AdamW from an fp32 gradient buffer, gated by an optional device flag
+
+template <int WDT, bool SKIP>
+__global__ void __launch_bounds__(kBlock)
+adamw_vec_kernel(const float *__restrict__ acc, float *__restrict__ W, float *__restrict__ M,
+                 float *__restrict__ V, uint16_t *__restrict__ out, int64_t nvec, Consts c,
+                 const uint32_t *__restrict__ skip) {
+    if constexpr (SKIP) {
+        if (*skip != 0u) return;
+    }
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec;
+         i += stride) {
+        const int64_t e0 = i * kVec;
+        const f32x4 g0 = load16(acc + e0), g1 = load16(acc + e0 + 4);
+        const f32x4 w0 = load16(W + e0), w1 = load16(W + e0 + 4);
+        const f32x4 m0 = load16(M + e0), m1 = load16(M + e0 + 4);
+        const f32x4 v0 = load16(V + e0), v1 = load16(V + e0 + 4);
+        const float a[kVec] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+        float w[kVec] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        float m[kVec] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+        float v[kVec] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) adamw_element(a[e] * c.s, w[e], m[e], v[e], c);
+        store16(W + e0, f32x4{w[0], w[1], w[2], w[3]});
+        store16(W + e0 + 4, f32x4{w[4], w[5], w[6], w[7]});
+        store16(M + e0, f32x4{m[0], m[1], m[2], m[3]});
+        store16(M + e0 + 4, f32x4{m[4], m[5], m[6], m[7]});
+        store16(V + e0, f32x4{v[0], v[1], v[2], v[3]});
+        store16(V + e0 + 4, f32x4{v[4], v[5], v[6], v[7]});
+        store16(out + e0, u32x4{narrow2<WDT>(w[0], w[1]), narrow2<WDT>(w[2], w[3]),
+                                narrow2<WDT>(w[4], w[5]), narrow2<WDT>(w[6], w[7])});
+    }
+}
+
+template <int WDT, bool SKIP>
+__global__ void __launch_bounds__(kBlock)
+adamw_scalar_kernel(const float *__restrict__ acc, float *__restrict__ W, float *__restrict__ M,
+                    float *__restrict__ V, uint16_t *__restrict__ out, int64_t len, Consts c,
+                    const uint32_t *__restrict__ skip) {
+    if constexpr (SKIP) {
+        if (*skip != 0u) return;
+    }
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < len;
+         j += stride) {
+        float w = W[j], m = M[j], v = V[j];
+        adamw_element(acc[j] * c.s, w, m, v, c);
+        W[j] = w;
+        M[j] = m;
+        V[j] = v;
+        out[j] = narrow1<WDT>(w);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side: validation, constants, dispatch
+
+template <int V>
+using IntC = std::integral_constant<int, V>;
+template <bool V>
+using BoolC = std::integral_constant<bool, V>;
+
+template <typename F>
+void with_dtype(int dt, F &&f) {
+    if (dt == ZERO_BF16) f(IntC<ZERO_BF16>{});
+    else f(IntC<ZERO_FP16>{});
+}
+
+template <typename F>
+void with_bool(bool b, F &&f) {
+    if (b) f(BoolC<true>{});
+    else f(BoolC<false>{});
+}
+
+// row counts with a compiled specialisation; others take the generic loop
+template <typename F>
+void with_ndp(int n, F &&f) {
+    switch (n) {
+    case 1: f(IntC<1>{}); break;
+    case 8: f(IntC<8>{}); break;
+    default: f(IntC<0>{}); break;
+    }
+}
+
+bool dtype_ok(int dt) { return dt == ZERO_BF16 || dt == ZERO_FP16; }
+
+bool layout_ok(const zero_layout *l) {
+    if (!l || l->n_dp < 1 || l->align < 1 || l->shard < 0 || l->n < 0) return false;
+    if (l->shard % l->align != 0) return false;
+    if (l->shard > 0 && l->n_dp > INT64_MAX / l->shard) return false;
+    return l->n_pad == l->shard * l->n_dp && l->n <= l->n_pad;
+}
+
+bool hparams_ok(const zero_adamw_hparams *hp) {
+    if (!hp || hp->step < 1) return false;
+    if (!std::isfinite(hp->lr)) return false;
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return false;
+    if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return false;
+    if (!(std::isfinite(hp->eps) && hp->eps > 0.0)) return false;
+    if (!(std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.0)) return false;
+    return std::isfinite(hp->grad_scale) && hp->grad_scale > 0.0;
+}
+
+// each constant in double, rounded once to fp32
+Consts make_consts(const zero_adamw_hparams &hp) {
+    const double t = static_cast<double>(hp.step);
+    Consts c;
+    c.s = static_cast<float>(hp.grad_scale);
+    c.b1 = static_cast<float>(hp.beta1);
+    c.c1 = static_cast<float>(1.0 - hp.beta1);
+    c.b2 = static_cast<float>(hp.beta2);
+    c.c2 = static_cast<float>(1.0 - hp.beta2);
+    c.bc1 = static_cast<float>(1.0 - std::pow(hp.beta1, t));
+    c.bc2 = static_cast<float>(1.0 - std::pow(hp.beta2, t));
+    c.lr = static_cast<float>(hp.lr);
+    c.eps = static_cast<float>(hp.eps);
+    c.d = static_cast<float>(1.0 - hp.lr * hp.weight_decay);
+    return c;
+}
+
+// byte ranges, for the disjointness checks
+struct Span {
+    uintptr_t lo, hi;
+};
+
+Span span_of(const void *p, int64_t count, int64_t elem) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, lo + static_cast<uintptr_t>(count) * static_cast<uintptr_t>(elem)};
+}
+
+bool overlap(const Span &a, const Span &b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+// true when any two outputs overlap, or an output overlaps a gradient row
+bool any_alias(const Span *outs, int n_out, const void *rows, int n_rows, int64_t ld,
+               int64_t len, const Span *ins = nullptr, int n_in = 0) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(outs[i], outs[j])) return true;
+        for (int j = 0; j < n_in; ++j)
+            if (overlap(outs[i], ins[j])) return true;
+        for (int k = 0; k < n_rows; ++k) {
+            const void *row = static_cast<const uint16_t *>(rows) + static_cast<int64_t>(k) * ld;
+            if (overlap(outs[i], span_of(row, len, 2))) return true;
+        }
+    }
+    return false;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+unsigned grid_for(int64_t items, bool flags) {
+    const int64_t cap = flags ? kMaxBlocksWithFlags : kMaxBlocks;
+    int64_t b = (items + kBlock - 1) / kBlock;
+    if (b > cap) b = cap;
+    if (b < 1) b = 1;
+    return static_cast<unsigned>(b);
+}
+
+zero_status launch_status() {
+    return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EDEVICE;
+}
+
+// rows of the gradient slab all fit in int64 and do not wrap
+bool rows_ok(int n_rows, int64_t ld, int64_t len) {
+    if (n_rows < 1 || len < 0 || ld < len) return false;
+    if (ld > 0 && static_cast<int64_t>(n_rows - 1) > (INT64_MAX - len) / ld) return false;
+    return true;
+}
+
+}  // namespace
+
+// ===========================================================================
+
+extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int32_t n_contrib,
+                                         int64_t ld, int64_t len, float *acc,
+                                         int32_t accumulate, uint32_t *overflow,
+                                         double *sumsq, void *stream) {
+    if (!dtype_ok(gdt) || !rows_ok(n_contrib, ld, len)) return ZERO_EINVAL;
+    if (len == 0) return ZERO_OK;
+    if (!grads || !acc) return ZERO_EINVAL;
+    Span outs[3];
+    int n_out = 0;
+    outs[n_out++] = span_of(acc, len, 4);
+    if (overflow) outs[n_out++] = span_of(overflow, 1, 4);
+    if (sumsq) outs[n_out++] = span_of(sumsq, 1, 8);
+    if (any_alias(outs, n_out, grads, n_contrib, ld, len)) return ZERO_EALIAS;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint16_t *g = static_cast<const uint16_t *>(grads);
+    const bool flags = overflow || sumsq;
+    const bool vec = aligned16(g) && (n_contrib == 1 || ld % kVec == 0) && aligned16(acc);
+    const int64_t nvec = vec ? len / kVec : 0;
+    const int64_t done = nvec * kVec;
+    with_dtype(gdt, [&](auto GD) {
+        with_bool(accumulate != 0, [&](auto AC) {
+            with_bool(overflow != nullptr, [&](auto OV) {
+                with_bool(sumsq != nullptr, [&](auto SS) {
+                    if (nvec > 0) {
+                        with_ndp(n_contrib, [&](auto ND) {
+                            reduce_vec_kernel<GD.value, ND.value, AC.value, OV.value, SS.value>
+                                <<<grid_for(nvec, flags), kBlock, 0, st>>>(g, ld, n_contrib, nvec,
+                                                                           acc, overflow, sumsq);
+                        });
+                    }
+                    if (len > done) {
+                        reduce_scalar_kernel<GD.value, AC.value, OV.value, SS.value>
+                            <<<grid_for(len - done, flags), kBlock, 0, st>>>(
+                                g + done, ld, n_contrib, len - done, acc + done, overflow, sumsq);
+                    }
+                });
+            });
+        });
+    });
+    return launch_status();
+}
+
+extern "C" zero_status zero_shard_adamw(const float *acc, float *master, float *m, float *v,
+                                        void *weight_full, zero_dtype wdt,
+                                        const zero_layout *layout, int32_t rank,
+                                        int64_t shard_off, int64_t len,
+                                        const zero_adamw_hparams *hp, const uint32_t *skip,
+                                        void *stream) {
+    if (!dtype_ok(wdt) || !layout_ok(layout) || !hparams_ok(hp)) return ZERO_EINVAL;
+    if (rank < 0 || rank >= layout->n_dp || shard_off < 0 || len < 0) return ZERO_EINVAL;
+    if (shard_off > layout->shard || len > layout->shard - shard_off) return ZERO_ERANGE;
+    if (len == 0) return ZERO_OK;
+    if (!acc || !master || !m || !v || !weight_full) return ZERO_EINVAL;
+    uint16_t *slot = static_cast<uint16_t *>(weight_full) +
+                     static_cast<int64_t>(rank) * layout->shard + shard_off;
+    const Span outs[4] = {span_of(master, len, 4), span_of(m, len, 4), span_of(v, len, 4),
+                          span_of(slot, len, 2)};
+    // acc and skip are read only, but no output may overlap them
+    Span ins[2];
+    int n_in = 0;
+    ins[n_in++] = span_of(acc, len, 4);
+    if (skip) ins[n_in++] = span_of(skip, 1, 4);
+    if (any_alias(outs, 4, nullptr, 0, 0, 0, ins, n_in)) return ZERO_EALIAS;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Consts c = make_consts(*hp);
+    const bool vec = aligned16(acc) && aligned16(master) && aligned16(m) && aligned16(v) &&
+                     aligned16(slot);
+    const int64_t nvec = vec ? len / kVec : 0;
+    const int64_t done = nvec * kVec;
+    with_dtype(wdt, [&](auto WD) {
+        with_bool(skip != nullptr, [&](auto SK) {
+            if (nvec > 0) {
+                adamw_vec_kernel<WD.value, SK.value><<<grid_for(nvec, false), kBlock, 0, st>>>(
+                    acc, master, m, v, slot, nvec, c, skip);
+            }
+            if (len > done) {
+                adamw_scalar_kernel<WD.value, SK.value>
+                    <<<grid_for(len - done, false), kBlock, 0, st>>>(
+                        acc + done, master + done, m + done, v + done, slot + done, len - done, c,
+                        skip);
+            }
+        });
+    });
+    return launch_status();
+}
+
+extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_t ld,
+                                       int64_t len, float *master, float *m, float *v,
+                                       void *weight_full, zero_dtype wdt,
+                                       const zero_layout *layout, int32_t rank,
+                                       int64_t shard_off, const zero_adamw_hparams *hp,
+                                       uint32_t *overflow, double *sumsq, void *stream) {
+    if (!dtype_ok(gdt) || !dtype_ok(wdt) || !layout_ok(layout) || !hparams_ok(hp))
+        return ZERO_EINVAL;
+    const int n_dp = layout->n_dp;
+    if (rank < 0 || rank >= n_dp || shard_off < 0 || !rows_ok(n_dp, ld, len)) return ZERO_EINVAL;
+    if (shard_off > layout->shard || len > layout->shard - shard_off) return ZERO_ERANGE;
+    if (len == 0) return ZERO_OK;
+    if (!grads || !master || !m || !v || !weight_full) return ZERO_EINVAL;
+    uint16_t *slot = static_cast<uint16_t *>(weight_full) +
+                     static_cast<int64_t>(rank) * layout->shard + shard_off;
+    Span outs[6];
+    int n_out = 0;
+    outs[n_out++] = span_of(master, len, 4);
+    outs[n_out++] = span_of(m, len, 4);
+    outs[n_out++] = span_of(v, len, 4);
+    outs[n_out++] = span_of(slot, len, 2);
+    if (overflow) outs[n_out++] = span_of(overflow, 1, 4);
+    if (sumsq) outs[n_out++] = span_of(sumsq, 1, 8);
+    if (any_alias(outs, n_out, grads, n_dp, ld, len)) return ZERO_EALIAS;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Consts c = make_consts(*hp);
+    const uint16_t *g = static_cast<const uint16_t *>(grads);
+    const bool flags = overflow || sumsq;
+    const bool vec = aligned16(g) && (n_dp == 1 || ld % kVec == 0) && aligned16(master) &&
+                     aligned16(m) && aligned16(v) && aligned16(slot);
+    const int64_t nvec = vec ? len / kVec : 0;
+    const int64_t done = nvec * kVec;
+    with_dtype(gdt, [&](auto GD) {
+        with_dtype(wdt, [&](auto WD) {
+            with_bool(overflow != nullptr, [&](auto OV) {
+                with_bool(sumsq != nullptr, [&](auto SS) {
+                    if (nvec > 0) {
+                        with_ndp(n_dp, [&](auto ND) {
+                            step_vec_kernel<GD.value, WD.value, ND.value, OV.value, SS.value>
+                                <<<grid_for(nvec, flags), kBlock, 0, st>>>(
+                                    g, ld, n_dp, nvec, master, m, v, slot, c, overflow, sumsq);
+                        });
+                    }
+                    if (len > done) {
+                        step_scalar_kernel<GD.value, WD.value, OV.value, SS.value>
+                            <<<grid_for(len - done, flags), kBlock, 0, st>>>(
+                                g + done, ld, n_dp, len - done, master + done, m + done,
+                                v + done, slot + done, c, overflow, sumsq);
+                    }
+                });
+            });
+        });
+    });
+    return launch_status();
+}
