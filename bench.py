@@ -47,7 +47,24 @@ def parse():
                    help="CPU baseline sample: 2^k parameters of the shard")
     p.add_argument("--cpu-steps", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB (the known-size "
+                        "reference that scales the HBM byte counters) --steps times and exit")
     return p.parse_args()
+
+
+def calibrate_copy(mib, steps):
+    """A plain copy kernel of known size: reads and writes mib MiB each."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "launches": steps}), flush=True)
 
 
 def source_digest():
@@ -80,6 +97,10 @@ def main():
               "ranks' gradient rows in one GPU's HBM, and no multi-GPU path is built. "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, args.steps)
+        return
 
     import numpy as np
     import torch
@@ -170,12 +191,12 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     if micro == 1:
         bytes_per_param = 2 * n_dp + 26
-        kernel = "step_vec_kernel (fused reduce + AdamW + cast)"
+        kernel = "step_quad_kernel (fused reduce + AdamW + cast)"
     else:
         # 4 B written by the first reduce, 2 n_dp + 8 by each later one,
         # 30 by the gated AdamW (acc 4 + state 12 read, state 12 + weight 2 written)
         bytes_per_param = (2 * n_dp + 4) + (micro - 1) * (2 * n_dp + 8) + 30
-        kernel = "adamw_vec_kernel (gated AdamW + cast; timed launch)"
+        kernel = "adamw_quad_kernel (gated AdamW + cast; timed launch)"
     step_bytes = bytes_per_param * S
     kms = [a.elapsed_time(b) for a, b in events]
     k_avg = statistics.fmean(kms)

@@ -34,7 +34,8 @@
  *    Buffers must stay valid until the stream has passed them.
  *  - Arguments are validated on the host before anything is launched; on any
  *    error status nothing is launched and nothing is written.
- *  - Element counts and offsets are in elements, never bytes.
+ *  - Element counts and offsets are in elements, never bytes; one call
+ *    processes at most 2^39 elements (EINVAL beyond).
  *  - Element j of the processed range is independent of every other element:
  *    any range can be processed by one call or split over several calls
  *    (buckets) with identical results.

@@ -10,12 +10,26 @@
 //
 // Nothing here is a contraction: the work is a stream over HBM of
 // 2 * n_dp + 26 bytes per element (fused step), so the kernels are built for
-// bandwidth.  Each thread owns 8-element chunks: every gradient row and the
-// master/m/v shard are read with 16-byte loads, all of a chunk's loads are
-// issued before any arithmetic, sums stay in registers, and results leave
-// with 16-byte non-temporal stores (nothing is re-read, so nothing should
-// stay in the caches).  LDS and wave reductions appear only in the optional
-// overflow flag and sum of squares.
+// bandwidth, shaped by measurement on MI355X:
+//  - Each lane owns 4 consecutive elements (a "quad").  A wave's load of a
+//    gradient row is then 8 bytes per lane and one contiguous 512-byte span,
+//    its load or store of an fp32 array 16 bytes per lane and one contiguous
+//    1 KiB span: every memory instruction of a wave touches whole cache
+//    lines, and all of a quad's loads are issued before its first add.
+//    (8 elements per lane -- 16-byte gradient loads but half-used 2 KiB
+//    spans for the fp32 arrays -- measured slower.)
+//  - The grid is one thread per quad, with no loop: waves that finish free
+//    their slot for the next workgroup, so the set of addresses in flight
+//    stays a compact, moving window (persistent grid-stride variants
+//    measured 10-15% slower, and even a loop that runs once costs ~1%).
+//  - Fewer waves per CU than the hardware allows: with 8 + 7 streams in
+//    flight the HBM controllers do better with about 8 waves per CU than
+//    with 32, so each launch requests enough (otherwise unused) LDS to cap
+//    the workgroups resident on a CU (per-kernel caps below).
+//  - Non-temporal loads and stores: nothing is re-read, nothing should stay
+//    in L2 or the Infinity Cache.
+// LDS and wave reductions appear only in the optional overflow flag and sum
+// of squares.
 //
 // Arithmetic is IEEE binary32, round-to-nearest-even, in a fixed order: the
 // build uses -ffp-contract=off (no fused multiply-add), HIP's correctly
@@ -30,20 +44,26 @@
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBlock = 256;  // threads per workgroup: 4 wave64s
-constexpr int kVec = 8;      // elements per chunk: 16 bytes of 16-bit data
-constexpr int kRowBatch = 8; // gradient rows loaded together per chunk
-// Grid caps.  A plain step launches one thread per chunk up to kMaxBlocks
-// workgroups; with a flag or sum requested the grid stays small so that
-// each workgroup's single atomic does not pile up on one address.
-constexpr int64_t kMaxBlocks = 1 << 20;
-constexpr int64_t kMaxBlocksWithFlags = 2048;
+constexpr int kBlock = 256;     // threads per workgroup: 4 wave64s
+constexpr int kQuad = 4;        // elements per lane
+constexpr int kRowBatch = 8;    // rows loaded together when n_dp is not specialised
+// Residency caps (workgroups of 4 waves per CU), measured per kernel at the
+// workloads' sizes: the fused step with 1 or 8 rows peaks at 2, with 64
+// rows (64 row loads in flight per lane) at 1; the reduce and the AdamW
+// from an fp32 buffer at 3.
+constexpr int step_workgroups_per_cu(int ndp) { return ndp == 64 ? 1 : 2; }
+constexpr int kReduceWorkgroupsPerCU = 3;
+constexpr int kAdamwWorkgroupsPerCU = 3;
+// One thread per quad (one per element on the unaligned path): a launch
+// covers at most 2^31 - 1 workgroups, so the entry points reject ranges of
+// more than kMaxLen elements (2^39, far beyond any HBM).
+constexpr int64_t kMaxLen = int64_t(1) << 39;
 
 // fp32 constants of the update, formed on the host (see zero_adamw_hparams)
 struct Consts {
@@ -84,16 +104,16 @@ __device__ __forceinline__ uint16_t narrow1(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// memory helpers: 16-byte loads/stores marked non-temporal (streamed once)
+// memory helpers: loads/stores marked non-temporal (streamed once)
 
-__device__ __forceinline__ u32x4 load16(const uint16_t *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+__device__ __forceinline__ u32x2 load8(const uint16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
 }
 __device__ __forceinline__ f32x4 load16(const float *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
 }
-__device__ __forceinline__ void store16(uint16_t *p, u32x4 x) {
-    __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(p));
+__device__ __forceinline__ void store8(uint16_t *p, u32x2 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x2 *>(p));
 }
 __device__ __forceinline__ void store16(float *p, f32x4 x) {
     __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
@@ -117,56 +137,73 @@ __device__ __forceinline__ void adamw_element(float g, float &w, float &m, float
     v = vt;
 }
 
-// Sum of the rows for one 8-element chunk: a[e] = G_0[e] + G_1[e] + ...,
-// left to right in fp32.  Rows are fetched kRowBatch at a time, all loads of
-// a batch issued before the first add.  NDP > 0 fixes the row count at
-// compile time; NDP == 0 reads it from n.
+template <int GDT>
+__device__ __forceinline__ void add_row(float a[kQuad], u32x2 x) {
+    const f32x2 t0 = widen2<GDT>(x[0]), t1 = widen2<GDT>(x[1]);
+    a[0] = a[0] + t0[0];
+    a[1] = a[1] + t0[1];
+    a[2] = a[2] + t1[0];
+    a[3] = a[3] + t1[1];
+}
+
+// Rows of one quad.  For NDP > 0 (row count fixed at compile time) the
+// loads and the sum are separate steps so that a kernel can issue every
+// load it needs -- rows and state -- before the first add (see
+// loads_issued()).  NDP == 0 reads the count at run time and fetches
+// kRowBatch rows at a time.
+template <int NDP>
+struct Rows {
+    u32x2 x[NDP > 0 ? NDP : kRowBatch];
+};
+
+template <int NDP>
+__device__ __forceinline__ void load_rows(Rows<NDP> &r, const uint16_t *__restrict__ p,
+                                          int64_t ld) {
+    if constexpr (NDP > 0) {
+#pragma unroll
+        for (int k = 0; k < NDP; ++k) r.x[k] = load8(p + static_cast<int64_t>(k) * ld);
+    }
+}
+
+// a[e] = G_0[e] + G_1[e] + ..., left to right in fp32
 template <int GDT, int NDP>
-__device__ __forceinline__ void reduce_chunk(const uint16_t *__restrict__ p, int64_t ld, int n,
-                                             float a[kVec]) {
-    const int rows = NDP > 0 ? NDP : n;
-    u32x4 x[kRowBatch];
+__device__ __forceinline__ void sum_rows(float a[kQuad], Rows<NDP> &r,
+                                         const uint16_t *__restrict__ p, int64_t ld, int n) {
+    if constexpr (NDP > 0) {
+        const f32x2 t0 = widen2<GDT>(r.x[0][0]), t1 = widen2<GDT>(r.x[0][1]);
+        a[0] = t0[0];
+        a[1] = t0[1];
+        a[2] = t1[0];
+        a[3] = t1[1];
 #pragma unroll
-    for (int b = 0; b < kRowBatch; ++b)
-        if (b < rows) x[b] = load16(p + static_cast<int64_t>(b) * ld);
+        for (int k = 1; k < NDP; ++k) add_row<GDT>(a, r.x[k]);
+    } else {
+        for (int k = 0; k < n; k += kRowBatch) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const f32x2 t = widen2<GDT>(x[0][q]);
-        a[2 * q] = t[0];
-        a[2 * q + 1] = t[1];
-    }
-#pragma unroll
-    for (int b = 1; b < kRowBatch; ++b) {
-        if (b < rows) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x2 t = widen2<GDT>(x[b][q]);
-                a[2 * q] = a[2 * q] + t[0];
-                a[2 * q + 1] = a[2 * q + 1] + t[1];
+            for (int b = 0; b < kRowBatch; ++b)
+                if (k + b < n) r.x[b] = load8(p + static_cast<int64_t>(k + b) * ld);
+            if (k == 0) {
+                const f32x2 t0 = widen2<GDT>(r.x[0][0]), t1 = widen2<GDT>(r.x[0][1]);
+                a[0] = t0[0];
+                a[1] = t0[1];
+                a[2] = t1[0];
+                a[3] = t1[1];
             }
-        }
-    }
-    for (int k = kRowBatch; k < rows; k += kRowBatch) {
 #pragma unroll
-        for (int b = 0; b < kRowBatch; ++b)
-            if (k + b < rows) x[b] = load16(p + static_cast<int64_t>(k + b) * ld);
-#pragma unroll
-        for (int b = 0; b < kRowBatch; ++b) {
-            if (k + b < rows) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x2 t = widen2<GDT>(x[b][q]);
-                    a[2 * q] = a[2 * q] + t[0];
-                    a[2 * q + 1] = a[2 * q + 1] + t[1];
-                }
-            }
+            for (int b = 0; b < kRowBatch; ++b)
+                if (k + b < n && k + b > 0) add_row<GDT>(a, r.x[b]);
         }
     }
 }
 
-// The optional shard-wide outputs: one atomic per wave for the flag, a wave
-// then workgroup reduction and one atomic per workgroup for the sum.  Every
-// thread of the workgroup must reach this point.
+// Keeps the compiler from sinking any of the loads issued so far below the
+// arithmetic that follows: one round trip to HBM per quad, not two.
+__device__ __forceinline__ void loads_issued() { __builtin_amdgcn_sched_barrier(0); }
+
+// The optional shard-wide outputs: one atomic per wave for the flag (only
+// when a lane saw a non-finite value), a wave then workgroup reduction and
+// one atomic add per workgroup for the sum.  Every thread of the workgroup
+// must reach this point.
 template <bool OVF, bool SSQ>
 __device__ __forceinline__ void flags_epilogue(bool bad, double ss, uint32_t *ovf, double *ssq) {
     if constexpr (OVF) {
@@ -182,7 +219,7 @@ __device__ __forceinline__ void flags_epilogue(bool bad, double ss, uint32_t *ov
             double t = 0.0;
 #pragma unroll
             for (int wv = 0; wv < kBlock / 64; ++wv) t += part[wv];
-            atomicAdd(ssq, t);
+            unsafeAtomicAdd(ssq, t);  // device memory: native global_atomic_add_f64
         }
     }
 }
@@ -192,39 +229,35 @@ __device__ __forceinline__ void flags_epilogue(bool bad, double ss, uint32_t *ov
 
 template <int GDT, int WDT, int NDP, bool OVF, bool SSQ>
 __global__ void __launch_bounds__(kBlock)
-step_vec_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int64_t nvec,
-                float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
-                uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
-                double *__restrict__ ssq) {
+step_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int64_t nquad,
+                 float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
+                 uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
+                 double *__restrict__ ssq) {
     bool bad = false;
     double ss = 0.0;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec;
-         i += stride) {
-        const int64_t e0 = i * kVec;
-        const f32x4 w0 = load16(W + e0), w1 = load16(W + e0 + 4);
-        const f32x4 m0 = load16(M + e0), m1 = load16(M + e0 + 4);
-        const f32x4 v0 = load16(V + e0), v1 = load16(V + e0 + 4);
-        float a[kVec];
-        reduce_chunk<GDT, NDP>(grads + e0, ld, n_dp, a);
-        float w[kVec] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-        float m[kVec] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
-        float v[kVec] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (q < nquad) {
+        const int64_t e0 = q * kQuad;
+        Rows<NDP> rows;
+        load_rows<NDP>(rows, grads + e0, ld);
+        const f32x4 w4 = load16(W + e0), m4 = load16(M + e0), v4 = load16(V + e0);
+        loads_issued();
+        float a[kQuad];
+        sum_rows<GDT, NDP>(a, rows, grads + e0, ld, n_dp);
+        float w[kQuad] = {w4[0], w4[1], w4[2], w4[3]};
+        float m[kQuad] = {m4[0], m4[1], m4[2], m4[3]};
+        float v[kQuad] = {v4[0], v4[1], v4[2], v4[3]};
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) {
+        for (int e = 0; e < kQuad; ++e) {
             if constexpr (OVF) bad |= !__builtin_isfinite(a[e]);
             const float g = a[e] * c.s;
             if constexpr (SSQ) ss += static_cast<double>(g) * static_cast<double>(g);
             adamw_element(g, w[e], m[e], v[e], c);
         }
         store16(W + e0, f32x4{w[0], w[1], w[2], w[3]});
-        store16(W + e0 + 4, f32x4{w[4], w[5], w[6], w[7]});
         store16(M + e0, f32x4{m[0], m[1], m[2], m[3]});
-        store16(M + e0 + 4, f32x4{m[4], m[5], m[6], m[7]});
         store16(V + e0, f32x4{v[0], v[1], v[2], v[3]});
-        store16(V + e0 + 4, f32x4{v[4], v[5], v[6], v[7]});
-        store16(out + e0, u32x4{narrow2<WDT>(w[0], w[1]), narrow2<WDT>(w[2], w[3]),
-                                narrow2<WDT>(w[4], w[5]), narrow2<WDT>(w[6], w[7])});
+        store8(out + e0, u32x2{narrow2<WDT>(w[0], w[1]), narrow2<WDT>(w[2], w[3])});
     }
     flags_epilogue<OVF, SSQ>(bad, ss, ovf, ssq);
 }
@@ -261,33 +294,31 @@ step_scalar_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int
 
 template <int GDT, int NDP, bool ACC, bool OVF, bool SSQ>
 __global__ void __launch_bounds__(kBlock)
-reduce_vec_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int64_t nvec,
-                  float *__restrict__ acc, uint32_t *__restrict__ ovf, double *__restrict__ ssq) {
+reduce_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int64_t nquad,
+                   float *__restrict__ acc, uint32_t *__restrict__ ovf,
+                   double *__restrict__ ssq) {
     bool bad = false;
     double ss = 0.0;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec;
-         i += stride) {
-        const int64_t e0 = i * kVec;
-        f32x4 p0 = {}, p1 = {};
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (q < nquad) {
+        const int64_t e0 = q * kQuad;
+        Rows<NDP> rows;
+        load_rows<NDP>(rows, grads + e0, ld);
+        f32x4 prev = {};
+        if constexpr (ACC) prev = load16(acc + e0);
+        loads_issued();
+        float a[kQuad];
+        sum_rows<GDT, NDP>(a, rows, grads + e0, ld, n);
         if constexpr (ACC) {
-            p0 = load16(acc + e0);
-            p1 = load16(acc + e0 + 4);
-        }
-        float a[kVec];
-        reduce_chunk<GDT, NDP>(grads + e0, ld, n, a);
-        if constexpr (ACC) {
-            const float prev[kVec] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) a[e] = prev[e] + a[e];
+            for (int e = 0; e < kQuad; ++e) a[e] = prev[e] + a[e];
         }
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) {
+        for (int e = 0; e < kQuad; ++e) {
             if constexpr (OVF) bad |= !__builtin_isfinite(a[e]);
             if constexpr (SSQ) ss += static_cast<double>(a[e]) * static_cast<double>(a[e]);
         }
         store16(acc + e0, f32x4{a[0], a[1], a[2], a[3]});
-        store16(acc + e0 + 4, f32x4{a[4], a[5], a[6], a[7]});
     }
     flags_epilogue<OVF, SSQ>(bad, ss, ovf, ssq);
 }
@@ -317,34 +348,26 @@ reduce_scalar_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int6
 
 template <int WDT, bool SKIP>
 __global__ void __launch_bounds__(kBlock)
-adamw_vec_kernel(const float *__restrict__ acc, float *__restrict__ W, float *__restrict__ M,
-                 float *__restrict__ V, uint16_t *__restrict__ out, int64_t nvec, Consts c,
-                 const uint32_t *__restrict__ skip) {
+adamw_quad_kernel(const float *__restrict__ acc, float *__restrict__ W, float *__restrict__ M,
+                  float *__restrict__ V, uint16_t *__restrict__ out, int64_t nquad, Consts c,
+                  const uint32_t *__restrict__ skip) {
     if constexpr (SKIP) {
         if (*skip != 0u) return;
     }
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec;
-         i += stride) {
-        const int64_t e0 = i * kVec;
-        const f32x4 g0 = load16(acc + e0), g1 = load16(acc + e0 + 4);
-        const f32x4 w0 = load16(W + e0), w1 = load16(W + e0 + 4);
-        const f32x4 m0 = load16(M + e0), m1 = load16(M + e0 + 4);
-        const f32x4 v0 = load16(V + e0), v1 = load16(V + e0 + 4);
-        const float a[kVec] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-        float w[kVec] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-        float m[kVec] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
-        float v[kVec] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (q < nquad) {
+        const int64_t e0 = q * kQuad;
+        const f32x4 g4 = load16(acc + e0);
+        const f32x4 w4 = load16(W + e0), m4 = load16(M + e0), v4 = load16(V + e0);
+        float w[kQuad] = {w4[0], w4[1], w4[2], w4[3]};
+        float m[kQuad] = {m4[0], m4[1], m4[2], m4[3]};
+        float v[kQuad] = {v4[0], v4[1], v4[2], v4[3]};
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) adamw_element(a[e] * c.s, w[e], m[e], v[e], c);
+        for (int e = 0; e < kQuad; ++e) adamw_element(g4[e] * c.s, w[e], m[e], v[e], c);
         store16(W + e0, f32x4{w[0], w[1], w[2], w[3]});
-        store16(W + e0 + 4, f32x4{w[4], w[5], w[6], w[7]});
         store16(M + e0, f32x4{m[0], m[1], m[2], m[3]});
-        store16(M + e0 + 4, f32x4{m[4], m[5], m[6], m[7]});
         store16(V + e0, f32x4{v[0], v[1], v[2], v[3]});
-        store16(V + e0 + 4, f32x4{v[4], v[5], v[6], v[7]});
-        store16(out + e0, u32x4{narrow2<WDT>(w[0], w[1]), narrow2<WDT>(w[2], w[3]),
-                                narrow2<WDT>(w[4], w[5]), narrow2<WDT>(w[6], w[7])});
+        store8(out + e0, u32x2{narrow2<WDT>(w[0], w[1]), narrow2<WDT>(w[2], w[3])});
     }
 }
 
@@ -388,12 +411,14 @@ void with_bool(bool b, F &&f) {
     else f(BoolC<false>{});
 }
 
-// row counts with a compiled specialisation; others take the generic loop
+// row counts with a compiled specialisation (the configurations' 1, 8 and
+// 64 ranks); others take the batched loop
 template <typename F>
 void with_ndp(int n, F &&f) {
     switch (n) {
     case 1: f(IntC<1>{}); break;
     case 8: f(IntC<8>{}); break;
+    case 64: f(IntC<64>{}); break;
     default: f(IntC<0>{}); break;
     }
 }
@@ -465,13 +490,28 @@ bool any_alias(const Span *outs, int n_out, const void *rows, int n_rows, int64_
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
-unsigned grid_for(int64_t items, bool flags) {
-    const int64_t cap = flags ? kMaxBlocksWithFlags : kMaxBlocks;
-    int64_t b = (items + kBlock - 1) / kBlock;
-    if (b > cap) b = cap;
-    if (b < 1) b = 1;
-    return static_cast<unsigned>(b);
+// one thread per item; the entry points keep items below kMaxBlocks * kBlock
+unsigned grid_for(int64_t items) {
+    const int64_t b = (items + kBlock - 1) / kBlock;
+    return static_cast<unsigned>(b < 1 ? 1 : b);
+}
+
+// Dynamic LDS requested by a streaming kernel so that at most wg_per_cu of
+// its workgroups are resident on a CU (the LDS itself is unused).
+size_t residency_lds_bytes(int wg_per_cu) {
+    int dev = 0, per_cu = 0, per_block = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              dev) != hipSuccess ||
+        hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess)
+        return 0;
+    // leave 1 KiB per workgroup for the kernels' own static LDS
+    int64_t b = (static_cast<int64_t>(per_cu) / wg_per_cu - 1024) & ~int64_t(255);
+    if (b > per_block) b = per_block & ~255;
+    return b > 0 ? static_cast<size_t>(b) : 0;
 }
 
 zero_status launch_status() {
@@ -493,7 +533,7 @@ extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int3
                                          int64_t ld, int64_t len, float *acc,
                                          int32_t accumulate, uint32_t *overflow,
                                          double *sumsq, void *stream) {
-    if (!dtype_ok(gdt) || !rows_ok(n_contrib, ld, len)) return ZERO_EINVAL;
+    if (!dtype_ok(gdt) || !rows_ok(n_contrib, ld, len) || len > kMaxLen) return ZERO_EINVAL;
     if (len == 0) return ZERO_OK;
     if (!grads || !acc) return ZERO_EINVAL;
     Span outs[3];
@@ -505,24 +545,24 @@ extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int3
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const uint16_t *g = static_cast<const uint16_t *>(grads);
-    const bool flags = overflow || sumsq;
-    const bool vec = aligned16(g) && (n_contrib == 1 || ld % kVec == 0) && aligned16(acc);
-    const int64_t nvec = vec ? len / kVec : 0;
-    const int64_t done = nvec * kVec;
+    const bool vec = aligned8(g) && (n_contrib == 1 || ld % kQuad == 0) && aligned16(acc);
+    const int64_t nquad = vec ? len / kQuad : 0;
+    const int64_t done = nquad * kQuad;
+    const size_t lds = residency_lds_bytes(kReduceWorkgroupsPerCU);
     with_dtype(gdt, [&](auto GD) {
         with_bool(accumulate != 0, [&](auto AC) {
             with_bool(overflow != nullptr, [&](auto OV) {
                 with_bool(sumsq != nullptr, [&](auto SS) {
-                    if (nvec > 0) {
+                    if (nquad > 0) {
                         with_ndp(n_contrib, [&](auto ND) {
-                            reduce_vec_kernel<GD.value, ND.value, AC.value, OV.value, SS.value>
-                                <<<grid_for(nvec, flags), kBlock, 0, st>>>(g, ld, n_contrib, nvec,
-                                                                           acc, overflow, sumsq);
+                            reduce_quad_kernel<GD.value, ND.value, AC.value, OV.value, SS.value>
+                                <<<grid_for(nquad), kBlock, lds, st>>>(g, ld, n_contrib, nquad,
+                                                                       acc, overflow, sumsq);
                         });
                     }
                     if (len > done) {
                         reduce_scalar_kernel<GD.value, AC.value, OV.value, SS.value>
-                            <<<grid_for(len - done, flags), kBlock, 0, st>>>(
+                            <<<grid_for(len - done), kBlock, 0, st>>>(
                                 g + done, ld, n_contrib, len - done, acc + done, overflow, sumsq);
                     }
                 });
@@ -539,7 +579,8 @@ extern "C" zero_status zero_shard_adamw(const float *acc, float *master, float *
                                         const zero_adamw_hparams *hp, const uint32_t *skip,
                                         void *stream) {
     if (!dtype_ok(wdt) || !layout_ok(layout) || !hparams_ok(hp)) return ZERO_EINVAL;
-    if (rank < 0 || rank >= layout->n_dp || shard_off < 0 || len < 0) return ZERO_EINVAL;
+    if (rank < 0 || rank >= layout->n_dp || shard_off < 0 || len < 0 || len > kMaxLen)
+        return ZERO_EINVAL;
     if (shard_off > layout->shard || len > layout->shard - shard_off) return ZERO_ERANGE;
     if (len == 0) return ZERO_OK;
     if (!acc || !master || !m || !v || !weight_full) return ZERO_EINVAL;
@@ -557,20 +598,20 @@ extern "C" zero_status zero_shard_adamw(const float *acc, float *master, float *
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Consts c = make_consts(*hp);
     const bool vec = aligned16(acc) && aligned16(master) && aligned16(m) && aligned16(v) &&
-                     aligned16(slot);
-    const int64_t nvec = vec ? len / kVec : 0;
-    const int64_t done = nvec * kVec;
+                     aligned8(slot);
+    const int64_t nquad = vec ? len / kQuad : 0;
+    const int64_t done = nquad * kQuad;
+    const size_t lds = residency_lds_bytes(kAdamwWorkgroupsPerCU);
     with_dtype(wdt, [&](auto WD) {
         with_bool(skip != nullptr, [&](auto SK) {
-            if (nvec > 0) {
-                adamw_vec_kernel<WD.value, SK.value><<<grid_for(nvec, false), kBlock, 0, st>>>(
-                    acc, master, m, v, slot, nvec, c, skip);
+            if (nquad > 0) {
+                adamw_quad_kernel<WD.value, SK.value><<<grid_for(nquad), kBlock, lds, st>>>(
+                    acc, master, m, v, slot, nquad, c, skip);
             }
             if (len > done) {
-                adamw_scalar_kernel<WD.value, SK.value>
-                    <<<grid_for(len - done, false), kBlock, 0, st>>>(
-                        acc + done, master + done, m + done, v + done, slot + done, len - done, c,
-                        skip);
+                adamw_scalar_kernel<WD.value, SK.value><<<grid_for(len - done), kBlock, 0, st>>>(
+                    acc + done, master + done, m + done, v + done, slot + done, len - done, c,
+                    skip);
             }
         });
     });
@@ -586,7 +627,8 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
     if (!dtype_ok(gdt) || !dtype_ok(wdt) || !layout_ok(layout) || !hparams_ok(hp))
         return ZERO_EINVAL;
     const int n_dp = layout->n_dp;
-    if (rank < 0 || rank >= n_dp || shard_off < 0 || !rows_ok(n_dp, ld, len)) return ZERO_EINVAL;
+    if (rank < 0 || rank >= n_dp || shard_off < 0 || !rows_ok(n_dp, ld, len) || len > kMaxLen)
+        return ZERO_EINVAL;
     if (shard_off > layout->shard || len > layout->shard - shard_off) return ZERO_ERANGE;
     if (len == 0) return ZERO_OK;
     if (!grads || !master || !m || !v || !weight_full) return ZERO_EINVAL;
@@ -605,25 +647,25 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Consts c = make_consts(*hp);
     const uint16_t *g = static_cast<const uint16_t *>(grads);
-    const bool flags = overflow || sumsq;
-    const bool vec = aligned16(g) && (n_dp == 1 || ld % kVec == 0) && aligned16(master) &&
-                     aligned16(m) && aligned16(v) && aligned16(slot);
-    const int64_t nvec = vec ? len / kVec : 0;
-    const int64_t done = nvec * kVec;
+    const bool vec = aligned8(g) && (n_dp == 1 || ld % kQuad == 0) && aligned16(master) &&
+                     aligned16(m) && aligned16(v) && aligned8(slot);
+    const int64_t nquad = vec ? len / kQuad : 0;
+    const int64_t done = nquad * kQuad;
     with_dtype(gdt, [&](auto GD) {
         with_dtype(wdt, [&](auto WD) {
             with_bool(overflow != nullptr, [&](auto OV) {
                 with_bool(sumsq != nullptr, [&](auto SS) {
-                    if (nvec > 0) {
+                    if (nquad > 0) {
                         with_ndp(n_dp, [&](auto ND) {
-                            step_vec_kernel<GD.value, WD.value, ND.value, OV.value, SS.value>
-                                <<<grid_for(nvec, flags), kBlock, 0, st>>>(
-                                    g, ld, n_dp, nvec, master, m, v, slot, c, overflow, sumsq);
+                            const size_t lds = residency_lds_bytes(step_workgroups_per_cu(ND.value));
+                            step_quad_kernel<GD.value, WD.value, ND.value, OV.value, SS.value>
+                                <<<grid_for(nquad), kBlock, lds, st>>>(
+                                    g, ld, n_dp, nquad, master, m, v, slot, c, overflow, sumsq);
                         });
                     }
                     if (len > done) {
                         step_scalar_kernel<GD.value, WD.value, OV.value, SS.value>
-                            <<<grid_for(len - done, flags), kBlock, 0, st>>>(
+                            <<<grid_for(len - done), kBlock, 0, st>>>(
                                 g + done, ld, n_dp, len - done, master + done, m + done,
                                 v + done, slot + done, c, overflow, sumsq);
                     }
