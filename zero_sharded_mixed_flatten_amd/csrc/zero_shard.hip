@@ -50,20 +50,26 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBlock = 256;     // threads per workgroup: 4 wave64s
+constexpr int kWave = 64;       // wave64
+constexpr int kBlock = 256;     // threads per workgroup of the element kernels and of
+                                // streaming kernels that also sum squares
 constexpr int kQuad = 4;        // elements per lane
 constexpr int kRowBatch = 8;    // rows loaded together when n_dp is not specialised
-// Residency caps (workgroups of 4 waves per CU), measured per kernel at the
-// workloads' sizes: the fused step with 1 or 8 rows peaks at 2, with 64
-// rows (64 row loads in flight per lane) at 1; the reduce and the AdamW
-// from an fp32 buffer at 3.
-constexpr int step_workgroups_per_cu(int ndp) { return ndp == 64 ? 1 : 2; }
-constexpr int kReduceWorkgroupsPerCU = 3;
-constexpr int kAdamwWorkgroupsPerCU = 3;
+// Residency caps in waves per CU, measured per kernel at the workloads'
+// sizes with one-wave workgroups (a finished wave's slot is refilled at
+// once; with four-wave workgroups a slot frees only when all four are done,
+// which cost 8-10%).  When a kernel also sums squares it runs four-wave
+// workgroups (one atomic per workgroup instead of four) at the same wave cap
+// rounded to whole workgroups.
+// Fused step: 10 waves with 1 row (56 B per lane in flight), 7 with 8 rows
+// (112 B), and with 64 rows the 152 VGPRs per lane already allow only 12.
+constexpr int step_waves_per_cu(int ndp) { return ndp == 1 ? 10 : ndp == 64 ? 12 : 7; }
+constexpr int kReduceWavesPerCU = 10;
+constexpr int kAdamwWavesPerCU = 10;
 // One thread per quad (one per element on the unaligned path): a launch
 // covers at most 2^31 - 1 workgroups, so the entry points reject ranges of
-// more than kMaxLen elements (2^39, far beyond any HBM).
-constexpr int64_t kMaxLen = int64_t(1) << 39;
+// more than kMaxLen elements (2^38, far beyond any HBM).
+constexpr int64_t kMaxLen = int64_t(1) << 38;
 
 // fp32 constants of the update, formed on the host (see zero_adamw_hparams)
 struct Consts {
@@ -204,21 +210,21 @@ __device__ __forceinline__ void loads_issued() { __builtin_amdgcn_sched_barrier(
 // when a lane saw a non-finite value), a wave then workgroup reduction and
 // one atomic add per workgroup for the sum.  Every thread of the workgroup
 // must reach this point.
-template <bool OVF, bool SSQ>
+template <int TPB, bool OVF, bool SSQ>
 __device__ __forceinline__ void flags_epilogue(bool bad, double ss, uint32_t *ovf, double *ssq) {
     if constexpr (OVF) {
-        if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) atomicOr(ovf, 1u);
+        if (__ballot(bad) != 0 && (threadIdx.x & (kWave - 1)) == 0) atomicOr(ovf, 1u);
     }
     if constexpr (SSQ) {
-        __shared__ double part[kBlock / 64];
+        __shared__ double part[TPB / kWave];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-        if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+        for (int off = kWave / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+        if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = ss;
         __syncthreads();
         if (threadIdx.x == 0) {
             double t = 0.0;
 #pragma unroll
-            for (int wv = 0; wv < kBlock / 64; ++wv) t += part[wv];
+            for (int wv = 0; wv < TPB / kWave; ++wv) t += part[wv];
             unsafeAtomicAdd(ssq, t);  // device memory: native global_atomic_add_f64
         }
     }
@@ -227,15 +233,15 @@ __device__ __forceinline__ void flags_epilogue(bool bad, double ss, uint32_t *ov
 // ---------------------------------------------------------------------------
 // fused step: reduce -> scale -> AdamW -> cast, one pass
 
-template <int GDT, int WDT, int NDP, bool OVF, bool SSQ>
-__global__ void __launch_bounds__(kBlock)
+template <int TPB, int GDT, int WDT, int NDP, bool OVF, bool SSQ>
+__global__ void __launch_bounds__(TPB)
 step_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int64_t nquad,
                  float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
                  uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
                  double *__restrict__ ssq) {
     bool bad = false;
     double ss = 0.0;
-    const int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
     if (q < nquad) {
         const int64_t e0 = q * kQuad;
         Rows<NDP> rows;
@@ -259,7 +265,7 @@ step_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int64
         store16(V + e0, f32x4{v[0], v[1], v[2], v[3]});
         store8(out + e0, u32x2{narrow2<WDT>(w[0], w[1]), narrow2<WDT>(w[2], w[3])});
     }
-    flags_epilogue<OVF, SSQ>(bad, ss, ovf, ssq);
+    flags_epilogue<TPB, OVF, SSQ>(bad, ss, ovf, ssq);
 }
 
 // element-per-thread variant for unaligned buffers and ragged tails
@@ -286,20 +292,20 @@ step_scalar_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int
         V[j] = v;
         out[j] = narrow1<WDT>(w);
     }
-    flags_epilogue<OVF, SSQ>(bad, ss, ovf, ssq);
+    flags_epilogue<kBlock, OVF, SSQ>(bad, ss, ovf, ssq);
 }
 
 // ---------------------------------------------------------------------------
 // reduce into an fp32 buffer (optionally accumulating across micro-batches)
 
-template <int GDT, int NDP, bool ACC, bool OVF, bool SSQ>
-__global__ void __launch_bounds__(kBlock)
+template <int TPB, int GDT, int NDP, bool ACC, bool OVF, bool SSQ>
+__global__ void __launch_bounds__(TPB)
 reduce_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int64_t nquad,
                    float *__restrict__ acc, uint32_t *__restrict__ ovf,
                    double *__restrict__ ssq) {
     bool bad = false;
     double ss = 0.0;
-    const int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
     if (q < nquad) {
         const int64_t e0 = q * kQuad;
         Rows<NDP> rows;
@@ -320,7 +326,7 @@ reduce_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int64_
         }
         store16(acc + e0, f32x4{a[0], a[1], a[2], a[3]});
     }
-    flags_epilogue<OVF, SSQ>(bad, ss, ovf, ssq);
+    flags_epilogue<TPB, OVF, SSQ>(bad, ss, ovf, ssq);
 }
 
 template <int GDT, bool ACC, bool OVF, bool SSQ>
@@ -340,21 +346,21 @@ reduce_scalar_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int6
         if constexpr (SSQ) ss += static_cast<double>(a) * static_cast<double>(a);
         acc[j] = a;
     }
-    flags_epilogue<OVF, SSQ>(bad, ss, ovf, ssq);
+    flags_epilogue<kBlock, OVF, SSQ>(bad, ss, ovf, ssq);
 }
 
 // ---------------------------------------------------------------------------
 // AdamW from an fp32 gradient buffer, gated by an optional device flag
 
-template <int WDT, bool SKIP>
-__global__ void __launch_bounds__(kBlock)
+template <int TPB, int WDT, bool SKIP>
+__global__ void __launch_bounds__(TPB)
 adamw_quad_kernel(const float *__restrict__ acc, float *__restrict__ W, float *__restrict__ M,
                   float *__restrict__ V, uint16_t *__restrict__ out, int64_t nquad, Consts c,
                   const uint32_t *__restrict__ skip) {
     if constexpr (SKIP) {
         if (*skip != 0u) return;
     }
-    const int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
     if (q < nquad) {
         const int64_t e0 = q * kQuad;
         const f32x4 g4 = load16(acc + e0);
@@ -492,15 +498,19 @@ bool any_alias(const Span *outs, int n_out, const void *rows, int n_rows, int64_
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
-// one thread per item; the entry points keep items below kMaxBlocks * kBlock
-unsigned grid_for(int64_t items) {
-    const int64_t b = (items + kBlock - 1) / kBlock;
+// one thread per item; kMaxLen keeps the count below 2^31 workgroups
+unsigned grid_for(int64_t items, int tpb = kBlock) {
+    const int64_t b = (items + tpb - 1) / tpb;
     return static_cast<unsigned>(b < 1 ? 1 : b);
 }
 
-// Dynamic LDS requested by a streaming kernel so that at most wg_per_cu of
-// its workgroups are resident on a CU (the LDS itself is unused).
-size_t residency_lds_bytes(int wg_per_cu) {
+// Dynamic LDS requested by a streaming kernel of tpb threads per workgroup
+// so that about waves_per_cu of its waves are resident on a CU (the LDS
+// itself is unused).
+size_t residency_lds_bytes(int waves_per_cu, int tpb) {
+    const int wave_per_wg = tpb / kWave;
+    int wg_per_cu = (waves_per_cu + wave_per_wg / 2) / wave_per_wg;
+    if (wg_per_cu < 1) wg_per_cu = 1;
     int dev = 0, per_cu = 0, per_block = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
@@ -548,16 +558,18 @@ extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int3
     const bool vec = aligned8(g) && (n_contrib == 1 || ld % kQuad == 0) && aligned16(acc);
     const int64_t nquad = vec ? len / kQuad : 0;
     const int64_t done = nquad * kQuad;
-    const size_t lds = residency_lds_bytes(kReduceWorkgroupsPerCU);
     with_dtype(gdt, [&](auto GD) {
         with_bool(accumulate != 0, [&](auto AC) {
             with_bool(overflow != nullptr, [&](auto OV) {
                 with_bool(sumsq != nullptr, [&](auto SS) {
                     if (nquad > 0) {
+                        constexpr int tpb = SS.value ? kBlock : kWave;
+                        const size_t lds = residency_lds_bytes(kReduceWavesPerCU, tpb);
                         with_ndp(n_contrib, [&](auto ND) {
-                            reduce_quad_kernel<GD.value, ND.value, AC.value, OV.value, SS.value>
-                                <<<grid_for(nquad), kBlock, lds, st>>>(g, ld, n_contrib, nquad,
-                                                                       acc, overflow, sumsq);
+                            reduce_quad_kernel<tpb, GD.value, ND.value, AC.value, OV.value,
+                                               SS.value>
+                                <<<grid_for(nquad, tpb), tpb, lds, st>>>(
+                                    g, ld, n_contrib, nquad, acc, overflow, sumsq);
                         });
                     }
                     if (len > done) {
@@ -601,12 +613,13 @@ extern "C" zero_status zero_shard_adamw(const float *acc, float *master, float *
                      aligned8(slot);
     const int64_t nquad = vec ? len / kQuad : 0;
     const int64_t done = nquad * kQuad;
-    const size_t lds = residency_lds_bytes(kAdamwWorkgroupsPerCU);
+    const size_t lds = residency_lds_bytes(kAdamwWavesPerCU, kWave);
     with_dtype(wdt, [&](auto WD) {
         with_bool(skip != nullptr, [&](auto SK) {
             if (nquad > 0) {
-                adamw_quad_kernel<WD.value, SK.value><<<grid_for(nquad), kBlock, lds, st>>>(
-                    acc, master, m, v, slot, nquad, c, skip);
+                adamw_quad_kernel<kWave, WD.value, SK.value>
+                    <<<grid_for(nquad, kWave), kWave, lds, st>>>(acc, master, m, v, slot, nquad,
+                                                                 c, skip);
             }
             if (len > done) {
                 adamw_scalar_kernel<WD.value, SK.value><<<grid_for(len - done), kBlock, 0, st>>>(
@@ -656,10 +669,13 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
             with_bool(overflow != nullptr, [&](auto OV) {
                 with_bool(sumsq != nullptr, [&](auto SS) {
                     if (nquad > 0) {
+                        constexpr int tpb = SS.value ? kBlock : kWave;
                         with_ndp(n_dp, [&](auto ND) {
-                            const size_t lds = residency_lds_bytes(step_workgroups_per_cu(ND.value));
-                            step_quad_kernel<GD.value, WD.value, ND.value, OV.value, SS.value>
-                                <<<grid_for(nquad), kBlock, lds, st>>>(
+                            const size_t lds =
+                                residency_lds_bytes(step_waves_per_cu(ND.value), tpb);
+                            step_quad_kernel<tpb, GD.value, WD.value, ND.value, OV.value,
+                                             SS.value>
+                                <<<grid_for(nquad, tpb), tpb, lds, st>>>(
                                     g, ld, n_dp, nquad, master, m, v, slot, c, overflow, sumsq);
                         });
                     }
