@@ -10,7 +10,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle_zero.so")
+# ORACLE_LIB selects another build of oracle_zero.c (the mutation tests load
+# deliberately broken copies to show that the pins catch them)
+LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(HERE, "liboracle_zero.so")
 
 BF16, FP16 = 0, 1
 

@@ -1,0 +1,104 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of oracle/oracle_zero.c -- a dropped
+term, a wrong sign, a transposed operand or index, an off-by-one -- builds
+it, and runs the pin tests against that build (ORACLE_LIB); they must fail.
+The unmodified copy must pass, so a failure is the mistake's, not the
+harness's.  Nothing here touches the GPU or the product library.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle_zero.c")
+
+PINS_MATH = ["tests/test_oracle_adamw.py", "tests/test_oracle_reduce.py"]
+PINS_LAYOUT = ["tests/test_oracle_layout.py"]
+PINS_ACCT = ["tests/test_oracle_accounting.py"]
+PINS_CONVERT = ["tests/test_oracle_convert.py"]
+
+# (name, original text, planted text, pin files that must catch it)
+MUTANTS = [
+    ("m_sign", "float mt = b1 * *m + c1 * g;", "float mt = b1 * *m - c1 * g;", PINS_MATH),
+    ("v_not_squared", "c2 * (g * g)", "c2 * g", PINS_MATH),
+    ("no_bias_correction_m", "float mhat = mt / bc1;", "float mhat = mt;", PINS_MATH),
+    ("no_bias_correction_v", "float vhat = vt / bc2;", "float vhat = vt;", PINS_MATH),
+    ("eps_inside_sqrt", "float den = sqrtf(vhat) + eps;", "float den = sqrtf(vhat + eps);", PINS_MATH),
+    ("no_weight_decay", "float wt = *w * d - lr * u;", "float wt = *w - lr * u;", PINS_MATH),
+    ("update_sign", "float wt = *w * d - lr * u;", "float wt = *w * d + lr * u;", PINS_MATH),
+    ("betas_swapped", "out10[1] = (float)beta1;", "out10[1] = (float)beta2;", PINS_MATH),
+    ("bias_step_off_by_one", "pow(beta1, (double)step)", "pow(beta1, (double)(step + 1))", PINS_MATH),
+    ("decay_without_lr", "out10[9] = (float)(1.0 - lr * wd);", "out10[9] = (float)(1.0 - wd);", PINS_MATH),
+    ("row_index_transposed", "widen(grads[(int64_t)k * ld + j], gdt)",
+     "widen(grads[(int64_t)j * ld + k], gdt)", PINS_MATH),
+    ("last_row_dropped", "for (int32_t k = 0; k < n; ++k) {", "for (int32_t k = 0; k < n - 1; ++k) {",
+     PINS_MATH),
+    ("average_not_applied", "float g = a * c[0];", "float g = a;", PINS_MATH),
+    ("accumulate_ignored", "float r = accumulate ? acc[j] + a : a;", "float r = a;", PINS_MATH),
+    ("overflow_never_set", "if (nonfinite(r)) bad = 1;", "(void)r;", PINS_MATH),
+    ("bf16_truncates", "if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) hi += 1;", "(void)lo;",
+     PINS_CONVERT),
+    ("bf16_ties_away", "(lo == 0x8000u && (hi & 1u))", "(lo == 0x8000u)", PINS_CONVERT),
+    ("f16_widen_bias", "((e + 112u) << 23)", "((e + 111u) << 23)", PINS_CONVERT),
+    ("f16_subnormal_shift", "shift = -e - 1;", "shift = -e;", PINS_CONVERT),
+    ("layout_floor", "int64_t units = (n + unit - 1) / unit;", "int64_t units = n / unit;", PINS_LAYOUT),
+    ("segment_offset", "quads[4 * count + 1] = s - a;\n                quads[4 * count + 2] = s - lo;",
+     "quads[4 * count + 1] = s - a;\n                quads[4 * count + 2] = s - lo + 1;", PINS_LAYOUT),
+    ("padding_segment_dropped", "    if (hi > s) {\n        if (count < cap) {\n            quads[4 * count + 0] = -1;",
+     "    if (0 && hi > s) {\n        if (count < cap) {\n            quads[4 * count + 0] = -1;", PINS_LAYOUT),
+    ("stage2_grads_unsharded", "case 2: return w + g / n_dp + o / n_dp;", "case 2: return w + g + o / n_dp;",
+     PINS_ACCT),
+    ("comm_factor", "double f = (n_dp - 1.0) / n_dp * n;", "double f = n;", PINS_ACCT),
+]
+
+
+def _build(src_text, out_dir, name):
+    c = os.path.join(out_dir, f"{name}.c")
+    so = os.path.join(out_dir, f"{name}.so")
+    with open(c, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+                    "-I", os.path.join(ROOT, "oracle"), "-o", so, c, "-lm"], check=True)
+    return so
+
+
+def _run_pins(so, files):
+    env = dict(os.environ, ORACLE_LIB=so)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "-m", "not gpu"] + files, cwd=ROOT, env=env, capture_output=True, text=True)
+    return r.returncode, r.stdout[-2000:]
+
+
+@pytest.fixture(scope="module")
+def results():
+    src = open(SRC).read()
+    jobs = [("unmodified", src, PINS_MATH + PINS_LAYOUT + PINS_ACCT, None)]
+    for name, old, new, files in MUTANTS:
+        assert src.count(old) == 1, f"mutant {name}: its target text must occur once in the oracle"
+        jobs.append((name, src.replace(old, new), files, old))
+    out = {}
+    with tempfile.TemporaryDirectory() as d:
+        sos = {name: _build(text, d, name) for name, text, _, _ in jobs}
+        with ThreadPoolExecutor(max_workers=4) as ex:
+            futs = {name: ex.submit(_run_pins, sos[name], files) for name, _, files, _ in jobs}
+            for name, f in futs.items():
+                out[name] = f.result()
+    return out
+
+
+def test_unmodified_copy_passes_the_pins(results):
+    rc, log = results["unmodified"]
+    assert rc == 0, log
+
+
+@pytest.mark.parametrize("name", [m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(results, name):
+    rc, log = results[name]
+    # a failed pin (exit 1) or a crash of the broken build (killed by a
+    # signal) -- not a usage error or an empty collection
+    assert rc == 1 or rc < 0, f"the pins did not catch mutant {name} (exit {rc}): {log}"
