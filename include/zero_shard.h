@@ -198,6 +198,65 @@ ZERO_API zero_status zero_shard_adamw(const float *acc, float *master, float *m,
                              const zero_adamw_hparams *hp,
                              const uint32_t *skip, void *stream);
 
+/* ---- step controls: clipping and dynamic loss scaling (device) ------------
+ * Both configs of "DeepSpeed ZeRO" ("A worked example") and "ZeRO Optimizer,
+ * in depth" ("Running it with DeepSpeed") clip the gradient to global norm
+ * 1.0, and fp16 training needs a loss scale ("DeepSpeed ZeRO", "Mixed
+ * precision").  Both are decided on the device, so a step never waits for
+ * the host:
+ *   1. zero_shard_reduce per micro-batch into acc, with overflow, and on the
+ *      last one sumsq (= the sum of acc^2 over this rank's shard);
+ *   2. all-reduce overflow (max) and sumsq (sum) over the ranks (on one GPU
+ *      the caller sums the ranks' partials);
+ *   3. zero_shard_adamw_ex with skip = overflow, sumsq, max_norm, loss_scale;
+ *   4. zero_loss_scale_update with the same overflow flag. */
+
+/* Dynamic loss scale in device memory (8 bytes, caller-owned). */
+typedef struct zero_loss_scale {
+    float scale;         /* current loss scale, finite and > 0 */
+    int32_t good_steps;  /* finite steps since the scale last changed */
+} zero_loss_scale;
+
+/* Optional controls of zero_shard_adamw_ex; every pointer is a nullable
+ * device address.
+ *   skip:       when *skip != 0 nothing is written.
+ *   sumsq:      the sum over the whole model (all ranks) of acc^2; with
+ *               max_norm > 0 the gradient is clipped: with norm =
+ *               sqrt(*sumsq) * s (double) and c = min(1, max_norm /
+ *               (norm + 1e-6)) rounded to fp32, every g = acc * s is
+ *               multiplied by c when c < 1.
+ *   loss_scale: s = fl(grad_scale / loss_scale->scale) (double division,
+ *               rounded once) instead of fl(grad_scale); grad_scale then
+ *               holds only 1 / (n_dp * micro_batches). */
+typedef struct zero_step_control {
+    const uint32_t *skip;
+    const double *sumsq;
+    double max_norm;
+    const zero_loss_scale *loss_scale;
+} zero_step_control;
+
+/* zero_shard_adamw with controls (ctl nullable = none).  Errors as for
+ * zero_shard_adamw; EINVAL also for a non-finite max_norm, EALIAS when a
+ * control overlaps an output. */
+ZERO_API zero_status zero_shard_adamw_ex(const float *acc, float *master, float *m,
+                                         float *v, void *weight_full, zero_dtype wdt,
+                                         const zero_layout *layout, int32_t rank,
+                                         int64_t shard_off, int64_t len,
+                                         const zero_adamw_hparams *hp,
+                                         const zero_step_control *ctl, void *stream);
+
+/* One step of the dynamic loss scale, on the device: if *overflow != 0 the
+ * scale is multiplied by backoff and good_steps restarts at 0; otherwise
+ * good_steps grows by one and on reaching interval the scale is multiplied
+ * by growth (unless that product would be infinite) and good_steps restarts
+ * (products in double, rounded to fp32).
+ * EINVAL: NULL state/overflow, growth not finite or < 1, backoff outside
+ * (0, 1], interval < 1.  EALIAS: state and overflow overlap. */
+ZERO_API zero_status zero_loss_scale_update(zero_loss_scale *state,
+                                            const uint32_t *overflow, double growth,
+                                            double backoff, int32_t interval,
+                                            void *stream);
+
 /* ---- fused step (device) ---------------------------------------------------
  * One pass over the range: reduce layout->n_dp rows in fp32 (as
  * zero_shard_reduce with accumulate = 0), scale by s, AdamW, cast into the

@@ -52,6 +52,14 @@ def lib():
                                ctypes.c_int64, vp, vp, vp, vp, ctypes.c_int, vp,
                                ctypes.c_int64, vp, vp]
         L.ora_step.restype = None
+        L.ora_clip_coef.argtypes = [ctypes.c_double, ctypes.c_float, ctypes.c_double]
+        L.ora_clip_coef.restype = ctypes.c_float
+        L.ora_adamw_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int64, vp,
+                                   ctypes.c_int64, vp, vp, ctypes.c_double, vp]
+        L.ora_adamw_ex.restype = None
+        L.ora_loss_scale_update.argtypes = [vp, vp, ctypes.c_uint32, ctypes.c_double,
+                                            ctypes.c_double, ctypes.c_int32]
+        L.ora_loss_scale_update.restype = None
         L.ora_model_state_bytes.argtypes = [ctypes.c_double, ctypes.c_double,
                                             ctypes.c_int, ctypes.c_double]
         L.ora_model_state_bytes.restype = ctypes.c_double
@@ -163,6 +171,31 @@ def adamw(acc, w, m, v, wout, wdt, length, step, lr=1e-4, beta1=0.9, beta2=0.999
     hp = _hp(lr, beta1, beta2, eps, weight_decay, grad_scale)
     lib().ora_adamw(_ptr(acc), _ptr(w), _ptr(m), _ptr(v), _ptr(wout), wdt, length,
                     _ptr(hp), step, _ptr(skip))
+
+
+def clip_coef(sumsq, s, max_norm):
+    return float(np.float32(lib().ora_clip_coef(float(sumsq), float(s), float(max_norm))))
+
+
+def adamw_ex(acc, w, m, v, wout, wdt, length, step, lr=1e-4, beta1=0.9, beta2=0.999,
+             eps=1e-8, weight_decay=0.1, grad_scale=1.0, skip=None, sumsq=None, max_norm=0.0,
+             loss_scale=None):
+    """adamw with clipping (sumsq float64[1], max_norm) and a dynamic loss scale
+    (loss_scale float32[1]: s = grad_scale / loss_scale)."""
+    for a, n in ((acc, "acc"), (w, "w"), (m, "m"), (v, "v")):
+        _need(a, np.float32, n)
+    _need(wout, np.uint16, "wout")
+    hp = _hp(lr, beta1, beta2, eps, weight_decay, grad_scale)
+    lib().ora_adamw_ex(_ptr(acc), _ptr(w), _ptr(m), _ptr(v), _ptr(wout), wdt, length, _ptr(hp),
+                       step, _ptr(skip), _ptr(sumsq), float(max_norm), _ptr(loss_scale))
+
+
+def loss_scale_update(scale, good_steps, overflow, growth=2.0, backoff=0.5, interval=2000):
+    """In place on scale (float32[1]) and good_steps (int32[1])."""
+    _need(scale, np.float32, "scale")
+    _need(good_steps, np.int32, "good_steps")
+    lib().ora_loss_scale_update(_ptr(scale), _ptr(good_steps), int(overflow), float(growth),
+                                float(backoff), int(interval))
 
 
 def step(grads, gdt, n_dp, ld, length, w, m, v, wout, wdt, step, lr=1e-4, beta1=0.9,

@@ -297,6 +297,52 @@ void ora_adamw(const float *acc, float *w, float *m, float *v, uint16_t *wout,
     }
 }
 
+/* Clipping.  Both configs of "DeepSpeed ZeRO" ("A worked example") and "ZeRO
+ * Optimizer, in depth" ("Running it with DeepSpeed") set gradient clipping
+ * to 1.0: the whole gradient is scaled down to norm max_norm when its
+ * global norm is larger (the usual min(1, max_norm / (norm + 1e-6))). */
+float ora_clip_coef(double sumsq, float s, double max_norm) {
+    double norm = sqrt(sumsq) * (double)s;
+    double c = max_norm / (norm + 1e-6);
+    return c < 1.0 ? (float)c : 1.0f;
+}
+
+void ora_adamw_ex(const float *acc, float *w, float *m, float *v, uint16_t *wout,
+                  int wdt, int64_t len, const double hp6[6], int64_t step,
+                  const uint32_t *skip, const double *sumsq, double max_norm,
+                  const float *loss_scale) {
+    if (skip && *skip) return;
+    float c[10];
+    ora_adamw_scalars(hp6, step, c);
+    if (loss_scale) c[0] = (float)(hp6[5] / (double)*loss_scale);
+    float clip = 1.0f;
+    if (sumsq && max_norm > 0.0) clip = ora_clip_coef(*sumsq, c[0], max_norm);
+    for (int64_t j = 0; j < len; ++j) {
+        float g = acc[j] * c[0];
+        if (clip < 1.0f) g = g * clip;
+        adamw_element(g, &w[j], &m[j], &v[j], c);
+        wout[j] = narrow(w[j], wdt);
+    }
+}
+
+/* Dynamic loss scaling: "DeepSpeed ZeRO", "Mixed precision" -- fp16 needs a
+ * loss scale; read as the usual back-off on overflow and growth after a run
+ * of finite steps. */
+void ora_loss_scale_update(float *scale, int32_t *good_steps, uint32_t overflow,
+                           double growth, double backoff, int32_t interval) {
+    if (overflow) {
+        *scale = (float)((double)*scale * backoff);
+        *good_steps = 0;
+        return;
+    }
+    *good_steps += 1;
+    if (*good_steps >= interval) {
+        float grown = (float)((double)*scale * growth);
+        if (!isinf(grown)) *scale = grown; /* never grows to infinity */
+        *good_steps = 0;
+    }
+}
+
 void ora_step(const uint16_t *grads, int gdt, int32_t n_dp, int64_t ld,
               int64_t len, float *w, float *m, float *v, uint16_t *wout,
               int wdt, const double hp6[6], int64_t step, uint32_t *overflow,

@@ -91,6 +91,29 @@ void ora_adamw(const float *acc, float *w, float *m, float *v, uint16_t *wout,
                int wdt, int64_t len, const double hp6[6], int64_t step,
                const uint32_t *skip);
 
+/* ---- clipping and dynamic loss scaling -------------------------------------
+ * Global-norm clipping coefficient: with s the fp32 scale applied to the
+ * accumulated gradient and sumsq the sum over the whole model of acc^2,
+ * norm = sqrt(sumsq) * s and c = min(1, max_norm / (norm + 1e-6)), all in
+ * double, rounded once to fp32. */
+float ora_clip_coef(double sumsq, float s, double max_norm);
+
+/* ora_adamw with the optional controls: skip (as before); loss_scale
+ * (nullable): s = fl(grad_scale / *loss_scale) instead of fl(grad_scale);
+ * sumsq (nullable) with max_norm > 0: every g = acc * s is then multiplied
+ * by c = ora_clip_coef(*sumsq, s, max_norm) when c < 1. */
+void ora_adamw_ex(const float *acc, float *w, float *m, float *v, uint16_t *wout,
+                  int wdt, int64_t len, const double hp6[6], int64_t step,
+                  const uint32_t *skip, const double *sumsq, double max_norm,
+                  const float *loss_scale);
+
+/* One step of the dynamic loss scale: on overflow scale *= backoff and the
+ * count of good steps restarts; otherwise the count grows and, on reaching
+ * interval, scale *= growth (kept unchanged if that would be infinite) and
+ * the count restarts (products in double, rounded to fp32). */
+void ora_loss_scale_update(float *scale, int32_t *good_steps, uint32_t overflow,
+                           double growth, double backoff, int32_t interval);
+
 /* ---- fused: reduce n_dp rows, then AdamW, then cast -----------------------
  * Equal, element by element, to ora_reduce(accumulate = 0) into a temporary
  * followed by ora_adamw.  overflow is set when a reduced a_j is non-finite

@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(zs.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -200,3 +200,27 @@ def test_reduce_and_adamw_reject_bad_arguments():
     bad = list(args)
     bad[1] = P(BASE + 4000)  # master over acc
     assert A(*bad) == zs.ZERO_EALIAS
+
+
+@cpu_only
+def test_controls_reject_bad_arguments():
+    U = L.zero_loss_scale_update
+    assert U(None, P(BASE + 64), 2.0, 0.5, 10, None) == zs.ZERO_EINVAL
+    assert U(P(BASE), None, 2.0, 0.5, 10, None) == zs.ZERO_EINVAL
+    assert U(P(BASE), P(BASE + 64), 0.5, 0.5, 10, None) == zs.ZERO_EINVAL      # growth < 1
+    assert U(P(BASE), P(BASE + 64), float("inf"), 0.5, 10, None) == zs.ZERO_EINVAL
+    assert U(P(BASE), P(BASE + 64), 2.0, 0.0, 10, None) == zs.ZERO_EINVAL      # backoff <= 0
+    assert U(P(BASE), P(BASE + 64), 2.0, 1.5, 10, None) == zs.ZERO_EINVAL      # backoff > 1
+    assert U(P(BASE), P(BASE + 64), 2.0, 0.5, 0, None) == zs.ZERO_EINVAL       # interval < 1
+    assert U(P(BASE), P(BASE + 4), 2.0, 0.5, 10, None) == zs.ZERO_EALIAS       # flag inside state
+    A = L.zero_shard_adamw_ex
+    lay = zs.zero_flatten_layout([4096], 4)[0]
+    hp = _hp()
+    base = [P(BASE), P(BASE + (1 << 30)), P(BASE + (2 << 30)), P(BASE + (3 << 30)),
+            P(BASE + (4 << 30)), 0, ctypes.byref(lay), 1, 0, 1024, ctypes.byref(hp)]
+    ctl = zs._StepControl(None, P(BASE + (1 << 30) + 8).value, 1.0, None)  # sumsq inside master
+    assert A(*base, ctypes.byref(ctl), None) == zs.ZERO_EALIAS
+    ctl = zs._StepControl(None, None, float("nan"), None)
+    assert A(*base, ctypes.byref(ctl), None) == zs.ZERO_EINVAL
+    ctl = zs._StepControl(None, None, 0.0, P(BASE + (2 << 30) + 100).value)  # loss scale inside m
+    assert A(*base, ctypes.byref(ctl), None) == zs.ZERO_EALIAS

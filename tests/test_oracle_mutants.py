@@ -21,6 +21,7 @@ PINS_MATH = ["tests/test_oracle_adamw.py", "tests/test_oracle_reduce.py"]
 PINS_LAYOUT = ["tests/test_oracle_layout.py"]
 PINS_ACCT = ["tests/test_oracle_accounting.py"]
 PINS_CONVERT = ["tests/test_oracle_convert.py"]
+PINS_CONTROL = ["tests/test_oracle_control.py"]
 
 # (name, original text, planted text, pin files that must catch it)
 MUTANTS = [
@@ -54,6 +55,17 @@ MUTANTS = [
     ("stage2_grads_unsharded", "case 2: return w + g / n_dp + o / n_dp;", "case 2: return w + g + o / n_dp;",
      PINS_ACCT),
     ("comm_factor", "double f = (n_dp - 1.0) / n_dp * n;", "double f = n;", PINS_ACCT),
+    ("clip_without_sqrt", "double norm = sqrt(sumsq) * (double)s;", "double norm = sumsq * (double)s;",
+     PINS_CONTROL),
+    ("clip_ignores_scale", "double norm = sqrt(sumsq) * (double)s;", "double norm = sqrt(sumsq);",
+     PINS_CONTROL),
+    ("clip_amplifies", "return c < 1.0 ? (float)c : 1.0f;", "return (float)c;", PINS_CONTROL),
+    ("scale_backoff_as_growth", "*scale = (float)((double)*scale * backoff);",
+     "*scale = (float)((double)*scale * growth);", PINS_CONTROL),
+    ("scale_count_not_reset", "        *good_steps = 0;\n        return;", "        return;",
+     PINS_CONTROL),
+    ("dynamic_scale_multiplied", "c[0] = (float)(hp6[5] / (double)*loss_scale);",
+     "c[0] = (float)(hp6[5] * (double)*loss_scale);", PINS_CONTROL),
 ]
 
 
@@ -77,7 +89,7 @@ def _run_pins(so, files):
 @pytest.fixture(scope="module")
 def results():
     src = open(SRC).read()
-    jobs = [("unmodified", src, PINS_MATH + PINS_LAYOUT + PINS_ACCT, None)]
+    jobs = [("unmodified", src, PINS_MATH + PINS_LAYOUT + PINS_ACCT + PINS_CONTROL, None)]
     for name, old, new, files in MUTANTS:
         assert src.count(old) == 1, f"mutant {name}: its target text must occur once in the oracle"
         jobs.append((name, src.replace(old, new), files, old))

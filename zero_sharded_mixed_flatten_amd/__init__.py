@@ -50,6 +50,11 @@ class _HParams(ctypes.Structure):
                 ("step", ctypes.c_int64)]
 
 
+class _StepControl(ctypes.Structure):
+    _fields_ = [("skip", ctypes.c_void_p), ("sumsq", ctypes.c_void_p),
+                ("max_norm", ctypes.c_double), ("loss_scale", ctypes.c_void_p)]
+
+
 class _Segment(ctypes.Structure):
     _fields_ = [("tensor", ctypes.c_int64), ("tensor_off", ctypes.c_int64),
                 ("shard_off", ctypes.c_int64), ("len", ctypes.c_int64)]
@@ -92,6 +97,11 @@ def _load():
     L.zero_shard_adamw.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, lay_p, i32, i64, i64,
                                    hp_p, vp, vp]
     L.zero_shard_adamw.restype = ctypes.c_int
+    L.zero_shard_adamw_ex.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, lay_p, i32, i64, i64,
+                                      hp_p, ctypes.POINTER(_StepControl), vp]
+    L.zero_shard_adamw_ex.restype = ctypes.c_int
+    L.zero_loss_scale_update.argtypes = [vp, vp, dbl, dbl, i32, vp]
+    L.zero_loss_scale_update.restype = ctypes.c_int
     L.zero_shard_step.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, ctypes.c_int,
                                   lay_p, i32, i64, hp_p, vp, vp, vp]
     L.zero_shard_step.restype = ctypes.c_int
@@ -200,6 +210,49 @@ def zero_shard_adamw(acc, master, m, v, weight_full, layout: ZeroLayout, rank: i
         _dev_ptr(skip, "skip", torch.int32), _stream(stream, master)), "zero_shard_adamw")
 
 
+def zero_shard_adamw_ex(acc, master, m, v, weight_full, layout: ZeroLayout, rank: int,
+                        hp: AdamWHParams, shard_off: int = 0, length: Optional[int] = None,
+                        skip=None, sumsq=None, max_norm: float = 0.0, loss_scale=None,
+                        stream=None):
+    """zero_shard_adamw with controls: skip (int32 flag), clipping from the
+    whole-model sum of squares (float64 scalar) to max_norm, and a dynamic
+    loss scale (see new_loss_scale)."""
+    import torch
+    if length is None:
+        length = master.numel()
+    hpc = hp._c()
+    ctl = _StepControl(_dev_ptr(skip, "skip", torch.int32), _dev_ptr(sumsq, "sumsq", torch.float64),
+                       float(max_norm), _dev_ptr(loss_scale, "loss_scale", torch.int32))
+    _check(_lib.zero_shard_adamw_ex(
+        _dev_ptr(acc, "acc", torch.float32), _dev_ptr(master, "master", torch.float32),
+        _dev_ptr(m, "m", torch.float32), _dev_ptr(v, "v", torch.float32),
+        _dev_ptr(weight_full, "weight_full"), _dtype_code(weight_full, "weight_full"),
+        ctypes.byref(layout), rank, shard_off, length, ctypes.byref(hpc), ctypes.byref(ctl),
+        _stream(stream, master)), "zero_shard_adamw_ex")
+
+
+def new_loss_scale(scale: float = 65536.0, device="cuda"):
+    """A device zero_loss_scale {float scale; int32 good_steps} as an int32[2] tensor."""
+    import torch
+    bits = int(np.array([scale], dtype=np.float32).view(np.int32)[0])
+    return torch.tensor([bits, 0], dtype=torch.int32, device=device)
+
+
+def read_loss_scale(t) -> Tuple[float, int]:
+    h = t.detach().cpu().numpy().astype(np.int32)
+    return float(h[:1].view(np.float32)[0]), int(h[1])
+
+
+def zero_loss_scale_update(loss_scale, overflow, growth: float = 2.0, backoff: float = 0.5,
+                           interval: int = 2000, stream=None):
+    """One step of the device-resident dynamic loss scale."""
+    import torch
+    _check(_lib.zero_loss_scale_update(
+        _dev_ptr(loss_scale, "loss_scale", torch.int32), _dev_ptr(overflow, "overflow", torch.int32),
+        float(growth), float(backoff), int(interval), _stream(stream, loss_scale)),
+        "zero_loss_scale_update")
+
+
 def zero_shard_step(grads, ld: int, length: int, master, m, v, weight_full,
                     layout: ZeroLayout, rank: int, hp: AdamWHParams, shard_off: int = 0,
                     overflow=None, sumsq=None, stream=None):
@@ -235,5 +288,6 @@ def library_path() -> str:
 
 
 __all__ = ["zero_flatten_layout", "zero_shard_segments", "zero_shard_reduce",
-           "zero_shard_adamw", "zero_shard_step", "zero_model_state_bytes", "zero_comm_bytes",
+           "zero_shard_adamw", "zero_shard_adamw_ex", "zero_loss_scale_update",
+           "new_loss_scale", "read_loss_scale", "zero_shard_step", "zero_model_state_bytes", "zero_comm_bytes",
            "AdamWHParams", "ZeroLayout", "ZeroError", "ZERO_BF16", "ZERO_FP16", "library_path"]

@@ -76,6 +76,15 @@ struct Consts {
     float s, b1, c1, b2, c2, bc1, bc2, lr, eps, d;
 };
 
+// Device-side step controls (zero_step_control with the static part of the
+// gradient scale alongside).
+struct Control {
+    const double *sumsq;
+    double max_norm;
+    const zero_loss_scale *loss_scale;
+    double grad_scale;
+};
+
 // ---------------------------------------------------------------------------
 // 16-bit <-> fp32.  Widening is exact.  Narrowing uses gfx950's packed
 // converts (v_cvt_pk_bf16_f32, v_cvt_pk_f16_f32): round to nearest even.
@@ -352,24 +361,47 @@ reduce_scalar_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int6
 // ---------------------------------------------------------------------------
 // AdamW from an fp32 gradient buffer, gated by an optional device flag
 
-template <int TPB, int WDT, bool SKIP>
+// The scale s and the clipping coefficient of a controlled step, from the
+// device-resident loss scale and whole-model sum of squares (every thread
+// computes the same value; double arithmetic, rounded once to fp32).
+__device__ __forceinline__ float resolve_controls(const Control &k, Consts &c) {
+    if (k.loss_scale) c.s = static_cast<float>(k.grad_scale / static_cast<double>(k.loss_scale->scale));
+    float clip = 1.0f;
+    if (k.sumsq && k.max_norm > 0.0) {
+        const double norm = sqrt(*k.sumsq) * static_cast<double>(c.s);
+        const double cc = k.max_norm / (norm + 1e-6);
+        if (cc < 1.0) clip = static_cast<float>(cc);
+    }
+    return clip;
+}
+
+template <int TPB, int WDT, bool SKIP, bool EXT>
 __global__ void __launch_bounds__(TPB)
 adamw_quad_kernel(const float *__restrict__ acc, float *__restrict__ W, float *__restrict__ M,
                   float *__restrict__ V, uint16_t *__restrict__ out, int64_t nquad, Consts c,
-                  const uint32_t *__restrict__ skip) {
+                  const uint32_t *__restrict__ skip, Control ctl) {
     if constexpr (SKIP) {
         if (*skip != 0u) return;
     }
+    float clip = 1.0f;
+    if constexpr (EXT) clip = resolve_controls(ctl, c);
     const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
     if (q < nquad) {
         const int64_t e0 = q * kQuad;
         const f32x4 g4 = load16(acc + e0);
         const f32x4 w4 = load16(W + e0), m4 = load16(M + e0), v4 = load16(V + e0);
+        loads_issued();
         float w[kQuad] = {w4[0], w4[1], w4[2], w4[3]};
         float m[kQuad] = {m4[0], m4[1], m4[2], m4[3]};
         float v[kQuad] = {v4[0], v4[1], v4[2], v4[3]};
 #pragma unroll
-        for (int e = 0; e < kQuad; ++e) adamw_element(g4[e] * c.s, w[e], m[e], v[e], c);
+        for (int e = 0; e < kQuad; ++e) {
+            float g = g4[e] * c.s;
+            if constexpr (EXT) {
+                if (clip < 1.0f) g = g * clip;
+            }
+            adamw_element(g, w[e], m[e], v[e], c);
+        }
         store16(W + e0, f32x4{w[0], w[1], w[2], w[3]});
         store16(M + e0, f32x4{m[0], m[1], m[2], m[3]});
         store16(V + e0, f32x4{v[0], v[1], v[2], v[3]});
@@ -377,24 +409,52 @@ adamw_quad_kernel(const float *__restrict__ acc, float *__restrict__ W, float *_
     }
 }
 
-template <int WDT, bool SKIP>
+template <int WDT, bool SKIP, bool EXT>
 __global__ void __launch_bounds__(kBlock)
 adamw_scalar_kernel(const float *__restrict__ acc, float *__restrict__ W, float *__restrict__ M,
                     float *__restrict__ V, uint16_t *__restrict__ out, int64_t len, Consts c,
-                    const uint32_t *__restrict__ skip) {
+                    const uint32_t *__restrict__ skip, Control ctl) {
     if constexpr (SKIP) {
         if (*skip != 0u) return;
     }
+    float clip = 1.0f;
+    if constexpr (EXT) clip = resolve_controls(ctl, c);
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
     for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < len;
          j += stride) {
         float w = W[j], m = M[j], v = V[j];
-        adamw_element(acc[j] * c.s, w, m, v, c);
+        float g = acc[j] * c.s;
+        if constexpr (EXT) {
+            if (clip < 1.0f) g = g * clip;
+        }
+        adamw_element(g, w, m, v, c);
         W[j] = w;
         M[j] = m;
         V[j] = v;
         out[j] = narrow1<WDT>(w);
     }
+}
+
+// One step of the dynamic loss scale (one thread).
+__global__ void loss_scale_kernel(zero_loss_scale *__restrict__ st,
+                                  const uint32_t *__restrict__ overflow, double growth,
+                                  double backoff, int32_t interval) {
+    if (blockIdx.x != 0 || threadIdx.x != 0) return;
+    float scale = st->scale;
+    int32_t good = st->good_steps;
+    if (*overflow != 0u) {
+        scale = static_cast<float>(static_cast<double>(scale) * backoff);
+        good = 0;
+    } else {
+        good += 1;
+        if (good >= interval) {
+            const float grown = static_cast<float>(static_cast<double>(scale) * growth);
+            if (!__builtin_isinf(grown)) scale = grown;  // never grows to infinity
+            good = 0;
+        }
+    }
+    st->scale = scale;
+    st->good_steps = good;
 }
 
 // ---------------------------------------------------------------------------
@@ -584,15 +644,16 @@ extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int3
     return launch_status();
 }
 
-extern "C" zero_status zero_shard_adamw(const float *acc, float *master, float *m, float *v,
-                                        void *weight_full, zero_dtype wdt,
-                                        const zero_layout *layout, int32_t rank,
-                                        int64_t shard_off, int64_t len,
-                                        const zero_adamw_hparams *hp, const uint32_t *skip,
-                                        void *stream) {
+namespace {
+
+zero_status adamw_impl(const float *acc, float *master, float *m, float *v, void *weight_full,
+                       zero_dtype wdt, const zero_layout *layout, int32_t rank, int64_t shard_off,
+                       int64_t len, const zero_adamw_hparams *hp, const zero_step_control *ctl,
+                       void *stream) {
     if (!dtype_ok(wdt) || !layout_ok(layout) || !hparams_ok(hp)) return ZERO_EINVAL;
     if (rank < 0 || rank >= layout->n_dp || shard_off < 0 || len < 0 || len > kMaxLen)
         return ZERO_EINVAL;
+    if (ctl && !std::isfinite(ctl->max_norm)) return ZERO_EINVAL;
     if (shard_off > layout->shard || len > layout->shard - shard_off) return ZERO_ERANGE;
     if (len == 0) return ZERO_OK;
     if (!acc || !master || !m || !v || !weight_full) return ZERO_EINVAL;
@@ -600,15 +661,21 @@ extern "C" zero_status zero_shard_adamw(const float *acc, float *master, float *
                      static_cast<int64_t>(rank) * layout->shard + shard_off;
     const Span outs[4] = {span_of(master, len, 4), span_of(m, len, 4), span_of(v, len, 4),
                           span_of(slot, len, 2)};
-    // acc and skip are read only, but no output may overlap them
-    Span ins[2];
+    // acc and the controls are read only, but no output may overlap them
+    const uint32_t *skip = ctl ? ctl->skip : nullptr;
+    Span ins[4];
     int n_in = 0;
     ins[n_in++] = span_of(acc, len, 4);
     if (skip) ins[n_in++] = span_of(skip, 1, 4);
+    if (ctl && ctl->sumsq) ins[n_in++] = span_of(ctl->sumsq, 1, 8);
+    if (ctl && ctl->loss_scale) ins[n_in++] = span_of(ctl->loss_scale, 1, sizeof(zero_loss_scale));
     if (any_alias(outs, 4, nullptr, 0, 0, 0, ins, n_in)) return ZERO_EALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Consts c = make_consts(*hp);
+    const bool ext = ctl && ((ctl->sumsq && ctl->max_norm > 0.0) || ctl->loss_scale);
+    const Control k{ctl ? ctl->sumsq : nullptr, ctl ? ctl->max_norm : 0.0,
+                    ctl ? ctl->loss_scale : nullptr, hp->grad_scale};
     const bool vec = aligned16(acc) && aligned16(master) && aligned16(m) && aligned16(v) &&
                      aligned8(slot);
     const int64_t nquad = vec ? len / kQuad : 0;
@@ -616,18 +683,57 @@ extern "C" zero_status zero_shard_adamw(const float *acc, float *master, float *
     const size_t lds = residency_lds_bytes(kAdamwWavesPerCU, kWave);
     with_dtype(wdt, [&](auto WD) {
         with_bool(skip != nullptr, [&](auto SK) {
-            if (nquad > 0) {
-                adamw_quad_kernel<kWave, WD.value, SK.value>
-                    <<<grid_for(nquad, kWave), kWave, lds, st>>>(acc, master, m, v, slot, nquad,
-                                                                 c, skip);
-            }
-            if (len > done) {
-                adamw_scalar_kernel<WD.value, SK.value><<<grid_for(len - done), kBlock, 0, st>>>(
-                    acc + done, master + done, m + done, v + done, slot + done, len - done, c,
-                    skip);
-            }
+            with_bool(ext, [&](auto EX) {
+                if (nquad > 0) {
+                    adamw_quad_kernel<kWave, WD.value, SK.value, EX.value>
+                        <<<grid_for(nquad, kWave), kWave, lds, st>>>(acc, master, m, v, slot,
+                                                                     nquad, c, skip, k);
+                }
+                if (len > done) {
+                    adamw_scalar_kernel<WD.value, SK.value, EX.value>
+                        <<<grid_for(len - done), kBlock, 0, st>>>(
+                            acc + done, master + done, m + done, v + done, slot + done,
+                            len - done, c, skip, k);
+                }
+            });
         });
     });
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" zero_status zero_shard_adamw(const float *acc, float *master, float *m, float *v,
+                                        void *weight_full, zero_dtype wdt,
+                                        const zero_layout *layout, int32_t rank,
+                                        int64_t shard_off, int64_t len,
+                                        const zero_adamw_hparams *hp, const uint32_t *skip,
+                                        void *stream) {
+    const zero_step_control ctl{skip, nullptr, 0.0, nullptr};
+    return adamw_impl(acc, master, m, v, weight_full, wdt, layout, rank, shard_off, len, hp,
+                      &ctl, stream);
+}
+
+extern "C" zero_status zero_shard_adamw_ex(const float *acc, float *master, float *m, float *v,
+                                           void *weight_full, zero_dtype wdt,
+                                           const zero_layout *layout, int32_t rank,
+                                           int64_t shard_off, int64_t len,
+                                           const zero_adamw_hparams *hp,
+                                           const zero_step_control *ctl, void *stream) {
+    return adamw_impl(acc, master, m, v, weight_full, wdt, layout, rank, shard_off, len, hp, ctl,
+                      stream);
+}
+
+extern "C" zero_status zero_loss_scale_update(zero_loss_scale *state, const uint32_t *overflow,
+                                              double growth, double backoff, int32_t interval,
+                                              void *stream) {
+    if (!state || !overflow || !std::isfinite(growth) || growth < 1.0 || !(backoff > 0.0) ||
+        backoff > 1.0 || interval < 1)
+        return ZERO_EINVAL;
+    if (overlap(span_of(state, 1, sizeof(zero_loss_scale)), span_of(overflow, 1, 4)))
+        return ZERO_EALIAS;
+    loss_scale_kernel<<<1, kWave, 0, static_cast<hipStream_t>(stream)>>>(state, overflow, growth,
+                                                                         backoff, interval);
     return launch_status();
 }
 
