@@ -60,6 +60,9 @@ def lib():
         L.ora_loss_scale_update.argtypes = [vp, vp, ctypes.c_uint32, ctypes.c_double,
                                             ctypes.c_double, ctypes.c_int32]
         L.ora_loss_scale_update.restype = None
+        L.ora_reshard.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, vp, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
+        L.ora_reshard.restype = None
         L.ora_model_state_bytes.argtypes = [ctypes.c_double, ctypes.c_double,
                                             ctypes.c_int, ctypes.c_double]
         L.ora_model_state_bytes.restype = ctypes.c_double
@@ -215,6 +218,20 @@ def step(grads, gdt, n_dp, ld, length, w, m, v, wout, wdt, step, lr=1e-4, beta1=
     hp = _hp(lr, beta1, beta2, eps, weight_decay, grad_scale)
     lib().ora_step(_ptr(grads), gdt, n_dp, ld, length, _ptr(w), _ptr(m), _ptr(v),
                    _ptr(wout), wdt, _ptr(hp), step, _ptr(overflow), _ptr(sumsq))
+
+
+def reshard(src_shards, n, dst_n_dp, dst_rank, dst_align=1):
+    """New rank dst_rank's shard (for dst_n_dp ranks) of the flat vector held
+    as the list of old shards src_shards (equal length numpy arrays)."""
+    src = [np.ascontiguousarray(a) for a in src_shards]
+    dt = src[0].dtype
+    assert all(a.dtype == dt and a.size == src[0].size for a in src)
+    _, _, _, dst_shard = flatten_layout([n], dst_n_dp, dst_align)
+    dst = np.empty(dst_shard, dtype=dt)
+    ptrs = (ctypes.c_void_p * len(src))(*[a.ctypes.data for a in src])
+    lib().ora_reshard(ptrs, len(src), src[0].size, _ptr(dst), dst_shard, dst_rank, n,
+                      dt.itemsize)
+    return dst
 
 
 def model_state_bytes(n, n_dp, stage, k=12):

@@ -364,6 +364,26 @@ void ora_step(const uint16_t *grads, int gdt, int32_t n_dp, int64_t ld,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Re-sharding: element by element, through the flat index. */
+
+void ora_reshard(const void *const *src, int32_t n_src, int64_t src_shard,
+                 void *dst, int64_t dst_shard, int32_t dst_rank, int64_t n,
+                 int32_t elem_bytes) {
+    (void)n_src;
+    for (int64_t j = 0; j < dst_shard; ++j) {
+        int64_t flat = (int64_t)dst_rank * dst_shard + j;
+        unsigned char *d = (unsigned char *)dst + j * elem_bytes;
+        if (flat < n) {
+            int64_t r = flat / src_shard, o = flat % src_shard;
+            const unsigned char *s = (const unsigned char *)src[r] + o * elem_bytes;
+            memcpy(d, s, (size_t)elem_bytes);
+        } else {
+            memset(d, 0, (size_t)elem_bytes);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Accounting.  "ZeRO and FSDP", "Memory per GPU": weights 2N, gradients 2N,
  * optimizer K N; stage 1 divides the optimizer term by n_dp, stage 2 also
  * the gradients, stage 3 also the weights. */

@@ -124,6 +124,18 @@ void ora_step(const uint16_t *grads, int gdt, int32_t n_dp, int64_t ld,
               int wdt, const double hp6[6], int64_t step, uint32_t *overflow,
               double *sumsq);
 
+/* ---- re-sharding (checkpoint conversion) ----------------------------------
+ * "ZeRO Optimizer, in depth", "Checkpoints: sharded on the way in,
+ * consolidated on the way out": a sharded checkpoint is tied to its layout;
+ * converting it to another GPU count (or consolidating it) moves each flat
+ * element to its new place.  src[r] is old rank r's shard of src_shard
+ * elements (n_src of them); dst receives new rank dst_rank's shard of
+ * dst_shard elements: dst[j] = flat[dst_rank * dst_shard + j] for flat
+ * indices below n, 0 beyond.  elem_bytes is 2 or 4. */
+void ora_reshard(const void *const *src, int32_t n_src, int64_t src_shard,
+                 void *dst, int64_t dst_shard, int32_t dst_rank, int64_t n,
+                 int32_t elem_bytes);
+
 /* ---- accounting ----------------------------------------------------------
  * Model-state bytes per GPU for stage 0..3 with 2-byte weights and grads and
  * K bytes of optimizer state per parameter; -1 for any other stage. */

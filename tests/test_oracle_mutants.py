@@ -22,6 +22,7 @@ PINS_LAYOUT = ["tests/test_oracle_layout.py"]
 PINS_ACCT = ["tests/test_oracle_accounting.py"]
 PINS_CONVERT = ["tests/test_oracle_convert.py"]
 PINS_CONTROL = ["tests/test_oracle_control.py"]
+PINS_RESHARD = ["tests/test_oracle_reshard.py"]
 
 # (name, original text, planted text, pin files that must catch it)
 MUTANTS = [
@@ -66,6 +67,12 @@ MUTANTS = [
      PINS_CONTROL),
     ("dynamic_scale_multiplied", "c[0] = (float)(hp6[5] / (double)*loss_scale);",
      "c[0] = (float)(hp6[5] * (double)*loss_scale);", PINS_CONTROL),
+    ("reshard_rank_offset", "int64_t flat = (int64_t)dst_rank * dst_shard + j;",
+     "int64_t flat = (int64_t)dst_rank * src_shard + j;", PINS_RESHARD),
+    ("reshard_padding_not_zeroed", "memset(d, 0, (size_t)elem_bytes);",
+     "memcpy(d, (const unsigned char *)src[0], (size_t)elem_bytes);", PINS_RESHARD),
+    ("reshard_half_elements", "(const unsigned char *)src[r] + o * elem_bytes;",
+     "(const unsigned char *)src[r] + o * 2;", PINS_RESHARD),
 ]
 
 
@@ -89,7 +96,7 @@ def _run_pins(so, files):
 @pytest.fixture(scope="module")
 def results():
     src = open(SRC).read()
-    jobs = [("unmodified", src, PINS_MATH + PINS_LAYOUT + PINS_ACCT + PINS_CONTROL, None)]
+    jobs = [("unmodified", src, PINS_MATH + PINS_LAYOUT + PINS_ACCT + PINS_CONTROL + PINS_RESHARD, None)]
     for name, old, new, files in MUTANTS:
         assert src.count(old) == 1, f"mutant {name}: its target text must occur once in the oracle"
         jobs.append((name, src.replace(old, new), files, old))
