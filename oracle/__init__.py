@@ -63,6 +63,16 @@ def lib():
         L.ora_reshard.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, vp, ctypes.c_int64,
                                   ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
         L.ora_reshard.restype = None
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.ora_flat_locate.argtypes = [i64p, i64p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                      i64p]
+        L.ora_flat_locate.restype = ctypes.c_int32
+        L.ora_flat_gather.argtypes = [vp, i64p, i64p, ctypes.c_int32, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int64, vp, ctypes.c_int32]
+        L.ora_flat_gather.restype = None
+        L.ora_flat_scatter.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, i64p, i64p,
+                                       ctypes.c_int32, ctypes.c_int32]
+        L.ora_flat_scatter.restype = None
         L.ora_model_state_bytes.argtypes = [ctypes.c_double, ctypes.c_double,
                                             ctypes.c_int, ctypes.c_double]
         L.ora_model_state_bytes.restype = ctypes.c_double
@@ -232,6 +242,43 @@ def reshard(src_shards, n, dst_n_dp, dst_rank, dst_align=1):
     lib().ora_reshard(ptrs, len(src), src[0].size, _ptr(dst), dst_shard, dst_rank, n,
                       dt.itemsize)
     return dst
+
+
+def _i64s(xs):
+    return (ctypes.c_int64 * max(1, len(xs)))(*[int(x) for x in xs])
+
+
+def flat_locate(pieces, n, i):
+    """(k, off) of flat index i among pieces [(flat_off, len), ...], or
+    (-1, None) when i >= n or no piece holds it."""
+    off = ctypes.c_int64(0)
+    k = lib().ora_flat_locate(_i64s([p[0] for p in pieces]), _i64s([p[1] for p in pieces]),
+                              len(pieces), n, i, ctypes.byref(off))
+    return (k, off.value) if k >= 0 else (-1, None)
+
+
+def flat_gather(sources, n, begin, count):
+    """dst[j] = flat[begin + j], 0 outside the pieces or beyond n.
+    sources: [(array, flat_off), ...], each array one piece."""
+    arrs = [np.ascontiguousarray(a) for a, _ in sources]
+    dt = arrs[0].dtype
+    assert all(a.dtype == dt for a in arrs)
+    dst = np.empty(count, dtype=dt)
+    ptrs = (ctypes.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+    lib().ora_flat_gather(ptrs, _i64s([o for _, o in sources]), _i64s([a.size for a in arrs]),
+                          len(arrs), n, begin, count, _ptr(dst), dt.itemsize)
+    return dst
+
+
+def flat_scatter(src, begin, dests):
+    """Writes src (flat indices [begin, begin + src.size)) into the pieces
+    dests [(array, flat_off), ...] in place, where they hold those indices."""
+    src = np.ascontiguousarray(src)
+    for a, _ in dests:
+        assert a.dtype == src.dtype and a.flags.c_contiguous
+    ptrs = (ctypes.c_void_p * len(dests))(*[a.ctypes.data for a, _ in dests])
+    lib().ora_flat_scatter(_ptr(src), begin, src.size, ptrs, _i64s([o for _, o in dests]),
+                           _i64s([a.size for a, _ in dests]), len(dests), src.dtype.itemsize)
 
 
 def model_state_bytes(n, n_dp, stage, k=12):

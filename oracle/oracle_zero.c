@@ -18,6 +18,10 @@
  *    gradient closed form, a high-precision brute force on tiny inputs, and
  *    sharded == unsharded.
  *  - ora_model_state_bytes / ora_comm_bytes: the numbers the pages print.
+ *  - ora_reshard / ora_flat_*: slicing and concatenation of the flat vector
+ *    in numpy, agreement of the two independent forms (equal shards against
+ *    general pieces), round trips n_dp -> n_dp' -> n_dp, scatter after
+ *    gather, and consolidation recovering every parameter tensor.
  * ora_step's sumsq output is order dependent and checked only against a
  * float64 sum within a bound (parity unpinned bitwise by design).
  */
@@ -380,6 +384,45 @@ void ora_reshard(const void *const *src, int32_t n_src, int64_t src_shard,
         } else {
             memset(d, 0, (size_t)elem_bytes);
         }
+    }
+}
+
+int32_t ora_flat_locate(const int64_t *flat_off, const int64_t *len,
+                        int32_t n_src, int64_t n, int64_t i, int64_t *off) {
+    if (i < 0 || i >= n) return -1;
+    for (int32_t k = 0; k < n_src; ++k) {
+        if (i >= flat_off[k] && i - flat_off[k] < len[k]) {
+            *off = i - flat_off[k];
+            return k;
+        }
+    }
+    return -1;
+}
+
+void ora_flat_gather(const void *const *src, const int64_t *flat_off,
+                     const int64_t *len, int32_t n_src, int64_t n,
+                     int64_t begin, int64_t count, void *dst,
+                     int32_t elem_bytes) {
+    for (int64_t j = 0; j < count; ++j) {
+        unsigned char *d = (unsigned char *)dst + j * elem_bytes;
+        int64_t off = 0;
+        int32_t k = ora_flat_locate(flat_off, len, n_src, n, begin + j, &off);
+        if (k >= 0)
+            memcpy(d, (const unsigned char *)src[k] + off * elem_bytes, (size_t)elem_bytes);
+        else
+            memset(d, 0, (size_t)elem_bytes);
+    }
+}
+
+void ora_flat_scatter(const void *src, int64_t begin, int64_t count,
+                      void *const *dst, const int64_t *flat_off,
+                      const int64_t *len, int32_t n_dst, int32_t elem_bytes) {
+    for (int64_t j = 0; j < count; ++j) {
+        int64_t off = 0;
+        int32_t k = ora_flat_locate(flat_off, len, n_dst, INT64_MAX, begin + j, &off);
+        if (k >= 0)
+            memcpy((unsigned char *)dst[k] + off * elem_bytes,
+                   (const unsigned char *)src + j * elem_bytes, (size_t)elem_bytes);
     }
 }
 

@@ -136,6 +136,25 @@ void ora_reshard(const void *const *src, int32_t n_src, int64_t src_shard,
                  void *dst, int64_t dst_shard, int32_t dst_rank, int64_t n,
                  int32_t elem_bytes);
 
+/* The general form, for flattening, unflattening and partial checkpoints.
+ * A "flat set" is n_src pieces of the flat vector, piece k holding flat
+ * indices [flat_off[k], flat_off[k] + len[k]) in src[k] (pieces that do not
+ * overlap).  ora_flat_locate returns the piece that holds flat index i
+ * (setting *off to the index inside it), or -1 when i >= n or no piece does.
+ * ora_flat_gather: dst[j] = flat[begin + j] for j < count, 0 where
+ * ora_flat_locate gives -1.  ora_flat_scatter is the inverse: for every flat
+ * index i in [begin, begin + count) that piece k holds, dst[k] at i's place
+ * receives src[i - begin]; nothing else is written. */
+int32_t ora_flat_locate(const int64_t *flat_off, const int64_t *len,
+                        int32_t n_src, int64_t n, int64_t i, int64_t *off);
+void ora_flat_gather(const void *const *src, const int64_t *flat_off,
+                     const int64_t *len, int32_t n_src, int64_t n,
+                     int64_t begin, int64_t count, void *dst,
+                     int32_t elem_bytes);
+void ora_flat_scatter(const void *src, int64_t begin, int64_t count,
+                      void *const *dst, const int64_t *flat_off,
+                      const int64_t *len, int32_t n_dst, int32_t elem_bytes);
+
 /* ---- accounting ----------------------------------------------------------
  * Model-state bytes per GPU for stage 0..3 with 2-byte weights and grads and
  * K bytes of optimizer state per parameter; -1 for any other stage. */

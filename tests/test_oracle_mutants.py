@@ -69,8 +69,15 @@ MUTANTS = [
      "c[0] = (float)(hp6[5] * (double)*loss_scale);", PINS_CONTROL),
     ("reshard_rank_offset", "int64_t flat = (int64_t)dst_rank * dst_shard + j;",
      "int64_t flat = (int64_t)dst_rank * src_shard + j;", PINS_RESHARD),
-    ("reshard_padding_not_zeroed", "memset(d, 0, (size_t)elem_bytes);",
-     "memcpy(d, (const unsigned char *)src[0], (size_t)elem_bytes);", PINS_RESHARD),
+    ("reshard_padding_not_zeroed", "} else {\n            memset(d, 0, (size_t)elem_bytes);",
+     "} else {\n            memcpy(d, (const unsigned char *)src[0], (size_t)elem_bytes);",
+     PINS_RESHARD),
+    ("locate_inclusive_end", "i - flat_off[k] < len[k]", "i - flat_off[k] <= len[k]", PINS_RESHARD),
+    ("locate_ignores_n", "if (i < 0 || i >= n) return -1;", "if (i < 0) return -1;", PINS_RESHARD),
+    ("scatter_range_from_zero", "n_dst, INT64_MAX, begin + j, &off)", "n_dst, INT64_MAX, j, &off)",
+     PINS_RESHARD),
+    ("gather_holes_not_zeroed", "else\n            memset(d, 0, (size_t)elem_bytes);",
+     "else\n            memset(d, 1, (size_t)elem_bytes);", PINS_RESHARD),
     ("reshard_half_elements", "(const unsigned char *)src[r] + o * elem_bytes;",
      "(const unsigned char *)src[r] + o * 2;", PINS_RESHARD),
 ]
