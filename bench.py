@@ -47,6 +47,11 @@ def parse():
                    help="CPU baseline sample: 2^k parameters of the shard")
     p.add_argument("--cpu-steps", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--op", choices=["step", "reshard", "consolidate"], default="step",
+                   help="step: the optimizer step (default); reshard: new rank 5 of 16's "
+                        "shard of the 7B fp32 master, m and v from the 8-rank shards; "
+                        "consolidate: the 8-rank fp32 master shards scattered into the "
+                        "7B model's 291 per-parameter fp32 tensors")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (the known-size "
                         "reference that scales the HBM byte counters) --steps times and exit")
@@ -100,6 +105,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, args.steps)
+        return
+    if args.op != "step":
+        bench_copies(args)
         return
 
     import numpy as np
@@ -242,6 +250,147 @@ def main():
         line["cpu_baseline"] = cpu_baseline(wl, S, rank, args.cpu_sample_log2, args.cpu_steps)
 
     print(json.dumps(line), flush=True)
+
+
+def bench_copies(args):
+    """Checkpoint conversion on the device ("ZeRO Optimizer, in depth",
+    "Checkpoints: sharded on the way in, consolidated on the way out"):
+    bitwise copies, 8 bytes of HBM traffic per fp32 element (4 read, 4
+    written).  A step converts one rank's worth of state."""
+    import torch
+
+    import synth
+    import zero_sharded_mixed_flatten_amd as zs
+    from synth import F32
+    from synth.synth_const import BUF_M, BUF_MASTER, BUF_V
+    from synth.workloads import llama7b_numels
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    numels = llama7b_numels()
+    old, offs = zs.zero_flatten_layout(numels, 8, 8)
+    n, s8 = old.n, old.shard
+    stream = torch.cuda.current_stream(dev)
+    events = []
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        return e0, e1
+
+    if args.op == "reshard":
+        new, _ = zs.zero_flatten_layout(numels, 16, 8)
+        rank, s16 = 5, new.shard
+        bufs = (BUF_MASTER, BUF_M, BUF_V)
+        src = [[torch.empty(s8, device=dev) for _ in range(8)] for _ in bufs]
+        for arr, b in zip(src, bufs):
+            for r, t in enumerate(arr):
+                synth.fill_device(t, F32, 1, synth.tag(b, 9), r * s8, 0.02)
+        dst = [torch.empty(s16, device=dev) for _ in bufs]
+
+        def step(record):
+            for arr, d in zip(src, dst):
+                call = lambda: zs.zero_reshard(arr, n, rank, d, stream=stream)
+                if record:
+                    events.append(timed(call))
+                else:
+                    call()
+        elems_per_step, launches = 3 * s16, 3
+        workload = "llama7b_fp32_state_reshard_8to16_rank5"
+        metric = "re-shard of one rank's fp32 master, m and v, 7B model, 8 to 16 ranks"
+        cfg = {"from_n_dp": 8, "to_n_dp": 16, "rank": rank, "arrays": 3, "shard": s16}
+    else:
+        src = [torch.empty(s8, device=dev) for _ in range(8)]
+        for r, t in enumerate(src):
+            synth.fill_device(t, F32, 1, synth.tag(BUF_MASTER, 9), r * s8, 0.02)
+        tensors = [torch.empty(k, device=dev) for k in numels]
+        pieces = list(zip(tensors, [int(o) for o in offs]))
+
+        def step(record):
+            for r in range(8):
+                call = lambda: zs.zero_flat_scatter(src[r], r * s8, pieces, stream=stream)
+                if record:
+                    events.append(timed(call))
+                else:
+                    call()
+        elems_per_step, launches = n, 8
+        workload = "llama7b_fp32_master_consolidate_8"
+        metric = "consolidation of the 7B fp32 master from 8 shards into per-parameter tensors"
+        cfg = {"from_n_dp": 8, "tensors": len(numels), "n_params": n}
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = [a.elapsed_time(b) for a, b in events]
+    launch_bytes = 8 * elems_per_step / launches
+    k_avg = statistics.fmean(kms)
+    achieved = launch_bytes / (k_avg * 1e-3) / 1e9
+    line = {
+        "metric": metric, "value": elems_per_step * args.steps / wall, "unit": "elements/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "hbm_gbps": 8 * elems_per_step * args.steps / wall / 1e9,
+        "hbm_frac": 8 * elems_per_step * args.steps / wall / 1e9 / HBM_PEAK_GBPS,
+        "config": dict(workload=workload, **cfg),
+        "roofline": {"bound": "hbm", "kernel": "flat_copy_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "launch_ms_avg": k_avg, "launch_ms_min": min(kms),
+                     "algorithmic_bytes_per_launch": launch_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del src
+        torch.cuda.empty_cache()
+        line["cpu_baseline"] = cpu_baseline_copy(args.op, s8, n)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_copy(op, s8, n):
+    """The oracle's element-by-element copies on a bounded sample (about
+    10 s, single-threaded).  reshard: new rank 5 of 16 built from 8 old
+    shards of 2^24 elements (the sample's new shard straddles two old ones,
+    as rank 5 of 16 does).  consolidate: the first 2^22 elements of old
+    shard 0 scattered into the 7B model's 291 parameter tensors."""
+    import numpy as np
+
+    import oracle
+    from synth.workloads import llama7b_numels
+    t0 = time.perf_counter()
+    reps = 0
+    if op == "reshard":
+        sample = 1 << 24
+        per_call = sample // 2
+        old = [np.full(sample, r, np.float32) for r in range(8)]
+        while time.perf_counter() - t0 < 10.0:
+            oracle.reshard(old, 8 * sample, 16, 5)
+            reps += 1
+        what = f"new rank 5 of 16 from 8 old shards of {sample} fp32 elements"
+    else:
+        per_call = 1 << 22
+        numels = llama7b_numels()
+        offs = np.concatenate([[0], np.cumsum(numels)[:-1]])
+        keep = [i for i, o in enumerate(offs) if o < per_call]
+        dests = [(np.zeros(numels[i], np.float32), int(offs[i])) for i in keep]
+        src = np.ones(per_call, np.float32)
+        while time.perf_counter() - t0 < 10.0:
+            oracle.flat_scatter(src, 0, dests)
+            reps += 1
+        what = f"the first {per_call} elements of shard 0 into the parameter tensors they cover"
+    dt = time.perf_counter() - t0
+    return {"value": reps * per_call / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what} ({per_call} elements per call, {reps} calls, single-threaded C "
+                      f"oracle, {dt:.1f} s)"}
 
 
 def cpu_baseline(wl, S, rank, log2n, steps):

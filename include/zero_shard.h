@@ -35,7 +35,7 @@
  *  - Arguments are validated on the host before anything is launched; on any
  *    error status nothing is launched and nothing is written.
  *  - Element counts and offsets are in elements, never bytes; one call
- *    processes at most 2^39 elements (EINVAL beyond).
+ *    processes at most 2^38 elements (EINVAL beyond).
  *  - Element j of the processed range is independent of every other element:
  *    any range can be processed by one call or split over several calls
  *    (buckets) with identical results.
@@ -279,6 +279,64 @@ ZERO_API zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_t 
                             const zero_layout *layout, int32_t rank,
                             int64_t shard_off, const zero_adamw_hparams *hp,
                             uint32_t *overflow, double *sumsq, void *stream);
+
+/* ---- moving flat ranges: flatten, unflatten, re-shard (device) -----------
+ * A sharded checkpoint is tied to the layout it was written with; resuming
+ * on another number of GPUs, or consolidating the shards into one set of
+ * per-parameter tensors, needs each flat element moved to its new place
+ * ("ZeRO Optimizer, in depth", "Checkpoints: sharded on the way in,
+ * consolidated on the way out", and its list of failure modes: resuming
+ * after a change of GPU count).  The same copies flatten parameter tensors
+ * into a rank's shard.  All of them move flat ranges between "pieces":
+ *
+ * One piece of the flat vector: flat indices [flat_off, flat_off + len)
+ * held contiguously at ptr (device memory, aligned to the element size).
+ * The pieces passed to one call must not overlap in flat index. */
+typedef struct zero_piece {
+    void *ptr;
+    int64_t flat_off;
+    int64_t len;
+} zero_piece;
+
+/* dst[j] = flat[begin + j] for j in [0, count): the element of the piece
+ * that holds flat index begin + j, or 0 where no piece holds it or the index
+ * is >= n (holes and padding read as zeros).
+ *   src:  host array of n_src piece descriptors (read only; their memory
+ *         is read only).  elem_bytes: 2 or 4 (16-bit or fp32 data; the copy
+ *         is bitwise).  dst: device, count elements.
+ * EINVAL: elem_bytes not 2 or 4; n, begin, count or a piece's flat_off or
+ * len negative; count > 2^38; an index range overflowing int64; a NULL
+ * pointer where len or count > 0; a pointer not aligned to elem_bytes;
+ * pieces that overlap in flat index.  EALIAS: dst overlaps a piece's
+ * memory.  count == 0 is a no-op. */
+ZERO_API zero_status zero_flat_gather(const zero_piece *src, int32_t n_src,
+                                      int64_t n, int32_t elem_bytes,
+                                      int64_t begin, int64_t count, void *dst,
+                                      void *stream);
+
+/* The inverse: src[j] holds flat index begin + j for j in [0, count); every
+ * piece of dst receives the elements of that range it holds, and nothing
+ * else of any piece is written.
+ * EINVAL as for zero_flat_gather.  EALIAS: two pieces overlap in memory, or
+ * a piece overlaps src. */
+ZERO_API zero_status zero_flat_scatter(const void *src, int64_t begin,
+                                       int64_t count, const zero_piece *dst,
+                                       int32_t n_dst, int32_t elem_bytes,
+                                       void *stream);
+
+/* Re-shard: old rank r's shard of src_shard elements is at src_shards[r]
+ * (host array of n_src device pointers, flat indices [r * src_shard,
+ * (r + 1) * src_shard)); dst (device, dst_shard elements) receives new rank
+ * dst_rank's shard, flat indices [dst_rank * dst_shard, ... + dst_shard),
+ * with zeros from flat index n on.  Consolidation is dst_rank = 0 with
+ * dst_shard >= n.  Equal to zero_flat_gather over those pieces.
+ * EINVAL: n_src < 1, src_shard < 0, n outside [0, n_src * src_shard],
+ * dst_rank < 0, dst_shard < 0, and as for zero_flat_gather.  EALIAS: dst
+ * overlaps an old shard. */
+ZERO_API zero_status zero_reshard(const void *const *src_shards, int32_t n_src,
+                                  int64_t src_shard, int64_t n,
+                                  int32_t elem_bytes, int32_t dst_rank,
+                                  int64_t dst_shard, void *dst, void *stream);
 
 /* ---- accounting (host only) ----------------------------------------------
  * Model-state bytes per GPU at ZeRO stage 0..3 for n parameters on n_dp

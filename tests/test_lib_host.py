@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     lib = ctypes.CDLL(zs.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -224,3 +224,54 @@ def test_controls_reject_bad_arguments():
     assert A(*base, ctypes.byref(ctl), None) == zs.ZERO_EINVAL
     ctl = zs._StepControl(None, None, 0.0, P(BASE + (2 << 30) + 100).value)  # loss scale inside m
     assert A(*base, ctypes.byref(ctl), None) == zs.ZERO_EALIAS
+
+
+def _pc(*pieces):
+    arr = (zs._Piece * max(1, len(pieces)))()
+    for i, (ptr, off, ln) in enumerate(pieces):
+        arr[i] = zs._Piece(ptr, off, ln)
+    return arr, len(pieces)
+
+
+@cpu_only
+def test_flat_copies_reject_bad_arguments():
+    G, S, RS = L.zero_flat_gather, L.zero_flat_scatter, L.zero_reshard
+    dst = P(BASE + (8 << 30))
+    ok, n_ok = _pc((BASE, 0, 100), (BASE + 4096, 100, 50))
+    assert G(ok, n_ok, 150, 3, 0, 10, dst, None) == zs.ZERO_EINVAL             # elem size 3
+    assert G(ok, n_ok, -1, 4, 0, 10, dst, None) == zs.ZERO_EINVAL              # n < 0
+    assert G(ok, n_ok, 150, 4, -1, 10, dst, None) == zs.ZERO_EINVAL            # begin < 0
+    assert G(ok, n_ok, 150, 4, 0, -1, dst, None) == zs.ZERO_EINVAL             # count < 0
+    assert G(ok, n_ok, 150, 4, 0, (1 << 38) + 1, dst, None) == zs.ZERO_EINVAL  # too long
+    assert G(ok, n_ok, 150, 4, (1 << 63) - 5, 10, dst, None) == zs.ZERO_EINVAL  # index overflow
+    assert G(ok, n_ok, 150, 4, 0, 10, None, None) == zs.ZERO_EINVAL
+    assert G(ok, n_ok, 150, 4, 0, 10, P(BASE + (8 << 30) + 2), None) == zs.ZERO_EINVAL  # misaligned
+    assert G(None, 2, 150, 4, 0, 10, dst, None) == zs.ZERO_EINVAL
+    ov, n_ov = _pc((BASE, 0, 100), (BASE + 4096, 99, 50))                      # flat overlap
+    assert G(ov, n_ov, 150, 4, 0, 10, dst, None) == zs.ZERO_EINVAL
+    nul, n_nul = _pc((None, 0, 100),)
+    assert G(nul, n_nul, 150, 4, 0, 10, dst, None) == zs.ZERO_EINVAL
+    mis, n_mis = _pc((BASE + 2, 0, 100),)
+    assert G(mis, n_mis, 150, 4, 0, 10, dst, None) == zs.ZERO_EINVAL
+    neg, n_neg = _pc((BASE, -5, 100),)
+    assert G(neg, n_neg, 150, 4, 0, 10, dst, None) == zs.ZERO_EINVAL
+    assert G(ok, n_ok, 150, 4, 0, 10, P(BASE + 396), None) == zs.ZERO_EALIAS   # dst on a piece
+    # empty requests need no buffers; empty pieces may be NULL
+    assert G(ok, n_ok, 150, 4, 0, 0, None, None) == zs.ZERO_OK
+    emp, n_emp = _pc((None, 0, 0), (None, 0, 0))
+    assert G(emp, n_emp, 150, 4, 0, 0, None, None) == zs.ZERO_OK
+    src = P(BASE + (9 << 30))
+    assert S(src, 0, 10, ov, n_ov, 4, None) == zs.ZERO_EINVAL
+    mem, n_mem = _pc((BASE, 0, 100), (BASE + 200, 100, 50))                    # memory overlap
+    assert S(src, 0, 10, mem, n_mem, 4, None) == zs.ZERO_EALIAS
+    assert S(P(BASE + 40), 0, 10, ok, n_ok, 4, None) == zs.ZERO_EALIAS          # src in a piece
+    assert S(None, 0, 10, ok, n_ok, 4, None) == zs.ZERO_EINVAL
+    assert S(None, 0, 0, ok, n_ok, 4, None) == zs.ZERO_OK
+    sh = (P * 2)(P(BASE), P(BASE + (1 << 30)))
+    assert RS(sh, 0, 100, 150, 4, 0, 75, dst, None) == zs.ZERO_EINVAL          # no old shards
+    assert RS(sh, 2, 100, 201, 4, 0, 75, dst, None) == zs.ZERO_EINVAL          # n > n_src * shard
+    assert RS(sh, 2, -1, 0, 4, 0, 75, dst, None) == zs.ZERO_EINVAL
+    assert RS(sh, 2, 100, 150, 4, -1, 75, dst, None) == zs.ZERO_EINVAL
+    assert RS(sh, 2, 100, 150, 4, 1, -75, dst, None) == zs.ZERO_EINVAL
+    assert RS(sh, 2, 100, 150, 4, 0, 75, P(BASE + 40), None) == zs.ZERO_EALIAS
+    assert RS(sh, 2, 100, 150, 4, 0, 0, None, None) == zs.ZERO_OK

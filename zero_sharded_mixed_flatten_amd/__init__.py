@@ -55,6 +55,10 @@ class _StepControl(ctypes.Structure):
                 ("max_norm", ctypes.c_double), ("loss_scale", ctypes.c_void_p)]
 
 
+class _Piece(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("flat_off", ctypes.c_int64), ("len", ctypes.c_int64)]
+
+
 class _Segment(ctypes.Structure):
     _fields_ = [("tensor", ctypes.c_int64), ("tensor_off", ctypes.c_int64),
                 ("shard_off", ctypes.c_int64), ("len", ctypes.c_int64)]
@@ -105,6 +109,13 @@ def _load():
     L.zero_shard_step.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, ctypes.c_int,
                                   lay_p, i32, i64, hp_p, vp, vp, vp]
     L.zero_shard_step.restype = ctypes.c_int
+    piece_p = ctypes.POINTER(_Piece)
+    L.zero_flat_gather.argtypes = [piece_p, i32, i64, i32, i64, i64, vp, vp]
+    L.zero_flat_gather.restype = ctypes.c_int
+    L.zero_flat_scatter.argtypes = [vp, i64, i64, piece_p, i32, i32, vp]
+    L.zero_flat_scatter.restype = ctypes.c_int
+    L.zero_reshard.argtypes = [ctypes.POINTER(vp), i32, i64, i64, i32, i32, i64, vp, vp]
+    L.zero_reshard.restype = ctypes.c_int
     L.zero_model_state_bytes.argtypes = [dbl, dbl, i32, dbl, ctypes.POINTER(dbl)]
     L.zero_model_state_bytes.restype = ctypes.c_int
     L.zero_comm_bytes.argtypes = [dbl, dbl, i32, dbl, dbl, ctypes.POINTER(dbl)]
@@ -268,6 +279,55 @@ def zero_shard_step(grads, ld: int, length: int, master, m, v, weight_full,
         _dev_ptr(sumsq, "sumsq", torch.float64), _stream(stream, master)), "zero_shard_step")
 
 
+def _elem_bytes(ts, what: str) -> int:
+    sizes = {t.element_size() for t in ts}
+    if len(sizes) != 1:
+        raise TypeError(f"{what}: all tensors must have one element size, got {sorted(sizes)}")
+    for t in ts:
+        if not t.is_contiguous():
+            raise TypeError(f"{what}: contiguous tensors expected")
+    return sizes.pop()
+
+
+def _pieces(pieces, what: str):
+    arr = (_Piece * max(1, len(pieces)))()
+    for i, (t, off) in enumerate(pieces):
+        arr[i] = _Piece(_dev_ptr(t, what), int(off), t.numel())
+    return arr
+
+
+def zero_flat_gather(pieces, n: int, begin: int, dst, stream=None):
+    """dst[j] = flat[begin + j] for j < dst.numel(), from pieces
+    [(tensor, flat_off), ...]; zeros where no piece holds the index or it is
+    >= n.  Bitwise, for 2- or 4-byte elements."""
+    eb = _elem_bytes([dst] + [t for t, _ in pieces], "zero_flat_gather")
+    _check(_lib.zero_flat_gather(_pieces(pieces, "piece"), len(pieces), n, eb, begin,
+                                 dst.numel(), _dev_ptr(dst, "dst"), _stream(stream, dst)),
+           "zero_flat_gather")
+
+
+def zero_flat_scatter(src, begin: int, pieces, stream=None):
+    """Writes src (flat indices [begin, begin + src.numel())) into the pieces
+    [(tensor, flat_off), ...] where they hold those indices."""
+    eb = _elem_bytes([src] + [t for t, _ in pieces], "zero_flat_scatter")
+    _check(_lib.zero_flat_scatter(_dev_ptr(src, "src"), begin, src.numel(),
+                                  _pieces(pieces, "piece"), len(pieces), eb,
+                                  _stream(stream, src)), "zero_flat_scatter")
+
+
+def zero_reshard(src_shards, n: int, dst_rank: int, dst, stream=None):
+    """dst (one shard of dst.numel() elements) = new rank dst_rank's shard of
+    the flat vector of n elements held as the equal old shards src_shards."""
+    eb = _elem_bytes([dst] + list(src_shards), "zero_reshard")
+    sizes = {t.numel() for t in src_shards}
+    if len(sizes) != 1:
+        raise ValueError("zero_reshard: the old shards must have one size")
+    ptrs = (ctypes.c_void_p * len(src_shards))(*[_dev_ptr(t, "src_shard").value
+                                                 for t in src_shards])
+    _check(_lib.zero_reshard(ptrs, len(src_shards), sizes.pop(), n, eb, dst_rank, dst.numel(),
+                             _dev_ptr(dst, "dst"), _stream(stream, dst)), "zero_reshard")
+
+
 def zero_model_state_bytes(n: float, n_dp: float, stage: int, k: float = 12) -> float:
     out = ctypes.c_double()
     _check(_lib.zero_model_state_bytes(n, n_dp, stage, k, ctypes.byref(out)),
@@ -289,5 +349,6 @@ def library_path() -> str:
 
 __all__ = ["zero_flatten_layout", "zero_shard_segments", "zero_shard_reduce",
            "zero_shard_adamw", "zero_shard_adamw_ex", "zero_loss_scale_update",
-           "new_loss_scale", "read_loss_scale", "zero_shard_step", "zero_model_state_bytes", "zero_comm_bytes",
+           "new_loss_scale", "read_loss_scale", "zero_shard_step", "zero_flat_gather",
+           "zero_flat_scatter", "zero_reshard", "zero_model_state_bytes", "zero_comm_bytes",
            "AdamWHParams", "ZeroLayout", "ZeroError", "ZERO_BF16", "ZERO_FP16", "library_path"]

@@ -40,9 +40,12 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "host_common.h"
 #include "zero_shard.h"
 
 namespace {
+
+using namespace zero_host;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -50,7 +53,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWave = 64;       // wave64
 constexpr int kBlock = 256;     // threads per workgroup of the element kernels and of
                                 // streaming kernels that also sum squares
 constexpr int kQuad = 4;        // elements per lane
@@ -525,20 +527,6 @@ Consts make_consts(const zero_adamw_hparams &hp) {
     return c;
 }
 
-// byte ranges, for the disjointness checks
-struct Span {
-    uintptr_t lo, hi;
-};
-
-Span span_of(const void *p, int64_t count, int64_t elem) {
-    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-    return Span{lo, lo + static_cast<uintptr_t>(count) * static_cast<uintptr_t>(elem)};
-}
-
-bool overlap(const Span &a, const Span &b) {
-    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
-}
-
 // true when any two outputs overlap, or an output overlaps a gradient row
 bool any_alias(const Span *outs, int n_out, const void *rows, int n_rows, int64_t ld,
                int64_t len, const Span *ins = nullptr, int n_in = 0) {
@@ -555,37 +543,10 @@ bool any_alias(const Span *outs, int n_out, const void *rows, int n_rows, int64_
     return false;
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
-
 // one thread per item; kMaxLen keeps the count below 2^31 workgroups
 unsigned grid_for(int64_t items, int tpb = kBlock) {
     const int64_t b = (items + tpb - 1) / tpb;
     return static_cast<unsigned>(b < 1 ? 1 : b);
-}
-
-// Dynamic LDS requested by a streaming kernel of tpb threads per workgroup
-// so that about waves_per_cu of its waves are resident on a CU (the LDS
-// itself is unused).
-size_t residency_lds_bytes(int waves_per_cu, int tpb) {
-    const int wave_per_wg = tpb / kWave;
-    int wg_per_cu = (waves_per_cu + wave_per_wg / 2) / wave_per_wg;
-    if (wg_per_cu < 1) wg_per_cu = 1;
-    int dev = 0, per_cu = 0, per_block = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
-                              dev) != hipSuccess ||
-        hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
-            hipSuccess)
-        return 0;
-    // leave 1 KiB per workgroup for the kernels' own static LDS
-    int64_t b = (static_cast<int64_t>(per_cu) / wg_per_cu - 1024) & ~int64_t(255);
-    if (b > per_block) b = per_block & ~255;
-    return b > 0 ? static_cast<size_t>(b) : 0;
-}
-
-zero_status launch_status() {
-    return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EDEVICE;
 }
 
 // rows of the gradient slab all fit in int64 and do not wrap
