@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "zero_sharded_mixed_flatten_amd", "csrc", "zero_shard.hip")
+COPY_SOURCE = os.path.join(ROOT, "zero_sharded_mixed_flatten_amd", "csrc", "flat_copy.hip")
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -72,11 +73,11 @@ def calibrate_copy(mib, steps):
                       "bytes_written_per_launch": n, "launches": steps}), flush=True)
 
 
-def source_digest():
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+def source_digest(source=KERNEL_SOURCE):
+    return hashlib.sha256(open(source, "rb").read()).hexdigest()
 
 
-def committed_traffic(workload_name, launches_per_step):
+def committed_traffic(workload_name, source=KERNEL_SOURCE):
     """Counter-measured HBM bytes per launch of the dominant kernel, from the
     committed counter summary -- only if it was taken on this kernel source."""
     path = os.path.join(COUNTERS_DIR, f"{workload_name}.counters.txt")
@@ -87,7 +88,7 @@ def committed_traffic(workload_name, launches_per_step):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != source_digest():
+    if kv.get("kernel_source_sha256") != source_digest(source):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -213,7 +214,7 @@ def main():
     else:
         launch_bytes = 30 * S
     achieved = launch_bytes / (k_avg * 1e-3) / 1e9
-    traffic = committed_traffic(wl.name, 1 if micro == 1 else micro + 1)
+    traffic = committed_traffic(wl.name) if micro == 1 else None
 
     line = {
         "metric": "sharded AdamW step params/s and HBM GB/s (% of 8 TB/s), 7B n_dp=8 shard",
@@ -345,8 +346,8 @@ def bench_copies(args):
         "config": dict(workload=workload, **cfg),
         "roofline": {"bound": "hbm", "kernel": "flat_copy_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "launch_ms_avg": k_avg, "launch_ms_min": min(kms),
-                     "algorithmic_bytes_per_launch": launch_bytes},
+                     "traffic": committed_traffic(workload, COPY_SOURCE), "launch_ms_avg": k_avg,
+                     "launch_ms_min": min(kms), "algorithmic_bytes_per_launch": launch_bytes},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -225,3 +225,55 @@ def test_full_size_reshard_8_to_16_sampled():
         del out
     del old
     torch.cuda.empty_cache()
+
+
+def test_resume_on_another_gpu_count_keeps_the_trajectory():
+    """3 steps on 4 ranks, the state (fp32 master, m, v and the bf16 weight
+    buffer) converted on the device to 3 ranks, 3 more steps: bit-identical
+    to the oracle's unsharded run over the same gradients (the average over
+    4 ranks' rows, then over 3 ranks' rows)."""
+    from tests.gpu_util import dev16, host_master, host_rows
+    from synth import BF16
+    from synth.workloads import GradDraw
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)
+    draw = GradDraw(BF16, 1e-3)
+    n, cfg = 50_001, 122
+    w = host_master(cfg, 0, n)
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    wout = np.zeros(n, np.uint16)
+    state, lay, wf = None, None, None
+    for t in range(1, 7):
+        n_dp = 4 if t <= 3 else 3
+        new_lay, _ = zs.zero_flatten_layout([n], n_dp, 8)
+        s = new_lay.shard
+        if state is None:
+            state = [[torch.from_numpy(host_master(cfg, r * s, s, pad_from=n)).cuda()
+                      for r in range(n_dp)], [torch.zeros(s, device="cuda") for _ in range(n_dp)],
+                     [torch.zeros(s, device="cuda") for _ in range(n_dp)]]
+            wf = torch.zeros(new_lay.n_pad, dtype=torch.bfloat16, device="cuda")
+        elif new_lay.n_dp != lay.n_dp:  # the GPU count changed: convert on the device
+            conv = []
+            for arr in state:
+                out = [torch.empty(s, device="cuda") for _ in range(n_dp)]
+                for r in range(n_dp):
+                    zs.zero_reshard(arr, n, r, out[r])
+                conv.append(out)
+            state = conv
+            wf_new = torch.empty(new_lay.n_pad, dtype=torch.bfloat16, device="cuda")
+            zs.zero_flat_gather([(wf, 0)], n, 0, wf_new)
+            wf = wf_new
+        lay = new_lay
+        for r in range(n_dp):
+            rows = host_rows(cfg, t, 0, n_dp, r * s, s, draw, pad_from=n)
+            zs.zero_shard_step(dev16(rows, zs.ZERO_BF16), s, s, state[0][r], state[1][r],
+                               state[2][r], wf, lay, r,
+                               zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **hp))
+        rows = host_rows(cfg, t, 0, n_dp, 0, n, draw)
+        oracle.step(rows, oracle.BF16, n_dp, n, n, w, m, v, wout, oracle.BF16, t,
+                    grad_scale=1.0 / n_dp, **hp)
+    torch.cuda.synchronize()
+    for arr, ref in zip(state, (w, m, v)):
+        got = torch.cat(arr).cpu().numpy()[:n]
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    got_w = wf.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got_w[:n], wout) and not np.any(got_w[n:])
