@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # deliberately broken copies to show that the pins catch them)
 LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(HERE, "liboracle_zero.so")
 
-BF16, FP16 = 0, 1
+BF16, FP16, FP32 = 0, 1, 2
 
 _lib = None
 
@@ -64,6 +64,12 @@ def lib():
                                   ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
         L.ora_reshard.restype = None
         i64p = ctypes.POINTER(ctypes.c_int64)
+        L.ora_dim0_layout.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                      vp, vp, vp]
+        L.ora_dim0_layout.restype = ctypes.c_int
+        L.ora_dim0_segments.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                        ctypes.c_int32, vp, ctypes.c_int64]
+        L.ora_dim0_segments.restype = ctypes.c_int64
         L.ora_flat_locate.argtypes = [i64p, i64p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                       i64p]
         L.ora_flat_locate.restype = ctypes.c_int32
@@ -119,6 +125,33 @@ def shard_segments(numels, n_dp, rank, align=1):
     return [tuple(int(x) for x in q[4 * i:4 * i + 4]) for i in range(cnt)]
 
 
+def dim0_layout(shapes, n_dp, align=1):
+    """shapes: [(rows, cols), ...] -> (packed_off, chunk_rows, N, S)."""
+    rows = np.ascontiguousarray([r for r, _ in shapes], dtype=np.int64)
+    cols = np.ascontiguousarray([c for _, c in shapes], dtype=np.int64)
+    offs = np.zeros(max(1, len(shapes)), dtype=np.int64)
+    chunk = np.zeros(max(1, len(shapes)), dtype=np.int64)
+    out = np.zeros(2, dtype=np.int64)
+    if lib().ora_dim0_layout(_ptr(rows), _ptr(cols), len(shapes), n_dp, align, _ptr(offs),
+                             _ptr(chunk), _ptr(out)) != 0:
+        raise ValueError("invalid dim-0 layout arguments")
+    return offs[:len(shapes)], chunk[:len(shapes)], int(out[0]), int(out[1])
+
+
+def dim0_segments(shapes, n_dp, rank, align=1):
+    """(tensor, tensor_off, shard_off, len) pieces of rank's packed buffer."""
+    rows = np.ascontiguousarray([r for r, _ in shapes], dtype=np.int64)
+    cols = np.ascontiguousarray([c for _, c in shapes], dtype=np.int64)
+    cnt = lib().ora_dim0_segments(_ptr(rows), _ptr(cols), len(shapes), n_dp, align, rank,
+                                  None, 0)
+    if cnt < 0:
+        raise ValueError("invalid dim-0 segment arguments")
+    q = np.zeros(4 * max(cnt, 1), dtype=np.int64)
+    lib().ora_dim0_segments(_ptr(rows), _ptr(cols), len(shapes), n_dp, align, rank, _ptr(q),
+                            cnt)
+    return [tuple(int(x) for x in q[4 * i:4 * i + 4]) for i in range(cnt)]
+
+
 def array_split_start(n, parts, i):
     return lib().ora_array_split_start(n, parts, i)
 
@@ -166,8 +199,9 @@ def adamw_scalars(step, lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=
 
 
 def reduce(grads, gdt, n_contrib, ld, length, acc, accumulate, overflow=None, sumsq=None):
-    """In place on acc (float32[length]); overflow uint32[1]; sumsq float64[1]."""
-    _need(grads, np.uint16, "grads")
+    """In place on acc (float32[length]); overflow uint32[1]; sumsq float64[1].
+    grads: uint16 rows (BF16, FP16) or float32 rows (FP32)."""
+    _need(grads, np.float32 if gdt == FP32 else np.uint16, "grads")
     _need(acc, np.float32, "acc")
     if length > 0 and grads.size < (n_contrib - 1) * ld + length:
         raise ValueError("grads too small")
@@ -217,7 +251,7 @@ def step(grads, gdt, n_dp, ld, length, w, m, v, wout, wdt, step, lr=1e-4, beta1=
     """Fused reduce + AdamW + cast, in place on w, m, v, wout.
 
     grad_scale defaults to 1/n_dp, the average over ranks."""
-    _need(grads, np.uint16, "grads")
+    _need(grads, np.float32 if gdt == FP32 else np.uint16, "grads")
     for a, n in ((w, "w"), (m, "m"), (v, "v")):
         _need(a, np.float32, n)
     _need(wout, np.uint16, "wout")

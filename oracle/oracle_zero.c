@@ -18,6 +18,11 @@
  *    gradient closed form, a high-precision brute force on tiny inputs, and
  *    sharded == unsharded.
  *  - ora_model_state_bytes / ora_comm_bytes: the numbers the pages print.
+ *  - ora_dim0_layout / ora_dim0_segments: torch.chunk's row boundaries per
+ *    tensor, packing every rank's buffer and unpacking it again rebuilds
+ *    every tensor, the 7B and GPT-2-XL totals.
+ *  - fp32 gradient rows (ORA_FP32): equal to the 16-bit path bit for bit on
+ *    values both formats hold, and exact sums within the summation bound.
  *  - ora_reshard / ora_flat_*: slicing and concatenation of the flat vector
  *    in numpy, agreement of the two independent forms (equal shards against
  *    general pieces), round trips n_dp -> n_dp' -> n_dp, scatter after
@@ -95,6 +100,78 @@ int64_t ora_shard_segments(const int64_t *numels, int64_t n_tensors,
 
 /* "A sharded Adam step": the shards are the pieces of numpy.array_split,
  * whose first (n mod parts) pieces are one element longer. */
+/* Per-parameter dim-0 sharding.  "ZeRO and FSDP", FSDP section: each
+ * parameter sharded along its first dimension, a unit's shards packed into
+ * one buffer per collective.  The cut is torch.chunk's: ceil(rows / n_dp)
+ * rows per rank, the last ranks possibly short or empty (padded). */
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int ora_dim0_layout(const int64_t *rows, const int64_t *cols, int64_t n_tensors,
+                    int32_t n_dp, int64_t align, int64_t *packed_off,
+                    int64_t *chunk_rows, int64_t out2[2]) {
+    if (n_tensors < 0 || n_dp < 1 || align < 1 || out2 == 0) return -1;
+    if (n_tensors > 0 && (rows == 0 || cols == 0)) return -1;
+    int64_t n = 0, p = 0;
+    for (int64_t i = 0; i < n_tensors; ++i) {
+        if (rows[i] < 0 || cols[i] < 0) return -1;
+        int64_t c = ceil_div(rows[i], n_dp);
+        if (packed_off) packed_off[i] = p;
+        if (chunk_rows) chunk_rows[i] = c;
+        p += c * cols[i];
+        n += rows[i] * cols[i];
+    }
+    out2[0] = n;
+    out2[1] = ceil_div(p, align) * align;
+    return 0;
+}
+
+int64_t ora_dim0_segments(const int64_t *rows, const int64_t *cols,
+                          int64_t n_tensors, int32_t n_dp, int64_t align,
+                          int32_t rank, int64_t *quads, int64_t cap) {
+    int64_t lay[2];
+    if (ora_dim0_layout(rows, cols, n_tensors, n_dp, align, 0, 0, lay) != 0)
+        return -1;
+    if (rank < 0 || rank >= n_dp) return -1;
+    int64_t count = 0, p = 0;
+    for (int64_t i = 0; i < n_tensors; ++i) {
+        int64_t c = ceil_div(rows[i], n_dp);
+        int64_t first = (int64_t)rank * c;            /* first row of the chunk */
+        int64_t have = rows[i] - first;               /* rows this rank holds */
+        if (have > c) have = c;
+        if (have < 0) have = 0;
+        if (have > 0) {
+            if (count < cap) {
+                quads[4 * count + 0] = i;
+                quads[4 * count + 1] = first * cols[i];
+                quads[4 * count + 2] = p;
+                quads[4 * count + 3] = have * cols[i];
+            }
+            ++count;
+        }
+        if (have < c && cols[i] > 0) {
+            if (count < cap) {
+                quads[4 * count + 0] = -1;
+                quads[4 * count + 1] = 0;
+                quads[4 * count + 2] = p + have * cols[i];
+                quads[4 * count + 3] = (c - have) * cols[i];
+            }
+            ++count;
+        }
+        p += c * cols[i];
+    }
+    if (lay[1] > p) {
+        if (count < cap) {
+            quads[4 * count + 0] = -1;
+            quads[4 * count + 1] = 0;
+            quads[4 * count + 2] = p;
+            quads[4 * count + 3] = lay[1] - p;
+        }
+        ++count;
+    }
+    return count;
+}
+
 int64_t ora_array_split_start(int64_t n, int64_t parts, int64_t i) {
     int64_t each = n / parts, extra = n % parts;
     return i * each + (i < extra ? i : extra);
@@ -202,6 +279,12 @@ static float widen(uint16_t h, int dt) {
     return dt == ORA_FP16 ? ora_f16_to_f32(h) : ora_bf16_to_f32(h);
 }
 
+/* element i of a gradient row buffer: fp32 as stored, 16-bit widened */
+static float grad_at(const void *grads, int gdt, int64_t i) {
+    if (gdt == ORA_FP32) return ((const float *)grads)[i];
+    return widen(((const uint16_t *)grads)[i], gdt);
+}
+
 static uint16_t narrow(float f, int dt) {
     return dt == ORA_FP16 ? ora_f32_to_f16(f) : ora_f32_to_bf16(f);
 }
@@ -254,7 +337,7 @@ static void adamw_element(float g, float *w, float *m, float *v,
 /* ------------------------------------------------------------------------ */
 /* The reduce.  "ZeRO and FSDP", "The idea, one stage at a time": the reduce-
  * scatter hands rank r the averaged gradient of shard r.  Here the n ranks'
- * 16-bit rows for that shard are widened and summed left to right (the
+ * rows for that shard (16-bit, widened; or fp32) are summed left to right (the
  * average's scale is applied with the update).
  * Overflow flag: "DeepSpeed ZeRO", "Mixed precision" says fp16 training
  * needs loss scaling; what scaling guards against is a gradient that is no
@@ -262,17 +345,17 @@ static void adamw_element(float g, float *w, float *m, float *v,
  * accumulated) fp32 gradient element is +-Inf or NaN, which covers every
  * non-finite input row and a sum that overflows. */
 
-static float row_sum(const uint16_t *grads, int gdt, int32_t n, int64_t ld,
+static float row_sum(const void *grads, int gdt, int32_t n, int64_t ld,
                      int64_t j) {
     float a = 0.0f;
     for (int32_t k = 0; k < n; ++k) {
-        float x = widen(grads[(int64_t)k * ld + j], gdt);
+        float x = grad_at(grads, gdt, (int64_t)k * ld + j);
         a = (k == 0) ? x : a + x;
     }
     return a;
 }
 
-void ora_reduce(const uint16_t *grads, int gdt, int32_t n_contrib, int64_t ld,
+void ora_reduce(const void *grads, int gdt, int32_t n_contrib, int64_t ld,
                 int64_t len, float *acc, int accumulate, uint32_t *overflow,
                 double *sumsq) {
     int bad = 0;
@@ -347,7 +430,7 @@ void ora_loss_scale_update(float *scale, int32_t *good_steps, uint32_t overflow,
     }
 }
 
-void ora_step(const uint16_t *grads, int gdt, int32_t n_dp, int64_t ld,
+void ora_step(const void *grads, int gdt, int32_t n_dp, int64_t ld,
               int64_t len, float *w, float *m, float *v, uint16_t *wout,
               int wdt, const double hp6[6], int64_t step, uint32_t *overflow,
               double *sumsq) {

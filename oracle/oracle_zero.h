@@ -37,8 +37,10 @@
 extern "C" {
 #endif
 
-/* 16-bit storage formats of gradients and weights. */
-enum { ORA_BF16 = 0, ORA_FP16 = 1 };
+/* Storage formats: 16-bit for gradients and weights; gradients may also
+ * arrive in fp32 ("ZeRO and FSDP", FSDP section: the float32 reduce-scatter
+ * of the mixed-precision policy; Llama 3 reduces its gradients in float32). */
+enum { ORA_BF16 = 0, ORA_FP16 = 1, ORA_FP32 = 2 };
 
 /* ---- layout: flatten + equal contiguous shards ---------------------------
  * numels[n_tensors] -> offsets[n_tensors] (prefix sums, nullable),
@@ -53,6 +55,28 @@ int ora_flatten_layout(const int64_t *numels, int64_t n_tensors, int32_t n_dp,
 int64_t ora_shard_segments(const int64_t *numels, int64_t n_tensors,
                            int32_t n_dp, int64_t align, int32_t rank,
                            int64_t *quads, int64_t cap);
+
+/* ---- per-parameter dim-0 sharding (FSDP2) ---------------------------------
+ * "ZeRO and FSDP", FSDP section: every parameter is a distributed tensor
+ * sharded along its first dimension, and a unit's shards are packed into one
+ * buffer for each collective.  Tensor i has rows[i] rows of cols[i]
+ * elements and is cut as torch.chunk cuts it: c_i = ceil(rows_i / n_dp) rows
+ * per rank, rank r holding rows [r c_i, min((r + 1) c_i, rows_i)) (maybe
+ * none).  Every rank's packed buffer holds tensor i's chunk at packed offset
+ * P_i = sum over j < i of c_j cols_j, zero-padded to c_i rows, and ends with
+ * zero padding up to S = align * ceil(sum c_i cols_i / align).
+ * packed_off, chunk_rows (nullable): P_i and c_i.  out2 = {N, S}.
+ * Returns 0, or -1 on invalid arguments (negative sizes, n_dp < 1, align < 1). */
+int ora_dim0_layout(const int64_t *rows, const int64_t *cols, int64_t n_tensors,
+                    int32_t n_dp, int64_t align, int64_t *packed_off,
+                    int64_t *chunk_rows, int64_t out2[2]);
+
+/* The pieces of rank `rank`'s packed buffer in buffer order: quads
+ * {tensor, tensor_off, shard_off, len}, tensor = -1 for padding.  Writes at
+ * most cap quads, returns the total count (or -1 on invalid arguments). */
+int64_t ora_dim0_segments(const int64_t *rows, const int64_t *cols,
+                          int64_t n_tensors, int32_t n_dp, int64_t align,
+                          int32_t rank, int64_t *quads, int64_t cap);
 
 /* Boundaries of numpy.array_split(range(n), parts): start of piece i. */
 int64_t ora_array_split_start(int64_t n, int64_t parts, int64_t i);
@@ -74,12 +98,14 @@ void ora_f16_to_f32_n(const uint16_t *x, float *y, int64_t n);
 void ora_adamw_scalars(const double hp6[6], int64_t step, float out10[10]);
 
 /* ---- the reduce (the reduce-scatter's arithmetic for one shard) -----------
- * a_j = G_0[j] + G_1[j] + ... + G_{n-1}[j], widened to fp32, left to right.
+ * a_j = G_0[j] + G_1[j] + ... + G_{n-1}[j], widened to fp32 (16-bit rows)
+ * or read as they are (gdt = ORA_FP32, grads then points at floats), summed
+ * left to right.
  * accumulate == 0: acc[j] = a_j; else acc[j] = acc[j] + a_j.
  * overflow (nullable): set to 1 if any acc[j] after the update is +-Inf or
  * NaN (so any non-finite input, or a sum that overflowed).
  * sumsq (nullable): += sum over j of acc[j]^2 (after the update), in double. */
-void ora_reduce(const uint16_t *grads, int gdt, int32_t n_contrib, int64_t ld,
+void ora_reduce(const void *grads, int gdt, int32_t n_contrib, int64_t ld,
                 int64_t len, float *acc, int accumulate, uint32_t *overflow,
                 double *sumsq);
 
@@ -119,7 +145,7 @@ void ora_loss_scale_update(float *scale, int32_t *good_steps, uint32_t overflow,
  * followed by ora_adamw.  overflow is set when a reduced a_j is non-finite
  * (the update is still applied); sumsq (nullable) += sum of g_j^2 with
  * g_j = a_j * s. */
-void ora_step(const uint16_t *grads, int gdt, int32_t n_dp, int64_t ld,
+void ora_step(const void *grads, int gdt, int32_t n_dp, int64_t ld,
               int64_t len, float *w, float *m, float *v, uint16_t *wout,
               int wdt, const double hp6[6], int64_t step, uint32_t *overflow,
               double *sumsq);

@@ -23,6 +23,7 @@ PINS_ACCT = ["tests/test_oracle_accounting.py"]
 PINS_CONVERT = ["tests/test_oracle_convert.py"]
 PINS_CONTROL = ["tests/test_oracle_control.py"]
 PINS_RESHARD = ["tests/test_oracle_reshard.py"]
+PINS_DIM0 = ["tests/test_oracle_dim0.py"]
 
 # (name, original text, planted text, pin files that must catch it)
 MUTANTS = [
@@ -36,8 +37,8 @@ MUTANTS = [
     ("betas_swapped", "out10[1] = (float)beta1;", "out10[1] = (float)beta2;", PINS_MATH),
     ("bias_step_off_by_one", "pow(beta1, (double)step)", "pow(beta1, (double)(step + 1))", PINS_MATH),
     ("decay_without_lr", "out10[9] = (float)(1.0 - lr * wd);", "out10[9] = (float)(1.0 - wd);", PINS_MATH),
-    ("row_index_transposed", "widen(grads[(int64_t)k * ld + j], gdt)",
-     "widen(grads[(int64_t)j * ld + k], gdt)", PINS_MATH),
+    ("row_index_transposed", "grad_at(grads, gdt, (int64_t)k * ld + j)",
+     "grad_at(grads, gdt, (int64_t)j * ld + k)", PINS_MATH),
     ("last_row_dropped", "for (int32_t k = 0; k < n; ++k) {", "for (int32_t k = 0; k < n - 1; ++k) {",
      PINS_MATH),
     ("average_not_applied", "float g = a * c[0];", "float g = a;", PINS_MATH),
@@ -76,6 +77,16 @@ MUTANTS = [
     ("locate_ignores_n", "if (i < 0 || i >= n) return -1;", "if (i < 0) return -1;", PINS_RESHARD),
     ("scatter_range_from_zero", "n_dst, INT64_MAX, begin + j, &off)", "n_dst, INT64_MAX, j, &off)",
      PINS_RESHARD),
+    ("dim0_chunk_floor", "int64_t c = ceil_div(rows[i], n_dp);\n        int64_t first",
+     "int64_t c = rows[i] / n_dp;\n        int64_t first", PINS_DIM0),
+    ("dim0_layout_chunk_floor", "int64_t c = ceil_div(rows[i], n_dp);\n        if (packed_off)",
+     "int64_t c = rows[i] / n_dp;\n        if (packed_off)", PINS_DIM0),
+    ("dim0_row_offset_not_scaled", "quads[4 * count + 1] = first * cols[i];",
+     "quads[4 * count + 1] = first;", PINS_DIM0),
+    ("dim0_padding_dropped", "if (have < c && cols[i] > 0) {", "if (0) {", PINS_DIM0),
+    ("dim0_size_not_aligned", "out2[1] = ceil_div(p, align) * align;", "out2[1] = p;", PINS_DIM0),
+    ("fp32_rows_read_as_16bit", "if (gdt == ORA_FP32) return ((const float *)grads)[i];",
+     "(void)0;", PINS_DIM0),
     ("gather_holes_not_zeroed", "else\n            memset(d, 0, (size_t)elem_bytes);",
      "else\n            memset(d, 1, (size_t)elem_bytes);", PINS_RESHARD),
     ("reshard_half_elements", "(const unsigned char *)src[r] + o * elem_bytes;",
@@ -103,7 +114,8 @@ def _run_pins(so, files):
 @pytest.fixture(scope="module")
 def results():
     src = open(SRC).read()
-    jobs = [("unmodified", src, PINS_MATH + PINS_LAYOUT + PINS_ACCT + PINS_CONTROL + PINS_RESHARD, None)]
+    jobs = [("unmodified", src, PINS_MATH + PINS_LAYOUT + PINS_ACCT + PINS_CONTROL + PINS_RESHARD + PINS_DIM0,
+             None)]
     for name, old, new, files in MUTANTS:
         assert src.count(old) == 1, f"mutant {name}: its target text must occur once in the oracle"
         jobs.append((name, src.replace(old, new), files, old))
