@@ -43,7 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=2,
                    help="workload: 1 GPT-2-XL n_dp=1, 2 7B n_dp=8 (default), "
-                        "3 7B n_dp=64, 4 7B n_dp=8 fp16 with 4 micro-batches")
+                        "3 7B n_dp=64, 4 7B n_dp=8 fp16 with 4 micro-batches, "
+                        "5 7B per-parameter dim-0 sharding n_dp=8 with fp32 gradients")
     p.add_argument("--cpu-sample-log2", type=int, default=25,
                    help="CPU baseline sample: 2^k parameters of the shard")
     p.add_argument("--cpu-steps", type=int, default=8)
@@ -126,11 +127,16 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     wl = workload(args.config)
-    lay, _ = zs.zero_flatten_layout(wl.numels, wl.n_dp)
+    if wl.layout == "dim0":
+        lay, _, _ = zs.zero_dim0_layout(wl.shapes, wl.n_dp)
+    else:
+        lay, _ = zs.zero_flatten_layout(wl.numels, wl.n_dp)
     S, n_dp, rank = lay.shard, wl.n_dp, wl.rank
     draw = wl.grad
-    gdt = zs.ZERO_BF16 if draw.kind == synth.BF16 else zs.ZERO_FP16
-    tdt = torch.bfloat16 if gdt == zs.ZERO_BF16 else torch.float16
+    gdt = {synth.BF16: zs.ZERO_BF16, synth.F16: zs.ZERO_FP16, synth.F32: zs.ZERO_FP32}[draw.kind]
+    tdt = {zs.ZERO_BF16: torch.bfloat16, zs.ZERO_FP16: torch.float16,
+           zs.ZERO_FP32: torch.float32}[gdt]
+    gbytes = 4 if gdt == zs.ZERO_FP32 else 2
     micro = wl.micro_batches
     hp_kw = dict(wl.hp)
 
@@ -199,12 +205,12 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
     if micro == 1:
-        bytes_per_param = 2 * n_dp + 26
+        bytes_per_param = gbytes * n_dp + 26
         kernel = "step_quad_kernel (fused reduce + AdamW + cast)"
     else:
         # 4 B written by the first reduce, 2 n_dp + 8 by each later one,
         # 30 by the gated AdamW (acc 4 + state 12 read, state 12 + weight 2 written)
-        bytes_per_param = (2 * n_dp + 4) + (micro - 1) * (2 * n_dp + 8) + 30
+        bytes_per_param = (gbytes * n_dp + 4) + (micro - 1) * (gbytes * n_dp + 8) + 30
         kernel = "adamw_quad_kernel (gated AdamW + cast; timed launch)"
     step_bytes = bytes_per_param * S
     kms = [a.elapsed_time(b) for a, b in events]
@@ -232,7 +238,9 @@ def main():
         "hbm_gbps": step_bytes / wall * args.steps / 1e9,
         "hbm_frac": step_bytes / wall * args.steps / 1e9 / HBM_PEAK_GBPS,
         "config": {"workload": wl.name, "n_params": lay.n, "n_dp": n_dp, "rank": rank,
-                   "shard": S, "grad_dtype": "bf16" if gdt == zs.ZERO_BF16 else "fp16",
+                   "shard": S, "layout": wl.layout,
+                   "grad_dtype": {zs.ZERO_BF16: "bf16", zs.ZERO_FP16: "fp16",
+                                  zs.ZERO_FP32: "fp32"}[gdt],
                    "state_dtype": "fp32", "weight_dtype": "bf16",
                    "micro_batches": micro, "bytes_per_param": bytes_per_param,
                    "launches_per_step": 1 if micro == 1 else micro + 1},
@@ -412,7 +420,7 @@ def cpu_baseline(wl, S, rank, log2n, steps):
     v = np.zeros(n, np.float32)
     wout = np.zeros(n, np.uint16)
     acc = np.zeros(n, np.float32)
-    gdt = oracle.BF16 if draw.kind == synth.BF16 else oracle.FP16
+    gdt = {synth.BF16: oracle.BF16, synth.F16: oracle.FP16, synth.F32: oracle.FP32}[draw.kind]
     t0 = time.perf_counter()
     for t in range(1, steps + 1):
         if wl.micro_batches == 1:

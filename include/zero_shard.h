@@ -74,8 +74,10 @@ typedef enum zero_status {
                          synchronisation instead */
 } zero_status;
 
-/* 16-bit storage formats for gradients and weights. */
-typedef enum zero_dtype { ZERO_BF16 = 0, ZERO_FP16 = 1 } zero_dtype;
+/* Storage formats.  Weights are 16-bit (BF16, FP16); gradient rows may also
+ * be fp32 (ZERO_FP32: the float32 reduce-scatter of the mixed-precision
+ * policy in "ZeRO and FSDP", FSDP section; 4 bytes per element). */
+typedef enum zero_dtype { ZERO_BF16 = 0, ZERO_FP16 = 1, ZERO_FP32 = 2 } zero_dtype;
 
 /* Flat layout: N parameters, n_dp shards of `shard` elements each,
  * n_pad = n_dp * shard >= n; elements [n, n_pad) are zero padding.
@@ -156,17 +158,54 @@ ZERO_API zero_status zero_shard_segments(const zero_layout *layout,
                                 int32_t rank, zero_segment *out, int64_t cap,
                                 int64_t *count);
 
+/* ---- per-parameter dim-0 sharding (host only) ------------------------------
+ * "ZeRO and FSDP", FSDP section: FSDP2 keeps every parameter as a tensor
+ * sharded along its first dimension and packs a unit's shards into one
+ * buffer for each collective.  Tensor i is rows[i] x cols[i] (cols = the
+ * product of its other dimensions; 1 for a vector).  It is cut as
+ * torch.chunk cuts it: c_i = ceil(rows_i / n_dp) rows per rank, rank r
+ * holding rows [r c_i, min((r + 1) c_i, rows_i)) -- possibly none.  Every
+ * rank's packed buffer holds tensor i's chunk at offset P_i = sum over j < i
+ * of c_j cols_j, zero-padded to c_i rows, and ends with zero padding up to
+ * shard = align * ceil(sum c_i cols_i / align).
+ * *out is a zero_layout that the device entry points take unchanged: n =
+ * sum rows_i cols_i, shard as above, n_pad = n_dp * shard; rank r's packed
+ * buffer is its shard, and weight_full is the all-gather buffer holding the
+ * ranks' packed buffers one after another.  packed_off and chunk_rows
+ * (nullable, n_tensors entries) receive P_i and c_i.
+ * EINVAL: out NULL, rows/cols NULL with n_tensors > 0, n_tensors < 0, a
+ * negative size, n_dp < 1, align < 1, or a size overflowing int64. */
+ZERO_API zero_status zero_dim0_layout(const int64_t *rows, const int64_t *cols,
+                                      int64_t n_tensors, int32_t n_dp, int64_t align,
+                                      int64_t *packed_off, int64_t *chunk_rows,
+                                      zero_layout *out);
+
+/* The pieces of rank `rank`'s packed buffer in buffer order: for each
+ * tensor its rows (tensor_off = first row * cols) and then its padding rows,
+ * and the end padding (tensor == -1 for padding).  Conventions as for
+ * zero_shard_segments; a piece list for zero_flat_gather (pack) and
+ * zero_flat_scatter (unpack) follows directly: tensor t's piece is
+ * (ptr_t + tensor_off, shard_off, len).
+ * EINVAL as for zero_shard_segments, or rows/cols inconsistent with the
+ * layout (which must come from zero_dim0_layout). */
+ZERO_API zero_status zero_dim0_segments(const zero_layout *layout, const int64_t *rows,
+                                        const int64_t *cols, int64_t n_tensors,
+                                        int32_t rank, zero_segment *out, int64_t cap,
+                                        int64_t *count);
+
 /* ---- the reduce (device) ------------------------------------------------
  * The reduce-scatter's arithmetic for one shard range, with optional
  * micro-batch accumulation (stage 2 reduces after every micro-batch).
- *   grads: device, dtype gdt, n_contrib rows; row k starts at element
+ *   grads: device, dtype gdt (BF16, FP16 or FP32), n_contrib rows; row k
+ *          starts at element
  *          k * ld and holds that rank's gradient for elements [0, len) of
  *          the range.  ld = len is a packed [n_contrib][len] slab; ld =
  *          N_pad with grads already offset to the shard start reads each
  *          rank's full flat gradient in place.  Read only.
  *   acc:   device fp32[len].  accumulate == 0: acc[j] = a_j; otherwise
  *          acc[j] = acc[j] + a_j, where a_j = G_0[j] + ... + G_{n-1}[j]
- *          summed left to right in fp32.  No scale is applied here.
+ *          summed left to right in fp32 (16-bit rows widened exactly, fp32
+ *          rows as stored).  No scale is applied here.
  *   overflow: device uint32 or NULL; set to 1 (never cleared) when some
  *          acc[j] after the update is +-Inf or NaN.
  *   sumsq: device double or NULL; the sum over j of acc[j]^2 is ADDED to
@@ -261,10 +300,12 @@ ZERO_API zero_status zero_loss_scale_update(zero_loss_scale *state,
  * One pass over the range: reduce layout->n_dp rows in fp32 (as
  * zero_shard_reduce with accumulate = 0), scale by s, AdamW, cast into the
  * slot -- bit-identical to zero_shard_reduce followed by zero_shard_adamw,
- * but each element's bytes cross HBM once: 2 * n_dp bytes of gradients and
- * 12 of state read, 12 of state and 2 of weight written.
- *   grads: device, dtype gdt, layout->n_dp rows of stride ld (elements), as
- *          for zero_shard_reduce.
+ * but each element's bytes cross HBM once: 2 * n_dp bytes of gradients (4 *
+ * n_dp for fp32 rows) and 12 of state read, 12 of state and 2 of weight
+ * written.
+ *   grads: device, dtype gdt (BF16, FP16 or FP32), layout->n_dp rows of
+ *          stride ld (elements), as for zero_shard_reduce.
+ *   wdt:   BF16 or FP16 (EINVAL otherwise).
  *   master, m, v: device fp32[len] at shard element shard_off.
  *   weight_full: device 16-bit buffer of layout->n_pad elements; elements
  *          [rank * shard + shard_off, ... + len) are written, nothing else.

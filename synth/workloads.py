@@ -15,7 +15,7 @@ Parameter lists (registration order; only the segment map depends on it):
 from dataclasses import dataclass, field
 from typing import List, Optional, Tuple
 
-from .synth_const import BF16, F16, outlier_threshold
+from .synth_const import BF16, F16, F32, outlier_threshold
 
 
 def llama7b_numels() -> List[int]:
@@ -24,6 +24,28 @@ def llama7b_numels() -> List[int]:
     for _ in range(layers):
         out += [d * d] * 4 + [ffn * d, ffn * d, d * ffn, d, d]
     out += [d, vocab * d]
+    return out
+
+
+def llama7b_shapes() -> List[Tuple[int, int]]:
+    """The 7B list as (rows, cols): dim 0 of each tensor, and the product of
+    its other dimensions (torch Linear weights are [out, in])."""
+    d, ffn, vocab, layers = 4096, 11008, 32000, 32
+    out = [(vocab, d)]
+    for _ in range(layers):
+        out += [(d, d)] * 4 + [(ffn, d), (ffn, d), (d, ffn), (d, 1), (d, 1)]
+    out += [(d, 1), (vocab, d)]
+    return out
+
+
+def gpt2xl_shapes() -> List[Tuple[int, int]]:
+    """The GPT-2-XL list as (rows, cols) (Conv1D weights are [in, out])."""
+    d, ffn, vocab, ctx, layers = 1600, 6400, 50257, 1024, 48
+    out = [(vocab, d), (ctx, d)]
+    for _ in range(layers):
+        out += [(d, 1), (d, 1), (d, 3 * d), (3 * d, 1), (d, d), (d, 1), (d, 1), (d, 1),
+                (d, ffn), (ffn, 1), (ffn, d), (d, 1)]
+    out += [(d, 1), (d, 1)]
     return out
 
 
@@ -38,7 +60,7 @@ def gpt2xl_numels() -> List[int]:
 
 @dataclass
 class GradDraw:
-    kind: int             # BF16 or F16
+    kind: int             # BF16, F16 or F32
     sigma: float          # standard deviation of the draw
     scale: float = 1.0    # multiplied into sigma (the fp16 loss scale)
     outlier_p: float = 0.0
@@ -70,10 +92,12 @@ class Workload:
                                                   eps=1e-8, weight_decay=0.1))
     seed: int = 0
     note: Optional[str] = None
+    layout: str = "flat"         # "flat" (one vector) or "dim0" (per-parameter)
+    shapes: Optional[List[Tuple[int, int]]] = None
 
 
 def workloads() -> List[Workload]:
-    """The five configurations, in order."""
+    """The configurations, in order."""
     l7 = llama7b_numels()
     return [
         Workload(0, "tiny_n10000_ndp4", [10000], 4, 1, GradDraw(BF16, 1e-3),
@@ -88,6 +112,10 @@ def workloads() -> List[Workload]:
         Workload(4, "llama7b_ndp8_fp16_accum4", l7, 8, 1,
                  GradDraw(F16, 1e-3, scale=65536.0), micro_batches=4,
                  loss_scale=65536.0, steps=(1,)),
+        Workload(5, "llama7b_dim0_ndp8_fp32grad", l7, 8, 1,
+                 GradDraw(F32, 1e-3, outlier_p=0.01, outlier_mul=100.0), steps=(1, 2, 3),
+                 layout="dim0", shapes=llama7b_shapes(),
+                 note="per-parameter dim-0 sharding (FSDP2), fp32 gradient rows"),
     ]
 
 

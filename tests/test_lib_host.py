@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     lib = ctypes.CDLL(zs.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -145,7 +145,7 @@ def _step(grads=BASE, ld=1024, length=1024, master=BASE + (1 << 30), m=BASE + (2
 @pytest.mark.parametrize("kw,status", [
     (dict(rank=4), zs.ZERO_EINVAL), (dict(rank=-1), zs.ZERO_EINVAL),
     (dict(ld=1000), zs.ZERO_EINVAL), (dict(length=-1), zs.ZERO_EINVAL),
-    (dict(gdt=2), zs.ZERO_EINVAL), (dict(wdt=5), zs.ZERO_EINVAL),
+    (dict(gdt=3), zs.ZERO_EINVAL), (dict(wdt=5), zs.ZERO_EINVAL),
     (dict(grads=0), zs.ZERO_EINVAL), (dict(master=0), zs.ZERO_EINVAL),
     (dict(hp=_hp(step=0)), zs.ZERO_EINVAL), (dict(hp=_hp(beta1=1.0)), zs.ZERO_EINVAL),
     (dict(hp=_hp(beta2=-0.1)), zs.ZERO_EINVAL), (dict(hp=_hp(eps=0.0)), zs.ZERO_EINVAL),
@@ -275,3 +275,55 @@ def test_flat_copies_reject_bad_arguments():
     assert RS(sh, 2, 100, 150, 4, 1, -75, dst, None) == zs.ZERO_EINVAL
     assert RS(sh, 2, 100, 150, 4, 0, 75, P(BASE + 40), None) == zs.ZERO_EALIAS
     assert RS(sh, 2, 100, 150, 4, 0, 0, None, None) == zs.ZERO_OK
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_dim0_layout_and_segments_match_oracle(seed):
+    rng = np.random.default_rng(500 + seed)
+    shapes = [(int(rng.integers(0, 70)), int(rng.choice([0, 1, 3, 16, 4096])))
+              for _ in range(int(rng.integers(0, 14)))]
+    n_dp = int(rng.integers(1, 70))
+    align = int(rng.choice([1, 4, 8]))
+    lay, offs, chunk = zs.zero_dim0_layout(shapes, n_dp, align)
+    o_offs, o_chunk, n, s = oracle.dim0_layout(shapes, n_dp, align)
+    assert (lay.n, lay.shard, lay.n_pad, lay.n_dp, lay.align) == (n, s, n_dp * s, n_dp, align)
+    assert np.array_equal(offs, o_offs) and np.array_equal(chunk, o_chunk)
+    for rank in sorted({0, n_dp - 1, int(rng.integers(0, n_dp))}):
+        want = [q for q in oracle.dim0_segments(shapes, n_dp, rank, align) if q[3] > 0]
+        assert zs.zero_dim0_segments(lay, shapes, rank) == want
+
+
+def test_dim0_llama7b_is_the_flat_shard_size():
+    d, ffn, vocab = 4096, 11008, 32000
+    shapes = [(vocab, d)] + [(d, d)] * 4 * 32 + [(ffn, d)] * 64 + [(d, ffn)] * 32 + \
+        [(d, 1)] * 65 + [(vocab, d)]
+    lay, _, _ = zs.zero_dim0_layout(shapes, 8)
+    flat, _ = zs.zero_flatten_layout(llama7b_numels(), 8)
+    assert (lay.n, lay.shard, lay.n_pad) == (flat.n, flat.shard, flat.n_pad)
+
+
+def test_dim0_rejects_invalid():
+    with pytest.raises(zs.ZeroError):
+        zs.zero_dim0_layout([(4, -1)], 2)
+    with pytest.raises(zs.ZeroError):
+        zs.zero_dim0_layout([(4, 1)], 0)
+    with pytest.raises(zs.ZeroError):
+        zs.zero_dim0_layout([(4, 1)], 2, 0)
+    with pytest.raises(zs.ZeroError):
+        zs.zero_dim0_layout([(1 << 62, 4)], 2)  # numel overflows
+    lay, _, _ = zs.zero_dim0_layout([(10, 3)], 4)
+    with pytest.raises(zs.ZeroError):
+        zs.zero_dim0_segments(lay, [(10, 4)], 0)  # inconsistent with the layout
+    with pytest.raises(zs.ZeroError):
+        zs.zero_dim0_segments(lay, [(10, 3)], 4)  # rank out of range
+
+
+@cpu_only
+def test_fp32_rows_validation():
+    R = L.zero_shard_reduce
+    # fp32 rows: 4 bytes per element in the alias check (16-bit would miss it)
+    assert R(P(BASE), 2, 2, 16, 16, P(BASE + 100), 0, None, None, None) == zs.ZERO_EALIAS
+    assert R(P(BASE), 3, 2, 16, 16, P(BASE + 4096), 0, None, None, None) == zs.ZERO_EINVAL
+    # weights cannot be fp32
+    assert _step(wdt=2) == zs.ZERO_EINVAL
+    assert _step(gdt=2, v=BASE + 3 * 1024 * 4 - 8) == zs.ZERO_EALIAS  # v over the fp32 rows

@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libzero_shard.so")
 
 ZERO_OK, ZERO_EINVAL, ZERO_EALIAS, ZERO_ERANGE, ZERO_EDEVICE = range(5)
-ZERO_BF16, ZERO_FP16 = 0, 1
+ZERO_BF16, ZERO_FP16, ZERO_FP32 = 0, 1, 2
 ABI_VERSION = 1
 
 
@@ -96,6 +96,10 @@ def _load():
     L.zero_flatten_layout.restype = ctypes.c_int
     L.zero_shard_segments.argtypes = [lay_p, vp, i64, i32, vp, i64, ctypes.POINTER(i64)]
     L.zero_shard_segments.restype = ctypes.c_int
+    L.zero_dim0_layout.argtypes = [vp, vp, i64, i32, i64, vp, vp, lay_p]
+    L.zero_dim0_layout.restype = ctypes.c_int
+    L.zero_dim0_segments.argtypes = [lay_p, vp, vp, i64, i32, vp, i64, ctypes.POINTER(i64)]
+    L.zero_dim0_segments.restype = ctypes.c_int
     L.zero_shard_reduce.argtypes = [vp, ctypes.c_int, i32, i64, i64, vp, i32, vp, vp, vp]
     L.zero_shard_reduce.restype = ctypes.c_int
     L.zero_shard_adamw.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, lay_p, i32, i64, i64,
@@ -137,13 +141,16 @@ def _check(status: int, what: str):
 # argument marshalling
 
 
-def _dtype_code(t, what: str) -> int:
+def _dtype_code(t, what: str, allow_fp32: bool = False) -> int:
     import torch
     if t.dtype in (torch.bfloat16,):
         return ZERO_BF16
     if t.dtype in (torch.float16,):
         return ZERO_FP16
-    raise TypeError(f"{what}: 16-bit tensor (bfloat16 or float16) expected, got {t.dtype}")
+    if allow_fp32 and t.dtype == torch.float32:
+        return ZERO_FP32
+    want = "bfloat16, float16 or float32" if allow_fp32 else "16-bit (bfloat16 or float16)"
+    raise TypeError(f"{what}: {want} tensor expected, got {t.dtype}")
 
 
 def _dev_ptr(t, what: str, dtype=None):
@@ -194,12 +201,49 @@ def zero_shard_segments(layout: ZeroLayout, numels: Sequence[int], rank: int
     return [(s.tensor, s.tensor_off, s.shard_off, s.len) for s in segs[:cnt.value]]
 
 
+def _shape_arrays(shapes):
+    rows = np.ascontiguousarray([int(r) for r, _ in shapes], dtype=np.int64)
+    cols = np.ascontiguousarray([int(c) for _, c in shapes], dtype=np.int64)
+    return rows, cols
+
+
+def zero_dim0_layout(shapes: Sequence[Tuple[int, int]], n_dp: int, align: int = 1
+                     ) -> Tuple[ZeroLayout, np.ndarray, np.ndarray]:
+    """Per-parameter dim-0 layout of tensors [(rows, cols), ...]: the layout,
+    each tensor's packed offset and its chunk of rows per rank."""
+    rows, cols = _shape_arrays(shapes)
+    offs = np.zeros(len(shapes), dtype=np.int64)
+    chunk = np.zeros(len(shapes), dtype=np.int64)
+    lay = ZeroLayout()
+    _check(_lib.zero_dim0_layout(rows.ctypes.data_as(ctypes.c_void_p),
+                                 cols.ctypes.data_as(ctypes.c_void_p), len(shapes), n_dp, align,
+                                 offs.ctypes.data_as(ctypes.c_void_p),
+                                 chunk.ctypes.data_as(ctypes.c_void_p), ctypes.byref(lay)),
+           "zero_dim0_layout")
+    return lay, offs, chunk
+
+
+def zero_dim0_segments(layout: ZeroLayout, shapes: Sequence[Tuple[int, int]], rank: int
+                       ) -> List[Tuple[int, int, int, int]]:
+    """(tensor, tensor_off, shard_off, len) pieces of rank's packed buffer."""
+    rows, cols = _shape_arrays(shapes)
+    r_p, c_p = rows.ctypes.data_as(ctypes.c_void_p), cols.ctypes.data_as(ctypes.c_void_p)
+    cnt = ctypes.c_int64(0)
+    _check(_lib.zero_dim0_segments(ctypes.byref(layout), r_p, c_p, len(shapes), rank, None, 0,
+                                   ctypes.byref(cnt)), "zero_dim0_segments")
+    segs = (_Segment * max(cnt.value, 1))()
+    _check(_lib.zero_dim0_segments(ctypes.byref(layout), r_p, c_p, len(shapes), rank, segs,
+                                   cnt.value, ctypes.byref(cnt)), "zero_dim0_segments")
+    return [(g.tensor, g.tensor_off, g.shard_off, g.len) for g in segs[:cnt.value]]
+
+
 def zero_shard_reduce(grads, n_contrib: int, ld: int, length: int, acc,
                       accumulate: bool = False, overflow=None, sumsq=None, stream=None):
-    """acc[:length] (+)= sum of n_contrib 16-bit rows of stride ld starting at grads."""
+    """acc[:length] (+)= sum of n_contrib rows (bf16, fp16 or fp32) of stride ld
+    starting at grads."""
     import torch
     _check(_lib.zero_shard_reduce(
-        _dev_ptr(grads, "grads"), _dtype_code(grads, "grads"), n_contrib, ld, length,
+        _dev_ptr(grads, "grads"), _dtype_code(grads, "grads", True), n_contrib, ld, length,
         _dev_ptr(acc, "acc", torch.float32), int(bool(accumulate)),
         _dev_ptr(overflow, "overflow", torch.int32), _dev_ptr(sumsq, "sumsq", torch.float64),
         _stream(stream, acc)), "zero_shard_reduce")
@@ -271,7 +315,7 @@ def zero_shard_step(grads, ld: int, length: int, master, m, v, weight_full,
     import torch
     hpc = hp._c()
     _check(_lib.zero_shard_step(
-        _dev_ptr(grads, "grads"), _dtype_code(grads, "grads"), ld, length,
+        _dev_ptr(grads, "grads"), _dtype_code(grads, "grads", True), ld, length,
         _dev_ptr(master, "master", torch.float32), _dev_ptr(m, "m", torch.float32),
         _dev_ptr(v, "v", torch.float32), _dev_ptr(weight_full, "weight_full"),
         _dtype_code(weight_full, "weight_full"), ctypes.byref(layout), rank, shard_off,
@@ -347,8 +391,8 @@ def library_path() -> str:
     return LIB_PATH
 
 
-__all__ = ["zero_flatten_layout", "zero_shard_segments", "zero_shard_reduce",
+__all__ = ["zero_flatten_layout", "zero_shard_segments", "zero_dim0_layout", "zero_dim0_segments", "zero_shard_reduce",
            "zero_shard_adamw", "zero_shard_adamw_ex", "zero_loss_scale_update",
            "new_loss_scale", "read_loss_scale", "zero_shard_step", "zero_flat_gather",
            "zero_flat_scatter", "zero_reshard", "zero_model_state_bytes", "zero_comm_bytes",
-           "AdamWHParams", "ZeroLayout", "ZeroError", "ZERO_BF16", "ZERO_FP16", "library_path"]
+           "AdamWHParams", "ZeroLayout", "ZeroError", "ZERO_BF16", "ZERO_FP16", "ZERO_FP32", "library_path"]

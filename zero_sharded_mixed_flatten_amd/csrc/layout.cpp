@@ -102,6 +102,96 @@ extern "C" zero_status zero_shard_segments(const zero_layout *layout, const int6
     return ZERO_OK;
 }
 
+// "ZeRO and FSDP", FSDP section: FSDP2 keeps each parameter as a tensor
+// sharded along its first dimension and packs a unit's shards into one
+// buffer per collective.  The cut is torch.chunk's: c = ceil(rows / n_dp)
+// rows per rank, the last ranks short or empty, each chunk zero-padded to c
+// rows in the packed buffer.
+namespace {
+
+struct Dim0 {
+    int64_t n, packed;  // parameters, packed elements before the end padding
+};
+
+// sizes of a dim-0 layout, or false on invalid or overflowing arguments
+bool dim0_sizes(const int64_t *rows, const int64_t *cols, int64_t n_tensors, int32_t n_dp,
+                int64_t *packed_off, int64_t *chunk_rows, Dim0 *out) {
+    if (n_tensors < 0 || n_dp < 1) return false;
+    if (n_tensors > 0 && (!rows || !cols)) return false;
+    int64_t n = 0, p = 0;
+    for (int64_t i = 0; i < n_tensors; ++i) {
+        const int64_t r = rows[i], c = cols[i];
+        if (r < 0 || c < 0) return false;
+        if (c > 0 && r > kI64Max / c) return false;
+        const int64_t numel = r * c;
+        const int64_t chunk = r / n_dp + (r % n_dp != 0 ? 1 : 0);
+        const int64_t piece = chunk * c;  // <= numel
+        if (numel > kI64Max - n || piece > kI64Max - p) return false;
+        if (packed_off) packed_off[i] = p;
+        if (chunk_rows) chunk_rows[i] = chunk;
+        n += numel;
+        p += piece;
+    }
+    out->n = n;
+    out->packed = p;
+    return true;
+}
+
+}  // namespace
+
+extern "C" zero_status zero_dim0_layout(const int64_t *rows, const int64_t *cols,
+                                        int64_t n_tensors, int32_t n_dp, int64_t align,
+                                        int64_t *packed_off, int64_t *chunk_rows,
+                                        zero_layout *out) {
+    if (!out || align < 1) return ZERO_EINVAL;
+    Dim0 d;
+    if (!dim0_sizes(rows, cols, n_tensors, n_dp, nullptr, nullptr, &d)) return ZERO_EINVAL;
+    const int64_t units = d.packed / align + (d.packed % align != 0 ? 1 : 0);
+    if (units > kI64Max / align) return ZERO_EINVAL;
+    const int64_t shard = units * align;
+    if (shard > 0 && n_dp > kI64Max / shard) return ZERO_EINVAL;
+    dim0_sizes(rows, cols, n_tensors, n_dp, packed_off, chunk_rows, &d);
+    out->n = d.n;
+    out->shard = shard;
+    out->n_pad = shard * n_dp;
+    out->align = align;
+    out->n_dp = n_dp;
+    out->reserved = 0;
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_dim0_segments(const zero_layout *layout, const int64_t *rows,
+                                          const int64_t *cols, int64_t n_tensors, int32_t rank,
+                                          zero_segment *out, int64_t cap, int64_t *count) {
+    if (!layout_ok(layout) || !count || cap < 0) return ZERO_EINVAL;
+    if (cap > 0 && !out) return ZERO_EINVAL;
+    if (rank < 0 || rank >= layout->n_dp) return ZERO_EINVAL;
+    Dim0 d;
+    if (!dim0_sizes(rows, cols, n_tensors, layout->n_dp, nullptr, nullptr, &d)) return ZERO_EINVAL;
+    const int64_t units = d.packed / layout->align + (d.packed % layout->align != 0 ? 1 : 0);
+    if (d.n != layout->n || units * layout->align != layout->shard) return ZERO_EINVAL;
+
+    int64_t found = 0;
+    auto emit = [&](int64_t tensor, int64_t tensor_off, int64_t shard_off, int64_t len) {
+        if (found < cap) out[found] = zero_segment{tensor, tensor_off, shard_off, len};
+        ++found;
+    };
+    int64_t p = 0;
+    for (int64_t i = 0; i < n_tensors; ++i) {
+        const int64_t chunk = rows[i] / layout->n_dp + (rows[i] % layout->n_dp != 0 ? 1 : 0);
+        const int64_t first = static_cast<int64_t>(rank) * chunk;
+        int64_t have = rows[i] - first;
+        have = have < 0 ? 0 : (have > chunk ? chunk : have);
+        if (have > 0 && cols[i] > 0) emit(i, first * cols[i], p, have * cols[i]);
+        if (have < chunk && cols[i] > 0)
+            emit(-1, 0, p + have * cols[i], (chunk - have) * cols[i]);
+        p += chunk * cols[i];
+    }
+    if (layout->shard > p) emit(-1, 0, p, layout->shard - p);
+    *count = found;
+    return ZERO_OK;
+}
+
 // "ZeRO and FSDP", "Memory per GPU": weights 2N, gradients 2N, optimizer
 // state kN per GPU; each stage moves one more term under 1/n_dp.
 extern "C" zero_status zero_model_state_bytes(double n, double n_dp, int32_t stage, double k,

@@ -65,7 +65,12 @@ constexpr int kRowBatch = 8;    // rows loaded together when n_dp is not special
 // rounded to whole workgroups.
 // Fused step: 10 waves with 1 row (56 B per lane in flight), 7 with 8 rows
 // (112 B), and with 64 rows the 152 VGPRs per lane already allow only 12.
-constexpr int step_waves_per_cu(int ndp) { return ndp == 1 ? 10 : ndp == 64 ? 12 : 7; }
+// With 8 fp32 rows (176 B per lane in flight) 5 waves per CU measured best
+// (79.6 % of 8 TB/s against 78.7 % at 7 and 76.9 % uncapped, random data).
+constexpr int step_waves_per_cu(int gdt, int ndp) {
+    if (gdt == ZERO_FP32) return ndp == 1 ? 10 : 5;
+    return ndp == 1 ? 10 : ndp == 64 ? 12 : 7;
+}
 constexpr int kReduceWavesPerCU = 10;
 constexpr int kAdamwWavesPerCU = 10;
 // One thread per quad (one per element on the unaligned path): a launch
@@ -110,9 +115,26 @@ __device__ __forceinline__ uint32_t narrow2(float lo, float hi) {
     }
 }
 
+// Gradient rows: 16-bit (4 elements of a quad = 8 bytes per lane) or fp32
+// (16 bytes per lane); the element type and the per-lane quad type.
+template <int GDT>
+struct GradT {
+    using elem = uint16_t;
+    using quad = u32x2;
+};
+template <>
+struct GradT<ZERO_FP32> {
+    using elem = float;
+    using quad = f32x4;
+};
+
 template <int DT>
-__device__ __forceinline__ float widen1(uint16_t h) {
-    return widen2<DT>(static_cast<uint32_t>(h))[0];
+__device__ __forceinline__ float widen1(typename GradT<DT>::elem h) {
+    if constexpr (DT == ZERO_FP32) {
+        return h;
+    } else {
+        return widen2<DT>(static_cast<uint32_t>(h))[0];
+    }
 }
 
 template <int DT>
@@ -128,6 +150,14 @@ __device__ __forceinline__ u32x2 load8(const uint16_t *p) {
 }
 __device__ __forceinline__ f32x4 load16(const float *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+}
+template <int GDT>
+__device__ __forceinline__ typename GradT<GDT>::quad load_quad(const typename GradT<GDT>::elem *p) {
+    if constexpr (GDT == ZERO_FP32) {
+        return load16(p);
+    } else {
+        return load8(p);
+    }
 }
 __device__ __forceinline__ void store8(uint16_t *p, u32x2 x) {
     __builtin_nontemporal_store(x, reinterpret_cast<u32x2 *>(p));
@@ -154,13 +184,27 @@ __device__ __forceinline__ void adamw_element(float g, float &w, float &m, float
     v = vt;
 }
 
+// the four fp32 values of one row's quad (16-bit widening is exact)
 template <int GDT>
-__device__ __forceinline__ void add_row(float a[kQuad], u32x2 x) {
-    const f32x2 t0 = widen2<GDT>(x[0]), t1 = widen2<GDT>(x[1]);
-    a[0] = a[0] + t0[0];
-    a[1] = a[1] + t0[1];
-    a[2] = a[2] + t1[0];
-    a[3] = a[3] + t1[1];
+__device__ __forceinline__ void widen_quad(float t[kQuad], typename GradT<GDT>::quad x) {
+    if constexpr (GDT == ZERO_FP32) {
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e) t[e] = x[e];
+    } else {
+        const f32x2 t0 = widen2<GDT>(x[0]), t1 = widen2<GDT>(x[1]);
+        t[0] = t0[0];
+        t[1] = t0[1];
+        t[2] = t1[0];
+        t[3] = t1[1];
+    }
+}
+
+template <int GDT>
+__device__ __forceinline__ void add_row(float a[kQuad], typename GradT<GDT>::quad x) {
+    float t[kQuad];
+    widen_quad<GDT>(t, x);
+#pragma unroll
+    for (int e = 0; e < kQuad; ++e) a[e] = a[e] + t[e];
 }
 
 // Rows of one quad.  For NDP > 0 (row count fixed at compile time) the
@@ -168,44 +212,36 @@ __device__ __forceinline__ void add_row(float a[kQuad], u32x2 x) {
 // load it needs -- rows and state -- before the first add (see
 // loads_issued()).  NDP == 0 reads the count at run time and fetches
 // kRowBatch rows at a time.
-template <int NDP>
+template <int GDT, int NDP>
 struct Rows {
-    u32x2 x[NDP > 0 ? NDP : kRowBatch];
+    typename GradT<GDT>::quad x[NDP > 0 ? NDP : kRowBatch];
 };
 
-template <int NDP>
-__device__ __forceinline__ void load_rows(Rows<NDP> &r, const uint16_t *__restrict__ p,
+template <int GDT, int NDP>
+__device__ __forceinline__ void load_rows(Rows<GDT, NDP> &r,
+                                          const typename GradT<GDT>::elem *__restrict__ p,
                                           int64_t ld) {
     if constexpr (NDP > 0) {
 #pragma unroll
-        for (int k = 0; k < NDP; ++k) r.x[k] = load8(p + static_cast<int64_t>(k) * ld);
+        for (int k = 0; k < NDP; ++k) r.x[k] = load_quad<GDT>(p + static_cast<int64_t>(k) * ld);
     }
 }
 
 // a[e] = G_0[e] + G_1[e] + ..., left to right in fp32
 template <int GDT, int NDP>
-__device__ __forceinline__ void sum_rows(float a[kQuad], Rows<NDP> &r,
-                                         const uint16_t *__restrict__ p, int64_t ld, int n) {
+__device__ __forceinline__ void sum_rows(float a[kQuad], Rows<GDT, NDP> &r,
+                                         const typename GradT<GDT>::elem *__restrict__ p,
+                                         int64_t ld, int n) {
     if constexpr (NDP > 0) {
-        const f32x2 t0 = widen2<GDT>(r.x[0][0]), t1 = widen2<GDT>(r.x[0][1]);
-        a[0] = t0[0];
-        a[1] = t0[1];
-        a[2] = t1[0];
-        a[3] = t1[1];
+        widen_quad<GDT>(a, r.x[0]);
 #pragma unroll
         for (int k = 1; k < NDP; ++k) add_row<GDT>(a, r.x[k]);
     } else {
         for (int k = 0; k < n; k += kRowBatch) {
 #pragma unroll
             for (int b = 0; b < kRowBatch; ++b)
-                if (k + b < n) r.x[b] = load8(p + static_cast<int64_t>(k + b) * ld);
-            if (k == 0) {
-                const f32x2 t0 = widen2<GDT>(r.x[0][0]), t1 = widen2<GDT>(r.x[0][1]);
-                a[0] = t0[0];
-                a[1] = t0[1];
-                a[2] = t1[0];
-                a[3] = t1[1];
-            }
+                if (k + b < n) r.x[b] = load_quad<GDT>(p + static_cast<int64_t>(k + b) * ld);
+            if (k == 0) widen_quad<GDT>(a, r.x[0]);
 #pragma unroll
             for (int b = 0; b < kRowBatch; ++b)
                 if (k + b < n && k + b > 0) add_row<GDT>(a, r.x[b]);
@@ -246,7 +282,8 @@ __device__ __forceinline__ void flags_epilogue(bool bad, double ss, uint32_t *ov
 
 template <int TPB, int GDT, int WDT, int NDP, bool OVF, bool SSQ>
 __global__ void __launch_bounds__(TPB)
-step_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int64_t nquad,
+step_quad_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld, int n_dp,
+                 int64_t nquad,
                  float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
                  uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
                  double *__restrict__ ssq) {
@@ -255,8 +292,8 @@ step_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int64
     const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
     if (q < nquad) {
         const int64_t e0 = q * kQuad;
-        Rows<NDP> rows;
-        load_rows<NDP>(rows, grads + e0, ld);
+        Rows<GDT, NDP> rows;
+        load_rows<GDT, NDP>(rows, grads + e0, ld);
         const f32x4 w4 = load16(W + e0), m4 = load16(M + e0), v4 = load16(V + e0);
         loads_issued();
         float a[kQuad];
@@ -282,7 +319,8 @@ step_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int64
 // element-per-thread variant for unaligned buffers and ragged tails
 template <int GDT, int WDT, bool OVF, bool SSQ>
 __global__ void __launch_bounds__(kBlock)
-step_scalar_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int64_t len,
+step_scalar_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld, int n_dp,
+                   int64_t len,
                    float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
                    uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
                    double *__restrict__ ssq) {
@@ -311,7 +349,8 @@ step_scalar_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n_dp, int
 
 template <int TPB, int GDT, int NDP, bool ACC, bool OVF, bool SSQ>
 __global__ void __launch_bounds__(TPB)
-reduce_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int64_t nquad,
+reduce_quad_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld, int n,
+                   int64_t nquad,
                    float *__restrict__ acc, uint32_t *__restrict__ ovf,
                    double *__restrict__ ssq) {
     bool bad = false;
@@ -319,8 +358,8 @@ reduce_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int64_
     const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
     if (q < nquad) {
         const int64_t e0 = q * kQuad;
-        Rows<NDP> rows;
-        load_rows<NDP>(rows, grads + e0, ld);
+        Rows<GDT, NDP> rows;
+        load_rows<GDT, NDP>(rows, grads + e0, ld);
         f32x4 prev = {};
         if constexpr (ACC) prev = load16(acc + e0);
         loads_issued();
@@ -342,7 +381,8 @@ reduce_quad_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int64_
 
 template <int GDT, bool ACC, bool OVF, bool SSQ>
 __global__ void __launch_bounds__(kBlock)
-reduce_scalar_kernel(const uint16_t *__restrict__ grads, int64_t ld, int n, int64_t len,
+reduce_scalar_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld, int n,
+                     int64_t len,
                      float *__restrict__ acc, uint32_t *__restrict__ ovf,
                      double *__restrict__ ssq) {
     bool bad = false;
@@ -473,6 +513,13 @@ void with_dtype(int dt, F &&f) {
     else f(IntC<ZERO_FP16>{});
 }
 
+// gradient row formats: the weight formats plus fp32
+template <typename F>
+void with_gdtype(int dt, F &&f) {
+    if (dt == ZERO_FP32) f(IntC<ZERO_FP32>{});
+    else with_dtype(dt, f);
+}
+
 template <typename F>
 void with_bool(bool b, F &&f) {
     if (b) f(BoolC<true>{});
@@ -480,18 +527,24 @@ void with_bool(bool b, F &&f) {
 }
 
 // row counts with a compiled specialisation (the configurations' 1, 8 and
-// 64 ranks); others take the batched loop
-template <typename F>
+// 64 ranks); others take the batched loop.  64 fp32 rows would hold 256
+// VGPRs per lane and take the batched loop too.
+template <int GDT, typename F>
 void with_ndp(int n, F &&f) {
     switch (n) {
     case 1: f(IntC<1>{}); break;
     case 8: f(IntC<8>{}); break;
-    case 64: f(IntC<64>{}); break;
+    case 64:
+        if constexpr (GDT == ZERO_FP32) f(IntC<0>{});
+        else f(IntC<64>{});
+        break;
     default: f(IntC<0>{}); break;
     }
 }
 
 bool dtype_ok(int dt) { return dt == ZERO_BF16 || dt == ZERO_FP16; }
+bool gdtype_ok(int dt) { return dtype_ok(dt) || dt == ZERO_FP32; }
+int64_t gdtype_bytes(int dt) { return dt == ZERO_FP32 ? 4 : 2; }
 
 bool layout_ok(const zero_layout *l) {
     if (!l || l->n_dp < 1 || l->align < 1 || l->shard < 0 || l->n < 0) return false;
@@ -527,20 +580,28 @@ Consts make_consts(const zero_adamw_hparams &hp) {
     return c;
 }
 
-// true when any two outputs overlap, or an output overlaps a gradient row
+// true when any two outputs overlap, or an output overlaps an input or a
+// gradient row (rows of elem bytes per element, ld elements apart)
 bool any_alias(const Span *outs, int n_out, const void *rows, int n_rows, int64_t ld,
-               int64_t len, const Span *ins = nullptr, int n_in = 0) {
+               int64_t len, int64_t elem, const Span *ins = nullptr, int n_in = 0) {
     for (int i = 0; i < n_out; ++i) {
         for (int j = i + 1; j < n_out; ++j)
             if (overlap(outs[i], outs[j])) return true;
         for (int j = 0; j < n_in; ++j)
             if (overlap(outs[i], ins[j])) return true;
         for (int k = 0; k < n_rows; ++k) {
-            const void *row = static_cast<const uint16_t *>(rows) + static_cast<int64_t>(k) * ld;
-            if (overlap(outs[i], span_of(row, len, 2))) return true;
+            const void *row = static_cast<const unsigned char *>(rows) +
+                              static_cast<int64_t>(k) * ld * elem;
+            if (overlap(outs[i], span_of(row, len, elem))) return true;
         }
     }
     return false;
+}
+
+// the vector path's alignment of a gradient row: one quad per lane
+bool rows_vec_ok(const void *g, int gdt, int n_rows, int64_t ld) {
+    const bool al = gdt == ZERO_FP32 ? aligned16(g) : aligned8(g);
+    return al && (n_rows == 1 || ld % kQuad == 0);
 }
 
 // one thread per item; kMaxLen keeps the count below 2^31 workgroups
@@ -564,7 +625,7 @@ extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int3
                                          int64_t ld, int64_t len, float *acc,
                                          int32_t accumulate, uint32_t *overflow,
                                          double *sumsq, void *stream) {
-    if (!dtype_ok(gdt) || !rows_ok(n_contrib, ld, len) || len > kMaxLen) return ZERO_EINVAL;
+    if (!gdtype_ok(gdt) || !rows_ok(n_contrib, ld, len) || len > kMaxLen) return ZERO_EINVAL;
     if (len == 0) return ZERO_OK;
     if (!grads || !acc) return ZERO_EINVAL;
     Span outs[3];
@@ -572,21 +633,22 @@ extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int3
     outs[n_out++] = span_of(acc, len, 4);
     if (overflow) outs[n_out++] = span_of(overflow, 1, 4);
     if (sumsq) outs[n_out++] = span_of(sumsq, 1, 8);
-    if (any_alias(outs, n_out, grads, n_contrib, ld, len)) return ZERO_EALIAS;
+    if (any_alias(outs, n_out, grads, n_contrib, ld, len, gdtype_bytes(gdt))) return ZERO_EALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const uint16_t *g = static_cast<const uint16_t *>(grads);
-    const bool vec = aligned8(g) && (n_contrib == 1 || ld % kQuad == 0) && aligned16(acc);
+    const bool vec = rows_vec_ok(grads, gdt, n_contrib, ld) && aligned16(acc);
     const int64_t nquad = vec ? len / kQuad : 0;
     const int64_t done = nquad * kQuad;
-    with_dtype(gdt, [&](auto GD) {
+    with_gdtype(gdt, [&](auto GD) {
+        using E = typename GradT<GD.value>::elem;
+        const E *g = static_cast<const E *>(grads);
         with_bool(accumulate != 0, [&](auto AC) {
             with_bool(overflow != nullptr, [&](auto OV) {
                 with_bool(sumsq != nullptr, [&](auto SS) {
                     if (nquad > 0) {
                         constexpr int tpb = SS.value ? kBlock : kWave;
                         const size_t lds = residency_lds_bytes(kReduceWavesPerCU, tpb);
-                        with_ndp(n_contrib, [&](auto ND) {
+                        with_ndp<GD.value>(n_contrib, [&](auto ND) {
                             reduce_quad_kernel<tpb, GD.value, ND.value, AC.value, OV.value,
                                                SS.value>
                                 <<<grid_for(nquad, tpb), tpb, lds, st>>>(
@@ -630,7 +692,7 @@ zero_status adamw_impl(const float *acc, float *master, float *m, float *v, void
     if (skip) ins[n_in++] = span_of(skip, 1, 4);
     if (ctl && ctl->sumsq) ins[n_in++] = span_of(ctl->sumsq, 1, 8);
     if (ctl && ctl->loss_scale) ins[n_in++] = span_of(ctl->loss_scale, 1, sizeof(zero_loss_scale));
-    if (any_alias(outs, 4, nullptr, 0, 0, 0, ins, n_in)) return ZERO_EALIAS;
+    if (any_alias(outs, 4, nullptr, 0, 0, 0, 4, ins, n_in)) return ZERO_EALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Consts c = make_consts(*hp);
@@ -704,7 +766,7 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
                                        const zero_layout *layout, int32_t rank,
                                        int64_t shard_off, const zero_adamw_hparams *hp,
                                        uint32_t *overflow, double *sumsq, void *stream) {
-    if (!dtype_ok(gdt) || !dtype_ok(wdt) || !layout_ok(layout) || !hparams_ok(hp))
+    if (!gdtype_ok(gdt) || !dtype_ok(wdt) || !layout_ok(layout) || !hparams_ok(hp))
         return ZERO_EINVAL;
     const int n_dp = layout->n_dp;
     if (rank < 0 || rank >= n_dp || shard_off < 0 || !rows_ok(n_dp, ld, len) || len > kMaxLen)
@@ -722,24 +784,25 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
     outs[n_out++] = span_of(slot, len, 2);
     if (overflow) outs[n_out++] = span_of(overflow, 1, 4);
     if (sumsq) outs[n_out++] = span_of(sumsq, 1, 8);
-    if (any_alias(outs, n_out, grads, n_dp, ld, len)) return ZERO_EALIAS;
+    if (any_alias(outs, n_out, grads, n_dp, ld, len, gdtype_bytes(gdt))) return ZERO_EALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Consts c = make_consts(*hp);
-    const uint16_t *g = static_cast<const uint16_t *>(grads);
-    const bool vec = aligned8(g) && (n_dp == 1 || ld % kQuad == 0) && aligned16(master) &&
-                     aligned16(m) && aligned16(v) && aligned8(slot);
+    const bool vec = rows_vec_ok(grads, gdt, n_dp, ld) && aligned16(master) && aligned16(m) &&
+                     aligned16(v) && aligned8(slot);
     const int64_t nquad = vec ? len / kQuad : 0;
     const int64_t done = nquad * kQuad;
-    with_dtype(gdt, [&](auto GD) {
+    with_gdtype(gdt, [&](auto GD) {
+        using E = typename GradT<GD.value>::elem;
+        const E *g = static_cast<const E *>(grads);
         with_dtype(wdt, [&](auto WD) {
             with_bool(overflow != nullptr, [&](auto OV) {
                 with_bool(sumsq != nullptr, [&](auto SS) {
                     if (nquad > 0) {
                         constexpr int tpb = SS.value ? kBlock : kWave;
-                        with_ndp(n_dp, [&](auto ND) {
-                            const size_t lds =
-                                residency_lds_bytes(step_waves_per_cu(ND.value), tpb);
+                        with_ndp<GD.value>(n_dp, [&](auto ND) {
+                            const size_t lds = residency_lds_bytes(
+                                step_waves_per_cu(GD.value, ND.value), tpb);
                             step_quad_kernel<tpb, GD.value, WD.value, ND.value, OV.value,
                                              SS.value>
                                 <<<grid_for(nquad, tpb), tpb, lds, st>>>(
