@@ -79,6 +79,13 @@ def lib():
         L.ora_flat_scatter.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, i64p, i64p,
                                        ctypes.c_int32, ctypes.c_int32]
         L.ora_flat_scatter.restype = None
+        L.ora_q8_quantize.argtypes = [vp, ctypes.c_int, ctypes.c_int64, vp, vp]
+        L.ora_q8_quantize.restype = None
+        L.ora_q8_dequantize.argtypes = [vp, vp, ctypes.c_int64, vp, ctypes.c_int]
+        L.ora_q8_dequantize.restype = None
+        L.ora_step_q8.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_int64, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp]
+        L.ora_step_q8.restype = None
         L.ora_model_state_bytes.argtypes = [ctypes.c_double, ctypes.c_double,
                                             ctypes.c_int, ctypes.c_double]
         L.ora_model_state_bytes.restype = ctypes.c_double
@@ -313,6 +320,46 @@ def flat_scatter(src, begin, dests):
     ptrs = (ctypes.c_void_p * len(dests))(*[a.ctypes.data for a, _ in dests])
     lib().ora_flat_scatter(_ptr(src), begin, src.size, ptrs, _i64s([o for _, o in dests]),
                            _i64s([a.size for a, _ in dests]), len(dests), src.dtype.itemsize)
+
+
+Q8_BLOCK = 256
+
+
+def q8_blocks(length):
+    return (length + Q8_BLOCK - 1) // Q8_BLOCK
+
+
+def q8_quantize(x, xdt):
+    """(int8 codes, float32 scales) of x (float32 with FP32, uint16 with BF16/FP16)."""
+    _need(x, np.float32 if xdt == FP32 else np.uint16, "x")
+    q = np.zeros(x.size, np.int8)
+    s = np.zeros(max(1, q8_blocks(x.size)), np.float32)
+    lib().ora_q8_quantize(_ptr(x), xdt, x.size, _ptr(q), _ptr(s))
+    return q, s[:q8_blocks(x.size)]
+
+
+def q8_dequantize(q, scales, ydt=FP32):
+    _need(q, np.int8, "q")
+    _need(scales, np.float32, "scales")
+    y = np.zeros(q.size, np.float32 if ydt == FP32 else np.uint16)
+    lib().ora_q8_dequantize(_ptr(q), _ptr(scales), q.size, _ptr(y), ydt)
+    return y
+
+
+def step_q8(gq, gs, n_dp, ld, sld, length, w, m, v, wq, wscales, step, lr=1e-4, beta1=0.9,
+            beta2=0.999, eps=1e-8, weight_decay=0.1, grad_scale=None, overflow=None, sumsq=None):
+    """Fused step with int8 rows (codes gq, scales gs) and int8 weights out."""
+    _need(gq, np.int8, "gq")
+    _need(gs, np.float32, "gs")
+    _need(wq, np.int8, "wq")
+    _need(wscales, np.float32, "wscales")
+    for a, n in ((w, "w"), (m, "m"), (v, "v")):
+        _need(a, np.float32, n)
+    if grad_scale is None:
+        grad_scale = 1.0 / n_dp
+    hp = _hp(lr, beta1, beta2, eps, weight_decay, grad_scale)
+    lib().ora_step_q8(_ptr(gq), _ptr(gs), n_dp, ld, sld, length, _ptr(w), _ptr(m), _ptr(v),
+                      _ptr(wq), _ptr(wscales), _ptr(hp), step, _ptr(overflow), _ptr(sumsq))
 
 
 def model_state_bytes(n, n_dp, stage, k=12):

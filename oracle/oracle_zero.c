@@ -23,6 +23,12 @@
  *    every tensor, the 7B and GPT-2-XL totals.
  *  - fp32 gradient rows (ORA_FP32): equal to the 16-bit path bit for bit on
  *    values both formats hold, and exact sums within the summation bound.
+ *  - ora_q8_*: PARITY UNPINNED against the pages (they define no quantizer);
+ *    pinned to the quantizer's own properties: codes in [-127, 127], the
+ *    block's largest magnitude coded +-127, the rounding bound s/2, exact
+ *    invariance under power-of-two scaling and sign flips, zero and
+ *    non-finite blocks; ora_step_q8 equal to dequantize + the fp32-row step
+ *    + quantize.
  *  - ora_reshard / ora_flat_*: slicing and concatenation of the flat vector
  *    in numpy, agreement of the two independent forms (equal shards against
  *    general pieces), round trips n_dp -> n_dp' -> n_dp, scatter after
@@ -446,6 +452,77 @@ void ora_step(const void *grads, int gdt, int32_t n_dp, int64_t ld,
         adamw_element(g, &w[j], &m[j], &v[j], c);
         wout[j] = narrow(w[j], wdt);
     }
+    if (overflow && bad) *overflow = 1u;
+    if (sumsq) *sumsq += ss;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 8-bit blockwise quantization.  The pages name ZeRO++'s 8-bit weight
+ * all-gather and quantized gradient reduce-scatter without a quantizer; this
+ * is the plain symmetric one, block by block (parity unpinned against the
+ * pages). */
+
+static float block_absmax(const void *x, int xdt, int64_t lo, int64_t hi) {
+    float m = 0.0f;
+    for (int64_t j = lo; j < hi; ++j) {
+        float a = fabsf(grad_at(x, xdt, j));
+        if (isnan(a) || a > m) m = a;
+        if (isnan(m)) break; /* NaN is sticky */
+    }
+    return m;
+}
+
+void ora_q8_quantize(const void *x, int xdt, int64_t len, int8_t *q, float *scales) {
+    for (int64_t lo = 0, b = 0; lo < len; lo += ORA_Q8_BLOCK, ++b) {
+        int64_t hi = lo + ORA_Q8_BLOCK < len ? lo + ORA_Q8_BLOCK : len;
+        float s = block_absmax(x, xdt, lo, hi) / 127.0f;
+        scales[b] = s;
+        for (int64_t j = lo; j < hi; ++j) {
+            if (s == 0.0f || isnan(s) || isinf(s)) {
+                q[j] = 0;
+                continue;
+            }
+            float r = rintf(grad_at(x, xdt, j) / s); /* ties to even */
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            q[j] = (int8_t)r;
+        }
+    }
+}
+
+static float dequant(const int8_t *q, const float *scales, int64_t j) {
+    return (float)q[j] * scales[j / ORA_Q8_BLOCK];
+}
+
+void ora_q8_dequantize(const int8_t *q, const float *scales, int64_t len, void *y,
+                       int ydt) {
+    for (int64_t j = 0; j < len; ++j) {
+        float f = dequant(q, scales, j);
+        if (ydt == ORA_FP32) ((float *)y)[j] = f;
+        else ((uint16_t *)y)[j] = narrow(f, ydt);
+    }
+}
+
+void ora_step_q8(const int8_t *gq, const float *gs, int32_t n_dp, int64_t ld,
+                 int64_t sld, int64_t len, float *w, float *m, float *v,
+                 int8_t *wq, float *wscales, const double hp6[6], int64_t step,
+                 uint32_t *overflow, double *sumsq) {
+    float c[10];
+    ora_adamw_scalars(hp6, step, c);
+    int bad = 0;
+    double ss = 0.0;
+    for (int64_t j = 0; j < len; ++j) {
+        float a = 0.0f;
+        for (int32_t k = 0; k < n_dp; ++k) {
+            float x = dequant(gq + (int64_t)k * ld, gs + (int64_t)k * sld, j);
+            a = (k == 0) ? x : a + x;
+        }
+        if (nonfinite(a)) bad = 1;
+        float g = a * c[0];
+        ss += (double)g * (double)g;
+        adamw_element(g, &w[j], &m[j], &v[j], c);
+    }
+    ora_q8_quantize(w, ORA_FP32, len, wq, wscales);
     if (overflow && bad) *overflow = 1u;
     if (sumsq) *sumsq += ss;
 }

@@ -181,6 +181,33 @@ void ora_flat_scatter(const void *src, int64_t begin, int64_t count,
                       void *const *dst, const int64_t *flat_off,
                       const int64_t *len, int32_t n_dst, int32_t elem_bytes);
 
+/* ---- 8-bit blockwise quantization (ZeRO++) --------------------------------
+ * "ZeRO: How DeepSpeed Made Trillion-Parameter Training Practical" and
+ * "ZeRO and FSDP" (FSDP section, "Fewer bytes on the wire"): ZeRO++
+ * quantizes the weight all-gather to 8 bits and the gradients of the
+ * reduce-scatter.  The pages define no quantizer; the one here is the plain
+ * symmetric blockwise int8 quantizer (PARITY UNPINNED against the pages: it
+ * is pinned only to its own mathematical properties).
+ * Blocks of ORA_Q8_BLOCK consecutive elements (the last one may be short);
+ * for block i: s_i = absmax_i / 127 in fp32 (absmax over the block, NaN if
+ * any element is NaN), q_j = rint(x_j / s_i) clamped to [-127, 127] with
+ * round-to-nearest-even; s_i == 0 or s_i not finite gives q_j = 0 (so a
+ * block with an Inf or NaN dequantizes to NaN).  Dequantized: q_j * s_i. */
+#define ORA_Q8_BLOCK 256
+void ora_q8_quantize(const void *x, int xdt, int64_t len, int8_t *q, float *scales);
+void ora_q8_dequantize(const int8_t *q, const float *scales, int64_t len, void *y,
+                       int ydt);
+
+/* Fused step with 8-bit communication on both sides: a_j = sum over k of
+ * q_k[j] * s_k[j / B] (each product rounded to fp32, summed left to right;
+ * row k at gq + k * ld, its scales at gs + k * sld), g = a * s, AdamW as
+ * ora_step, then the new w quantized into wq / wscales (blocks from
+ * element 0 of the range).  overflow / sumsq as ora_step. */
+void ora_step_q8(const int8_t *gq, const float *gs, int32_t n_dp, int64_t ld,
+                 int64_t sld, int64_t len, float *w, float *m, float *v,
+                 int8_t *wq, float *wscales, const double hp6[6], int64_t step,
+                 uint32_t *overflow, double *sumsq);
+
 /* ---- accounting ----------------------------------------------------------
  * Model-state bytes per GPU for stage 0..3 with 2-byte weights and grads and
  * K bytes of optimizer state per parameter; -1 for any other stage. */

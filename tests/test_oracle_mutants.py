@@ -24,6 +24,7 @@ PINS_CONVERT = ["tests/test_oracle_convert.py"]
 PINS_CONTROL = ["tests/test_oracle_control.py"]
 PINS_RESHARD = ["tests/test_oracle_reshard.py"]
 PINS_DIM0 = ["tests/test_oracle_dim0.py"]
+PINS_Q8 = ["tests/test_oracle_q8.py"]
 
 # (name, original text, planted text, pin files that must catch it)
 MUTANTS = [
@@ -41,7 +42,10 @@ MUTANTS = [
      "grad_at(grads, gdt, (int64_t)j * ld + k)", PINS_MATH),
     ("last_row_dropped", "for (int32_t k = 0; k < n; ++k) {", "for (int32_t k = 0; k < n - 1; ++k) {",
      PINS_MATH),
-    ("average_not_applied", "float g = a * c[0];", "float g = a;", PINS_MATH),
+    ("average_not_applied", "float g = a * c[0];\n        ss += (double)g * (double)g;\n"
+     "        adamw_element(g, &w[j], &m[j], &v[j], c);\n        wout[j]",
+     "float g = a;\n        ss += (double)g * (double)g;\n"
+     "        adamw_element(g, &w[j], &m[j], &v[j], c);\n        wout[j]", PINS_MATH),
     ("accumulate_ignored", "float r = accumulate ? acc[j] + a : a;", "float r = a;", PINS_MATH),
     ("overflow_never_set", "if (nonfinite(r)) bad = 1;", "(void)r;", PINS_MATH),
     ("bf16_truncates", "if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) hi += 1;", "(void)lo;",
@@ -87,6 +91,17 @@ MUTANTS = [
     ("dim0_size_not_aligned", "out2[1] = ceil_div(p, align) * align;", "out2[1] = p;", PINS_DIM0),
     ("fp32_rows_read_as_16bit", "if (gdt == ORA_FP32) return ((const float *)grads)[i];",
      "(void)0;", PINS_DIM0),
+    ("q8_scale_128", "float s = block_absmax(x, xdt, lo, hi) / 127.0f;",
+     "float s = block_absmax(x, xdt, lo, hi) / 128.0f;", PINS_Q8),
+    ("q8_ties_away", "float r = rintf(grad_at(x, xdt, j) / s);",
+     "float r = roundf(grad_at(x, xdt, j) / s);", PINS_Q8),
+    ("q8_scale_multiplied", "float r = rintf(grad_at(x, xdt, j) / s);",
+     "float r = rintf(grad_at(x, xdt, j) * s);", PINS_Q8),
+    ("q8_dequant_block_off_by_one", "return (float)q[j] * scales[j / ORA_Q8_BLOCK];",
+     "return (float)q[j] * scales[(j + 1) / ORA_Q8_BLOCK];", PINS_Q8),
+    ("q8_nan_not_sticky", "if (isnan(a) || a > m) m = a;", "if (a > m) m = a;", PINS_Q8),
+    ("q8_step_quantizes_m", "ora_q8_quantize(w, ORA_FP32, len, wq, wscales);",
+     "ora_q8_quantize(m, ORA_FP32, len, wq, wscales);", PINS_Q8),
     ("gather_holes_not_zeroed", "else\n            memset(d, 0, (size_t)elem_bytes);",
      "else\n            memset(d, 1, (size_t)elem_bytes);", PINS_RESHARD),
     ("reshard_half_elements", "(const unsigned char *)src[r] + o * elem_bytes;",
@@ -114,7 +129,8 @@ def _run_pins(so, files):
 @pytest.fixture(scope="module")
 def results():
     src = open(SRC).read()
-    jobs = [("unmodified", src, PINS_MATH + PINS_LAYOUT + PINS_ACCT + PINS_CONTROL + PINS_RESHARD + PINS_DIM0,
+    jobs = [("unmodified", src,
+             PINS_MATH + PINS_LAYOUT + PINS_ACCT + PINS_CONTROL + PINS_RESHARD + PINS_DIM0 + PINS_Q8,
              None)]
     for name, old, new, files in MUTANTS:
         assert src.count(old) == 1, f"mutant {name}: its target text must occur once in the oracle"

@@ -1,0 +1,129 @@
+"""Pins of the oracle's 8-bit blockwise quantizer and quantized step (CPU).
+
+The pages name ZeRO++'s 8-bit weight all-gather and quantized gradient
+reduce-scatter ("ZeRO and FSDP", FSDP section; "ZeRO: How DeepSpeed Made
+Trillion-Parameter Training Practical"; "ZeRO Optimizer, in depth",
+"Offload and ZeRO++") but define no quantizer.  PARITY UNPINNED against the
+pages: these tests pin the stated quantizer (symmetric, one fp32 scale per
+256-element block, s = absmax / 127, q = rint(x / s)) to its mathematical
+properties and to a hand-worked example."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import F32, tag
+
+U = 2.0 ** -24
+B = oracle.Q8_BLOCK
+
+
+def _x(n, seed, sigma=1.0):
+    return synth.fill_host(F32, seed, tag(5, 150), 0, n, sigma,
+                           synth.synth_const.outlier_threshold(0.01), 100.0)
+
+
+def test_hand_worked_block():
+    # s = fl(1/127); 1/s = 127, 0.5/s = 63.5 -> 64 (tie to even), -0.25/s = -31.75 -> -32,
+    # 0.1/s = 12.7 -> 13, 0.0236/s = 2.997 -> 3
+    x = np.array([1.0, 0.5, -0.25, 0.1, 0.0236, 0.0], np.float32)
+    q, s = oracle.q8_quantize(x, oracle.FP32)
+    assert s[0] == np.float32(1.0) / np.float32(127.0)
+    assert q.tolist() == [127, 64, -32, 13, 3, 0]
+    # absmax 127 makes s exactly 1: the quotients are the values themselves,
+    # and ties go to the even code (62.5 -> 62, -0.5 -> 0, 2.5 -> 2, -3.5 -> -4)
+    x = np.array([127.0, 62.5, -0.5, 1.5, 2.5, -3.5, -127.0], np.float32)
+    q, s = oracle.q8_quantize(x, oracle.FP32)
+    assert s[0] == 1.0 and q.tolist() == [127, 62, 0, 2, 2, -4, -127]
+
+
+@pytest.mark.parametrize("n", [1, 255, 256, 257, 4096, 10_001])
+def test_codes_range_absmax_and_rounding_bound(n):
+    x = _x(n, n)
+    q, s = oracle.q8_quantize(x, oracle.FP32)
+    assert s.size == (n + B - 1) // B
+    assert q.min() >= -127 and q.max() <= 127
+    for b in range(s.size):
+        blk, qb = x[b * B:(b + 1) * B], q[b * B:(b + 1) * B]
+        amax = np.abs(blk).max()
+        assert s[b] == np.float32(amax) / np.float32(127.0)
+        if amax > 0:
+            assert np.abs(qb).max() == 127
+            assert qb[np.argmax(np.abs(blk))] == np.sign(blk[np.argmax(np.abs(blk))]) * 127
+        err = np.abs(blk.astype(np.float64) - qb.astype(np.float64) * float(s[b]))
+        assert np.all(err <= float(s[b]) * (0.5 + 128 * U))
+
+
+@pytest.mark.parametrize("k", [-20, -3, 1, 7, 30])
+def test_power_of_two_scaling_is_exact(k):
+    x = _x(3000, 7, sigma=1e-2)
+    q, s = oracle.q8_quantize(x, oracle.FP32)
+    q2, s2 = oracle.q8_quantize((x * np.float32(2.0 ** k)).astype(np.float32), oracle.FP32)
+    assert np.array_equal(q, q2)
+    assert np.array_equal(s2, (s * np.float32(2.0 ** k)).astype(np.float32))
+
+
+def test_sign_symmetry():
+    x = _x(5000, 8)
+    q, s = oracle.q8_quantize(x, oracle.FP32)
+    qn, sn = oracle.q8_quantize(-x, oracle.FP32)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+
+
+def test_zero_and_nonfinite_blocks():
+    x = _x(4 * B, 9)
+    x[:B] = 0.0
+    x[B + 17] = np.inf
+    x[2 * B + 5] = np.nan
+    q, s = oracle.q8_quantize(x, oracle.FP32)
+    assert s[0] == 0 and not q[:B].any()
+    assert np.isinf(s[1]) and not q[B:2 * B].any()
+    assert np.isnan(s[2]) and not q[2 * B:3 * B].any()
+    y = oracle.q8_dequantize(q, s)
+    assert np.all(y[:B] == 0) and np.all(np.isnan(y[B:3 * B])) and np.all(np.isfinite(y[3 * B:]))
+
+
+def test_bf16_input_equals_its_fp32_widening():
+    h = synth.fill_host(synth.BF16, 1, tag(5, 151), 0, 3001, 1e-3)
+    q1, s1 = oracle.q8_quantize(h, oracle.BF16)
+    q2, s2 = oracle.q8_quantize(oracle.bf16_to_f32(h), oracle.FP32)
+    assert np.array_equal(q1, q2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+
+
+def test_dequantize_16bit_is_the_rounded_fp32_value():
+    x = _x(2000, 10)
+    q, s = oracle.q8_quantize(x, oracle.FP32)
+    y32 = oracle.q8_dequantize(q, s, oracle.FP32)
+    assert np.array_equal(y32, (q.astype(np.float32) * np.repeat(s, B)[:q.size]).astype(np.float32))
+    assert np.array_equal(oracle.q8_dequantize(q, s, oracle.BF16), oracle.f32_to_bf16(y32))
+    assert np.array_equal(oracle.q8_dequantize(q, s, oracle.FP16), oracle.f32_to_f16(y32))
+
+
+@pytest.mark.parametrize("n_dp", [1, 3, 8])
+def test_quantized_step_is_dequantize_step_quantize(n_dp):
+    """ora_step_q8 = dequantize each row to fp32, the fp32-row step (pinned
+    elsewhere), then quantize the new master -- bit for bit."""
+    length, ld = 3 * B + 77, 4 * B
+    sld = ld // B
+    rows = np.stack([_x(ld, 20 + k, 1e-3) for k in range(n_dp)])
+    qs = [oracle.q8_quantize(rows[k], oracle.FP32) for k in range(n_dp)]
+    gq = np.concatenate([q for q, _ in qs])
+    gs = np.concatenate([s for _, s in qs])
+    w0 = _x(length, 30, 0.02)
+    hp = dict(lr=1e-3, weight_decay=0.1)
+    w, m, v = w0.copy(), np.zeros(length, np.float32), np.zeros(length, np.float32)
+    wq = np.zeros(length, np.int8)
+    ws = np.zeros(oracle.q8_blocks(length), np.float32)
+    ss = np.zeros(1)
+    oracle.step_q8(gq, gs, n_dp, ld, sld, length, w, m, v, wq, ws, 1, sumsq=ss, **hp)
+    deq = np.stack([oracle.q8_dequantize(q, s) for q, s in qs])
+    w2, m2, v2 = w0.copy(), np.zeros(length, np.float32), np.zeros(length, np.float32)
+    wo = np.zeros(length, np.uint16)
+    ss2 = np.zeros(1)
+    oracle.step(deq.reshape(-1), oracle.FP32, n_dp, ld, length, w2, m2, v2, wo, oracle.BF16, 1,
+                sumsq=ss2, **hp)
+    for a, b in ((w, w2), (m, m2), (v, v2)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    q3, s3 = oracle.q8_quantize(w2, oracle.FP32)
+    assert np.array_equal(wq, q3) and np.array_equal(ws.view(np.uint32), s3.view(np.uint32))
+    assert ss[0] == ss2[0]
