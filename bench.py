@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "zero_sharded_mixed_flatten_amd", "csrc", "zero_shard.hip")
 COPY_SOURCE = os.path.join(ROOT, "zero_sharded_mixed_flatten_amd", "csrc", "flat_copy.hip")
+Q8_SOURCE = os.path.join(ROOT, "zero_sharded_mixed_flatten_amd", "csrc", "quant8.hip")
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -44,7 +45,8 @@ def parse():
     p.add_argument("--config", type=int, default=2,
                    help="workload: 1 GPT-2-XL n_dp=1, 2 7B n_dp=8 (default), "
                         "3 7B n_dp=64, 4 7B n_dp=8 fp16 with 4 micro-batches, "
-                        "5 7B per-parameter dim-0 sharding n_dp=8 with fp32 gradients")
+                        "5 7B per-parameter dim-0 sharding n_dp=8 with fp32 gradients, "
+                        "6 7B n_dp=8 with 8-bit blockwise rows and weights (ZeRO++)")
     p.add_argument("--cpu-sample-log2", type=int, default=25,
                    help="CPU baseline sample: 2^k parameters of the shard")
     p.add_argument("--cpu-steps", type=int, default=8)
@@ -127,10 +129,11 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     wl = workload(args.config)
+    q8 = wl.comm == "q8"
     if wl.layout == "dim0":
         lay, _, _ = zs.zero_dim0_layout(wl.shapes, wl.n_dp)
     else:
-        lay, _ = zs.zero_flatten_layout(wl.numels, wl.n_dp)
+        lay, _ = zs.zero_flatten_layout(wl.numels, wl.n_dp, zs.ZERO_Q8_BLOCK if q8 else 1)
     S, n_dp, rank = lay.shard, wl.n_dp, wl.rank
     draw = wl.grad
     gdt = {synth.BF16: zs.ZERO_BF16, synth.F16: zs.ZERO_FP16, synth.F32: zs.ZERO_FP32}[draw.kind]
@@ -141,17 +144,34 @@ def main():
     hp_kw = dict(wl.hp)
 
     # ---- inputs, resident in HBM -------------------------------------------
-    slab = torch.empty((n_dp, S), dtype=tdt, device=dev)
-    for k in range(n_dp):
-        synth.fill_device(slab[k], draw.kind, wl.seed,
-                          synth.tag(BUF_GRAD, wl.cid, 1, 0, k), rank * S,
-                          draw.eff_sigma, draw.thr, draw.outlier_mul)
+    if q8:
+        # what each sender puts on the wire: its fp32 gradient for this shard,
+        # quantized (before the timed region)
+        nb = S // zs.ZERO_Q8_BLOCK
+        slab = torch.empty((n_dp, S), dtype=torch.int8, device=dev)
+        slab_s = torch.empty((n_dp, nb), dtype=torch.float32, device=dev)
+        tmp = torch.empty(S, dtype=torch.float32, device=dev)
+        for k in range(n_dp):
+            synth.fill_device(tmp, draw.kind, wl.seed, synth.tag(BUF_GRAD, wl.cid, 1, 0, k),
+                              rank * S, draw.eff_sigma, draw.thr, draw.outlier_mul)
+            zs.zero_q8_quantize(tmp, slab[k], slab_s[k])
+        del tmp
+    else:
+        slab = torch.empty((n_dp, S), dtype=tdt, device=dev)
+        for k in range(n_dp):
+            synth.fill_device(slab[k], draw.kind, wl.seed,
+                              synth.tag(BUF_GRAD, wl.cid, 1, 0, k), rank * S,
+                              draw.eff_sigma, draw.thr, draw.outlier_mul)
     master = torch.empty(S, dtype=torch.float32, device=dev)
     synth.fill_device(master, F32, wl.seed, synth.tag(BUF_MASTER, wl.cid), rank * S,
                       wl.master_sigma)
     m = torch.zeros(S, dtype=torch.float32, device=dev)
     v = torch.zeros(S, dtype=torch.float32, device=dev)
-    wfull = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device=dev)
+    if q8:
+        wfull = torch.zeros(lay.n_pad, dtype=torch.int8, device=dev)
+        wfull_s = torch.zeros(lay.n_pad // zs.ZERO_Q8_BLOCK, dtype=torch.float32, device=dev)
+    else:
+        wfull = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device=dev)
     acc = torch.empty(S, dtype=torch.float32, device=dev) if micro > 1 else None
     flag = torch.zeros(1, dtype=torch.int32, device=dev) if micro > 1 else None
     stream = torch.cuda.current_stream(dev)
@@ -167,7 +187,11 @@ def main():
             e1 = torch.cuda.Event(enable_timing=True) if timed else None
             if timed:
                 e0.record(stream)
-            zs.zero_shard_step(slab, S, S, master, m, v, wfull, lay, rank, hp, stream=stream)
+            if q8:
+                zs.zero_shard_step_q8(slab, slab_s, S, nb, S, master, m, v, wfull, wfull_s, lay,
+                                      rank, hp, stream=stream)
+            else:
+                zs.zero_shard_step(slab, S, S, master, m, v, wfull, lay, rank, hp, stream=stream)
             if timed:
                 e1.record(stream)
                 events.append((e0, e1))
@@ -204,7 +228,10 @@ def main():
     wall = time.perf_counter() - t0
 
     ms_per_step = wall * 1e3 / args.steps
-    if micro == 1:
+    if q8:
+        bytes_per_param = n_dp * (1 + 4 / zs.ZERO_Q8_BLOCK) + 12 + 12 + 1 + 4 / zs.ZERO_Q8_BLOCK
+        kernel = "step_q8_kernel (fused dequantize + reduce + AdamW + quantize)"
+    elif micro == 1:
         bytes_per_param = gbytes * n_dp + 26
         kernel = "step_quad_kernel (fused reduce + AdamW + cast)"
     else:
@@ -220,7 +247,7 @@ def main():
     else:
         launch_bytes = 30 * S
     achieved = launch_bytes / (k_avg * 1e-3) / 1e9
-    traffic = committed_traffic(wl.name) if micro == 1 else None
+    traffic = committed_traffic(wl.name, Q8_SOURCE if q8 else KERNEL_SOURCE) if micro == 1 else None
 
     line = {
         "metric": "sharded AdamW step params/s and HBM GB/s (% of 8 TB/s), 7B n_dp=8 shard",
@@ -239,9 +266,10 @@ def main():
         "hbm_frac": step_bytes / wall * args.steps / 1e9 / HBM_PEAK_GBPS,
         "config": {"workload": wl.name, "n_params": lay.n, "n_dp": n_dp, "rank": rank,
                    "shard": S, "layout": wl.layout,
-                   "grad_dtype": {zs.ZERO_BF16: "bf16", zs.ZERO_FP16: "fp16",
-                                  zs.ZERO_FP32: "fp32"}[gdt],
-                   "state_dtype": "fp32", "weight_dtype": "bf16",
+                   "grad_dtype": "int8 blocks of 256 + fp32 scale" if q8 else
+                   {zs.ZERO_BF16: "bf16", zs.ZERO_FP16: "fp16", zs.ZERO_FP32: "fp32"}[gdt],
+                   "state_dtype": "fp32",
+                   "weight_dtype": "int8 blocks of 256 + fp32 scale" if q8 else "bf16",
                    "micro_batches": micro, "bytes_per_param": bytes_per_param,
                    "launches_per_step": 1 if micro == 1 else micro + 1},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
@@ -255,6 +283,8 @@ def main():
     # ---- the oracle on the host: a reported baseline, never the target ------
     if not args.no_cpu_baseline:
         del slab, master, m, v, wfull, acc
+        if q8:
+            del slab_s, wfull_s
         torch.cuda.empty_cache()
         line["cpu_baseline"] = cpu_baseline(wl, S, rank, args.cpu_sample_log2, args.cpu_steps)
 
@@ -421,6 +451,20 @@ def cpu_baseline(wl, S, rank, log2n, steps):
     wout = np.zeros(n, np.uint16)
     acc = np.zeros(n, np.float32)
     gdt = {synth.BF16: oracle.BF16, synth.F16: oracle.FP16, synth.F32: oracle.FP32}[draw.kind]
+    if wl.comm == "q8":
+        qs = [oracle.q8_quantize(rows[k], oracle.FP32) for k in range(wl.n_dp)]
+        gq = np.concatenate([q for q, _ in qs])
+        gs = np.concatenate([s for _, s in qs])
+        wq = np.zeros(n, np.int8)
+        wsc = np.zeros(oracle.q8_blocks(n), np.float32)
+        t0 = time.perf_counter()
+        for t in range(1, steps + 1):
+            oracle.step_q8(gq, gs, wl.n_dp, n, oracle.q8_blocks(n), n, w, m, v, wq, wsc, t,
+                           grad_scale=1.0 / wl.n_dp, **wl.hp)
+        dt = time.perf_counter() - t0
+        return {"value": n * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+                "sample": f"first {n} parameters of rank {rank}'s shard, {wl.n_dp} 8-bit rows, "
+                          f"{steps} optimizer steps, single-threaded C oracle ({dt:.1f} s)"}
     t0 = time.perf_counter()
     for t in range(1, steps + 1):
         if wl.micro_batches == 1:

@@ -379,6 +379,61 @@ ZERO_API zero_status zero_reshard(const void *const *src_shards, int32_t n_src,
                                   int32_t elem_bytes, int32_t dst_rank,
                                   int64_t dst_shard, void *dst, void *stream);
 
+/* ---- 8-bit blockwise quantization for communication (ZeRO++) ------------
+ * ZeRO++ quantizes the weight all-gather to 8 bits and the gradients of the
+ * reduce-scatter ("ZeRO and FSDP", FSDP section, fewer bytes on the wire;
+ * "ZeRO Optimizer, in depth", "Offload and ZeRO++").  The pages define no
+ * quantizer; this library uses the plain symmetric blockwise one:
+ *   a vector of len elements is cut into blocks of ZERO_Q8_BLOCK (the last
+ *   one may be short); block i has one fp32 scale s_i = absmax_i / 127
+ *   (absmax NaN if the block holds a NaN) and codes q_j = rint(x_j / s_i)
+ *   clamped to [-127, 127], ties to even (q_j = 0 when s_i is 0, Inf or NaN,
+ *   so a non-finite block dequantizes to NaN); the value is q_j * s_i.
+ * Codes: int8[len]; scales: float[ceil(len / ZERO_Q8_BLOCK)]. */
+#define ZERO_Q8_BLOCK 256
+
+/* Quantize x (device, xdt = BF16, FP16 or FP32, len elements) into q and
+ * scales (device).  Any alignment (16-byte fp32 / 8-byte 16-bit input and
+ * 4-byte codes take the vector path).
+ * EINVAL: bad xdt, len < 0 or > 2^38, NULL pointers with len > 0.
+ * EALIAS: any two of x, q, scales overlap. */
+ZERO_API zero_status zero_q8_quantize(const void *x, zero_dtype xdt, int64_t len, int8_t *q,
+                                      float *scales, void *stream);
+
+/* y[j] = q[j] * scales[j / ZERO_Q8_BLOCK] in fp32, stored as ydt (BF16 and
+ * FP16 rounded to nearest even).  Errors as for zero_q8_quantize. */
+ZERO_API zero_status zero_q8_dequantize(const int8_t *q, const float *scales, int64_t len,
+                                        void *y, zero_dtype ydt, void *stream);
+
+/* Fused step with 8-bit communication on both sides: the n_dp ranks'
+ * contributions arrive as quantized rows (what each sender puts on the wire
+ * for this shard range), and the updated master leaves quantized (the
+ * all-gather's 8-bit payload).  Per element j of the range:
+ *   a_j = sum over k of q_k[j] * s_k[j / B] (each product rounded to fp32,
+ *         summed left to right), g = a_j * s, AdamW as zero_shard_step;
+ * then the new master of each block of B = ZERO_Q8_BLOCK elements of the
+ * range is quantized into wq_full / wscales_full.
+ *   gq:  device int8, layout->n_dp rows of stride ld (elements); gscales:
+ *        device fp32, the rows' block scales, row k at gscales + k * sld,
+ *        entry i for the range's block i.
+ *   master, m, v: device fp32[len] at shard element shard_off.
+ *   wq_full: device int8[n_pad]; wscales_full: device fp32[n_pad / B];
+ *        elements [rank * shard + shard_off, ... + len) and their block
+ *        scales are written, nothing else.
+ *   overflow, sumsq: as zero_shard_step (the update is applied regardless).
+ * Requirements (EINVAL otherwise): layout->shard and shard_off multiples of
+ * B; gq and wq_full 4-byte aligned, ld a multiple of 4 when n_dp > 1,
+ * sld >= ceil(len / B) when n_dp > 1; master, m, v 16-byte aligned.
+ * Errors otherwise as for zero_shard_step; EALIAS covers the scale rows and
+ * slots too.  Bytes per element: n_dp (1 + 4/B) + 12 read, 12 + 1 + 4/B
+ * written. */
+ZERO_API zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales, int64_t ld,
+                                        int64_t sld, int64_t len, float *master, float *m,
+                                        float *v, int8_t *wq_full, float *wscales_full,
+                                        const zero_layout *layout, int32_t rank,
+                                        int64_t shard_off, const zero_adamw_hparams *hp,
+                                        uint32_t *overflow, double *sumsq, void *stream);
+
 /* ---- accounting (host only) ----------------------------------------------
  * Model-state bytes per GPU at ZeRO stage 0..3 for n parameters on n_dp
  * ranks with 2-byte weights and gradients and k bytes of optimizer state

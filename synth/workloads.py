@@ -93,6 +93,7 @@ class Workload:
     seed: int = 0
     note: Optional[str] = None
     layout: str = "flat"         # "flat" (one vector) or "dim0" (per-parameter)
+    comm: str = "16bit"          # "16bit" rows / weights, or "q8" (8-bit blockwise, ZeRO++)
     shapes: Optional[List[Tuple[int, int]]] = None
 
 
@@ -116,6 +117,11 @@ def workloads() -> List[Workload]:
                  GradDraw(F32, 1e-3, outlier_p=0.01, outlier_mul=100.0), steps=(1, 2, 3),
                  layout="dim0", shapes=llama7b_shapes(),
                  note="per-parameter dim-0 sharding (FSDP2), fp32 gradient rows"),
+        Workload(6, "llama7b_ndp8_q8", l7, 8, 1,
+                 GradDraw(F32, 1e-3, outlier_p=0.01, outlier_mul=100.0), steps=(1, 2),
+                 comm="q8",
+                 note="8-bit blockwise rows in, 8-bit weights out (ZeRO++ quantized "
+                      "reduce-scatter and all-gather); rows quantized from fp32 draws"),
     ]
 
 

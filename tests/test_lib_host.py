@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     lib = ctypes.CDLL(zs.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -327,3 +327,36 @@ def test_fp32_rows_validation():
     # weights cannot be fp32
     assert _step(wdt=2) == zs.ZERO_EINVAL
     assert _step(gdt=2, v=BASE + 3 * 1024 * 4 - 8) == zs.ZERO_EALIAS  # v over the fp32 rows
+
+
+@cpu_only
+def test_q8_entry_points_reject_bad_arguments():
+    Q, D, S8 = L.zero_q8_quantize, L.zero_q8_dequantize, L.zero_shard_step_q8
+    assert Q(P(BASE), 3, 100, P(BASE + 4096), P(BASE + 8192), None) == zs.ZERO_EINVAL
+    assert Q(P(BASE), 2, -1, P(BASE + 4096), P(BASE + 8192), None) == zs.ZERO_EINVAL
+    assert Q(None, 2, 100, P(BASE + 4096), P(BASE + 8192), None) == zs.ZERO_EINVAL
+    assert Q(P(BASE), 2, 1000, P(BASE + 100), P(BASE + 8192), None) == zs.ZERO_EALIAS
+    assert Q(P(BASE), 2, 1000, P(BASE + 8192), P(BASE + 8192 + 500), None) == zs.ZERO_EALIAS
+    assert Q(None, 2, 0, None, None, None) == zs.ZERO_OK
+    assert D(P(BASE), P(BASE + 4096), 1000, P(BASE + 500), 0, None) == zs.ZERO_EALIAS
+    assert D(P(BASE), P(BASE + 4096), 1000, P(BASE + 8192), 7, None) == zs.ZERO_EINVAL
+    lay = zs.zero_flatten_layout([8 * 4096], 8, 256)[0]
+    hp = _hp()
+
+    def step(gq=BASE, gs=BASE + (1 << 28), ld=4096, sld=16, length=4096, w=BASE + (2 << 28),
+             m=BASE + (3 << 28), v=BASE + (4 << 28), wq=BASE + (5 << 28), ws=BASE + (6 << 28),
+             lay=lay, rank=1, off=0):
+        return S8(P(gq), P(gs), ld, sld, length, P(w), P(m), P(v), P(wq), P(ws),
+                  ctypes.byref(lay), rank, off, ctypes.byref(hp), None, None, None)
+    assert step(off=128) == zs.ZERO_EINVAL                          # not a block boundary
+    assert step(sld=15) == zs.ZERO_EINVAL                           # scale rows too short
+    assert step(ld=4098) == zs.ZERO_EINVAL                          # row stride not % 4
+    assert step(gq=BASE + 2) == zs.ZERO_EINVAL                      # codes misaligned
+    assert step(w=BASE + (2 << 28) + 4) == zs.ZERO_EINVAL           # master misaligned
+    assert step(length=4096, off=256) == zs.ZERO_ERANGE
+    odd = zs.zero_flatten_layout([8 * 4000], 8)[0]                  # shard 4000: not % 256
+    assert step(lay=odd, length=1000) == zs.ZERO_EINVAL
+    assert step(m=BASE + (2 << 28) + 16 * 1000) == zs.ZERO_EALIAS   # m inside master
+    assert step(ws=BASE + (1 << 28) + 64) == zs.ZERO_EALIAS         # scale slot over row scales
+    assert step(w=BASE + 7 * 4096) == zs.ZERO_EALIAS                # master over the last row
+    assert step(length=0, gq=0, gs=0, w=0, m=0, v=0, wq=0, ws=0) == zs.ZERO_OK

@@ -1,0 +1,43 @@
+"""The library's kernels keep the operation order the oracle defines (CPU):
+every HIP source is compiled for gfx950 to AMD assembly and checked for the
+instruction forms that would change rounding behind the source's back --
+mixed-precision FMAs (v_fma_mix*, v_mad_mix*: one rounding to 16 bits where
+the definition rounds to fp32 first) and packed fp32 arithmetic (disabled
+for this hardware).  Plain v_fma_f32 is not listed: the correctly rounded
+division and square root sequences use it internally; contraction of the
+source's own multiply-adds is off in the build and the bitwise GPU tests
+would show it."""
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "zero_sharded_mixed_flatten_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SOURCES = ["zero_shard.hip", "quant8.hip", "flat_copy.hip"]
+
+FORBIDDEN = [r"\bv_fma_mix", r"\bv_mad_mix", r"\bv_pk_fma_f32", r"\bv_pk_mul_f32",
+             r"\bv_pk_add_f32"]
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_rounding_changing_instructions(src):
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        # the library's own flags (build.py), device code only, as assembly
+        subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17",
+                        "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang",
+                        "-packed-fp32-ops", "--offload-device-only", "-S",
+                        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+                        os.path.join(CSRC, src), "-o", out],
+                       check=True, capture_output=True)
+        asm = open(out).read()
+    kernels = len(re.findall(r"^\s*\.amdhsa_kernel\b", asm, flags=re.M))
+    assert kernels > 0
+    for pat in FORBIDDEN:
+        hits = re.findall(pat + r"[^\n]*", asm)
+        assert not hits, f"{src}: {len(hits)} x {hits[0]}"

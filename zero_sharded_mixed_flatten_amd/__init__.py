@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libzero_shard.so")
 
 ZERO_OK, ZERO_EINVAL, ZERO_EALIAS, ZERO_ERANGE, ZERO_EDEVICE = range(5)
 ZERO_BF16, ZERO_FP16, ZERO_FP32 = 0, 1, 2
+ZERO_Q8_BLOCK = 256
 ABI_VERSION = 1
 
 
@@ -31,6 +32,11 @@ class ZeroError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
         super().__init__(f"{what}: {_lib.zero_status_string(status).decode()}")
+
+
+class ZeroValueError(ZeroError, ValueError):
+    """Invalid arguments (EINVAL, EALIAS, ERANGE): a ValueError, the pages'
+    convention for an unsupported stage or argument."""
 
 
 class ZeroLayout(ctypes.Structure):
@@ -120,6 +126,13 @@ def _load():
     L.zero_flat_scatter.restype = ctypes.c_int
     L.zero_reshard.argtypes = [ctypes.POINTER(vp), i32, i64, i64, i32, i32, i64, vp, vp]
     L.zero_reshard.restype = ctypes.c_int
+    L.zero_q8_quantize.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp]
+    L.zero_q8_quantize.restype = ctypes.c_int
+    L.zero_q8_dequantize.argtypes = [vp, vp, i64, vp, ctypes.c_int, vp]
+    L.zero_q8_dequantize.restype = ctypes.c_int
+    L.zero_shard_step_q8.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, lay_p, i32, i64,
+                                     hp_p, vp, vp, vp]
+    L.zero_shard_step_q8.restype = ctypes.c_int
     L.zero_model_state_bytes.argtypes = [dbl, dbl, i32, dbl, ctypes.POINTER(dbl)]
     L.zero_model_state_bytes.restype = ctypes.c_int
     L.zero_comm_bytes.argtypes = [dbl, dbl, i32, dbl, dbl, ctypes.POINTER(dbl)]
@@ -133,8 +146,11 @@ _lib = _load()
 
 
 def _check(status: int, what: str):
-    if status != ZERO_OK:
-        raise ZeroError(status, what)
+    if status == ZERO_OK:
+        return
+    if status in (ZERO_EINVAL, ZERO_EALIAS, ZERO_ERANGE):
+        raise ZeroValueError(status, what)
+    raise ZeroError(status, what)
 
 
 # ---------------------------------------------------------------------------
@@ -372,6 +388,110 @@ def zero_reshard(src_shards, n: int, dst_rank: int, dst, stream=None):
                              _dev_ptr(dst, "dst"), _stream(stream, dst)), "zero_reshard")
 
 
+def q8_blocks(length: int) -> int:
+    """Scales of a quantized vector of `length` elements."""
+    return (length + ZERO_Q8_BLOCK - 1) // ZERO_Q8_BLOCK
+
+
+def zero_q8_quantize(x, q, scales, stream=None):
+    """Blockwise int8 codes (int8 tensor q) and fp32 scales of x (bf16,
+    fp16 or fp32), one scale per ZERO_Q8_BLOCK elements."""
+    import torch
+    _check(_lib.zero_q8_quantize(_dev_ptr(x, "x"), _dtype_code(x, "x", True), x.numel(),
+                                 _dev_ptr(q, "q", torch.int8), _dev_ptr(scales, "scales", torch.float32),
+                                 _stream(stream, x)), "zero_q8_quantize")
+
+
+def zero_q8_dequantize(q, scales, y, stream=None):
+    """y = codes x block scale, stored in y's dtype (bf16, fp16 or fp32)."""
+    import torch
+    _check(_lib.zero_q8_dequantize(_dev_ptr(q, "q", torch.int8),
+                                   _dev_ptr(scales, "scales", torch.float32), q.numel(),
+                                   _dev_ptr(y, "y"), _dtype_code(y, "y", True), _stream(stream, q)),
+           "zero_q8_dequantize")
+
+
+def zero_shard_step_q8(gq, gscales, ld: int, sld: int, length: int, master, m, v, wq_full,
+                       wscales_full, layout: ZeroLayout, rank: int, hp: AdamWHParams,
+                       shard_off: int = 0, overflow=None, sumsq=None, stream=None):
+    """Fused step with 8-bit rows in (codes gq, scales gscales) and 8-bit
+    weights out (wq_full, wscales_full: the all-gather buffer)."""
+    import torch
+    hpc = hp._c()
+    _check(_lib.zero_shard_step_q8(
+        _dev_ptr(gq, "gq", torch.int8), _dev_ptr(gscales, "gscales", torch.float32), ld, sld,
+        length, _dev_ptr(master, "master", torch.float32), _dev_ptr(m, "m", torch.float32),
+        _dev_ptr(v, "v", torch.float32), _dev_ptr(wq_full, "wq_full", torch.int8),
+        _dev_ptr(wscales_full, "wscales_full", torch.float32), ctypes.byref(layout), rank,
+        shard_off, ctypes.byref(hpc), _dev_ptr(overflow, "overflow", torch.int32),
+        _dev_ptr(sumsq, "sumsq", torch.float64), _stream(stream, master)), "zero_shard_step_q8")
+
+
+def zero_adam_step(grads, w_shards, m_shards, v_shards, t: int, lr: float = 1e-3,
+                   b1: float = 0.9, b2: float = 0.999, eps: float = 1e-8,
+                   weight_decay: float = 0.0, stream=None):
+    """The functional form of one sharded Adam step for n_dp ranks simulated
+    on one GPU ("ZeRO and FSDP", "A sharded Adam step").
+
+    grads[r]: rank r's full local gradient (1-D, length n; fp32, bf16 or
+    fp16); w_shards[r], m_shards[r], v_shards[r]: rank r's fp32 piece of
+    numpy.array_split(range(n), n_dp).  Returns (full_w, w_shards, m_shards,
+    v_shards): full_w[r] is rank r's fp32 copy of the whole updated weight
+    vector (the all-gather's result), the shard lists are new tensors, and
+    no input is modified.  Rank r's gradient is the average over ranks of
+    its piece (the reduce-scatter's arithmetic: a left-to-right fp32 sum
+    times fl(1/n_dp)); Adam with bias correction from t = 1 (AdamW with
+    weight_decay > 0).  Every step runs in the library's kernels: the flat
+    copies build the gradient slab, clone the shards and gather the full
+    weights; the reduce and AdamW kernels update each rank's piece."""
+    import torch
+    n_dp = len(grads)
+    if n_dp < 1 or not (len(w_shards) == len(m_shards) == len(v_shards) == n_dp):
+        raise ValueError("zero_adam_step: one gradient and one shard of each state per rank")
+    n = grads[0].numel()
+    if any(g.numel() != n or g.dtype != grads[0].dtype for g in grads):
+        raise ValueError("zero_adam_step: every rank's gradient is one vector of n elements")
+    base, extra = divmod(n, n_dp)
+    lens = [base + (1 if r < extra else 0) for r in range(n_dp)]   # numpy.array_split
+    starts = [sum(lens[:r]) for r in range(n_dp)]
+    for shards in (w_shards, m_shards, v_shards):
+        for r, x in enumerate(shards):
+            if x.numel() != lens[r] or x.dtype != torch.float32:
+                raise ValueError(f"zero_adam_step: shard {r} must be fp32 of {lens[r]} elements")
+    dev = grads[0].device
+    # the contributions as one [n_dp][n] slab (row k = rank k's gradient)
+    slab = torch.empty(n_dp * n, dtype=grads[0].dtype, device=dev)
+    zero_flat_gather([(g.reshape(-1), k * n) for k, g in enumerate(grads)], n_dp * n, 0, slab,
+                     stream=stream)
+
+    def clone(x):
+        y = torch.empty_like(x)
+        zero_flat_gather([(x.reshape(-1), 0)], x.numel(), 0, y, stream=stream)
+        return y
+
+    new_w = [clone(x) for x in w_shards]
+    new_m = [clone(x) for x in m_shards]
+    new_v = [clone(x) for x in v_shards]
+    whole, _ = zero_flatten_layout([n], 1)         # one slot: the 16-bit weights of all n
+    w16 = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    hp = AdamWHParams(lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=weight_decay,
+                      grad_scale=1.0 / n_dp, step=t)
+    for r in range(n_dp):
+        if lens[r] == 0:
+            continue
+        acc = torch.empty(lens[r], dtype=torch.float32, device=dev)
+        zero_shard_reduce(slab[starts[r]:], n_dp, n, lens[r], acc, stream=stream)
+        zero_shard_adamw(acc, new_w[r], new_m[r], new_v[r], w16, whole, 0, hp,
+                         shard_off=starts[r], length=lens[r], stream=stream)
+    pieces = [(x, s0) for x, s0 in zip(new_w, starts) if x.numel() > 0]
+    full_w = []
+    for _ in range(n_dp):  # the all-gather: every rank receives the whole vector
+        f = torch.empty(n, dtype=torch.float32, device=dev)
+        zero_flat_gather(pieces, n, 0, f, stream=stream)
+        full_w.append(f)
+    return full_w, new_w, new_m, new_v
+
+
 def zero_model_state_bytes(n: float, n_dp: float, stage: int, k: float = 12) -> float:
     out = ctypes.c_double()
     _check(_lib.zero_model_state_bytes(n, n_dp, stage, k, ctypes.byref(out)),
@@ -394,5 +514,6 @@ def library_path() -> str:
 __all__ = ["zero_flatten_layout", "zero_shard_segments", "zero_dim0_layout", "zero_dim0_segments", "zero_shard_reduce",
            "zero_shard_adamw", "zero_shard_adamw_ex", "zero_loss_scale_update",
            "new_loss_scale", "read_loss_scale", "zero_shard_step", "zero_flat_gather",
-           "zero_flat_scatter", "zero_reshard", "zero_model_state_bytes", "zero_comm_bytes",
-           "AdamWHParams", "ZeroLayout", "ZeroError", "ZERO_BF16", "ZERO_FP16", "ZERO_FP32", "library_path"]
+           "zero_flat_scatter", "zero_reshard", "zero_q8_quantize", "zero_q8_dequantize",
+           "zero_shard_step_q8", "q8_blocks", "ZERO_Q8_BLOCK", "zero_model_state_bytes", "zero_comm_bytes",
+           "zero_adam_step", "AdamWHParams", "ZeroLayout", "ZeroError", "ZeroValueError", "ZERO_BF16", "ZERO_FP16", "ZERO_FP32", "library_path"]

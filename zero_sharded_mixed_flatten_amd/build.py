@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libzero_shard.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("zero_shard.hip", "flat_copy.hip", "layout.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("zero_shard.hip", "quant8.hip", "flat_copy.hip", "layout.cpp")]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1,0 +1,460 @@
+// quant8.hip -- gfx950 kernels for 8-bit blockwise communication (ZeRO++).
+//
+// ZeRO++ quantizes the weight all-gather to 8 bits and the gradients of the
+// reduce-scatter ("ZeRO and FSDP", FSDP section; "ZeRO Optimizer, in depth",
+// "Offload and ZeRO++").  The pages give no quantizer; the one here is the
+// plain symmetric blockwise int8 quantizer, one fp32 scale per block of 256
+// elements (s = absmax / 127, q = rint(x / s), ties to even).
+//
+// A block is exactly one wave's quad layout: 64 lanes x 4 consecutive
+// elements, so a block's absmax is one wave reduction (six xor-shuffles) and
+// needs no LDS.  Every kernel is a one-shot grid of one wave per block (four
+// per workgroup when a sum of squares is requested, for one atomic per
+// workgroup), loads issued before arithmetic, non-temporal streaming access
+// -- the layout of the 16-bit step kernels with 4-byte code loads (one
+// contiguous 256-byte span per wave and row) and one scale per row and block
+// read through the scalar cache.
+//
+// Arithmetic matches the oracle's definition operation for operation:
+// correctly rounded fp32 division for x / s and absmax / 127, v_rndne_f32
+// for the rounding, and q * s rounded once to fp32.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <type_traits>
+
+#include "host_common.h"
+#include "step_common.h"
+#include "zero_shard.h"
+
+namespace {
+
+using namespace zero_host;
+using namespace zero_step;
+
+constexpr int kB = ZERO_Q8_BLOCK;
+static_assert(kB == kWave * kQuad, "a quantization block is one wave of quads");
+constexpr int kRowBatchQ8 = 8;          // rows per batch when n_dp is not specialised
+// The fused 8-bit step carries ~125 VALU operations per element (AdamW's
+// divisions and square root, 8 dequantizations, the quantization) against
+// 33 bytes: it needs more waves than the 16-bit step to hide that work under
+// memory time.  Measured on the 7B shard (8 rows, random data), waves per
+// CU: 8 -> 66.8 %, 12 -> 76.4 %, 16 -> 78.4 %, 20 -> 76.7 %, 32 -> 75.0 %.
+constexpr int kQ8StepWavesPerCU = 16;   // residency cap of the fused 8-bit step
+constexpr int kQ8CodecWavesPerCU = 16;  // quantize / dequantize
+
+// max with NaN winning (order independent): the scale of a block holding a
+// NaN is NaN
+__device__ __forceinline__ float nanmax(float a, float b) { return (a != a || a > b) ? a : b; }
+
+__device__ __forceinline__ float wave_nanmax(float m) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) m = nanmax(m, __shfl_xor(m, off, kWave));
+    return m;
+}
+
+// the scale of a block from the four values of each lane (invalid ones 0)
+__device__ __forceinline__ float block_scale(const float x[kQuad]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kQuad; ++e) m = nanmax(fabsf(x[e]), m);
+    return wave_nanmax(m) / 127.0f;
+}
+
+// four codes, byte e = element e; all zero for a zero or non-finite scale
+__device__ __forceinline__ uint32_t quantize4(const float x[kQuad], float s) {
+    if (!(s > 0.0f) || __builtin_isinf(s)) return 0u;
+    uint32_t packed = 0u;
+#pragma unroll
+    for (int e = 0; e < kQuad; ++e) {
+        float r = __builtin_rintf(x[e] / s);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        packed |= (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu) << (8 * e);
+    }
+    return packed;
+}
+
+__device__ __forceinline__ float code(uint32_t packed, int e) {
+    return static_cast<float>(static_cast<int8_t>((packed >> (8 * e)) & 0xFFu));
+}
+
+__device__ __forceinline__ uint32_t load_codes(const int8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+}
+__device__ __forceinline__ void store_codes(int8_t *p, uint32_t x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<uint32_t *>(p));
+}
+
+// the block handled by this wave, made wave-uniform (scalar) for the scale
+// loads; a launch covers at most 2^30 blocks (kMaxLen / kB)
+// Workgroups go round-robin over the 8 XCDs (each with its own L2), so the
+// 32 blocks whose scales share a 128-byte line run on all eight and each L2
+// fetches the line: the 7B step reads 1.06 x its algorithmic bytes.
+// Remapping workgroups so that each XCD takes whole chunks of consecutive
+// blocks removes the re-reads (1.01 x) but costs more than it saves
+// (measured at 16 waves per CU: 4.43 ms in plain order; chunks of 4, 8, 16
+// and 32 blocks: 4.53, 4.61, 4.70 and 4.97 ms), so the order stays plain.
+template <int TPB>
+__device__ __forceinline__ int64_t wave_block() {
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    return static_cast<int64_t>(blockIdx.x) * (TPB / kWave) + w;
+}
+
+// ---------------------------------------------------------------------------
+// quantize / dequantize
+
+template <int XDT, bool VEC>
+__global__ void __launch_bounds__(kWave)
+q8_quantize_kernel(const typename GradT<XDT>::elem *__restrict__ x, int64_t len,
+                   int8_t *__restrict__ q, float *__restrict__ scales) {
+    const int64_t b = wave_block<kWave>();
+    const int lane = threadIdx.x;
+    const int64_t e0 = b * kB + lane * kQuad;
+    float v[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const bool full = e0 + kQuad <= len;
+    if (VEC && full) {
+        widen_quad<XDT>(v, load_quad<XDT>(x + e0));
+    } else {
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e)
+            if (e0 + e < len) v[e] = widen1<XDT>(x[e0 + e]);
+    }
+    const float s = block_scale(v);
+    if (lane == 0) scales[b] = s;
+    const uint32_t c = quantize4(v, s);
+    if (VEC && full) {
+        store_codes(q + e0, c);
+    } else {
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e)
+            if (e0 + e < len) q[e0 + e] = static_cast<int8_t>((c >> (8 * e)) & 0xFFu);
+    }
+}
+
+template <int YDT>
+__device__ __forceinline__ void store_quad_any(void *y, int64_t e0, const float v[kQuad]) {
+    if constexpr (YDT == ZERO_FP32) {
+        store16(static_cast<float *>(y) + e0, f32x4{v[0], v[1], v[2], v[3]});
+    } else {
+        store8(static_cast<uint16_t *>(y) + e0,
+               u32x2{narrow2<YDT>(v[0], v[1]), narrow2<YDT>(v[2], v[3])});
+    }
+}
+
+template <int YDT>
+__device__ __forceinline__ void store_one(void *y, int64_t e, float v) {
+    if constexpr (YDT == ZERO_FP32) static_cast<float *>(y)[e] = v;
+    else static_cast<uint16_t *>(y)[e] = narrow1<YDT>(v);
+}
+
+template <int YDT, bool VEC>
+__global__ void __launch_bounds__(kWave)
+q8_dequantize_kernel(const int8_t *__restrict__ q, const float *__restrict__ scales, int64_t len,
+                     void *__restrict__ y) {
+    const int64_t b = wave_block<kWave>();
+    const int64_t e0 = b * kB + static_cast<int>(threadIdx.x) * kQuad;
+    const float s = scales[b];
+    if (VEC && e0 + kQuad <= len) {
+        const uint32_t c = load_codes(q + e0);
+        float v[kQuad];
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e) v[e] = as_rounded_f32(code(c, e) * s);
+        store_quad_any<YDT>(y, e0, v);
+    } else {
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e)
+            if (e0 + e < len)
+                store_one<YDT>(y, e0 + e, as_rounded_f32(static_cast<float>(q[e0 + e]) * s));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fused step: dequantize + reduce -> scale -> AdamW -> quantize, one pass
+
+template <int NDP>
+struct CodeRows {
+    uint32_t c[NDP > 0 ? NDP : kRowBatchQ8];
+    float s[NDP > 0 ? NDP : kRowBatchQ8];
+};
+
+// a[e] += q_k[e] * s_k for the rows in r (first row assigns)
+template <int NR>
+__device__ __forceinline__ void add_code_rows(float a[kQuad], const uint32_t *c, const float *s,
+                                              int count, bool first) {
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        if (k >= count) break;
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e) {
+            const float x = code(c[k], e) * s[k];
+            a[e] = (first && k == 0) ? x : a[e] + x;
+        }
+    }
+}
+
+// the codes of row k for this lane's quad: vector when the quad is whole,
+// else the valid bytes (0 beyond len)
+__device__ __forceinline__ uint32_t row_codes(const int8_t *__restrict__ p, bool full, int valid) {
+    if (full) return load_codes(p);
+    uint32_t c = 0u;
+    for (int e = 0; e < valid; ++e) c |= (static_cast<uint32_t>(static_cast<uint8_t>(p[e]))) << (8 * e);
+    return c;
+}
+
+// One lane's inputs: NDP rows of codes (the batched path loads its rows
+// later) and the state.  FULL (wave-uniform: every quad of the block lies
+// in the range) takes straight-line vector loads; otherwise each lane loads
+// its valid elements one by one.
+template <int NDP, bool FULL>
+__device__ __forceinline__ void load_inputs(CodeRows<NDP> &r, float w[kQuad], float m[kQuad],
+                                            float v[kQuad], const int8_t *__restrict__ gq,
+                                            const float *__restrict__ gs, int64_t ld, int64_t sld,
+                                            int64_t b, int64_t e0, int valid,
+                                            const float *__restrict__ W,
+                                            const float *__restrict__ M,
+                                            const float *__restrict__ V) {
+    if constexpr (NDP > 0) {
+#pragma unroll
+        for (int k = 0; k < NDP; ++k) {
+            r.c[k] = FULL ? load_codes(gq + k * ld + e0) : row_codes(gq + k * ld + e0, false, valid);
+            r.s[k] = gs[k * sld + b];
+        }
+    }
+    if constexpr (FULL) {
+        const f32x4 w4 = load16(W + e0), m4 = load16(M + e0), v4 = load16(V + e0);
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e) {
+            w[e] = w4[e];
+            m[e] = m4[e];
+            v[e] = v4[e];
+        }
+    } else {
+        for (int e = 0; e < valid; ++e) {
+            w[e] = W[e0 + e];
+            m[e] = M[e0 + e];
+            v[e] = V[e0 + e];
+        }
+    }
+}
+
+template <int TPB, int NDP, bool OVF, bool SSQ>
+__global__ void __launch_bounds__(TPB)
+step_q8_kernel(const int8_t *__restrict__ gq, const float *__restrict__ gs, int64_t ld,
+               int64_t sld, int n_dp, int64_t len, int64_t nblocks, float *__restrict__ W,
+               float *__restrict__ M, float *__restrict__ V, int8_t *__restrict__ wq,
+               float *__restrict__ wsc, Consts c, uint32_t *__restrict__ ovf,
+               double *__restrict__ ssq) {
+    bool bad = false;
+    double ss = 0.0;
+    const int64_t b = wave_block<TPB>();
+    if (b < nblocks) {  // wave-uniform
+        const int lane = static_cast<int>(threadIdx.x) % kWave;
+        const int64_t e0 = b * kB + lane * kQuad;
+        const bool block_full = (b + 1) * kB <= len;  // wave-uniform
+        const int valid = e0 + kQuad <= len ? kQuad : (e0 < len ? static_cast<int>(len - e0) : 0);
+        float a[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float w[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float m[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float v[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
+        CodeRows<NDP> r;
+        if (block_full) {
+            load_inputs<NDP, true>(r, w, m, v, gq, gs, ld, sld, b, e0, valid, W, M, V);
+        } else {
+            load_inputs<NDP, false>(r, w, m, v, gq, gs, ld, sld, b, e0, valid, W, M, V);
+        }
+        loads_issued();
+        if constexpr (NDP > 0) {
+            add_code_rows<NDP>(a, r.c, r.s, NDP, true);
+        } else {
+            for (int k0 = 0; k0 < n_dp; k0 += kRowBatchQ8) {
+                const int cnt = n_dp - k0 < kRowBatchQ8 ? n_dp - k0 : kRowBatchQ8;
+#pragma unroll
+                for (int k = 0; k < kRowBatchQ8; ++k) {
+                    if (k < cnt) {
+                        r.c[k] = row_codes(gq + (k0 + k) * ld + e0, valid == kQuad, valid);
+                        r.s[k] = gs[(k0 + k) * sld + b];
+                    }
+                }
+                add_code_rows<kRowBatchQ8>(a, r.c, r.s, cnt, k0 == 0);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e) {
+            if (e < valid) {
+                if constexpr (OVF) bad |= !__builtin_isfinite(a[e]);
+                const float g = a[e] * c.s;
+                if constexpr (SSQ) ss += static_cast<double>(g) * static_cast<double>(g);
+                adamw_element(g, w[e], m[e], v[e], c);
+            } else {
+                w[e] = 0.0f;  // outside the range: no part of the block's scale
+            }
+        }
+        const float s = block_scale(w);
+        const uint32_t codes = quantize4(w, s);
+        if (lane == 0) wsc[b] = s;
+        if (block_full) {
+            store16(W + e0, f32x4{w[0], w[1], w[2], w[3]});
+            store16(M + e0, f32x4{m[0], m[1], m[2], m[3]});
+            store16(V + e0, f32x4{v[0], v[1], v[2], v[3]});
+            store_codes(wq + e0, codes);
+        } else {
+            for (int e = 0; e < valid; ++e) {
+                W[e0 + e] = w[e];
+                M[e0 + e] = m[e];
+                V[e0 + e] = v[e];
+                wq[e0 + e] = static_cast<int8_t>((codes >> (8 * e)) & 0xFFu);
+            }
+        }
+    }
+    flags_epilogue<TPB, OVF, SSQ>(bad, ss, ovf, ssq);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+template <int V>
+using IntC = std::integral_constant<int, V>;
+template <bool V>
+using BoolC = std::integral_constant<bool, V>;
+
+template <typename F>
+void with_xdt(int dt, F &&f) {
+    if (dt == ZERO_BF16) f(IntC<ZERO_BF16>{});
+    else if (dt == ZERO_FP16) f(IntC<ZERO_FP16>{});
+    else f(IntC<ZERO_FP32>{});
+}
+
+template <typename F>
+void with_bool(bool b, F &&f) {
+    if (b) f(BoolC<true>{});
+    else f(BoolC<false>{});
+}
+
+bool xdt_ok(int dt) { return dt == ZERO_BF16 || dt == ZERO_FP16 || dt == ZERO_FP32; }
+int64_t xdt_bytes(int dt) { return dt == ZERO_FP32 ? 4 : 2; }
+int64_t blocks_of(int64_t len) { return (len + kB - 1) / kB; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool quad_aligned(const void *p, int dt) { return dt == ZERO_FP32 ? aligned16(p) : aligned8(p); }
+
+// any two of the spans overlap
+bool spans_overlap(const Span *s, int n) {
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j)
+            if (overlap(s[i], s[j])) return true;
+    return false;
+}
+
+// the launch grid of a one-shot kernel of `blocks` waves, tpb threads each
+unsigned grid_waves(int64_t blocks, int tpb) {
+    const int64_t per = tpb / kWave;
+    return static_cast<unsigned>((blocks + per - 1) / per);
+}
+
+}  // namespace
+
+extern "C" zero_status zero_q8_quantize(const void *x, zero_dtype xdt, int64_t len, int8_t *q,
+                                        float *scales, void *stream) {
+    if (!xdt_ok(xdt) || len < 0 || len > kMaxLen) return ZERO_EINVAL;
+    if (len == 0) return ZERO_OK;
+    if (!x || !q || !scales) return ZERO_EINVAL;
+    const Span sp[3] = {span_of(x, len, xdt_bytes(xdt)), span_of(q, len, 1),
+                        span_of(scales, blocks_of(len), 4)};
+    if (spans_overlap(sp, 3)) return ZERO_EALIAS;
+    const bool vec = quad_aligned(x, xdt) && aligned4(q);
+    const int64_t nb = blocks_of(len);
+    const size_t lds = residency_lds_bytes(kQ8CodecWavesPerCU, kWave);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    with_xdt(xdt, [&](auto XD) {
+        using E = typename GradT<XD.value>::elem;
+        with_bool(vec, [&](auto VC) {
+            q8_quantize_kernel<XD.value, VC.value><<<grid_waves(nb, kWave), kWave, lds, st>>>(
+                static_cast<const E *>(x), len, q, scales);
+        });
+    });
+    return launch_status();
+}
+
+extern "C" zero_status zero_q8_dequantize(const int8_t *q, const float *scales, int64_t len,
+                                          void *y, zero_dtype ydt, void *stream) {
+    if (!xdt_ok(ydt) || len < 0 || len > kMaxLen) return ZERO_EINVAL;
+    if (len == 0) return ZERO_OK;
+    if (!y || !q || !scales) return ZERO_EINVAL;
+    const Span sp[3] = {span_of(y, len, xdt_bytes(ydt)), span_of(q, len, 1),
+                        span_of(scales, blocks_of(len), 4)};
+    if (spans_overlap(sp, 3)) return ZERO_EALIAS;
+    const bool vec = quad_aligned(y, ydt) && aligned4(q);
+    const int64_t nb = blocks_of(len);
+    const size_t lds = residency_lds_bytes(kQ8CodecWavesPerCU, kWave);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    with_xdt(ydt, [&](auto YD) {
+        with_bool(vec, [&](auto VC) {
+            q8_dequantize_kernel<YD.value, VC.value><<<grid_waves(nb, kWave), kWave, lds, st>>>(
+                q, scales, len, y);
+        });
+    });
+    return launch_status();
+}
+
+extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales, int64_t ld,
+                                          int64_t sld, int64_t len, float *master, float *m,
+                                          float *v, int8_t *wq_full, float *wscales_full,
+                                          const zero_layout *layout, int32_t rank,
+                                          int64_t shard_off, const zero_adamw_hparams *hp,
+                                          uint32_t *overflow, double *sumsq, void *stream) {
+    if (!layout_ok(layout) || !hparams_ok(hp)) return ZERO_EINVAL;
+    const int n_dp = layout->n_dp;
+    if (rank < 0 || rank >= n_dp || shard_off < 0 || len < 0 || len > kMaxLen || ld < len)
+        return ZERO_EINVAL;
+    if (layout->shard % kB != 0 || shard_off % kB != 0) return ZERO_EINVAL;
+    const int64_t nb = blocks_of(len);
+    if (n_dp > 1 && (ld % kQuad != 0 || sld < nb)) return ZERO_EINVAL;
+    if (n_dp > 1 && (static_cast<int64_t>(n_dp - 1) > (INT64_MAX - len) / (ld > 0 ? ld : 1) ||
+                     sld > INT64_MAX / n_dp))
+        return ZERO_EINVAL;
+    if (shard_off > layout->shard || len > layout->shard - shard_off) return ZERO_ERANGE;
+    if (len == 0) return ZERO_OK;
+    if (!gq || !gscales || !master || !m || !v || !wq_full || !wscales_full) return ZERO_EINVAL;
+    const int64_t first = static_cast<int64_t>(rank) * layout->shard + shard_off;
+    int8_t *wq = wq_full + first;
+    float *wsc = wscales_full + first / kB;
+    if (!aligned4(gq) || !aligned4(wq) || !aligned16(master) || !aligned16(m) || !aligned16(v))
+        return ZERO_EINVAL;
+    // outputs pairwise disjoint, and disjoint from every code and scale row
+    Span outs[8];
+    int n_out = 0;
+    outs[n_out++] = span_of(master, len, 4);
+    outs[n_out++] = span_of(m, len, 4);
+    outs[n_out++] = span_of(v, len, 4);
+    outs[n_out++] = span_of(wq, len, 1);
+    outs[n_out++] = span_of(wsc, nb, 4);
+    if (overflow) outs[n_out++] = span_of(overflow, 1, 4);
+    if (sumsq) outs[n_out++] = span_of(sumsq, 1, 8);
+    if (spans_overlap(outs, n_out)) return ZERO_EALIAS;
+    for (int i = 0; i < n_out; ++i) {
+        for (int k = 0; k < n_dp; ++k) {
+            if (overlap(outs[i], span_of(gq + static_cast<int64_t>(k) * ld, len, 1)) ||
+                overlap(outs[i], span_of(gscales + static_cast<int64_t>(k) * sld, nb, 4)))
+                return ZERO_EALIAS;
+        }
+    }
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Consts c = make_consts(*hp);
+    with_bool(overflow != nullptr, [&](auto OV) {
+        with_bool(sumsq != nullptr, [&](auto SS) {
+            constexpr int tpb = SS.value ? 4 * kWave : kWave;
+            const size_t lds = residency_lds_bytes(kQ8StepWavesPerCU, tpb);
+            auto go = [&](auto ND) {
+                step_q8_kernel<tpb, ND.value, OV.value, SS.value>
+                    <<<grid_waves(nb, tpb), tpb, lds, st>>>(gq, gscales, ld, sld, n_dp, len, nb,
+                                                            master, m, v, wq, wsc, c, overflow,
+                                                            sumsq);
+            };
+            if (n_dp == 1) go(IntC<1>{});
+            else if (n_dp == 8) go(IntC<8>{});
+            else go(IntC<0>{});
+        });
+    });
+    return launch_status();
+}

@@ -1,0 +1,221 @@
+// step_common.h -- pieces shared by the library's step kernels (internal:
+// not installed, not part of the C ABI): vector types, the fp32 constants of
+// the AdamW update and their host-side formation, argument validators, the
+// 16-bit conversions, streaming loads and stores, and the arithmetic of one
+// element.
+#ifndef ZERO_SHARD_STEP_COMMON_H
+#define ZERO_SHARD_STEP_COMMON_H
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "host_common.h"
+#include "zero_shard.h"
+
+namespace zero_step {
+
+using zero_host::kWave;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kQuad = 4;  // elements per lane
+
+// One thread per quad (one per element on the unaligned path): a launch
+// covers at most 2^31 - 1 workgroups, so the entry points reject ranges of
+// more than kMaxLen elements (2^38, far beyond any HBM).
+constexpr int64_t kMaxLen = int64_t(1) << 38;
+
+// fp32 constants of the update, formed on the host (see zero_adamw_hparams)
+struct Consts {
+    float s, b1, c1, b2, c2, bc1, bc2, lr, eps, d;
+};
+
+inline bool dtype_ok(int dt) { return dt == ZERO_BF16 || dt == ZERO_FP16; }
+
+inline bool layout_ok(const zero_layout *l) {
+    if (!l || l->n_dp < 1 || l->align < 1 || l->shard < 0 || l->n < 0) return false;
+    if (l->shard % l->align != 0) return false;
+    if (l->shard > 0 && l->n_dp > INT64_MAX / l->shard) return false;
+    return l->n_pad == l->shard * l->n_dp && l->n <= l->n_pad;
+}
+
+inline bool hparams_ok(const zero_adamw_hparams *hp) {
+    if (!hp || hp->step < 1) return false;
+    if (!std::isfinite(hp->lr)) return false;
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return false;
+    if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return false;
+    if (!(std::isfinite(hp->eps) && hp->eps > 0.0)) return false;
+    if (!(std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.0)) return false;
+    return std::isfinite(hp->grad_scale) && hp->grad_scale > 0.0;
+}
+
+// each constant in double, rounded once to fp32
+inline Consts make_consts(const zero_adamw_hparams &hp) {
+    const double t = static_cast<double>(hp.step);
+    Consts c;
+    c.s = static_cast<float>(hp.grad_scale);
+    c.b1 = static_cast<float>(hp.beta1);
+    c.c1 = static_cast<float>(1.0 - hp.beta1);
+    c.b2 = static_cast<float>(hp.beta2);
+    c.c2 = static_cast<float>(1.0 - hp.beta2);
+    c.bc1 = static_cast<float>(1.0 - std::pow(hp.beta1, t));
+    c.bc2 = static_cast<float>(1.0 - std::pow(hp.beta2, t));
+    c.lr = static_cast<float>(hp.lr);
+    c.eps = static_cast<float>(hp.eps);
+    c.d = static_cast<float>(1.0 - hp.lr * hp.weight_decay);
+    return c;
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit <-> fp32.  Widening is exact.  Narrowing uses gfx950's packed
+// converts (v_cvt_pk_bf16_f32, v_cvt_pk_f16_f32): round to nearest even.
+
+template <int DT>
+__device__ __forceinline__ f32x2 widen2(uint32_t w) {
+    if constexpr (DT == ZERO_BF16) {
+        return f32x2{__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
+    } else {
+        return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t narrow2(float lo, float hi) {
+    const f32x2 x{lo, hi};
+    if constexpr (DT == ZERO_BF16) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+    } else {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+    }
+}
+
+// An fp32 value as rounded: the compiler may not fold the operation that
+// produced it into a later 16-bit conversion (v_fma_mix* would round the
+// exact result once, to 16 bits, instead of to fp32 and then to 16 bits).
+__device__ __forceinline__ float as_rounded_f32(float x) {
+    asm("" : "+v"(x));
+    return x;
+}
+
+template <int DT>
+__device__ __forceinline__ uint16_t narrow1(float f) {
+    return static_cast<uint16_t>(narrow2<DT>(f, 0.0f) & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// memory helpers: loads/stores marked non-temporal (streamed once)
+
+__device__ __forceinline__ u32x2 load8(const uint16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
+__device__ __forceinline__ f32x4 load16(const float *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+}
+__device__ __forceinline__ void store8(uint16_t *p, u32x2 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x2 *>(p));
+}
+__device__ __forceinline__ void store16(float *p, f32x4 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
+}
+
+// Gradient rows: 16-bit (4 elements of a quad = 8 bytes per lane) or fp32
+// (16 bytes per lane); the element type and the per-lane quad type.
+template <int GDT>
+struct GradT {
+    using elem = uint16_t;
+    using quad = u32x2;
+};
+template <>
+struct GradT<ZERO_FP32> {
+    using elem = float;
+    using quad = f32x4;
+};
+
+template <int DT>
+__device__ __forceinline__ float widen1(typename GradT<DT>::elem h) {
+    if constexpr (DT == ZERO_FP32) {
+        return h;
+    } else {
+        return widen2<DT>(static_cast<uint32_t>(h))[0];
+    }
+}
+
+// a row's quad, non-temporal (streamed once)
+template <int GDT>
+__device__ __forceinline__ typename GradT<GDT>::quad load_quad(const typename GradT<GDT>::elem *p) {
+    if constexpr (GDT == ZERO_FP32) {
+        return load16(p);
+    } else {
+        return load8(p);
+    }
+}
+// the four fp32 values of one row's quad (16-bit widening is exact)
+template <int GDT>
+__device__ __forceinline__ void widen_quad(float t[kQuad], typename GradT<GDT>::quad x) {
+    if constexpr (GDT == ZERO_FP32) {
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e) t[e] = x[e];
+    } else {
+        const f32x2 t0 = widen2<GDT>(x[0]), t1 = widen2<GDT>(x[1]);
+        t[0] = t0[0];
+        t[1] = t0[1];
+        t[2] = t1[0];
+        t[3] = t1[1];
+    }
+}
+
+// Keeps the compiler from sinking any of the loads issued so far below the
+// arithmetic that follows: one round trip to HBM per quad, not two.
+__device__ __forceinline__ void loads_issued() { __builtin_amdgcn_sched_barrier(0); }
+
+// The optional shard-wide outputs: one atomic per wave for the flag (only
+// when a lane saw a non-finite value), a wave then workgroup reduction and
+// one atomic add per workgroup for the sum.  Every thread of the workgroup
+// must reach this point.
+template <int TPB, bool OVF, bool SSQ>
+__device__ __forceinline__ void flags_epilogue(bool bad, double ss, uint32_t *ovf, double *ssq) {
+    if constexpr (OVF) {
+        if (__ballot(bad) != 0 && (threadIdx.x & (kWave - 1)) == 0) atomicOr(ovf, 1u);
+    }
+    if constexpr (SSQ) {
+        __shared__ double part[TPB / kWave];
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+        if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = ss;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double t = 0.0;
+#pragma unroll
+            for (int wv = 0; wv < TPB / kWave; ++wv) t += part[wv];
+            unsafeAtomicAdd(ssq, t);  // device memory: native global_atomic_add_f64
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the arithmetic of one element
+
+// AdamW ("ZeRO and FSDP", "A sharded Adam step", with decoupled decay):
+// m = b1 m + c1 g; v = b2 v + c2 g^2; w = w d - lr (m / bc1) / (sqrt(v / bc2) + eps)
+__device__ __forceinline__ void adamw_element(float g, float &w, float &m, float &v,
+                                              const Consts &c) {
+    const float mt = c.b1 * m + c.c1 * g;
+    const float vt = c.b2 * v + c.c2 * (g * g);
+    const float mhat = mt / c.bc1;
+    const float vhat = vt / c.bc2;
+    const float den = sqrtf(vhat) + c.eps;
+    const float upd = mhat / den;
+    w = w * c.d - c.lr * upd;
+    m = mt;
+    v = vt;
+}
+
+}  // namespace zero_step
+
+#endif
