@@ -46,7 +46,8 @@ def parse():
                    help="workload: 1 GPT-2-XL n_dp=1, 2 7B n_dp=8 (default), "
                         "3 7B n_dp=64, 4 7B n_dp=8 fp16 with 4 micro-batches, "
                         "5 7B per-parameter dim-0 sharding n_dp=8 with fp32 gradients, "
-                        "6 7B n_dp=8 with 8-bit blockwise rows and weights (ZeRO++)")
+                        "6 7B n_dp=8 with 8-bit blockwise rows and weights (ZeRO++), "
+                        "7 configuration 4 with clipping and a dynamic loss scale")
     p.add_argument("--cpu-sample-log2", type=int, default=25,
                    help="CPU baseline sample: 2^k parameters of the shard")
     p.add_argument("--cpu-steps", type=int, default=8)
@@ -174,6 +175,9 @@ def main():
         wfull = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device=dev)
     acc = torch.empty(S, dtype=torch.float32, device=dev) if micro > 1 else None
     flag = torch.zeros(1, dtype=torch.int32, device=dev) if micro > 1 else None
+    if wl.controls:
+        sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+        loss_scale = zs.new_loss_scale(wl.loss_scale, dev)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
@@ -200,20 +204,35 @@ def main():
             # resident slab stands in for each micro-batch's rows), then
             # AdamW gated on the overflow flag
             flag.zero_()
+            if wl.controls:
+                sumsq.zero_()
             for mb in range(micro):
+                last = mb == micro - 1
                 zs.zero_shard_reduce(slab, n_dp, S, S, acc, accumulate=mb > 0, overflow=flag,
+                                     sumsq=sumsq if wl.controls and last else None,
                                      stream=stream)
-            hp = zs.AdamWHParams(step=t, grad_scale=1.0 / (n_dp * wl.loss_scale * micro),
-                                 **hp_kw)
+            if wl.controls:
+                # the loss scale lives on the device: grad_scale keeps the average only
+                hp = zs.AdamWHParams(step=t, grad_scale=1.0 / (n_dp * micro), **hp_kw)
+            else:
+                hp = zs.AdamWHParams(step=t, grad_scale=1.0 / (n_dp * wl.loss_scale * micro),
+                                     **hp_kw)
             e0 = torch.cuda.Event(enable_timing=True) if timed else None
             e1 = torch.cuda.Event(enable_timing=True) if timed else None
             if timed:
                 e0.record(stream)
-            zs.zero_shard_adamw(acc, master, m, v, wfull, lay, rank, hp, skip=flag,
-                                stream=stream)
+            if wl.controls:
+                zs.zero_shard_adamw_ex(acc, master, m, v, wfull, lay, rank, hp, skip=flag,
+                                       sumsq=sumsq, max_norm=1.0, loss_scale=loss_scale,
+                                       stream=stream)
+            else:
+                zs.zero_shard_adamw(acc, master, m, v, wfull, lay, rank, hp, skip=flag,
+                                    stream=stream)
             if timed:
                 e1.record(stream)
                 events.append((e0, e1))
+            if wl.controls:
+                zs.zero_loss_scale_update(loss_scale, flag, 2.0, 0.5, 2000, stream=stream)
 
     t = 0
     for _ in range(args.warmup):
@@ -238,7 +257,9 @@ def main():
         # 4 B written by the first reduce, 2 n_dp + 8 by each later one,
         # 30 by the gated AdamW (acc 4 + state 12 read, state 12 + weight 2 written)
         bytes_per_param = (gbytes * n_dp + 4) + (micro - 1) * (gbytes * n_dp + 8) + 30
-        kernel = "adamw_quad_kernel (gated AdamW + cast; timed launch)"
+        kernel = ("adamw_quad_kernel (gated AdamW with clipping and dynamic loss scale + cast; "
+                  "timed launch)" if wl.controls else
+                  "adamw_quad_kernel (gated AdamW + cast; timed launch)")
     step_bytes = bytes_per_param * S
     kms = [a.elapsed_time(b) for a, b in events]
     k_avg = statistics.fmean(kms)
@@ -271,7 +292,8 @@ def main():
                    "state_dtype": "fp32",
                    "weight_dtype": "int8 blocks of 256 + fp32 scale" if q8 else "bf16",
                    "micro_batches": micro, "bytes_per_param": bytes_per_param,
-                   "launches_per_step": 1 if micro == 1 else micro + 1},
+                   "controls": "clip 1.0 + dynamic loss scale" if wl.controls else None,
+                   "launches_per_step": 1 if micro == 1 else micro + 1 + int(wl.controls)},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "launch_ms_avg": k_avg, "launch_ms_min": min(kms),
@@ -465,6 +487,8 @@ def cpu_baseline(wl, S, rank, log2n, steps):
         return {"value": n * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
                 "sample": f"first {n} parameters of rank {rank}'s shard, {wl.n_dp} 8-bit rows, "
                           f"{steps} optimizer steps, single-threaded C oracle ({dt:.1f} s)"}
+    scale = np.array([wl.loss_scale], np.float32)
+    good = np.zeros(1, np.int32)
     t0 = time.perf_counter()
     for t in range(1, steps + 1):
         if wl.micro_batches == 1:
@@ -472,11 +496,20 @@ def cpu_baseline(wl, S, rank, log2n, steps):
                         grad_scale=1.0 / wl.n_dp, **wl.hp)
         else:
             flag = np.zeros(1, np.uint32)
+            ss = np.zeros(1, np.float64)
             for mb in range(wl.micro_batches):
-                oracle.reduce(rows, gdt, wl.n_dp, n, n, acc, mb > 0, overflow=flag)
-            oracle.adamw(acc, w, m, v, wout, oracle.BF16, n, t,
-                         grad_scale=1.0 / (wl.n_dp * wl.loss_scale * wl.micro_batches),
-                         skip=flag, **wl.hp)
+                last = mb == wl.micro_batches - 1
+                oracle.reduce(rows, gdt, wl.n_dp, n, n, acc, mb > 0, overflow=flag,
+                              sumsq=ss if wl.controls and last else None)
+            if wl.controls:
+                oracle.adamw_ex(acc, w, m, v, wout, oracle.BF16, n, t,
+                                grad_scale=1.0 / (wl.n_dp * wl.micro_batches), skip=flag,
+                                sumsq=ss, max_norm=1.0, loss_scale=scale, **wl.hp)
+                oracle.loss_scale_update(scale, good, int(flag[0]), 2.0, 0.5, 2000)
+            else:
+                oracle.adamw(acc, w, m, v, wout, oracle.BF16, n, t,
+                             grad_scale=1.0 / (wl.n_dp * wl.loss_scale * wl.micro_batches),
+                             skip=flag, **wl.hp)
     dt = time.perf_counter() - t0
     return {"value": n * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} parameters of rank {rank}'s shard, {wl.n_dp} gradient rows, "

@@ -94,6 +94,7 @@ class Workload:
     note: Optional[str] = None
     layout: str = "flat"         # "flat" (one vector) or "dim0" (per-parameter)
     comm: str = "16bit"          # "16bit" rows / weights, or "q8" (8-bit blockwise, ZeRO++)
+    controls: bool = False       # global-norm clipping and a dynamic loss scale on the device
     shapes: Optional[List[Tuple[int, int]]] = None
 
 
@@ -122,6 +123,12 @@ def workloads() -> List[Workload]:
                  comm="q8",
                  note="8-bit blockwise rows in, 8-bit weights out (ZeRO++ quantized "
                       "reduce-scatter and all-gather); rows quantized from fp32 draws"),
+        Workload(7, "llama7b_ndp8_fp16_accum4_clip", l7, 8, 1,
+                 GradDraw(F16, 1e-3, scale=65536.0), micro_batches=4,
+                 loss_scale=65536.0, steps=(1,), controls=True,
+                 note="configuration 4 with the step controls: the last reduce sums the "
+                      "squares, AdamW clips to global norm 1.0 with the device-resident "
+                      "dynamic loss scale, and the scale is updated on the device"),
     ]
 
 

@@ -8,9 +8,9 @@
 //
 // A block is exactly one wave's quad layout: 64 lanes x 4 consecutive
 // elements, so a block's absmax is one wave reduction (six xor-shuffles) and
-// needs no LDS.  Every kernel is a one-shot grid of one wave per block (four
-// per workgroup when a sum of squares is requested, for one atomic per
-// workgroup), loads issued before arithmetic, non-temporal streaming access
+// needs no LDS.  Every kernel is a one-shot grid of one wave per block (16
+// per workgroup when a sum of squares is requested, for one atomic per 4096
+// elements), loads issued before arithmetic, non-temporal streaming access
 // -- the layout of the 16-bit step kernels with 4-byte code loads (one
 // contiguous 256-byte span per wave and row) and one scale per row and block
 // read through the scalar cache.
@@ -443,7 +443,10 @@ extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales
     const Consts c = make_consts(*hp);
     with_bool(overflow != nullptr, [&](auto OV) {
         with_bool(sumsq != nullptr, [&](auto SS) {
-            constexpr int tpb = SS.value ? 4 * kWave : kWave;
+            // with a sum of squares: one fp64 atomic per workgroup into one
+            // address, so 16 blocks (4096 elements) per workgroup keep the
+            // atomics below the rate that would set the time
+            constexpr int tpb = SS.value ? 16 * kWave : kWave;
             const size_t lds = residency_lds_bytes(kQ8StepWavesPerCU, tpb);
             auto go = [&](auto ND) {
                 step_q8_kernel<tpb, ND.value, OV.value, SS.value>

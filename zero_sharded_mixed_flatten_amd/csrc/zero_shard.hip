@@ -55,9 +55,8 @@ constexpr int kRowBatch = 8;    // rows loaded together when n_dp is not special
 // Residency caps in waves per CU, measured per kernel at the workloads'
 // sizes with one-wave workgroups (a finished wave's slot is refilled at
 // once; with four-wave workgroups a slot frees only when all four are done,
-// which cost 8-10%).  When a kernel also sums squares it runs four-wave
-// workgroups (one atomic per workgroup instead of four) at the same wave cap
-// rounded to whole workgroups.
+// which cost 8-10%).  The variants that also sum squares are shaped by
+// their atomics instead (kSsqBlock below).
 // Fused step: 10 waves with 1 row (56 B per lane in flight), 7 with 8 rows
 // (112 B), and with 64 rows the 152 VGPRs per lane already allow only 12.
 // With 8 fp32 rows (176 B per lane in flight) 5 waves per CU measured best
@@ -67,6 +66,17 @@ constexpr int step_waves_per_cu(int gdt, int ndp) {
     return ndp == 1 ? 10 : ndp == 64 ? 12 : 7;
 }
 constexpr int kReduceWavesPerCU = 10;
+// Variants that sum squares end with one fp64 atomic per workgroup into one
+// address, and the atomics, not memory, then set the time: the 7B reduce
+// with four-wave workgroups (one atomic per 1024 elements) took 10.4 ms
+// against 3.0 ms without the sum.  Eight-wave workgroups with two quads per
+// lane (one atomic per 4096 elements) at 16 waves per CU: 3.46 ms.  64 rows
+// keep one quad per lane (VGPRs); their workgroups cover 2048 elements.
+constexpr int kSsqBlock = 512;
+constexpr int kSsqWavesPerCU = 16;
+constexpr int ssq_quads(int ndp) { return ndp == 64 ? 1 : 2; }
+// the element-wise kernels loop; with a sum their grid is capped
+constexpr int64_t kSsqScalarBlocks = 4096;
 constexpr int kAdamwWavesPerCU = 10;
 // Device-side step controls (zero_step_control with the static part of the
 // gradient scale alongside).
@@ -130,7 +140,39 @@ __device__ __forceinline__ void sum_rows(float a[kQuad], Rows<GDT, NDP> &r,
 // ---------------------------------------------------------------------------
 // fused step: reduce -> scale -> AdamW -> cast, one pass
 
-template <int TPB, int GDT, int WDT, int NDP, bool OVF, bool SSQ>
+// One quad of the fused step after its loads: reduce the rows, AdamW, store.
+template <int GDT, int WDT, int NDP, bool OVF, bool SSQ>
+__device__ __forceinline__ void step_quad_finish(Rows<GDT, NDP> &rows, f32x4 w4, f32x4 m4,
+                                                 f32x4 v4,
+                                                 const typename GradT<GDT>::elem *__restrict__ g,
+                                                 int64_t ld, int n_dp, int64_t e0,
+                                                 float *__restrict__ W, float *__restrict__ M,
+                                                 float *__restrict__ V,
+                                                 uint16_t *__restrict__ out, const Consts &c,
+                                                 bool &bad, double &ss) {
+    float a[kQuad];
+    sum_rows<GDT, NDP>(a, rows, g, ld, n_dp);
+    float w[kQuad] = {w4[0], w4[1], w4[2], w4[3]};
+    float m[kQuad] = {m4[0], m4[1], m4[2], m4[3]};
+    float v[kQuad] = {v4[0], v4[1], v4[2], v4[3]};
+#pragma unroll
+    for (int e = 0; e < kQuad; ++e) {
+        if constexpr (OVF) bad |= !__builtin_isfinite(a[e]);
+        const float gr = a[e] * c.s;
+        if constexpr (SSQ) ss += static_cast<double>(gr) * static_cast<double>(gr);
+        adamw_element(gr, w[e], m[e], v[e], c);
+    }
+    store16(W + e0, f32x4{w[0], w[1], w[2], w[3]});
+    store16(M + e0, f32x4{m[0], m[1], m[2], m[3]});
+    store16(V + e0, f32x4{v[0], v[1], v[2], v[3]});
+    store8(out + e0, u32x2{narrow2<WDT>(w[0], w[1]), narrow2<WDT>(w[2], w[3])});
+}
+
+// Q quads per lane, TPB * kQuad elements apart (every load instruction of a
+// wave still covers one contiguous span), all loaded before the first add.
+// Q > 1 only serves the variants that sum squares, to cut their atomics
+// (kSsqBlock); Q == 1 keeps the single guarded body of the hot path.
+template <int TPB, int Q, int GDT, int WDT, int NDP, bool OVF, bool SSQ>
 __global__ void __launch_bounds__(TPB)
 step_quad_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld, int n_dp,
                  int64_t nquad,
@@ -139,29 +181,42 @@ step_quad_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld
                  double *__restrict__ ssq) {
     bool bad = false;
     double ss = 0.0;
-    const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
-    if (q < nquad) {
-        const int64_t e0 = q * kQuad;
-        Rows<GDT, NDP> rows;
-        load_rows<GDT, NDP>(rows, grads + e0, ld);
-        const f32x4 w4 = load16(W + e0), m4 = load16(M + e0), v4 = load16(V + e0);
-        loads_issued();
-        float a[kQuad];
-        sum_rows<GDT, NDP>(a, rows, grads + e0, ld, n_dp);
-        float w[kQuad] = {w4[0], w4[1], w4[2], w4[3]};
-        float m[kQuad] = {m4[0], m4[1], m4[2], m4[3]};
-        float v[kQuad] = {v4[0], v4[1], v4[2], v4[3]};
-#pragma unroll
-        for (int e = 0; e < kQuad; ++e) {
-            if constexpr (OVF) bad |= !__builtin_isfinite(a[e]);
-            const float g = a[e] * c.s;
-            if constexpr (SSQ) ss += static_cast<double>(g) * static_cast<double>(g);
-            adamw_element(g, w[e], m[e], v[e], c);
+    if constexpr (Q == 1) {
+        const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
+        if (q < nquad) {
+            const int64_t e0 = q * kQuad;
+            Rows<GDT, NDP> rows;
+            load_rows<GDT, NDP>(rows, grads + e0, ld);
+            const f32x4 w4 = load16(W + e0), m4 = load16(M + e0), v4 = load16(V + e0);
+            loads_issued();
+            step_quad_finish<GDT, WDT, NDP, OVF, SSQ>(rows, w4, m4, v4, grads + e0, ld, n_dp, e0,
+                                                      W, M, V, out, c, bad, ss);
         }
-        store16(W + e0, f32x4{w[0], w[1], w[2], w[3]});
-        store16(M + e0, f32x4{m[0], m[1], m[2], m[3]});
-        store16(V + e0, f32x4{v[0], v[1], v[2], v[3]});
-        store8(out + e0, u32x2{narrow2<WDT>(w[0], w[1]), narrow2<WDT>(w[2], w[3])});
+    } else {
+        int64_t qi[Q];
+        Rows<GDT, NDP> rows[Q];
+        f32x4 w4[Q], m4[Q], v4[Q];
+#pragma unroll
+        for (int u = 0; u < Q; ++u) {
+            qi[u] = (static_cast<int64_t>(blockIdx.x) * Q + u) * TPB + threadIdx.x;
+            if (qi[u] < nquad) {
+                const int64_t e0 = qi[u] * kQuad;
+                load_rows<GDT, NDP>(rows[u], grads + e0, ld);
+                w4[u] = load16(W + e0);
+                m4[u] = load16(M + e0);
+                v4[u] = load16(V + e0);
+            }
+        }
+        loads_issued();
+#pragma unroll
+        for (int u = 0; u < Q; ++u) {
+            if (qi[u] < nquad) {
+                const int64_t e0 = qi[u] * kQuad;
+                step_quad_finish<GDT, WDT, NDP, OVF, SSQ>(rows[u], w4[u], m4[u], v4[u],
+                                                          grads + e0, ld, n_dp, e0, W, M, V,
+                                                          out, c, bad, ss);
+            }
+        }
     }
     flags_epilogue<TPB, OVF, SSQ>(bad, ss, ovf, ssq);
 }
@@ -197,7 +252,28 @@ step_scalar_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t 
 // ---------------------------------------------------------------------------
 // reduce into an fp32 buffer (optionally accumulating across micro-batches)
 
-template <int TPB, int GDT, int NDP, bool ACC, bool OVF, bool SSQ>
+// One quad of the reduce after its loads: sum, accumulate, flags, store.
+template <int GDT, int NDP, bool ACC, bool OVF, bool SSQ>
+__device__ __forceinline__ void reduce_quad_finish(Rows<GDT, NDP> &rows, f32x4 prev,
+                                                   const typename GradT<GDT>::elem *__restrict__ g,
+                                                   int64_t ld, int n, int64_t e0,
+                                                   float *__restrict__ acc, bool &bad,
+                                                   double &ss) {
+    float a[kQuad];
+    sum_rows<GDT, NDP>(a, rows, g, ld, n);
+    if constexpr (ACC) {
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e) a[e] = prev[e] + a[e];
+    }
+#pragma unroll
+    for (int e = 0; e < kQuad; ++e) {
+        if constexpr (OVF) bad |= !__builtin_isfinite(a[e]);
+        if constexpr (SSQ) ss += static_cast<double>(a[e]) * static_cast<double>(a[e]);
+    }
+    store16(acc + e0, f32x4{a[0], a[1], a[2], a[3]});
+}
+
+template <int TPB, int Q, int GDT, int NDP, bool ACC, bool OVF, bool SSQ>
 __global__ void __launch_bounds__(TPB)
 reduce_quad_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld, int n,
                    int64_t nquad,
@@ -205,26 +281,41 @@ reduce_quad_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t 
                    double *__restrict__ ssq) {
     bool bad = false;
     double ss = 0.0;
-    const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
-    if (q < nquad) {
-        const int64_t e0 = q * kQuad;
-        Rows<GDT, NDP> rows;
-        load_rows<GDT, NDP>(rows, grads + e0, ld);
-        f32x4 prev = {};
-        if constexpr (ACC) prev = load16(acc + e0);
+    if constexpr (Q == 1) {
+        const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
+        if (q < nquad) {
+            const int64_t e0 = q * kQuad;
+            Rows<GDT, NDP> rows;
+            load_rows<GDT, NDP>(rows, grads + e0, ld);
+            f32x4 prev = {};
+            if constexpr (ACC) prev = load16(acc + e0);
+            loads_issued();
+            reduce_quad_finish<GDT, NDP, ACC, OVF, SSQ>(rows, prev, grads + e0, ld, n, e0, acc,
+                                                        bad, ss);
+        }
+    } else {
+        int64_t qi[Q];
+        Rows<GDT, NDP> rows[Q];
+        f32x4 prev[Q];
+#pragma unroll
+        for (int u = 0; u < Q; ++u) {
+            qi[u] = (static_cast<int64_t>(blockIdx.x) * Q + u) * TPB + threadIdx.x;
+            prev[u] = f32x4{};
+            if (qi[u] < nquad) {
+                const int64_t e0 = qi[u] * kQuad;
+                load_rows<GDT, NDP>(rows[u], grads + e0, ld);
+                if constexpr (ACC) prev[u] = load16(acc + e0);
+            }
+        }
         loads_issued();
-        float a[kQuad];
-        sum_rows<GDT, NDP>(a, rows, grads + e0, ld, n);
-        if constexpr (ACC) {
 #pragma unroll
-            for (int e = 0; e < kQuad; ++e) a[e] = prev[e] + a[e];
+        for (int u = 0; u < Q; ++u) {
+            if (qi[u] < nquad) {
+                const int64_t e0 = qi[u] * kQuad;
+                reduce_quad_finish<GDT, NDP, ACC, OVF, SSQ>(rows[u], prev[u], grads + e0, ld, n,
+                                                            e0, acc, bad, ss);
+            }
         }
-#pragma unroll
-        for (int e = 0; e < kQuad; ++e) {
-            if constexpr (OVF) bad |= !__builtin_isfinite(a[e]);
-            if constexpr (SSQ) ss += static_cast<double>(a[e]) * static_cast<double>(a[e]);
-        }
-        store16(acc + e0, f32x4{a[0], a[1], a[2], a[3]});
     }
     flags_epilogue<TPB, OVF, SSQ>(bad, ss, ovf, ssq);
 }
@@ -425,6 +516,13 @@ unsigned grid_for(int64_t items, int tpb = kBlock) {
     return static_cast<unsigned>(b < 1 ? 1 : b);
 }
 
+// grid of an element-wise (grid-stride) kernel: one thread per element, or
+// at most kSsqScalarBlocks workgroups when it ends in a sum's atomic
+unsigned scalar_grid(int64_t items, bool ssq) {
+    const unsigned g = grid_for(items);
+    return ssq && g > kSsqScalarBlocks ? static_cast<unsigned>(kSsqScalarBlocks) : g;
+}
+
 // rows of the gradient slab all fit in int64 and do not wrap
 bool rows_ok(int n_rows, int64_t ld, int64_t len) {
     if (n_rows < 1 || len < 0 || ld < len) return false;
@@ -461,18 +559,20 @@ extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int3
             with_bool(overflow != nullptr, [&](auto OV) {
                 with_bool(sumsq != nullptr, [&](auto SS) {
                     if (nquad > 0) {
-                        constexpr int tpb = SS.value ? kBlock : kWave;
-                        const size_t lds = residency_lds_bytes(kReduceWavesPerCU, tpb);
+                        constexpr int tpb = SS.value ? kSsqBlock : kWave;
+                        const size_t lds = residency_lds_bytes(
+                            SS.value ? kSsqWavesPerCU : kReduceWavesPerCU, tpb);
                         with_ndp<GD.value>(n_contrib, [&](auto ND) {
-                            reduce_quad_kernel<tpb, GD.value, ND.value, AC.value, OV.value,
+                            constexpr int q = SS.value ? ssq_quads(ND.value) : 1;
+                            reduce_quad_kernel<tpb, q, GD.value, ND.value, AC.value, OV.value,
                                                SS.value>
-                                <<<grid_for(nquad, tpb), tpb, lds, st>>>(
+                                <<<grid_for(nquad, tpb * q), tpb, lds, st>>>(
                                     g, ld, n_contrib, nquad, acc, overflow, sumsq);
                         });
                     }
                     if (len > done) {
                         reduce_scalar_kernel<GD.value, AC.value, OV.value, SS.value>
-                            <<<grid_for(len - done), kBlock, 0, st>>>(
+                            <<<scalar_grid(len - done, SS.value), kBlock, 0, st>>>(
                                 g + done, ld, n_contrib, len - done, acc + done, overflow, sumsq);
                     }
                 });
@@ -614,19 +714,21 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
             with_bool(overflow != nullptr, [&](auto OV) {
                 with_bool(sumsq != nullptr, [&](auto SS) {
                     if (nquad > 0) {
-                        constexpr int tpb = SS.value ? kBlock : kWave;
+                        constexpr int tpb = SS.value ? kSsqBlock : kWave;
                         with_ndp<GD.value>(n_dp, [&](auto ND) {
+                            constexpr int q = SS.value ? ssq_quads(ND.value) : 1;
                             const size_t lds = residency_lds_bytes(
-                                step_waves_per_cu(GD.value, ND.value), tpb);
-                            step_quad_kernel<tpb, GD.value, WD.value, ND.value, OV.value,
+                                SS.value ? kSsqWavesPerCU : step_waves_per_cu(GD.value, ND.value),
+                                tpb);
+                            step_quad_kernel<tpb, q, GD.value, WD.value, ND.value, OV.value,
                                              SS.value>
-                                <<<grid_for(nquad, tpb), tpb, lds, st>>>(
+                                <<<grid_for(nquad, tpb * q), tpb, lds, st>>>(
                                     g, ld, n_dp, nquad, master, m, v, slot, c, overflow, sumsq);
                         });
                     }
                     if (len > done) {
                         step_scalar_kernel<GD.value, WD.value, OV.value, SS.value>
-                            <<<grid_for(len - done), kBlock, 0, st>>>(
+                            <<<scalar_grid(len - done, SS.value), kBlock, 0, st>>>(
                                 g + done, ld, n_dp, len - done, master + done, m + done,
                                 v + done, slot + done, c, overflow, sumsq);
                     }
