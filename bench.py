@@ -52,11 +52,14 @@ def parse():
                    help="CPU baseline sample: 2^k parameters of the shard")
     p.add_argument("--cpu-steps", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--op", choices=["step", "reshard", "consolidate"], default="step",
+    p.add_argument("--op", choices=["step", "reshard", "consolidate", "quantize", "dequantize"],
+                   default="step",
                    help="step: the optimizer step (default); reshard: new rank 5 of 16's "
                         "shard of the 7B fp32 master, m and v from the 8-rank shards; "
                         "consolidate: the 8-rank fp32 master shards scattered into the "
-                        "7B model's 291 per-parameter fp32 tensors")
+                        "7B model's 291 per-parameter fp32 tensors; quantize / dequantize: "
+                        "the 8-bit codec on rank 1's fp32 gradient of the 7B shard (to int8 "
+                        "blocks, and back to bf16)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (the known-size "
                         "reference that scales the HBM byte counters) --steps times and exit")
@@ -110,6 +113,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, args.steps)
+        return
+    if args.op in ("quantize", "dequantize"):
+        bench_codec(args)
         return
     if args.op != "step":
         bench_copies(args)
@@ -414,6 +420,98 @@ def bench_copies(args):
         del src
         torch.cuda.empty_cache()
         line["cpu_baseline"] = cpu_baseline_copy(args.op, s8, n)
+    print(json.dumps(line), flush=True)
+
+
+def bench_codec(args):
+    """The 8-bit blockwise codec of ZeRO++-style communication on the 7B
+    shard (8 ranks, rank 1, 842,301,952 elements): quantize fp32 -> int8
+    codes + fp32 block scales (4 bytes read, 1 + 4/256 written per element),
+    or dequantize them to bf16 (1 + 4/256 read, 2 written)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import zero_sharded_mixed_flatten_amd as zs
+    from synth import F32
+    from synth.synth_const import BUF_GRAD, outlier_threshold
+    from synth.workloads import llama7b_numels
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lay, _ = zs.zero_flatten_layout(llama7b_numels(), 8, zs.ZERO_Q8_BLOCK)
+    S, rank = lay.shard, 1
+    x = torch.empty(S, dtype=torch.float32, device=dev)
+    synth.fill_device(x, F32, 0, synth.tag(BUF_GRAD, 6, 1, 0, 0), rank * S, 1e-3,
+                      outlier_threshold(0.01), 100.0)
+    q = torch.empty(S, dtype=torch.int8, device=dev)
+    sc = torch.empty(zs.q8_blocks(S), dtype=torch.float32, device=dev)
+    y = torch.empty(S, dtype=torch.bfloat16, device=dev)
+    zs.zero_q8_quantize(x, q, sc)
+    stream = torch.cuda.current_stream(dev)
+    if args.op == "quantize":
+        call = lambda: zs.zero_q8_quantize(x, q, sc, stream=stream)
+        per_elem = 4 + 1 + 4 / zs.ZERO_Q8_BLOCK
+        kernel = "q8_quantize_kernel"
+    else:
+        call = lambda: zs.zero_q8_dequantize(q, sc, y, stream=stream)
+        per_elem = 1 + 4 / zs.ZERO_Q8_BLOCK + 2
+        kernel = "q8_dequantize_kernel"
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        events.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = [a.elapsed_time(b) for a, b in events]
+    k_avg = statistics.fmean(kms)
+    launch_bytes = per_elem * S
+    achieved = launch_bytes / (k_avg * 1e-3) / 1e9
+    line = {
+        "metric": f"8-bit blockwise {args.op} of one rank's 7B gradient shard, elements/s",
+        "value": S * args.steps / wall, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "hbm_gbps": launch_bytes * args.steps / wall / 1e9,
+        "hbm_frac": launch_bytes * args.steps / wall / 1e9 / HBM_PEAK_GBPS,
+        "config": {"workload": f"llama7b_ndp8_q8_{args.op}", "elements": S,
+                   "block": zs.ZERO_Q8_BLOCK, "bytes_per_element": per_elem},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "launch_ms_avg": k_avg, "launch_ms_min": min(kms),
+                     "algorithmic_bytes_per_launch": launch_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n = 1 << 22
+        xs = synth.fill_host(F32, 0, synth.tag(BUF_GRAD, 6, 1, 0, 0), rank * S, n, 1e-3,
+                             outlier_threshold(0.01), 100.0)
+        qq, ss = oracle.q8_quantize(xs, oracle.FP32)
+        t1 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t1 < 10.0:
+            if args.op == "quantize":
+                oracle.q8_quantize(xs, oracle.FP32)
+            else:
+                oracle.q8_dequantize(qq, ss, oracle.BF16)
+            reps += 1
+        dt = time.perf_counter() - t1
+        line["cpu_baseline"] = {"value": reps * n / dt, "unit": "elements/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"the first {n} elements of the shard, {reps} calls, "
+                                          f"single-threaded C oracle ({dt:.1f} s)"}
     print(json.dumps(line), flush=True)
 
 

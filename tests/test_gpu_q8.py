@@ -57,7 +57,9 @@ def test_quantize_and_dequantize_bitwise(kind, n, lead):
         x[2 * B + 7] = nan
     d = _dev(np.concatenate([np.zeros(lead, x.dtype), x]), kind)[lead:]
     q = torch.empty(n + lead, dtype=torch.int8, device="cuda")[lead:]
-    s = torch.empty(zs.q8_blocks(n), dtype=torch.float32, device="cuda")
+    # the scales off 16-byte alignment too when lead > 0 (the quantizer then
+    # stores them one by one)
+    s = torch.empty(zs.q8_blocks(n) + lead, dtype=torch.float32, device="cuda")[lead:]
     zs.zero_q8_quantize(d, q, s)
     oq, os_ = oracle.q8_quantize(x, ODT[kind])
     assert np.array_equal(q.cpu().numpy(), oq)
