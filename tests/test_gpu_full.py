@@ -183,3 +183,73 @@ def test_sum_of_squares_full_size():
     torch.cuda.synchronize()
     assert int(ovf.item()) == 0
     assert abs(ss.item() - ref) <= 1e-9 * ref
+
+
+def test_controlled_fp16_step_full_size():
+    """Configuration 7 at full size: 4 micro-batches of 8 fp16 rows reduced
+    into the fp32 accumulator, the last reduce also summing squares; AdamW
+    with the skip flag, clipping to a norm it must clip to, and the
+    device-resident loss scale; then the scale update.  The accumulator and
+    the state against the oracle on sampled elements (bit for bit, the
+    oracle given the device's sum of squares), the device's sum of squares
+    against a float64 sum of the accumulator's squares over the whole shard
+    (order-independent reference)."""
+    wl = workload(7)
+    lay, _ = zs.zero_flatten_layout(wl.numels, wl.n_dp)
+    S, n_dp, rank, micro = lay.shard, wl.n_dp, wl.rank, wl.micro_batches
+    print(f"\n[full] config 7 rank {rank} S={S} micro={micro}", flush=True)
+    dev = torch.device("cuda")
+    slab = torch.empty((n_dp, S), dtype=torch.float16, device=dev)
+    acc = torch.empty(S, dtype=torch.float32, device=dev)
+    W = torch.empty(S, dtype=torch.float32, device=dev)
+    synth.fill_device(W, F32, wl.seed, synth.tag(BUF_MASTER, 7), rank * S, wl.master_sigma)
+    M = torch.zeros(S, dtype=torch.float32, device=dev)
+    V = torch.zeros(S, dtype=torch.float32, device=dev)
+    wf = torch.full((lay.n_pad,), CANARY, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    ss = torch.zeros(1, dtype=torch.float64, device=dev)
+    dls = zs.new_loss_scale(wl.loss_scale)
+    for mb in range(micro):
+        _fill_rows(slab, wl, 1, mb, rank * S)
+        zs.zero_shard_reduce(slab, n_dp, S, S, acc, accumulate=mb > 0, overflow=flag,
+                             sumsq=ss if mb == micro - 1 else None)
+    torch.cuda.synchronize()
+    # the whole shard's sum of squares, float64, in chunks on the device
+    ref = 0.0
+    for lo in range(0, S, 1 << 27):
+        a = acc[lo:lo + (1 << 27)].double()
+        ref += float((a * a).sum().item())
+    d_ss = float(ss.item())
+    assert abs(d_ss - ref) <= 1e-9 * ref
+    # the clip must bite: norm = sqrt(ss) * s with s = 1 / (n_dp * micro * scale)
+    s = 1.0 / (n_dp * micro) / wl.loss_scale
+    max_norm = 0.5 * (d_ss ** 0.5) * s
+    hp = zs.AdamWHParams(step=1, grad_scale=1.0 / (n_dp * micro), **wl.hp)
+    zs.zero_shard_adamw_ex(acc, W, M, V, wf, lay, rank, hp, skip=flag, sumsq=ss,
+                           max_norm=max_norm, loss_scale=dls)
+    zs.zero_loss_scale_update(dls, flag, 2.0, 0.5, 2000)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    assert zs.read_loss_scale(dls) == (wl.loss_scale, 1)
+    idx = _sample(S, seed=77)
+    flat = rank * S + idx
+    a = np.zeros(idx.size, np.float32)
+    o_flag = np.zeros(1, np.uint32)
+    for mb in range(micro):
+        oracle.reduce(_gather_rows(wl, 1, mb, flat), oracle.FP16, n_dp, idx.size, idx.size, a,
+                      mb > 0, overflow=o_flag)
+    assert oracle.clip_coef(d_ss, np.float32(s), max_norm) < 1.0
+    w = synth.gather_host(F32, wl.seed, synth.tag(BUF_MASTER, 7), flat, wl.master_sigma)
+    m = np.zeros(idx.size, np.float32)
+    v = np.zeros(idx.size, np.float32)
+    out = np.zeros(idx.size, np.uint16)
+    oracle.adamw_ex(a, w, m, v, out, oracle.BF16, idx.size, 1, grad_scale=1.0 / (n_dp * micro),
+                    skip=o_flag, sumsq=np.array([d_ss]), max_norm=max_norm,
+                    loss_scale=np.array([wl.loss_scale], np.float32), **wl.hp)
+    di = torch.from_numpy(idx).to(dev)
+    diff = check_f32(acc[di].cpu().numpy(), a, "acc")
+    diff += check_f32(W[di].cpu().numpy(), w, "master") + check_f32(M[di].cpu().numpy(), m, "m")
+    diff += check_f32(V[di].cpu().numpy(), v, "v")
+    diff += check_16(wf.view(torch.int16)[di + rank * S].cpu().numpy().view(np.uint16), out, 0, "w")
+    assert diff == 0
+    assert _canaries_ok(wf, rank * S, (rank + 1) * S)
