@@ -24,14 +24,14 @@ def _x(n, seed, sigma=1.0):
 
 
 def test_hand_worked_block():
-    # s = fl(1/127); 1/s = 127, 0.5/s = 63.5 -> 64 (tie to even), -0.25/s = -31.75 -> -32,
-    # 0.1/s = 12.7 -> 13, 0.0236/s = 2.997 -> 3
+    # absmax 1: s = fl(1/127), r = 127 exactly; 0.5 r = 63.5 -> 64 (tie to even),
+    # -0.25 r = -31.75 -> -32, 0.1 r = 12.7 -> 13, 0.0236 r = 2.997 -> 3
     x = np.array([1.0, 0.5, -0.25, 0.1, 0.0236, 0.0], np.float32)
     q, s = oracle.q8_quantize(x, oracle.FP32)
     assert s[0] == np.float32(1.0) / np.float32(127.0)
     assert q.tolist() == [127, 64, -32, 13, 3, 0]
-    # absmax 127 makes s exactly 1: the quotients are the values themselves,
-    # and ties go to the even code (62.5 -> 62, -0.5 -> 0, 2.5 -> 2, -3.5 -> -4)
+    # absmax 127 makes s and r exactly 1: the codes are the values rounded,
+    # ties to the even code (62.5 -> 62, -0.5 -> 0, 2.5 -> 2, -3.5 -> -4)
     x = np.array([127.0, 62.5, -0.5, 1.5, 2.5, -3.5, -127.0], np.float32)
     q, s = oracle.q8_quantize(x, oracle.FP32)
     assert s[0] == 1.0 and q.tolist() == [127, 62, 0, 2, 2, -4, -127]
@@ -81,6 +81,19 @@ def test_zero_and_nonfinite_blocks():
     assert np.isnan(s[2]) and not q[2 * B:3 * B].any()
     y = oracle.q8_dequantize(q, s)
     assert np.all(y[:B] == 0) and np.all(np.isnan(y[B:3 * B])) and np.all(np.isfinite(y[3 * B:]))
+
+
+def test_blocks_too_small_for_a_finite_reciprocal_code_zero():
+    """r = 127 / absmax overflows below absmax ~ 3.7e-37: such a block codes
+    as zeros (its scale is still absmax / 127)."""
+    x = np.zeros(2 * B, np.float32)
+    x[:B] = np.float32(1e-38) * np.sign(_x(B, 11))      # r infinite
+    x[B:] = np.float32(1e-36) * np.sign(_x(B, 12))      # r finite
+    q, s = oracle.q8_quantize(x, oracle.FP32)
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(127.0) / np.float32(1e-38))
+    assert s[0] == np.float32(1e-38) / np.float32(127.0) and not q[:B].any()
+    assert np.abs(q[B:]).max() == 127
 
 
 def test_bf16_input_equals_its_fp32_widening():
