@@ -5,8 +5,8 @@ reduce-scatter ("ZeRO and FSDP", FSDP section; "ZeRO: How DeepSpeed Made
 Trillion-Parameter Training Practical"; "ZeRO Optimizer, in depth",
 "Offload and ZeRO++") but define no quantizer.  PARITY UNPINNED against the
 pages: these tests pin the stated quantizer (symmetric, one fp32 scale per
-256-element block, s = absmax / 127, q = rint(x / s)) to its mathematical
-properties and to a hand-worked example."""
+256-element block, s = absmax / 127, q = rint(x * (127 / absmax))) to its
+mathematical properties and to a hand-worked example."""
 import numpy as np
 import pytest
 

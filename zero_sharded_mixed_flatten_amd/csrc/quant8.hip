@@ -4,7 +4,8 @@
 // reduce-scatter ("ZeRO and FSDP", FSDP section; "ZeRO Optimizer, in depth",
 // "Offload and ZeRO++").  The pages give no quantizer; the one here is the
 // plain symmetric blockwise int8 quantizer, one fp32 scale per block of 256
-// elements (s = absmax / 127, q = rint(x / s), ties to even).
+// elements (s = absmax / 127 stored, codes q = rint(x * r) with the block's
+// reciprocal r = 127 / absmax, ties to even).
 //
 // A block is exactly one wave's quad layout: 64 lanes x 4 consecutive
 // elements, so a block's absmax is one wave reduction (six xor-shuffles) and
@@ -16,8 +17,9 @@
 // read through the scalar cache.
 //
 // Arithmetic matches the oracle's definition operation for operation:
-// correctly rounded fp32 division for x / s and absmax / 127, v_rndne_f32
-// for the rounding, and q * s rounded once to fp32.
+// correctly rounded fp32 divisions for absmax / 127 and 127 / absmax, one
+// rounded product x * r, v_rndne_f32 for the rounding, and q * s rounded
+// once to fp32.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -77,21 +79,29 @@ __device__ __forceinline__ float wave_nanmax(float m) {
     return nanmax(nanmax(r0, r1), nanmax(r2, r3));
 }
 
-// the scale of a block from the four values of each lane (invalid ones 0)
-__device__ __forceinline__ float block_scale(const float x[kQuad]) {
+// A block's scale s = absmax / 127 (stored; value = code * s) and the
+// reciprocal r = 127 / absmax the codes are formed with, from the four
+// values of each lane (invalid ones 0).  Two divisions per lane per block.
+struct BlockScale {
+    float s, r;
+};
+
+__device__ __forceinline__ BlockScale block_scale(const float x[kQuad]) {
     float m = 0.0f;
 #pragma unroll
     for (int e = 0; e < kQuad; ++e) m = nanmax(fabsf(x[e]), m);
-    return wave_nanmax(m) / 127.0f;
+    const float amax = wave_nanmax(m);
+    return BlockScale{amax / 127.0f, 127.0f / amax};
 }
 
-// four codes, byte e = element e; all zero for a zero or non-finite scale
-__device__ __forceinline__ uint32_t quantize4(const float x[kQuad], float s) {
-    if (!(s > 0.0f) || __builtin_isinf(s)) return 0u;
+// four codes rint(x * r), byte e = element e; all zero when s is zero or not
+// finite or r is infinite (absmax below what a code can carry)
+__device__ __forceinline__ uint32_t quantize4(const float x[kQuad], BlockScale bs) {
+    if (!(bs.s > 0.0f) || __builtin_isinf(bs.s) || __builtin_isinf(bs.r)) return 0u;
     uint32_t packed = 0u;
 #pragma unroll
     for (int e = 0; e < kQuad; ++e) {
-        float r = __builtin_rintf(x[e] / s);
+        float r = __builtin_rintf(x[e] * bs.r);
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         packed |= (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu) << (8 * e);
     }
@@ -159,10 +169,10 @@ q8_quantize_kernel(const typename GradT<XDT>::elem *__restrict__ x, int64_t len,
         const int64_t b = b0 + u;
         if (b * kB >= len) break;  // wave-uniform
         const int64_t e0 = b * kB + lane * kQuad;
-        const float s = block_scale(v[u]);
-        sc[u] = s;
-        if (lane == 0 && !group_store) scales[b] = s;
-        const uint32_t c = quantize4(v[u], s);
+        const BlockScale bs = block_scale(v[u]);
+        sc[u] = bs.s;
+        if (lane == 0 && !group_store) scales[b] = bs.s;
+        const uint32_t c = quantize4(v[u], bs);
         if (VEC && e0 + kQuad <= len) {
             store_codes(q + e0, c);
         } else {
@@ -351,9 +361,9 @@ step_q8_kernel(const int8_t *__restrict__ gq, const float *__restrict__ gs, int6
                 w[e] = 0.0f;  // outside the range: no part of the block's scale
             }
         }
-        const float s = block_scale(w);
-        const uint32_t codes = quantize4(w, s);
-        if (lane == 0) wsc[b] = s;
+        const BlockScale bs = block_scale(w);
+        const uint32_t codes = quantize4(w, bs);
+        if (lane == 0) wsc[b] = bs.s;
         if (block_full) {
             store16(W + e0, f32x4{w[0], w[1], w[2], w[3]});
             store16(M + e0, f32x4{m[0], m[1], m[2], m[3]});
