@@ -459,7 +459,7 @@ def bench_codec(args):
     else:
         call = lambda: zs.zero_q8_dequantize(q, sc, y, stream=stream)
         per_elem = 1 + 4 / zs.ZERO_Q8_BLOCK + 2
-        kernel = "q8_dequantize_kernel"
+        kernel = "q8_dequantize_pair_kernel"
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         call()

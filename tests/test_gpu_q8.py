@@ -46,7 +46,7 @@ def _same_f32(a, b):
 
 @pytest.mark.parametrize("kind", [F32, BF16, F16])
 @pytest.mark.parametrize("n,lead", [(1, 0), (255, 0), (256, 0), (257, 1), (100_003, 0),
-                                    (1_048_589, 3)])
+                                    (1_048_589, 3), (513, 8), (100_003, 8)])
 def test_quantize_and_dequantize_bitwise(kind, n, lead):
     x = _draw(kind, n, n % 97 + lead)
     if n > 3 * B:  # a zero block, an infinite block, a NaN block
@@ -58,7 +58,9 @@ def test_quantize_and_dequantize_bitwise(kind, n, lead):
     d = _dev(np.concatenate([np.zeros(lead, x.dtype), x]), kind)[lead:]
     q = torch.empty(n + lead, dtype=torch.int8, device="cuda")[lead:]
     # the scales off 16-byte alignment too when lead > 0 (the quantizer then
-    # stores them one by one)
+    # stores them one by one); lead 8 keeps the codes 8-byte and 16-bit
+    # values 16-byte aligned (the vector path of the 16-bit dequantize) at an
+    # offset
     s = torch.empty(zs.q8_blocks(n) + lead, dtype=torch.float32, device="cuda")[lead:]
     zs.zero_q8_quantize(d, q, s)
     oq, os_ = oracle.q8_quantize(x, ODT[kind])

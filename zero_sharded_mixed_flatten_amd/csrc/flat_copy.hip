@@ -48,6 +48,12 @@ constexpr int kCopyChunks = 4;      // chunks per lane, a wave's 1 KiB apart
 constexpr int kCopyWavesPerCU = 16; // residency cap of the copy kernel (measured)
 constexpr int kMaxSegs = 64;        // segments per launch (by-value table)
 constexpr int64_t kMaxLen = int64_t(1) << 38;
+// A dispatch counts its grid in work-items in 32 bits: one launch takes at
+// most kMaxCopyBlocks one-wave workgroups (2^31 work-items), and a copy
+// longer than kCopyPieceBytes goes in as several segments (a multiple of the
+// chunk, so each keeps the copy's alignment phase).
+constexpr int64_t kMaxCopyBlocks = (int64_t(1) << 31) / kWave;
+constexpr int64_t kCopyPieceBytes = int64_t(1) << 32;
 
 struct Seg {
     const unsigned char *src;  // nullptr: the segment is zero-filled
@@ -193,14 +199,17 @@ zero_status launch_copies(const std::vector<Copy> &cs, int waves_per_cu, hipStre
         blocks = 0;
         return hipGetLastError() == hipSuccess;
     };
-    for (const Copy &c : cs) {
-        if (c.bytes <= 0) continue;
-        const int64_t nb = (chunks_of(c) + kWave * CH - 1) / (kWave * CH);
-        if (t.n == kMaxSegs || blocks + nb > INT32_MAX) {
-            if (!flush()) return ZERO_EDEVICE;
+    for (const Copy &whole : cs) {
+        for (int64_t off = 0; off < whole.bytes; off += kCopyPieceBytes) {
+            const Copy c{whole.src ? whole.src + off : nullptr, whole.dst + off,
+                         std::min(kCopyPieceBytes, whole.bytes - off)};
+            const int64_t nb = (chunks_of(c) + kWave * CH - 1) / (kWave * CH);
+            if (t.n == kMaxSegs || blocks + nb > kMaxCopyBlocks) {
+                if (!flush()) return ZERO_EDEVICE;
+            }
+            t.s[t.n++] = Seg{c.src, c.dst, c.bytes, blocks};
+            blocks += nb;
         }
-        t.s[t.n++] = Seg{c.src, c.dst, c.bytes, blocks};
-        blocks += nb;
     }
     return flush() ? ZERO_OK : ZERO_EDEVICE;
 }

@@ -8,13 +8,17 @@
 // reciprocal r = 127 / absmax, ties to even).
 //
 // A block is exactly one wave's quad layout: 64 lanes x 4 consecutive
-// elements, so a block's absmax is one wave reduction (six xor-shuffles) and
-// needs no LDS.  Every kernel is a one-shot grid of one wave per block (16
-// per workgroup when a sum of squares is requested, for one atomic per 4096
-// elements), loads issued before arithmetic, non-temporal streaming access
-// -- the layout of the 16-bit step kernels with 4-byte code loads (one
-// contiguous 256-byte span per wave and row) and one scale per row and block
-// read through the scalar cache.
+// elements, so a block's absmax is one wave reduction (DPP within each row
+// of 16 lanes, then one lane per row) and needs no LDS.  The kernels are
+// one-shot grids, loads issued before arithmetic, non-temporal streaming
+// access -- the layout of the 16-bit step kernels with 4-byte code loads
+// (one contiguous 256-byte span per wave and row) and one scale per row and
+// block read through the scalar cache.  The fused step takes one block per
+// wave (16 per workgroup when a sum of squares is requested, for one atomic
+// per 4096 elements), quantize and dequantize to fp32 two consecutive blocks
+// per wave, and dequantize to 16 bits a pair of blocks per wave at 8 codes
+// per lane, so that both its code loads and its 16-byte stores are
+// contiguous across the wave.
 //
 // Arithmetic matches the oracle's definition operation for operation:
 // correctly rounded fp32 divisions for absmax / 127 and 127 / absmax, one
@@ -35,6 +39,8 @@ namespace {
 using namespace zero_host;
 using namespace zero_step;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kB = ZERO_Q8_BLOCK;
 static_assert(kB == kWave * kQuad, "a quantization block is one wave of quads");
 constexpr int kRowBatchQ8 = 8;          // rows per batch when n_dp is not specialised
@@ -44,12 +50,21 @@ constexpr int kRowBatchQ8 = 8;          // rows per batch when n_dp is not speci
 // memory time.  Measured on the 7B shard (8 rows, random data), waves per
 // CU: 8 -> 66.8 %, 12 -> 76.4 %, 16 -> 78.4 %, 20 -> 76.7 %, 32 -> 75.0 %.
 constexpr int kQ8StepWavesPerCU = 16;   // residency cap of the fused 8-bit step
-// Quantize / dequantize: 4 blocks per wave, loads first, at the hardware's
-// 32 waves per CU (7B shard, measured: quantize 1.28 ms with one block per
-// wave and shuffle-based maxima at 16 waves, 0.76 ms with this shape;
-// dequantize 0.93 -> 0.47 ms).
-constexpr int kQ8CodecWavesPerCU = 32;
-constexpr int kQ8CodecBlocks = 4;
+// Quantize and dequantize to fp32: Q blocks per wave, loads first.  Sweep on
+// the 7B shard (blocks per wave x waves per CU), quantize fp32 -> int8 +
+// scales: 1 x 32 -> 0.79 ms, 2 x 24 -> 0.67, 2 x 32 -> 0.63, 4 x 16 -> 0.68,
+// 4 x 24 -> 0.67, 8 x 16 -> 0.67; dequantize to fp32: 1 x 32 -> 0.79 ms,
+// 2 x 24 -> 0.65, 2 x 32 -> 0.70, 4 x 12 -> 0.65, 4 x 24 -> 0.68.
+constexpr int kQ8QuantizeBlocks = 2;
+constexpr int kQ8QuantizeWavesPerCU = 32;
+constexpr int kQ8DequantizeF32Blocks = 2;
+constexpr int kQ8DequantizeF32WavesPerCU = 24;
+// Dequantize to 16 bits: one pair of blocks per wave at 8 codes per lane,
+// waves per CU (to bf16): 16 -> 0.59 ms, 24 -> 0.43, 32 -> 0.37 (85 % of
+// 8 TB/s); two and four pairs per wave: 0.39 and 0.40 ms; the quad layout
+// (4-byte code loads, 8-byte stores) at best 0.46 ms; 16 codes per lane
+// (16-byte stores at a 32-byte stride): 0.85 ms.
+constexpr int kQ8DequantizeWavesPerCU = 32;
 
 // max with NaN winning (order independent): the scale of a block holding a
 // NaN is NaN
@@ -137,6 +152,14 @@ __device__ __forceinline__ int64_t wave_block() {
 // ---------------------------------------------------------------------------
 // quantize / dequantize
 
+// The codec kernels split on a wave-uniform test: a wave whose blocks all
+// lie in the range (with aligned buffers) takes straight-line vector loads,
+// all issued before any arithmetic; the rest (the range's last wave, or
+// unaligned buffers) take per-lane guards.  A per-lane choice between a
+// vector load and element loads in the load phase would make the compiler
+// wait for each load before issuing the next (the branches write the same
+// registers), one load in flight per wave.
+
 // Q consecutive blocks per wave, every load issued before the first block's
 // reduction (more bytes in flight per wave).
 template <int XDT, bool VEC, int Q>
@@ -145,6 +168,41 @@ q8_quantize_kernel(const typename GradT<XDT>::elem *__restrict__ x, int64_t len,
                    int8_t *__restrict__ q, float *__restrict__ scales) {
     const int64_t b0 = wave_block<kWave>() * Q;
     const int lane = threadIdx.x;
+    if (VEC && (b0 + Q) * kB <= len) {  // wave-uniform: Q whole blocks
+        float v[Q][kQuad];
+#pragma unroll
+        for (int u = 0; u < Q; ++u)
+            widen_quad<XDT>(v[u], load_quad<XDT>(x + (b0 + u) * kB + lane * kQuad));
+        loads_issued();
+        float sc[Q];
+#pragma unroll
+        for (int u = 0; u < Q; ++u) {
+            const BlockScale bs = block_scale(v[u]);
+            sc[u] = bs.s;
+            store_codes(q + (b0 + u) * kB + lane * kQuad, quantize4(v[u], bs));
+        }
+        if (lane == 0) {
+            // the wave's scales as one store when aligned (b0 is a multiple of Q)
+            const uintptr_t sa = reinterpret_cast<uintptr_t>(scales);
+            bool done = false;
+            if constexpr (Q == 4) {
+                if ((sa & 15u) == 0) {
+                    *reinterpret_cast<f32x4 *>(scales + b0) = f32x4{sc[0], sc[1], sc[2], sc[3]};
+                    done = true;
+                }
+            } else if constexpr (Q == 2) {
+                if ((sa & 7u) == 0) {
+                    *reinterpret_cast<f32x2 *>(scales + b0) = f32x2{sc[0], sc[1]};
+                    done = true;
+                }
+            }
+            if (!done) {
+#pragma unroll
+                for (int u = 0; u < Q; ++u) scales[b0 + u] = sc[u];
+            }
+        }
+        return;
+    }
     float v[Q][kQuad];
 #pragma unroll
     for (int u = 0; u < Q; ++u) {
@@ -160,18 +218,13 @@ q8_quantize_kernel(const typename GradT<XDT>::elem *__restrict__ x, int64_t len,
         }
     }
     loads_issued();
-    float sc[Q];
-    // whole group of 4 blocks and a 16-byte aligned scale array: one store
-    const bool group_store = Q == 4 && (b0 + Q) * kB <= len &&
-                             (reinterpret_cast<uintptr_t>(scales) & 15u) == 0;  // wave-uniform
 #pragma unroll
     for (int u = 0; u < Q; ++u) {
         const int64_t b = b0 + u;
         if (b * kB >= len) break;  // wave-uniform
         const int64_t e0 = b * kB + lane * kQuad;
         const BlockScale bs = block_scale(v[u]);
-        sc[u] = bs.s;
-        if (lane == 0 && !group_store) scales[b] = bs.s;
+        if (lane == 0) scales[b] = bs.s;
         const uint32_t c = quantize4(v[u], bs);
         if (VEC && e0 + kQuad <= len) {
             store_codes(q + e0, c);
@@ -180,11 +233,6 @@ q8_quantize_kernel(const typename GradT<XDT>::elem *__restrict__ x, int64_t len,
             for (int e = 0; e < kQuad; ++e)
                 if (e0 + e < len) q[e0 + e] = static_cast<int8_t>((c >> (8 * e)) & 0xFFu);
         }
-    }
-    // the wave's four scales as one 16-byte store (b0 is a multiple of 4)
-    if constexpr (Q == 4) {
-        if (group_store && lane == 0)
-            *reinterpret_cast<f32x4 *>(scales + b0) = f32x4{sc[0], sc[1], sc[2], sc[3]};
     }
 }
 
@@ -210,6 +258,24 @@ q8_dequantize_kernel(const int8_t *__restrict__ q, const float *__restrict__ sca
                      void *__restrict__ y) {
     const int64_t b0 = wave_block<kWave>() * Q;
     const int lane = threadIdx.x;
+    if (VEC && (b0 + Q) * kB <= len) {  // wave-uniform: Q whole blocks
+        uint32_t c[Q];
+        float s[Q];
+#pragma unroll
+        for (int u = 0; u < Q; ++u) {
+            c[u] = load_codes(q + (b0 + u) * kB + lane * kQuad);
+            s[u] = scales[b0 + u];
+        }
+        loads_issued();
+#pragma unroll
+        for (int u = 0; u < Q; ++u) {
+            float v[kQuad];
+#pragma unroll
+            for (int e = 0; e < kQuad; ++e) v[e] = as_rounded_f32(code(c[u], e) * s[u]);
+            store_quad_any<YDT>(y, (b0 + u) * kB + lane * kQuad, v);
+        }
+        return;
+    }
     uint32_t c[Q];
     float s[Q];
 #pragma unroll
@@ -238,6 +304,42 @@ q8_dequantize_kernel(const int8_t *__restrict__ q, const float *__restrict__ sca
                     store_one<YDT>(y, e0 + e, as_rounded_f32(static_cast<float>(q[e0 + e]) * s[u]));
         }
     }
+}
+
+// Dequantize to 16 bits: a wave takes the pair of blocks 2p, 2p + 1, lanes
+// 0-31 the first and 32-63 the second, 8 codes per lane (one 8-byte load,
+// one 16-byte store).  Every launched wave has its first block in range.
+template <int YDT, bool VEC>
+__global__ void __launch_bounds__(kWave)
+q8_dequantize_pair_kernel(const int8_t *__restrict__ q, const float *__restrict__ scales,
+                          int64_t len, uint16_t *__restrict__ y) {
+    constexpr int kPer = 2 * kQuad;  // codes per lane
+    const int64_t p = wave_block<kWave>();
+    const int lane = threadIdx.x;
+    const int64_t b0 = 2 * p;
+    const int64_t e0 = p * (2 * kB) + lane * kPer;
+    if (VEC && (b0 + 2) * kB <= len) {  // wave-uniform: both blocks whole
+        const u32x2 c = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(q + e0));
+        const float s0 = scales[b0], s1 = scales[b0 + 1];
+        loads_issued();
+        const float s = lane < kWave / 2 ? s0 : s1;
+        float v[kPer];
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e) {
+            v[e] = as_rounded_f32(code(c[0], e) * s);
+            v[kQuad + e] = as_rounded_f32(code(c[1], e) * s);
+        }
+        const u32x4 o{narrow2<YDT>(v[0], v[1]), narrow2<YDT>(v[2], v[3]),
+                      narrow2<YDT>(v[4], v[5]), narrow2<YDT>(v[6], v[7])};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(y + e0));
+        return;
+    }
+    // the range's last wave, or unaligned buffers: element by element
+    const float s0 = scales[b0];
+    const float s1 = (b0 + 1) * kB < len ? scales[b0 + 1] : 0.0f;  // wave-uniform
+    const float s = lane < kWave / 2 ? s0 : s1;
+    for (int e = 0; e < kPer; ++e)
+        if (e0 + e < len) y[e0 + e] = narrow1<YDT>(as_rounded_f32(static_cast<float>(q[e0 + e]) * s));
 }
 
 // ---------------------------------------------------------------------------
@@ -422,6 +524,14 @@ unsigned grid_waves(int64_t blocks, int tpb) {
     return static_cast<unsigned>((blocks + per - 1) / per);
 }
 
+// [0, len) in launches of at most kLaunchElems elements (a multiple of the
+// block): f(first element, elements) issues one
+template <typename F>
+void for_launches(int64_t len, F &&f) {
+    static_assert(kLaunchElems % kB == 0, "launch pieces hold whole blocks");
+    for (int64_t o = 0; o < len; o += kLaunchElems) f(o, len - o < kLaunchElems ? len - o : kLaunchElems);
+}
+
 }  // namespace
 
 extern "C" zero_status zero_q8_quantize(const void *x, zero_dtype xdt, int64_t len, int8_t *q,
@@ -433,15 +543,17 @@ extern "C" zero_status zero_q8_quantize(const void *x, zero_dtype xdt, int64_t l
                         span_of(scales, blocks_of(len), 4)};
     if (spans_overlap(sp, 3)) return ZERO_EALIAS;
     const bool vec = quad_aligned(x, xdt) && aligned4(q);
-    const int64_t nb = blocks_of(len);
-    const size_t lds = residency_lds_bytes(kQ8CodecWavesPerCU, kWave);
+    const size_t lds = residency_lds_bytes(kQ8QuantizeWavesPerCU, kWave);
     hipStream_t st = static_cast<hipStream_t>(stream);
     with_xdt(xdt, [&](auto XD) {
         using E = typename GradT<XD.value>::elem;
         with_bool(vec, [&](auto VC) {
-            q8_quantize_kernel<XD.value, VC.value, kQ8CodecBlocks>
-                <<<grid_waves((nb + kQ8CodecBlocks - 1) / kQ8CodecBlocks, kWave), kWave, lds, st>>>(
-                    static_cast<const E *>(x), len, q, scales);
+            for_launches(len, [&](int64_t o, int64_t n) {
+                const int64_t nb = blocks_of(n);
+                q8_quantize_kernel<XD.value, VC.value, kQ8QuantizeBlocks>
+                    <<<grid_waves((nb + kQ8QuantizeBlocks - 1) / kQ8QuantizeBlocks, kWave), kWave,
+                       lds, st>>>(static_cast<const E *>(x) + o, n, q + o, scales + o / kB);
+            });
         });
     });
     return launch_status();
@@ -455,16 +567,33 @@ extern "C" zero_status zero_q8_dequantize(const int8_t *q, const float *scales, 
     const Span sp[3] = {span_of(y, len, xdt_bytes(ydt)), span_of(q, len, 1),
                         span_of(scales, blocks_of(len), 4)};
     if (spans_overlap(sp, 3)) return ZERO_EALIAS;
-    const bool vec = quad_aligned(y, ydt) && aligned4(q);
-    const int64_t nb = blocks_of(len);
-    const size_t lds = residency_lds_bytes(kQ8CodecWavesPerCU, kWave);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    with_xdt(ydt, [&](auto YD) {
+    if (ydt == ZERO_FP32) {
+        const bool vec = aligned16(y) && aligned4(q);
+        const size_t lds = residency_lds_bytes(kQ8DequantizeF32WavesPerCU, kWave);
+        constexpr int64_t kQ = kQ8DequantizeF32Blocks;
         with_bool(vec, [&](auto VC) {
-            q8_dequantize_kernel<YD.value, VC.value, kQ8CodecBlocks>
-                <<<grid_waves((nb + kQ8CodecBlocks - 1) / kQ8CodecBlocks, kWave), kWave, lds, st>>>(
-                    q, scales, len, y);
+            for_launches(len, [&](int64_t o, int64_t n) {
+                q8_dequantize_kernel<ZERO_FP32, VC.value, kQ>
+                    <<<grid_waves((blocks_of(n) + kQ - 1) / kQ, kWave), kWave, lds, st>>>(
+                        q + o, scales + o / kB, n, static_cast<float *>(y) + o);
+            });
         });
+        return launch_status();
+    }
+    const size_t lds = residency_lds_bytes(kQ8DequantizeWavesPerCU, kWave);
+    // 16-bit values: 8-byte code loads and 16-byte stores
+    const bool vec = aligned16(y) && aligned8(q);
+    with_xdt(ydt, [&](auto YD) {
+        if constexpr (YD.value != ZERO_FP32) {
+            with_bool(vec, [&](auto VC) {
+                for_launches(len, [&](int64_t o, int64_t n) {
+                    q8_dequantize_pair_kernel<YD.value, VC.value>
+                        <<<grid_waves((blocks_of(n) + 1) / 2, kWave), kWave, lds, st>>>(
+                            q + o, scales + o / kB, n, static_cast<uint16_t *>(y) + o);
+                });
+            });
+        }
     });
     return launch_status();
 }
@@ -522,10 +651,13 @@ extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales
             constexpr int tpb = SS.value ? 16 * kWave : kWave;
             const size_t lds = residency_lds_bytes(kQ8StepWavesPerCU, tpb);
             auto go = [&](auto ND) {
-                step_q8_kernel<tpb, ND.value, OV.value, SS.value>
-                    <<<grid_waves(nb, tpb), tpb, lds, st>>>(gq, gscales, ld, sld, n_dp, len, nb,
-                                                            master, m, v, wq, wsc, c, overflow,
-                                                            sumsq);
+                for_launches(len, [&](int64_t o, int64_t n) {
+                    const int64_t ob = o / kB, nbn = blocks_of(n);
+                    step_q8_kernel<tpb, ND.value, OV.value, SS.value>
+                        <<<grid_waves(nbn, tpb), tpb, lds, st>>>(
+                            gq + o, gscales + ob, ld, sld, n_dp, n, nbn, master + o, m + o,
+                            v + o, wq + o, wsc + ob, c, overflow, sumsq);
+                });
             };
             if (n_dp == 1) go(IntC<1>{});
             else if (n_dp == 8) go(IntC<8>{});

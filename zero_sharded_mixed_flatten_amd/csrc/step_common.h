@@ -26,10 +26,19 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQuad = 4;  // elements per lane
 
-// One thread per quad (one per element on the unaligned path): a launch
-// covers at most 2^31 - 1 workgroups, so the entry points reject ranges of
-// more than kMaxLen elements (2^38, far beyond any HBM).
+// Ranges beyond kMaxLen elements (2^38, far beyond any HBM) are rejected.
 constexpr int64_t kMaxLen = int64_t(1) << 38;
+
+// A dispatch counts its grid in work-items in 32 bits, so one launch of a
+// one-shot kernel (a thread per quad or per block lane) covers at most
+// kLaunchElems elements and longer ranges go out as consecutive launches.
+// 2^31 is a multiple of every quad, block and alignment unit: each piece
+// starts where the range's alignment holds.
+constexpr int64_t kLaunchElems = int64_t(1) << 31;
+
+// the grid-stride (one element per thread) kernels take at most this many
+// workgroups and loop over the rest
+constexpr int64_t kMaxStrideBlocks = int64_t(1) << 20;
 
 // fp32 constants of the update, formed on the host (see zero_adamw_hparams)
 struct Consts {

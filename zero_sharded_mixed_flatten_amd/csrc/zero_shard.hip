@@ -510,17 +510,27 @@ bool rows_vec_ok(const void *g, int gdt, int n_rows, int64_t ld) {
     return al && (n_rows == 1 || ld % kQuad == 0);
 }
 
-// one thread per item; kMaxLen keeps the count below 2^31 workgroups
+// one thread per item of a one-shot launch (at most kLaunchElems items)
 unsigned grid_for(int64_t items, int tpb = kBlock) {
     const int64_t b = (items + tpb - 1) / tpb;
     return static_cast<unsigned>(b < 1 ? 1 : b);
 }
 
-// grid of an element-wise (grid-stride) kernel: one thread per element, or
-// at most kSsqScalarBlocks workgroups when it ends in a sum's atomic
+// grid of an element-wise (grid-stride) kernel: one thread per element up
+// to kMaxStrideBlocks workgroups, or at most kSsqScalarBlocks when it ends
+// in a sum's atomic
 unsigned scalar_grid(int64_t items, bool ssq) {
-    const unsigned g = grid_for(items);
-    return ssq && g > kSsqScalarBlocks ? static_cast<unsigned>(kSsqScalarBlocks) : g;
+    const int64_t b = (items + kBlock - 1) / kBlock;
+    const int64_t cap = ssq ? kSsqScalarBlocks : kMaxStrideBlocks;
+    return static_cast<unsigned>(b < 1 ? 1 : (b > cap ? cap : b));
+}
+
+// The one-shot quad kernels run over [0, nquad) in launches of at most
+// kLaunchElems elements; f(first quad, quads) issues one.
+template <typename F>
+void for_launches(int64_t nquad, F &&f) {
+    constexpr int64_t per = kLaunchElems / kQuad;
+    for (int64_t q0 = 0; q0 < nquad; q0 += per) f(q0, nquad - q0 < per ? nquad - q0 : per);
 }
 
 // rows of the gradient slab all fit in int64 and do not wrap
@@ -564,10 +574,13 @@ extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int3
                             SS.value ? kSsqWavesPerCU : kReduceWavesPerCU, tpb);
                         with_ndp<GD.value>(n_contrib, [&](auto ND) {
                             constexpr int q = SS.value ? ssq_quads(ND.value) : 1;
-                            reduce_quad_kernel<tpb, q, GD.value, ND.value, AC.value, OV.value,
-                                               SS.value>
-                                <<<grid_for(nquad, tpb * q), tpb, lds, st>>>(
-                                    g, ld, n_contrib, nquad, acc, overflow, sumsq);
+                            for_launches(nquad, [&](int64_t q0, int64_t nq) {
+                                const int64_t o = q0 * kQuad;
+                                reduce_quad_kernel<tpb, q, GD.value, ND.value, AC.value,
+                                                   OV.value, SS.value>
+                                    <<<grid_for(nq, tpb * q), tpb, lds, st>>>(
+                                        g + o, ld, n_contrib, nq, acc + o, overflow, sumsq);
+                            });
                         });
                     }
                     if (len > done) {
@@ -622,14 +635,15 @@ zero_status adamw_impl(const float *acc, float *master, float *m, float *v, void
     with_dtype(wdt, [&](auto WD) {
         with_bool(skip != nullptr, [&](auto SK) {
             with_bool(ext, [&](auto EX) {
-                if (nquad > 0) {
+                for_launches(nquad, [&](int64_t q0, int64_t nq) {
+                    const int64_t o = q0 * kQuad;
                     adamw_quad_kernel<kWave, WD.value, SK.value, EX.value>
-                        <<<grid_for(nquad, kWave), kWave, lds, st>>>(acc, master, m, v, slot,
-                                                                     nquad, c, skip, k);
-                }
+                        <<<grid_for(nq, kWave), kWave, lds, st>>>(acc + o, master + o, m + o,
+                                                                  v + o, slot + o, nq, c, skip, k);
+                });
                 if (len > done) {
                     adamw_scalar_kernel<WD.value, SK.value, EX.value>
-                        <<<grid_for(len - done), kBlock, 0, st>>>(
+                        <<<scalar_grid(len - done, false), kBlock, 0, st>>>(
                             acc + done, master + done, m + done, v + done, slot + done,
                             len - done, c, skip, k);
                 }
@@ -720,10 +734,14 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
                             const size_t lds = residency_lds_bytes(
                                 SS.value ? kSsqWavesPerCU : step_waves_per_cu(GD.value, ND.value),
                                 tpb);
-                            step_quad_kernel<tpb, q, GD.value, WD.value, ND.value, OV.value,
-                                             SS.value>
-                                <<<grid_for(nquad, tpb * q), tpb, lds, st>>>(
-                                    g, ld, n_dp, nquad, master, m, v, slot, c, overflow, sumsq);
+                            for_launches(nquad, [&](int64_t q0, int64_t nq) {
+                                const int64_t o = q0 * kQuad;
+                                step_quad_kernel<tpb, q, GD.value, WD.value, ND.value, OV.value,
+                                                 SS.value>
+                                    <<<grid_for(nq, tpb * q), tpb, lds, st>>>(
+                                        g + o, ld, n_dp, nq, master + o, m + o, v + o, slot + o,
+                                        c, overflow, sumsq);
+                            });
                         });
                     }
                     if (len > done) {
