@@ -489,7 +489,8 @@ def bench_codec(args):
                    "block": zs.ZERO_Q8_BLOCK, "bytes_per_element": per_elem},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "launch_ms_avg": k_avg, "launch_ms_min": min(kms),
+                     "traffic": committed_traffic(f"llama7b_ndp8_q8_{args.op}", Q8_SOURCE),
+                     "launch_ms_avg": k_avg, "launch_ms_min": min(kms),
                      "algorithmic_bytes_per_launch": launch_bytes},
         "cpu_baseline": None,
     }
