@@ -315,6 +315,9 @@ def main():
             del slab_s, wfull_s
         torch.cuda.empty_cache()
         line["cpu_baseline"] = cpu_baseline(wl, S, rank, args.cpu_sample_log2, args.cpu_steps)
+        if micro == 1 and not q8:
+            line["cpu_baseline_all_cores"] = cpu_baseline_all_cores(
+                wl, S, rank, args.cpu_sample_log2, 8 * args.cpu_steps)
 
     print(json.dumps(line), flush=True)
 
@@ -613,6 +616,62 @@ def cpu_baseline(wl, S, rank, log2n, steps):
     return {"value": n * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} parameters of rank {rank}'s shard, {wl.n_dp} gradient rows, "
                       f"{steps} optimizer steps, single-threaded C oracle ({dt:.1f} s)"}
+
+
+def host_threads():
+    """Worker threads for the all-core baseline: the cores this process may
+    run on, at most 16 (one GPU's share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline_all_cores(wl, S, rank, log2n, steps):
+    """The same single-threaded oracle step run on every host core at once:
+    the sample is cut into one contiguous element range per thread and each
+    thread steps its range (the update is element-wise, so the ranges are
+    independent).  The oracle itself is unchanged; ctypes releases the GIL
+    for the duration of each call."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    import synth
+    from synth import F32
+    from synth.synth_const import BUF_GRAD, BUF_MASTER
+
+    n = min(1 << log2n, S)
+    draw = wl.grad
+    rows = np.stack([synth.fill_host(draw.kind, wl.seed, synth.tag(BUF_GRAD, wl.cid, 1, 0, k),
+                                     rank * S, n, draw.eff_sigma, draw.thr, draw.outlier_mul)
+                     for k in range(wl.n_dp)])
+    flat = rows.reshape(-1)
+    w = synth.fill_host(F32, wl.seed, synth.tag(BUF_MASTER, wl.cid), rank * S, n, wl.master_sigma)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    wout = np.zeros(n, np.uint16)
+    gdt = {synth.BF16: oracle.BF16, synth.F16: oracle.FP16, synth.F32: oracle.FP32}[draw.kind]
+    threads = host_threads()
+    cuts = [n * i // threads for i in range(threads + 1)]
+
+    def run(i):
+        a, b = cuts[i], cuts[i + 1]
+        for t in range(1, steps + 1):
+            # row k of the range starts at flat[a + k * n]
+            oracle.step(flat[a:], gdt, wl.n_dp, n, b - a, w[a:b], m[a:b], v[a:b], wout[a:b],
+                        oracle.BF16, t, grad_scale=1.0 / wl.n_dp, **wl.hp)
+
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(run, range(threads)))
+        dt = time.perf_counter() - t0
+    return {"value": n * steps / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} parameters of rank {rank}'s shard, {wl.n_dp} gradient rows, "
+                      f"{steps} optimizer steps, the single-threaded C oracle on {threads} "
+                      f"contiguous ranges in {threads} threads ({dt:.1f} s)"}
 
 
 if __name__ == "__main__":
