@@ -180,6 +180,51 @@ def _dev_ptr(t, what: str, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _buf(t, what: str, need: int, dtype=None, device=None):
+    """Device address of a contiguous CUDA tensor of at least `need` elements
+    (None -> NULL) on `device`.  The kernels take plain pointers and sizes,
+    so this is where a tensor too short for the sizes passed beside it, a
+    strided or expanded view, or a tensor on another GPU is refused --
+    before anything is launched."""
+    if t is None:
+        return None
+    p = _dev_ptr(t, what, dtype)
+    if device is not None and t.device != device:
+        raise ValueError(f"{what}: on {t.device}, the call's tensors are on {device}")
+    if not t.is_contiguous():
+        raise TypeError(f"{what}: a contiguous tensor is required")
+    if t.numel() < need:
+        raise ValueError(f"{what}: {need} elements needed, the tensor holds {t.numel()}")
+    return p
+
+
+def _rows_need(n_rows: int, ld: int, length: int) -> int:
+    """Elements spanned by n_rows rows of stride ld, length each."""
+    return 0 if length <= 0 or n_rows < 1 else (n_rows - 1) * ld + length
+
+
+def _rows(t, what: str, n_rows: int, ld: int, length: int, dtype=None, device=None):
+    """Device address of n_rows rows of `length` elements, row k at element
+    k * ld: a contiguous tensor spanning them, or a 2-D view [rows][cols]
+    with row stride ld (a column range of a wider slab) holding them."""
+    if t is None:
+        return None
+    p = _dev_ptr(t, what, dtype)
+    if device is not None and t.device != device:
+        raise ValueError(f"{what}: on {t.device}, the call's tensors are on {device}")
+    need = _rows_need(n_rows, ld, length)
+    if t.is_contiguous():
+        if t.numel() < need:
+            raise ValueError(f"{what}: {need} elements needed, the tensor holds {t.numel()}")
+        return p
+    if not (t.dim() == 2 and t.stride(1) == 1 and t.stride(0) == ld):
+        raise TypeError(f"{what}: contiguous rows, or a 2-D view of row stride {ld}, required")
+    if need and (t.shape[0] < n_rows or t.shape[1] < length):
+        raise ValueError(f"{what}: {n_rows} rows of {length} elements needed, "
+                         f"the view is {tuple(t.shape)}")
+    return p
+
+
 def _stream(stream, like):
     import torch
     if stream is None:
@@ -258,10 +303,12 @@ def zero_shard_reduce(grads, n_contrib: int, ld: int, length: int, acc,
     """acc[:length] (+)= sum of n_contrib rows (bf16, fp16 or fp32) of stride ld
     starting at grads."""
     import torch
+    d = acc.device
     _check(_lib.zero_shard_reduce(
-        _dev_ptr(grads, "grads"), _dtype_code(grads, "grads", True), n_contrib, ld, length,
-        _dev_ptr(acc, "acc", torch.float32), int(bool(accumulate)),
-        _dev_ptr(overflow, "overflow", torch.int32), _dev_ptr(sumsq, "sumsq", torch.float64),
+        _rows(grads, "grads", n_contrib, ld, length, device=d),
+        _dtype_code(grads, "grads", True), n_contrib, ld, length,
+        _buf(acc, "acc", length, torch.float32), int(bool(accumulate)),
+        _buf(overflow, "overflow", 1, torch.int32, d), _buf(sumsq, "sumsq", 1, torch.float64, d),
         _stream(stream, acc)), "zero_shard_reduce")
 
 
@@ -273,12 +320,14 @@ def zero_shard_adamw(acc, master, m, v, weight_full, layout: ZeroLayout, rank: i
     if length is None:
         length = master.numel()
     hpc = hp._c()
+    d = master.device
     _check(_lib.zero_shard_adamw(
-        _dev_ptr(acc, "acc", torch.float32), _dev_ptr(master, "master", torch.float32),
-        _dev_ptr(m, "m", torch.float32), _dev_ptr(v, "v", torch.float32),
-        _dev_ptr(weight_full, "weight_full"), _dtype_code(weight_full, "weight_full"),
+        _buf(acc, "acc", length, torch.float32, d), _buf(master, "master", length, torch.float32),
+        _buf(m, "m", length, torch.float32, d), _buf(v, "v", length, torch.float32, d),
+        _buf(weight_full, "weight_full", _slot_end(layout, rank, shard_off, length), device=d),
+        _dtype_code(weight_full, "weight_full"),
         ctypes.byref(layout), rank, shard_off, length, ctypes.byref(hpc),
-        _dev_ptr(skip, "skip", torch.int32), _stream(stream, master)), "zero_shard_adamw")
+        _buf(skip, "skip", 1, torch.int32, d), _stream(stream, master)), "zero_shard_adamw")
 
 
 def zero_shard_adamw_ex(acc, master, m, v, weight_full, layout: ZeroLayout, rank: int,
@@ -292,12 +341,15 @@ def zero_shard_adamw_ex(acc, master, m, v, weight_full, layout: ZeroLayout, rank
     if length is None:
         length = master.numel()
     hpc = hp._c()
-    ctl = _StepControl(_dev_ptr(skip, "skip", torch.int32), _dev_ptr(sumsq, "sumsq", torch.float64),
-                       float(max_norm), _dev_ptr(loss_scale, "loss_scale", torch.int32))
+    d = master.device
+    ctl = _StepControl(_buf(skip, "skip", 1, torch.int32, d),
+                       _buf(sumsq, "sumsq", 1, torch.float64, d), float(max_norm),
+                       _buf(loss_scale, "loss_scale", 2, torch.int32, d))
     _check(_lib.zero_shard_adamw_ex(
-        _dev_ptr(acc, "acc", torch.float32), _dev_ptr(master, "master", torch.float32),
-        _dev_ptr(m, "m", torch.float32), _dev_ptr(v, "v", torch.float32),
-        _dev_ptr(weight_full, "weight_full"), _dtype_code(weight_full, "weight_full"),
+        _buf(acc, "acc", length, torch.float32, d), _buf(master, "master", length, torch.float32),
+        _buf(m, "m", length, torch.float32, d), _buf(v, "v", length, torch.float32, d),
+        _buf(weight_full, "weight_full", _slot_end(layout, rank, shard_off, length), device=d),
+        _dtype_code(weight_full, "weight_full"),
         ctypes.byref(layout), rank, shard_off, length, ctypes.byref(hpc), ctypes.byref(ctl),
         _stream(stream, master)), "zero_shard_adamw_ex")
 
@@ -319,7 +371,8 @@ def zero_loss_scale_update(loss_scale, overflow, growth: float = 2.0, backoff: f
     """One step of the device-resident dynamic loss scale."""
     import torch
     _check(_lib.zero_loss_scale_update(
-        _dev_ptr(loss_scale, "loss_scale", torch.int32), _dev_ptr(overflow, "overflow", torch.int32),
+        _buf(loss_scale, "loss_scale", 2, torch.int32),
+        _buf(overflow, "overflow", 1, torch.int32, loss_scale.device),
         float(growth), float(backoff), int(interval), _stream(stream, loss_scale)),
         "zero_loss_scale_update")
 
@@ -330,13 +383,21 @@ def zero_shard_step(grads, ld: int, length: int, master, m, v, weight_full,
     """Fused reduce of layout.n_dp rows + AdamW + cast into the weight slot."""
     import torch
     hpc = hp._c()
+    d = master.device
     _check(_lib.zero_shard_step(
-        _dev_ptr(grads, "grads"), _dtype_code(grads, "grads", True), ld, length,
-        _dev_ptr(master, "master", torch.float32), _dev_ptr(m, "m", torch.float32),
-        _dev_ptr(v, "v", torch.float32), _dev_ptr(weight_full, "weight_full"),
+        _rows(grads, "grads", layout.n_dp, ld, length, device=d),
+        _dtype_code(grads, "grads", True), ld, length,
+        _buf(master, "master", length, torch.float32), _buf(m, "m", length, torch.float32, d),
+        _buf(v, "v", length, torch.float32, d),
+        _buf(weight_full, "weight_full", _slot_end(layout, rank, shard_off, length), device=d),
         _dtype_code(weight_full, "weight_full"), ctypes.byref(layout), rank, shard_off,
-        ctypes.byref(hpc), _dev_ptr(overflow, "overflow", torch.int32),
-        _dev_ptr(sumsq, "sumsq", torch.float64), _stream(stream, master)), "zero_shard_step")
+        ctypes.byref(hpc), _buf(overflow, "overflow", 1, torch.int32, d),
+        _buf(sumsq, "sumsq", 1, torch.float64, d), _stream(stream, master)), "zero_shard_step")
+
+
+def _slot_end(layout: ZeroLayout, rank: int, shard_off: int, length: int) -> int:
+    """One past the last element of the weight buffer a call writes."""
+    return 0 if length <= 0 else rank * layout.shard + shard_off + length
 
 
 def _elem_bytes(ts, what: str) -> int:
@@ -349,10 +410,10 @@ def _elem_bytes(ts, what: str) -> int:
     return sizes.pop()
 
 
-def _pieces(pieces, what: str):
+def _pieces(pieces, what: str, device):
     arr = (_Piece * max(1, len(pieces)))()
     for i, (t, off) in enumerate(pieces):
-        arr[i] = _Piece(_dev_ptr(t, what), int(off), t.numel())
+        arr[i] = _Piece(_buf(t, what, 0, device=device), int(off), t.numel())
     return arr
 
 
@@ -361,7 +422,7 @@ def zero_flat_gather(pieces, n: int, begin: int, dst, stream=None):
     [(tensor, flat_off), ...]; zeros where no piece holds the index or it is
     >= n.  Bitwise, for 2- or 4-byte elements."""
     eb = _elem_bytes([dst] + [t for t, _ in pieces], "zero_flat_gather")
-    _check(_lib.zero_flat_gather(_pieces(pieces, "piece"), len(pieces), n, eb, begin,
+    _check(_lib.zero_flat_gather(_pieces(pieces, "piece", dst.device), len(pieces), n, eb, begin,
                                  dst.numel(), _dev_ptr(dst, "dst"), _stream(stream, dst)),
            "zero_flat_gather")
 
@@ -371,7 +432,7 @@ def zero_flat_scatter(src, begin: int, pieces, stream=None):
     [(tensor, flat_off), ...] where they hold those indices."""
     eb = _elem_bytes([src] + [t for t, _ in pieces], "zero_flat_scatter")
     _check(_lib.zero_flat_scatter(_dev_ptr(src, "src"), begin, src.numel(),
-                                  _pieces(pieces, "piece"), len(pieces), eb,
+                                  _pieces(pieces, "piece", src.device), len(pieces), eb,
                                   _stream(stream, src)), "zero_flat_scatter")
 
 
@@ -382,7 +443,7 @@ def zero_reshard(src_shards, n: int, dst_rank: int, dst, stream=None):
     sizes = {t.numel() for t in src_shards}
     if len(sizes) != 1:
         raise ValueError("zero_reshard: the old shards must have one size")
-    ptrs = (ctypes.c_void_p * len(src_shards))(*[_dev_ptr(t, "src_shard").value
+    ptrs = (ctypes.c_void_p * len(src_shards))(*[_buf(t, "src_shard", 0, device=dst.device).value
                                                  for t in src_shards])
     _check(_lib.zero_reshard(ptrs, len(src_shards), sizes.pop(), n, eb, dst_rank, dst.numel(),
                              _dev_ptr(dst, "dst"), _stream(stream, dst)), "zero_reshard")
@@ -397,18 +458,21 @@ def zero_q8_quantize(x, q, scales, stream=None):
     """Blockwise int8 codes (int8 tensor q) and fp32 scales of x (bf16,
     fp16 or fp32), one scale per ZERO_Q8_BLOCK elements."""
     import torch
-    _check(_lib.zero_q8_quantize(_dev_ptr(x, "x"), _dtype_code(x, "x", True), x.numel(),
-                                 _dev_ptr(q, "q", torch.int8), _dev_ptr(scales, "scales", torch.float32),
+    n, d = x.numel(), x.device
+    _check(_lib.zero_q8_quantize(_buf(x, "x", n), _dtype_code(x, "x", True), n,
+                                 _buf(q, "q", n, torch.int8, d),
+                                 _buf(scales, "scales", q8_blocks(n), torch.float32, d),
                                  _stream(stream, x)), "zero_q8_quantize")
 
 
 def zero_q8_dequantize(q, scales, y, stream=None):
     """y = codes x block scale, stored in y's dtype (bf16, fp16 or fp32)."""
     import torch
-    _check(_lib.zero_q8_dequantize(_dev_ptr(q, "q", torch.int8),
-                                   _dev_ptr(scales, "scales", torch.float32), q.numel(),
-                                   _dev_ptr(y, "y"), _dtype_code(y, "y", True), _stream(stream, q)),
-           "zero_q8_dequantize")
+    n, d = q.numel(), q.device
+    _check(_lib.zero_q8_dequantize(_buf(q, "q", n, torch.int8),
+                                   _buf(scales, "scales", q8_blocks(n), torch.float32, d), n,
+                                   _buf(y, "y", n, device=d), _dtype_code(y, "y", True),
+                                   _stream(stream, q)), "zero_q8_dequantize")
 
 
 def zero_shard_step_q8(gq, gscales, ld: int, sld: int, length: int, master, m, v, wq_full,
@@ -418,13 +482,19 @@ def zero_shard_step_q8(gq, gscales, ld: int, sld: int, length: int, master, m, v
     weights out (wq_full, wscales_full: the all-gather buffer)."""
     import torch
     hpc = hp._c()
+    d = master.device
+    nb = q8_blocks(length)
+    end = _slot_end(layout, rank, shard_off, length)
     _check(_lib.zero_shard_step_q8(
-        _dev_ptr(gq, "gq", torch.int8), _dev_ptr(gscales, "gscales", torch.float32), ld, sld,
-        length, _dev_ptr(master, "master", torch.float32), _dev_ptr(m, "m", torch.float32),
-        _dev_ptr(v, "v", torch.float32), _dev_ptr(wq_full, "wq_full", torch.int8),
-        _dev_ptr(wscales_full, "wscales_full", torch.float32), ctypes.byref(layout), rank,
-        shard_off, ctypes.byref(hpc), _dev_ptr(overflow, "overflow", torch.int32),
-        _dev_ptr(sumsq, "sumsq", torch.float64), _stream(stream, master)), "zero_shard_step_q8")
+        _rows(gq, "gq", layout.n_dp, ld, length, torch.int8, d),
+        _rows(gscales, "gscales", layout.n_dp, sld, nb, torch.float32, d), ld, sld,
+        length, _buf(master, "master", length, torch.float32), _buf(m, "m", length, torch.float32, d),
+        _buf(v, "v", length, torch.float32, d), _buf(wq_full, "wq_full", end, torch.int8, d),
+        _buf(wscales_full, "wscales_full",
+             0 if length <= 0 else (end - length) // ZERO_Q8_BLOCK + nb, torch.float32, d),
+        ctypes.byref(layout), rank, shard_off, ctypes.byref(hpc),
+        _buf(overflow, "overflow", 1, torch.int32, d), _buf(sumsq, "sumsq", 1, torch.float64, d),
+        _stream(stream, master)), "zero_shard_step_q8")
 
 
 def zero_adam_step(grads, w_shards, m_shards, v_shards, t: int, lr: float = 1e-3,
