@@ -52,6 +52,9 @@ def parse():
                    help="CPU baseline sample: 2^k parameters of the shard")
     p.add_argument("--cpu-steps", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--flags", action="store_true",
+                   help="single-launch steps: also raise the overflow flag and sum the squares "
+                        "of the scaled gradient (the shard's part of the global norm)")
     p.add_argument("--op", choices=["step", "reshard", "consolidate", "quantize", "dequantize"],
                    default="step",
                    help="step: the optimizer step (default); reshard: new rank 5 of 16's "
@@ -180,9 +183,10 @@ def main():
     else:
         wfull = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device=dev)
     acc = torch.empty(S, dtype=torch.float32, device=dev) if micro > 1 else None
-    flag = torch.zeros(1, dtype=torch.int32, device=dev) if micro > 1 else None
-    if wl.controls:
+    flag = torch.zeros(1, dtype=torch.int32, device=dev) if micro > 1 or args.flags else None
+    if wl.controls or args.flags:
         sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+    if wl.controls:
         loss_scale = zs.new_loss_scale(wl.loss_scale, dev)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
@@ -195,13 +199,18 @@ def main():
             hp = zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **hp_kw)
             e0 = torch.cuda.Event(enable_timing=True) if timed else None
             e1 = torch.cuda.Event(enable_timing=True) if timed else None
+            fl = dict(overflow=flag, sumsq=sumsq) if args.flags else {}
+            if args.flags:  # caller-zeroed, outside the timed launch
+                flag.zero_()
+                sumsq.zero_()
             if timed:
                 e0.record(stream)
             if q8:
                 zs.zero_shard_step_q8(slab, slab_s, S, nb, S, master, m, v, wfull, wfull_s, lay,
-                                      rank, hp, stream=stream)
+                                      rank, hp, stream=stream, **fl)
             else:
-                zs.zero_shard_step(slab, S, S, master, m, v, wfull, lay, rank, hp, stream=stream)
+                zs.zero_shard_step(slab, S, S, master, m, v, wfull, lay, rank, hp, stream=stream,
+                                   **fl)
             if timed:
                 e1.record(stream)
                 events.append((e0, e1))
@@ -253,12 +262,13 @@ def main():
     wall = time.perf_counter() - t0
 
     ms_per_step = wall * 1e3 / args.steps
+    with_flags = " with the overflow flag and the sum of squares" if args.flags else ""
     if q8:
         bytes_per_param = n_dp * (1 + 4 / zs.ZERO_Q8_BLOCK) + 12 + 12 + 1 + 4 / zs.ZERO_Q8_BLOCK
-        kernel = "step_q8_kernel (fused dequantize + reduce + AdamW + quantize)"
+        kernel = f"step_q8_kernel (fused dequantize + reduce + AdamW + quantize{with_flags})"
     elif micro == 1:
         bytes_per_param = gbytes * n_dp + 26
-        kernel = "step_quad_kernel (fused reduce + AdamW + cast)"
+        kernel = f"step_quad_kernel (fused reduce + AdamW + cast{with_flags})"
     else:
         # 4 B written by the first reduce, 2 n_dp + 8 by each later one,
         # 30 by the gated AdamW (acc 4 + state 12 read, state 12 + weight 2 written)
@@ -274,7 +284,9 @@ def main():
     else:
         launch_bytes = 30 * S
     achieved = launch_bytes / (k_avg * 1e-3) / 1e9
-    traffic = committed_traffic(wl.name, Q8_SOURCE if q8 else KERNEL_SOURCE) if micro == 1 else None
+    # the committed counter summaries cover the variant without the flags
+    traffic = (committed_traffic(wl.name, Q8_SOURCE if q8 else KERNEL_SOURCE)
+               if micro == 1 and not args.flags else None)
 
     line = {
         "metric": "sharded AdamW step params/s and HBM GB/s (% of 8 TB/s), 7B n_dp=8 shard",
@@ -299,6 +311,7 @@ def main():
                    "weight_dtype": "int8 blocks of 256 + fp32 scale" if q8 else "bf16",
                    "micro_batches": micro, "bytes_per_param": bytes_per_param,
                    "controls": "clip 1.0 + dynamic loss scale" if wl.controls else None,
+                   "flags": "overflow + sum of squares" if args.flags and micro == 1 else None,
                    "launches_per_step": 1 if micro == 1 else micro + 1 + int(wl.controls)},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,

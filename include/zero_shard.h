@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define ZERO_SHARD_ABI_VERSION 1
+#define ZERO_SHARD_ABI_VERSION 2
 
 /* every entry point is exported from the shared library */
 #if defined(__GNUC__) || defined(__clang__)
@@ -193,6 +193,19 @@ ZERO_API zero_status zero_dim0_segments(const zero_layout *layout, const int64_t
                                         int32_t rank, zero_segment *out, int64_t cap,
                                         int64_t *count);
 
+/* ---- the sum of squares' workspace ----------------------------------------
+ * A call that sums squares (sumsq != NULL: zero_shard_reduce,
+ * zero_shard_step, zero_shard_step_q8) stores one fp64 partial per
+ * workgroup in a caller-provided device workspace, then adds the partials
+ * into *sumsq in an order fixed by len and the buffers' alignment alone --
+ * the same inputs give the same bits on every run.  The workspace holds at
+ * least zero_sumsq_workspace_bytes(len) bytes (8 * (256 + ceil(len / 256) +
+ * 4096): 8 bytes per 256 elements plus 34 KiB), is 8-byte aligned,
+ * overlaps no other argument, and is scratch: its contents on entry are
+ * ignored and on exit unspecified.  Calls that share a workspace must not
+ * run concurrently.  Returns -1 for len < 0 or len > 2^38. */
+ZERO_API int64_t zero_sumsq_workspace_bytes(int64_t len);
+
 /* ---- the reduce (device) ------------------------------------------------
  * The reduce-scatter's arithmetic for one shard range, with optional
  * micro-batch accumulation (stage 2 reduces after every micro-batch).
@@ -208,15 +221,19 @@ ZERO_API zero_status zero_dim0_segments(const zero_layout *layout, const int64_t
  *          rows as stored).  No scale is applied here.
  *   overflow: device uint32 or NULL; set to 1 (never cleared) when some
  *          acc[j] after the update is +-Inf or NaN.
- *   sumsq: device double or NULL; the sum over j of acc[j]^2 is ADDED to
- *          it (order unspecified).  The caller zeroes both before a pass.
- * EINVAL: n_contrib < 1, len < 0, ld < len, bad gdt, or a NULL grads/acc
- * with len > 0.  EALIAS: acc, overflow, sumsq overlap each other or a row.
- * len == 0 is a no-op. */
+ *   sumsq: device double or NULL; the sum over j of acc[j]^2 (in fp64) is
+ *          ADDED to it, through workspace (see zero_sumsq_workspace_bytes;
+ *          ignored when sumsq is NULL).  The caller zeroes overflow and
+ *          sumsq before a pass.
+ * EINVAL: n_contrib < 1, len < 0, ld < len, bad gdt, a NULL grads/acc
+ * with len > 0, or sumsq given with a missing, unaligned or short
+ * workspace.  EALIAS: acc, overflow, sumsq, the workspace overlap each
+ * other or a row.  len == 0 is a no-op. */
 ZERO_API zero_status zero_shard_reduce(const void *grads, zero_dtype gdt,
                               int32_t n_contrib, int64_t ld, int64_t len,
                               float *acc, int32_t accumulate,
-                              uint32_t *overflow, double *sumsq, void *stream);
+                              uint32_t *overflow, double *sumsq, void *workspace,
+                              int64_t workspace_bytes, void *stream);
 
 /* ---- AdamW from an fp32 gradient buffer (device) -------------------------
  * For j in [0, len): g = acc[j] * s, the AdamW update of master[j], m[j],
@@ -312,14 +329,18 @@ ZERO_API zero_status zero_loss_scale_update(zero_loss_scale *state,
  *   overflow: device uint32 or NULL; set to 1 when some a_j is non-finite.
  *          The update is applied regardless (a single pass cannot wait for
  *          the whole shard's verdict); use reduce + adamw with skip to gate.
- *   sumsq: device double or NULL; the sum over j of g^2 is ADDED to it.
+ *   sumsq: device double or NULL; the sum over j of g^2 (in fp64) is ADDED
+ *          to it, through workspace as for zero_shard_reduce.  It is the
+ *          shard's part of the global norm of this step's gradient, known
+ *          only after the update (clipping by it needs reduce + adamw_ex).
  * Errors as for zero_shard_reduce and zero_shard_adamw. */
 ZERO_API zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_t ld,
                             int64_t len, float *master, float *m, float *v,
                             void *weight_full, zero_dtype wdt,
                             const zero_layout *layout, int32_t rank,
                             int64_t shard_off, const zero_adamw_hparams *hp,
-                            uint32_t *overflow, double *sumsq, void *stream);
+                            uint32_t *overflow, double *sumsq, void *workspace,
+                            int64_t workspace_bytes, void *stream);
 
 /* ---- moving flat ranges: flatten, unflatten, re-shard (device) -----------
  * A sharded checkpoint is tied to the layout it was written with; resuming
@@ -422,7 +443,8 @@ ZERO_API zero_status zero_q8_dequantize(const int8_t *q, const float *scales, in
  *   wq_full: device int8[n_pad]; wscales_full: device fp32[n_pad / B];
  *        elements [rank * shard + shard_off, ... + len) and their block
  *        scales are written, nothing else.
- *   overflow, sumsq: as zero_shard_step (the update is applied regardless).
+ *   overflow, sumsq, workspace: as zero_shard_step (the update is applied
+ *        regardless).
  * Requirements (EINVAL otherwise): layout->shard and shard_off multiples of
  * B; gq and wq_full 4-byte aligned, ld a multiple of 4 when n_dp > 1,
  * sld >= ceil(len / B) when n_dp > 1; master, m, v 16-byte aligned.
@@ -434,7 +456,8 @@ ZERO_API zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales, 
                                         float *v, int8_t *wq_full, float *wscales_full,
                                         const zero_layout *layout, int32_t rank,
                                         int64_t shard_off, const zero_adamw_hparams *hp,
-                                        uint32_t *overflow, double *sumsq, void *stream);
+                                        uint32_t *overflow, double *sumsq, void *workspace,
+                                        int64_t workspace_bytes, void *stream);
 
 /* ---- accounting (host only) ----------------------------------------------
  * Model-state bytes per GPU at ZeRO stage 0..3 for n parameters on n_dp

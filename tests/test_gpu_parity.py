@@ -263,3 +263,43 @@ def test_cast_every_fp32_pattern(wdt):
 
 def zs_tdt(dt):
     return torch.bfloat16 if dt == zs.ZERO_BF16 else torch.float16
+
+
+@pytest.mark.parametrize("n_dp,length,lead", [(3, 1_048_589, 0), (8, 300_001, 0), (8, 70_001, 1)])
+def test_sum_of_squares_is_reproducible(n_dp, length, lead):
+    """The sum of squares goes through per-workgroup partials and a fixed-
+    order finish: the same inputs give the same bits on every call (the
+    quad kernel with a ragged tail, or -- lead 1, unaligned rows -- the
+    element kernel alone), for the fused step and the reduce; and the value
+    is the oracle's sequential fp64 sum of g^2 within 1e-10 relative (the
+    summation orders differ; n * 2^-53 bounds the sequential sum's error
+    for 10^6 positive terms)."""
+    draw = GradDraw(BF16, 1e-3)
+    rows = host_rows(150 + n_dp, 1, 0, n_dp, 0, length, draw)
+    lay, _ = zs.zero_flatten_layout([length * n_dp], n_dp)
+    buf = np.zeros(n_dp * length + lead, np.uint16)
+    buf[lead:] = rows.reshape(-1)
+    g = dev16(buf, zs.ZERO_BF16)[lead:]
+    w0 = host_master(150 + n_dp, 0, length)
+    hp = zs.AdamWHParams(step=1, grad_scale=1.0 / n_dp, **HP)
+    sums = []
+    for _ in range(2):
+        dw, dm, dv = devf(w0), devf(np.zeros(length, np.float32)), devf(np.zeros(length, np.float32))
+        wf = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device="cuda")
+        ss = torch.zeros(1, dtype=torch.float64, device="cuda")
+        zs.zero_shard_step(g, length, length, dw, dm, dv, wf, lay, 0, hp, sumsq=ss)
+        acc = torch.empty(length, device="cuda")
+        rs = torch.zeros(1, dtype=torch.float64, device="cuda")
+        zs.zero_shard_reduce(g, n_dp, length, length, acc, sumsq=rs)
+        torch.cuda.synchronize()
+        sums.append((ss.item(), rs.item()))
+    assert np.array(sums[0]).view(np.uint64).tolist() == np.array(sums[1]).view(np.uint64).tolist()
+    o_ss = np.zeros(1)
+    w, m, v = w0.copy(), np.zeros(length, np.float32), np.zeros(length, np.float32)
+    oracle.step(rows, oracle.BF16, n_dp, length, length, w, m, v, np.zeros(length, np.uint16),
+                oracle.BF16, 1, grad_scale=1.0 / n_dp, sumsq=o_ss, **HP)
+    o_rs = np.zeros(1)
+    oracle.reduce(rows, oracle.BF16, n_dp, length, length, np.zeros(length, np.float32), False,
+                  sumsq=o_rs)
+    assert abs(sums[0][0] - o_ss[0]) <= 1e-10 * o_ss[0]
+    assert abs(sums[0][1] - o_rs[0]) <= 1e-10 * o_rs[0]

@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     lib = ctypes.CDLL(zs.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -132,13 +132,18 @@ def _hp(**kw):
 
 def _step(grads=BASE, ld=1024, length=1024, master=BASE + (1 << 30), m=BASE + (2 << 30),
           v=BASE + (3 << 30), wfull=BASE + (4 << 30), lay=None, rank=1, shard_off=0,
-          hp=None, ovf=None, ssq=None, gdt=0, wdt=0):
+          hp=None, ovf=None, ssq=None, gdt=0, wdt=0, ws=None, ws_bytes=None):
     if lay is None:
         lay = zs.zero_flatten_layout([4096], 4)[0]
     hp = hp or _hp()
+    if ssq and ws is None:
+        ws = BASE + (5 << 30)
+    if ws_bytes is None:
+        ws_bytes = zs.zero_sumsq_workspace_bytes(max(length, 0)) if ws else 0
     return L.zero_shard_step(P(grads), gdt, ld, length, P(master), P(m), P(v), P(wfull), wdt,
                              ctypes.byref(lay), rank, shard_off, ctypes.byref(hp),
-                             P(ovf) if ovf else None, P(ssq) if ssq else None, None)
+                             P(ovf) if ovf else None, P(ssq) if ssq else None,
+                             P(ws) if ws else None, ws_bytes, None)
 
 
 @cpu_only
@@ -161,6 +166,13 @@ def _step(grads=BASE, ld=1024, length=1024, master=BASE + (1 << 30), m=BASE + (2
     (dict(wfull=BASE + (3 << 30) - 2 * 1024), zs.ZERO_EALIAS),  # slot over v
     (dict(ovf=BASE + 100), zs.ZERO_EALIAS),
     (dict(ssq=BASE + (2 << 30) + 8), zs.ZERO_EALIAS),
+    # the sum of squares' workspace: required, 8-byte aligned, large enough, disjoint
+    (dict(ssq=BASE + (6 << 30), ws=0), zs.ZERO_EINVAL),
+    (dict(ssq=BASE + (6 << 30), ws=BASE + (5 << 30) + 4), zs.ZERO_EINVAL),
+    (dict(ssq=BASE + (6 << 30), ws_bytes=zs.zero_sumsq_workspace_bytes(1024) - 1),
+     zs.ZERO_EINVAL),
+    (dict(ssq=BASE + (6 << 30), ws=BASE + (3 << 30)), zs.ZERO_EALIAS),      # over v
+    (dict(ssq=BASE + (5 << 30) + 64), zs.ZERO_EALIAS),                      # sumsq inside it
 ])
 def test_step_rejects_bad_arguments(kw, status):
     assert _step(**kw) == status
@@ -178,13 +190,29 @@ def test_step_bad_layout_and_empty_range():
 @cpu_only
 def test_reduce_and_adamw_reject_bad_arguments():
     R = L.zero_shard_reduce
-    assert R(P(BASE), 0, 0, 16, 16, P(BASE + 4096), 0, None, None, None) == zs.ZERO_EINVAL
-    assert R(P(BASE), 0, 2, 8, 16, P(BASE + 4096), 0, None, None, None) == zs.ZERO_EINVAL
-    assert R(P(BASE), 3, 2, 16, 16, P(BASE + 4096), 0, None, None, None) == zs.ZERO_EINVAL
-    assert R(P(BASE), 0, 2, 16, 16, P(BASE + 40), 0, None, None, None) == zs.ZERO_EALIAS
-    assert R(P(BASE), 0, 2, 16, 16, P(BASE + 4096), 0, P(BASE + 4096 + 60), None,
+    assert R(P(BASE), 0, 0, 16, 16, P(BASE + 4096), 0, None, None, None, 0,
+             None) == zs.ZERO_EINVAL
+    assert R(P(BASE), 0, 2, 8, 16, P(BASE + 4096), 0, None, None, None, 0,
+             None) == zs.ZERO_EINVAL
+    assert R(P(BASE), 3, 2, 16, 16, P(BASE + 4096), 0, None, None, None, 0,
+             None) == zs.ZERO_EINVAL
+    assert R(P(BASE), 0, 2, 16, 16, P(BASE + 40), 0, None, None, None, 0,
              None) == zs.ZERO_EALIAS
-    assert R(None, 0, 2, 16, 0, None, 0, None, None, None) == zs.ZERO_OK
+    assert R(P(BASE), 0, 2, 16, 16, P(BASE + 4096), 0, P(BASE + 4096 + 60), None,
+             None, 0, None) == zs.ZERO_EALIAS
+    assert R(None, 0, 2, 16, 0, None, 0, None, None, None, 0, None) == zs.ZERO_OK
+    wsb = zs.zero_sumsq_workspace_bytes(16)
+    ssq, ws = P(BASE + 8192), P(BASE + 16384)
+    assert R(P(BASE), 0, 2, 16, 16, P(BASE + 4096), 0, None, ssq, None, 0,
+             None) == zs.ZERO_EINVAL                                      # no workspace
+    assert R(P(BASE), 0, 2, 16, 16, P(BASE + 4096), 0, None, ssq, ws, wsb - 8,
+             None) == zs.ZERO_EINVAL                                      # too small
+    assert R(P(BASE), 0, 2, 16, 16, P(BASE + 4096), 0, None, ssq, P(BASE + 4000), wsb,
+             None) == zs.ZERO_EALIAS                                      # over acc
+    assert zs.zero_sumsq_workspace_bytes(0) == 8 * (256 + 4096)
+    assert zs.zero_sumsq_workspace_bytes(257) == 8 * (256 + 2 + 4096)
+    with pytest.raises(ValueError):
+        zs.zero_sumsq_workspace_bytes(-1)
     A = L.zero_shard_adamw
     lay = zs.zero_flatten_layout([4096], 4)[0]
     hp = _hp()
@@ -322,8 +350,10 @@ def test_dim0_rejects_invalid():
 def test_fp32_rows_validation():
     R = L.zero_shard_reduce
     # fp32 rows: 4 bytes per element in the alias check (16-bit would miss it)
-    assert R(P(BASE), 2, 2, 16, 16, P(BASE + 100), 0, None, None, None) == zs.ZERO_EALIAS
-    assert R(P(BASE), 3, 2, 16, 16, P(BASE + 4096), 0, None, None, None) == zs.ZERO_EINVAL
+    assert R(P(BASE), 2, 2, 16, 16, P(BASE + 100), 0, None, None, None, 0,
+             None) == zs.ZERO_EALIAS
+    assert R(P(BASE), 3, 2, 16, 16, P(BASE + 4096), 0, None, None, None, 0,
+             None) == zs.ZERO_EINVAL
     # weights cannot be fp32
     assert _step(wdt=2) == zs.ZERO_EINVAL
     assert _step(gdt=2, v=BASE + 3 * 1024 * 4 - 8) == zs.ZERO_EALIAS  # v over the fp32 rows
@@ -345,9 +375,10 @@ def test_q8_entry_points_reject_bad_arguments():
 
     def step(gq=BASE, gs=BASE + (1 << 28), ld=4096, sld=16, length=4096, w=BASE + (2 << 28),
              m=BASE + (3 << 28), v=BASE + (4 << 28), wq=BASE + (5 << 28), ws=BASE + (6 << 28),
-             lay=lay, rank=1, off=0):
+             lay=lay, rank=1, off=0, ssq=None, wk=None, wk_bytes=0):
         return S8(P(gq), P(gs), ld, sld, length, P(w), P(m), P(v), P(wq), P(ws),
-                  ctypes.byref(lay), rank, off, ctypes.byref(hp), None, None, None)
+                  ctypes.byref(lay), rank, off, ctypes.byref(hp), None,
+                  P(ssq) if ssq else None, P(wk) if wk else None, wk_bytes, None)
     assert step(off=128) == zs.ZERO_EINVAL                          # not a block boundary
     assert step(sld=15) == zs.ZERO_EINVAL                           # scale rows too short
     assert step(ld=4098) == zs.ZERO_EINVAL                          # row stride not % 4
@@ -360,3 +391,9 @@ def test_q8_entry_points_reject_bad_arguments():
     assert step(ws=BASE + (1 << 28) + 64) == zs.ZERO_EALIAS         # scale slot over row scales
     assert step(w=BASE + 7 * 4096) == zs.ZERO_EALIAS                # master over the last row
     assert step(length=0, gq=0, gs=0, w=0, m=0, v=0, wq=0, ws=0) == zs.ZERO_OK
+    wkb = zs.zero_sumsq_workspace_bytes(4096)
+    assert step(ssq=BASE + (7 << 28)) == zs.ZERO_EINVAL             # sum without workspace
+    assert step(ssq=BASE + (7 << 28), wk=BASE + (7 << 28) + 4096,
+                wk_bytes=wkb - 1) == zs.ZERO_EINVAL                  # workspace too small
+    assert step(ssq=BASE + (7 << 28), wk=BASE + (4 << 28),
+                wk_bytes=wkb) == zs.ZERO_EALIAS                      # workspace over v

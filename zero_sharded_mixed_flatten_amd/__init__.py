@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libzero_shard.so")
 ZERO_OK, ZERO_EINVAL, ZERO_EALIAS, ZERO_ERANGE, ZERO_EDEVICE = range(5)
 ZERO_BF16, ZERO_FP16, ZERO_FP32 = 0, 1, 2
 ZERO_Q8_BLOCK = 256
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class ZeroError(RuntimeError):
@@ -106,7 +106,10 @@ def _load():
     L.zero_dim0_layout.restype = ctypes.c_int
     L.zero_dim0_segments.argtypes = [lay_p, vp, vp, i64, i32, vp, i64, ctypes.POINTER(i64)]
     L.zero_dim0_segments.restype = ctypes.c_int
-    L.zero_shard_reduce.argtypes = [vp, ctypes.c_int, i32, i64, i64, vp, i32, vp, vp, vp]
+    L.zero_sumsq_workspace_bytes.argtypes = [i64]
+    L.zero_sumsq_workspace_bytes.restype = i64
+    L.zero_shard_reduce.argtypes = [vp, ctypes.c_int, i32, i64, i64, vp, i32, vp, vp, vp, i64,
+                                    vp]
     L.zero_shard_reduce.restype = ctypes.c_int
     L.zero_shard_adamw.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, lay_p, i32, i64, i64,
                                    hp_p, vp, vp]
@@ -117,7 +120,7 @@ def _load():
     L.zero_loss_scale_update.argtypes = [vp, vp, dbl, dbl, i32, vp]
     L.zero_loss_scale_update.restype = ctypes.c_int
     L.zero_shard_step.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, ctypes.c_int,
-                                  lay_p, i32, i64, hp_p, vp, vp, vp]
+                                  lay_p, i32, i64, hp_p, vp, vp, vp, i64, vp]
     L.zero_shard_step.restype = ctypes.c_int
     piece_p = ctypes.POINTER(_Piece)
     L.zero_flat_gather.argtypes = [piece_p, i32, i64, i32, i64, i64, vp, vp]
@@ -131,7 +134,7 @@ def _load():
     L.zero_q8_dequantize.argtypes = [vp, vp, i64, vp, ctypes.c_int, vp]
     L.zero_q8_dequantize.restype = ctypes.c_int
     L.zero_shard_step_q8.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, lay_p, i32, i64,
-                                     hp_p, vp, vp, vp]
+                                     hp_p, vp, vp, vp, i64, vp]
     L.zero_shard_step_q8.restype = ctypes.c_int
     L.zero_model_state_bytes.argtypes = [dbl, dbl, i32, dbl, ctypes.POINTER(dbl)]
     L.zero_model_state_bytes.restype = ctypes.c_int
@@ -225,6 +228,30 @@ def _rows(t, what: str, n_rows: int, ld: int, length: int, dtype=None, device=No
     return p
 
 
+def zero_sumsq_workspace_bytes(length: int) -> int:
+    """Bytes of device workspace a call over `length` elements that sums
+    squares needs (8 bytes per 256 elements plus 34 KiB)."""
+    n = _lib.zero_sumsq_workspace_bytes(int(length))
+    if n < 0:
+        raise ValueError(f"zero_sumsq_workspace_bytes: length {length} out of range")
+    return n
+
+
+def _workspace(sumsq, workspace, length: int, device):
+    """(pointer, bytes) of the sum's workspace: the caller's (checked for
+    size) or a new one; (NULL, 0) without a sum."""
+    import torch
+    if sumsq is None:
+        return None, 0
+    need = zero_sumsq_workspace_bytes(max(0, length))
+    if workspace is None:
+        workspace = torch.empty((need + 7) // 8, dtype=torch.float64, device=device)
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace: {need} bytes needed, the tensor holds {nbytes}")
+    return _buf(workspace, "workspace", 0, device=device), nbytes
+
+
 def _stream(stream, like):
     import torch
     if stream is None:
@@ -299,17 +326,21 @@ def zero_dim0_segments(layout: ZeroLayout, shapes: Sequence[Tuple[int, int]], ra
 
 
 def zero_shard_reduce(grads, n_contrib: int, ld: int, length: int, acc,
-                      accumulate: bool = False, overflow=None, sumsq=None, stream=None):
+                      accumulate: bool = False, overflow=None, sumsq=None, stream=None,
+                      workspace=None):
     """acc[:length] (+)= sum of n_contrib rows (bf16, fp16 or fp32) of stride ld
-    starting at grads."""
+    starting at grads; with sumsq, the sum of acc^2 is added to it (a
+    workspace tensor is allocated unless one of at least
+    zero_sumsq_workspace_bytes(length) bytes is passed)."""
     import torch
     d = acc.device
+    ws, ws_bytes = _workspace(sumsq, workspace, length, d)
     _check(_lib.zero_shard_reduce(
         _rows(grads, "grads", n_contrib, ld, length, device=d),
         _dtype_code(grads, "grads", True), n_contrib, ld, length,
         _buf(acc, "acc", length, torch.float32), int(bool(accumulate)),
         _buf(overflow, "overflow", 1, torch.int32, d), _buf(sumsq, "sumsq", 1, torch.float64, d),
-        _stream(stream, acc)), "zero_shard_reduce")
+        ws, ws_bytes, _stream(stream, acc)), "zero_shard_reduce")
 
 
 def zero_shard_adamw(acc, master, m, v, weight_full, layout: ZeroLayout, rank: int,
@@ -379,11 +410,13 @@ def zero_loss_scale_update(loss_scale, overflow, growth: float = 2.0, backoff: f
 
 def zero_shard_step(grads, ld: int, length: int, master, m, v, weight_full,
                     layout: ZeroLayout, rank: int, hp: AdamWHParams, shard_off: int = 0,
-                    overflow=None, sumsq=None, stream=None):
-    """Fused reduce of layout.n_dp rows + AdamW + cast into the weight slot."""
+                    overflow=None, sumsq=None, stream=None, workspace=None):
+    """Fused reduce of layout.n_dp rows + AdamW + cast into the weight slot
+    (sumsq and workspace as for zero_shard_reduce)."""
     import torch
     hpc = hp._c()
     d = master.device
+    ws, ws_bytes = _workspace(sumsq, workspace, length, d)
     _check(_lib.zero_shard_step(
         _rows(grads, "grads", layout.n_dp, ld, length, device=d),
         _dtype_code(grads, "grads", True), ld, length,
@@ -392,7 +425,8 @@ def zero_shard_step(grads, ld: int, length: int, master, m, v, weight_full,
         _buf(weight_full, "weight_full", _slot_end(layout, rank, shard_off, length), device=d),
         _dtype_code(weight_full, "weight_full"), ctypes.byref(layout), rank, shard_off,
         ctypes.byref(hpc), _buf(overflow, "overflow", 1, torch.int32, d),
-        _buf(sumsq, "sumsq", 1, torch.float64, d), _stream(stream, master)), "zero_shard_step")
+        _buf(sumsq, "sumsq", 1, torch.float64, d), ws, ws_bytes, _stream(stream, master)),
+        "zero_shard_step")
 
 
 def _slot_end(layout: ZeroLayout, rank: int, shard_off: int, length: int) -> int:
@@ -477,12 +511,15 @@ def zero_q8_dequantize(q, scales, y, stream=None):
 
 def zero_shard_step_q8(gq, gscales, ld: int, sld: int, length: int, master, m, v, wq_full,
                        wscales_full, layout: ZeroLayout, rank: int, hp: AdamWHParams,
-                       shard_off: int = 0, overflow=None, sumsq=None, stream=None):
+                       shard_off: int = 0, overflow=None, sumsq=None, stream=None,
+                       workspace=None):
     """Fused step with 8-bit rows in (codes gq, scales gscales) and 8-bit
-    weights out (wq_full, wscales_full: the all-gather buffer)."""
+    weights out (wq_full, wscales_full: the all-gather buffer); sumsq and
+    workspace as for zero_shard_reduce."""
     import torch
     hpc = hp._c()
     d = master.device
+    ws, ws_bytes = _workspace(sumsq, workspace, length, d)
     nb = q8_blocks(length)
     end = _slot_end(layout, rank, shard_off, length)
     _check(_lib.zero_shard_step_q8(
@@ -494,7 +531,7 @@ def zero_shard_step_q8(gq, gscales, ld: int, sld: int, length: int, master, m, v
              0 if length <= 0 else (end - length) // ZERO_Q8_BLOCK + nb, torch.float32, d),
         ctypes.byref(layout), rank, shard_off, ctypes.byref(hpc),
         _buf(overflow, "overflow", 1, torch.int32, d), _buf(sumsq, "sumsq", 1, torch.float64, d),
-        _stream(stream, master)), "zero_shard_step_q8")
+        ws, ws_bytes, _stream(stream, master)), "zero_shard_step_q8")
 
 
 def zero_adam_step(grads, w_shards, m_shards, v_shards, t: int, lr: float = 1e-3,
@@ -585,5 +622,5 @@ __all__ = ["zero_flatten_layout", "zero_shard_segments", "zero_dim0_layout", "ze
            "zero_shard_adamw", "zero_shard_adamw_ex", "zero_loss_scale_update",
            "new_loss_scale", "read_loss_scale", "zero_shard_step", "zero_flat_gather",
            "zero_flat_scatter", "zero_reshard", "zero_q8_quantize", "zero_q8_dequantize",
-           "zero_shard_step_q8", "q8_blocks", "ZERO_Q8_BLOCK", "zero_model_state_bytes", "zero_comm_bytes",
+           "zero_shard_step_q8", "zero_sumsq_workspace_bytes", "q8_blocks", "ZERO_Q8_BLOCK", "zero_model_state_bytes", "zero_comm_bytes",
            "zero_adam_step", "AdamWHParams", "ZeroLayout", "ZeroError", "ZeroValueError", "ZERO_BF16", "ZERO_FP16", "ZERO_FP32", "library_path"]

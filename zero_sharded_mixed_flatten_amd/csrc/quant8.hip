@@ -417,7 +417,7 @@ step_q8_kernel(const int8_t *__restrict__ gq, const float *__restrict__ gs, int6
                int64_t sld, int n_dp, int64_t len, int64_t nblocks, float *__restrict__ W,
                float *__restrict__ M, float *__restrict__ V, int8_t *__restrict__ wq,
                float *__restrict__ wsc, Consts c, uint32_t *__restrict__ ovf,
-               double *__restrict__ ssq) {
+               double *__restrict__ part) {
     bool bad = false;
     double ss = 0.0;
     const int64_t b = wave_block<TPB>();
@@ -480,7 +480,7 @@ step_q8_kernel(const int8_t *__restrict__ gq, const float *__restrict__ gs, int6
             }
         }
     }
-    flags_epilogue<TPB, OVF, SSQ>(bad, ss, ovf, ssq);
+    flags_epilogue<TPB, OVF, SSQ>(bad, ss, ovf, part);
 }
 
 // ---------------------------------------------------------------------------
@@ -603,7 +603,8 @@ extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales
                                           float *v, int8_t *wq_full, float *wscales_full,
                                           const zero_layout *layout, int32_t rank,
                                           int64_t shard_off, const zero_adamw_hparams *hp,
-                                          uint32_t *overflow, double *sumsq, void *stream) {
+                                          uint32_t *overflow, double *sumsq, void *workspace,
+                                          int64_t workspace_bytes, void *stream) {
     if (!layout_ok(layout) || !hparams_ok(hp)) return ZERO_EINVAL;
     const int n_dp = layout->n_dp;
     if (rank < 0 || rank >= n_dp || shard_off < 0 || len < 0 || len > kMaxLen || ld < len)
@@ -617,13 +618,16 @@ extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales
     if (shard_off > layout->shard || len > layout->shard - shard_off) return ZERO_ERANGE;
     if (len == 0) return ZERO_OK;
     if (!gq || !gscales || !master || !m || !v || !wq_full || !wscales_full) return ZERO_EINVAL;
+    if (sumsq && (!workspace || !aligned8(workspace) ||
+                  workspace_bytes < zero_sumsq_workspace_bytes(len)))
+        return ZERO_EINVAL;
     const int64_t first = static_cast<int64_t>(rank) * layout->shard + shard_off;
     int8_t *wq = wq_full + first;
     float *wsc = wscales_full + first / kB;
     if (!aligned4(gq) || !aligned4(wq) || !aligned16(master) || !aligned16(m) || !aligned16(v))
         return ZERO_EINVAL;
     // outputs pairwise disjoint, and disjoint from every code and scale row
-    Span outs[8];
+    Span outs[9];
     int n_out = 0;
     outs[n_out++] = span_of(master, len, 4);
     outs[n_out++] = span_of(m, len, 4);
@@ -632,6 +636,7 @@ extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales
     outs[n_out++] = span_of(wsc, nb, 4);
     if (overflow) outs[n_out++] = span_of(overflow, 1, 4);
     if (sumsq) outs[n_out++] = span_of(sumsq, 1, 8);
+    if (sumsq) outs[n_out++] = span_of(workspace, workspace_bytes, 1);
     if (spans_overlap(outs, n_out)) return ZERO_EALIAS;
     for (int i = 0; i < n_out; ++i) {
         for (int k = 0; k < n_dp; ++k) {
@@ -643,20 +648,19 @@ extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Consts c = make_consts(*hp);
+    // with a sum of squares each wave (one block) stores its partial
+    double *part = sumsq ? ssq_partials(workspace) : nullptr;
     with_bool(overflow != nullptr, [&](auto OV) {
         with_bool(sumsq != nullptr, [&](auto SS) {
-            // with a sum of squares: one fp64 atomic per workgroup into one
-            // address, so 16 blocks (4096 elements) per workgroup keep the
-            // atomics below the rate that would set the time
-            constexpr int tpb = SS.value ? 16 * kWave : kWave;
-            const size_t lds = residency_lds_bytes(kQ8StepWavesPerCU, tpb);
+            const size_t lds = residency_lds_bytes(kQ8StepWavesPerCU, kWave);
             auto go = [&](auto ND) {
                 for_launches(len, [&](int64_t o, int64_t n) {
                     const int64_t ob = o / kB, nbn = blocks_of(n);
-                    step_q8_kernel<tpb, ND.value, OV.value, SS.value>
-                        <<<grid_waves(nbn, tpb), tpb, lds, st>>>(
+                    step_q8_kernel<kWave, ND.value, OV.value, SS.value>
+                        <<<grid_waves(nbn, kWave), kWave, lds, st>>>(
                             gq + o, gscales + ob, ld, sld, n_dp, n, nbn, master + o, m + o,
-                            v + o, wq + o, wsc + ob, c, overflow, sumsq);
+                            v + o, wq + o, wsc + ob, c, overflow,
+                            SS.value ? part + ob : nullptr);
                 });
             };
             if (n_dp == 1) go(IntC<1>{});
@@ -664,5 +668,10 @@ extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales
             else go(IntC<0>{});
         });
     });
+    if (sumsq) {
+        const zero_status s1 = launch_status();
+        if (s1 != ZERO_OK) return s1;
+        return finish_sumsq(workspace, nb, sumsq, st);
+    }
     return launch_status();
 }

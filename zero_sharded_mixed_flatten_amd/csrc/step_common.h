@@ -184,28 +184,50 @@ __device__ __forceinline__ void widen_quad(float t[kQuad], typename GradT<GDT>::
 __device__ __forceinline__ void loads_issued() { __builtin_amdgcn_sched_barrier(0); }
 
 // The optional shard-wide outputs: one atomic per wave for the flag (only
-// when a lane saw a non-finite value), a wave then workgroup reduction and
-// one atomic add per workgroup for the sum.  Every thread of the workgroup
-// must reach this point.
+// when a lane saw a non-finite value); for the sum, a fixed-order wave
+// (then workgroup) reduction and one plain store of the workgroup's partial
+// to part[blockIdx.x] -- finish_sumsq() adds the partials into the caller's
+// scalar afterwards, in a fixed order.  (One atomic add per workgroup into
+// one address instead would cap the rate at about 80 M workgroups/s and
+// force large workgroups, which the streaming kernels lose 10 % to.)
+// Every thread of the workgroup must reach this point.
 template <int TPB, bool OVF, bool SSQ>
-__device__ __forceinline__ void flags_epilogue(bool bad, double ss, uint32_t *ovf, double *ssq) {
+__device__ __forceinline__ void flags_epilogue(bool bad, double ss, uint32_t *ovf, double *part) {
     if constexpr (OVF) {
         if (__ballot(bad) != 0 && (threadIdx.x & (kWave - 1)) == 0) atomicOr(ovf, 1u);
     }
     if constexpr (SSQ) {
-        __shared__ double part[TPB / kWave];
 #pragma unroll
         for (int off = kWave / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
-        if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = ss;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            double t = 0.0;
+        if constexpr (TPB == kWave) {
+            if (threadIdx.x == 0) part[blockIdx.x] = ss;
+        } else {
+            __shared__ double wave_part[TPB / kWave];
+            if ((threadIdx.x & (kWave - 1)) == 0) wave_part[threadIdx.x / kWave] = ss;
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                double t = wave_part[0];
 #pragma unroll
-            for (int wv = 0; wv < TPB / kWave; ++wv) t += part[wv];
-            unsafeAtomicAdd(ssq, t);  // device memory: native global_atomic_add_f64
+                for (int wv = 1; wv < TPB / kWave; ++wv) t += wave_part[wv];
+                part[blockIdx.x] = t;
+            }
         }
     }
 }
+
+// Sum of squares: partials of one call's workgroups, then the fixed-order
+// finish.  A workspace of zero_sumsq_workspace_bytes(len) holds
+// kSsqStage2 stage-two sums followed by the partials (at most
+// blocks_of(len) + kSsqScalarBlocks of them).
+constexpr int kSsqStage2 = 256;           // stage-two workgroups (and sums)
+constexpr int64_t kSsqScalarBlocks = 4096; // grid cap of the summing element kernels
+inline int64_t ssq_partials_cap(int64_t len) { return (len + 255) / 256 + kSsqScalarBlocks; }
+inline double *ssq_partials(void *workspace) {
+    return static_cast<double *>(workspace) + kSsqStage2;
+}
+// *sumsq += the sum of part[0, count), in an order fixed by count alone
+// (defined with the library's other kernels; launches two small kernels)
+zero_status finish_sumsq(void *workspace, int64_t count, double *sumsq, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // the arithmetic of one element

@@ -49,34 +49,30 @@ namespace {
 using namespace zero_host;
 using namespace zero_step;
 
-constexpr int kBlock = 256;     // threads per workgroup of the element kernels and of
-                                // streaming kernels that also sum squares
+constexpr int kBlock = 256;     // threads per workgroup of the element kernels
 constexpr int kRowBatch = 8;    // rows loaded together when n_dp is not specialised
 // Residency caps in waves per CU, measured per kernel at the workloads'
 // sizes with one-wave workgroups (a finished wave's slot is refilled at
 // once; with four-wave workgroups a slot frees only when all four are done,
-// which cost 8-10%).  The variants that also sum squares are shaped by
-// their atomics instead (kSsqBlock below).
+// which cost 8-10%).  The variants that also sum squares take the same
+// one-wave shape and store one partial per wave (flags_epilogue).
 // Fused step: 10 waves with 1 row (56 B per lane in flight), 7 with 8 rows
 // (112 B), and with 64 rows the 152 VGPRs per lane already allow only 12.
 // With 8 fp32 rows (176 B per lane in flight) 5 waves per CU measured best
 // (79.6 % of 8 TB/s against 78.7 % at 7 and 76.9 % uncapped, random data).
-constexpr int step_waves_per_cu(int gdt, int ndp) {
-    if (gdt == ZERO_FP32) return ndp == 1 ? 10 : 5;
+// The summing variants carry a double accumulation per element and store a
+// partial per wave; swept separately (7B shard; GPT-2-XL list for 1 row):
+// 1 row 10 -> 79.2 %, 12 -> 82.3 %, 14 -> 80.9 %; 8 rows 7 -> 77.8 %,
+// 8 -> 81.0 %, 10 -> 80.8 %; 64 rows 12 -> 72.6 %, 16 -> 72.4 %; 8 fp32
+// rows 5 -> 78.6 %, 6 -> 80.9 %, 7 -> 80.9 %; the accumulating fp16 reduce
+// 10 -> 82.2 %, 12 -> 83.9 %, 16 -> 80.9 %.
+constexpr int step_waves_per_cu(int gdt, int ndp, bool ssq = false) {
+    if (gdt == ZERO_FP32) return ndp == 1 ? 10 : ssq ? 6 : 5;
+    if (ssq) return ndp == 1 || ndp == 64 ? 12 : 8;
     return ndp == 1 ? 10 : ndp == 64 ? 12 : 7;
 }
 constexpr int kReduceWavesPerCU = 10;
-// Variants that sum squares end with one fp64 atomic per workgroup into one
-// address, and the atomics, not memory, then set the time: the 7B reduce
-// with four-wave workgroups (one atomic per 1024 elements) took 10.4 ms
-// against 3.0 ms without the sum.  Eight-wave workgroups with two quads per
-// lane (one atomic per 4096 elements) at 16 waves per CU: 3.46 ms.  64 rows
-// keep one quad per lane (VGPRs); their workgroups cover 2048 elements.
-constexpr int kSsqBlock = 512;
-constexpr int kSsqWavesPerCU = 16;
-constexpr int ssq_quads(int ndp) { return ndp == 64 ? 1 : 2; }
-// the element-wise kernels loop; with a sum their grid is capped
-constexpr int64_t kSsqScalarBlocks = 4096;
+constexpr int kReduceSsqWavesPerCU = 12;
 constexpr int kAdamwWavesPerCU = 10;
 // Device-side step controls (zero_step_control with the static part of the
 // gradient scale alongside).
@@ -168,57 +164,29 @@ __device__ __forceinline__ void step_quad_finish(Rows<GDT, NDP> &rows, f32x4 w4,
     store8(out + e0, u32x2{narrow2<WDT>(w[0], w[1]), narrow2<WDT>(w[2], w[3])});
 }
 
-// Q quads per lane, TPB * kQuad elements apart (every load instruction of a
-// wave still covers one contiguous span), all loaded before the first add.
-// Q > 1 only serves the variants that sum squares, to cut their atomics
-// (kSsqBlock); Q == 1 keeps the single guarded body of the hot path.
-template <int TPB, int Q, int GDT, int WDT, int NDP, bool OVF, bool SSQ>
+// One quad per lane, one-wave workgroups (TPB == kWave): the rows and the
+// state of the quad are all loaded before the first add.  With SSQ the
+// wave's partial sum of squares goes to part[blockIdx.x].
+template <int TPB, int GDT, int WDT, int NDP, bool OVF, bool SSQ>
 __global__ void __launch_bounds__(TPB)
 step_quad_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld, int n_dp,
                  int64_t nquad,
                  float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
                  uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
-                 double *__restrict__ ssq) {
+                 double *__restrict__ part) {
     bool bad = false;
     double ss = 0.0;
-    if constexpr (Q == 1) {
-        const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
-        if (q < nquad) {
-            const int64_t e0 = q * kQuad;
-            Rows<GDT, NDP> rows;
-            load_rows<GDT, NDP>(rows, grads + e0, ld);
-            const f32x4 w4 = load16(W + e0), m4 = load16(M + e0), v4 = load16(V + e0);
-            loads_issued();
-            step_quad_finish<GDT, WDT, NDP, OVF, SSQ>(rows, w4, m4, v4, grads + e0, ld, n_dp, e0,
-                                                      W, M, V, out, c, bad, ss);
-        }
-    } else {
-        int64_t qi[Q];
-        Rows<GDT, NDP> rows[Q];
-        f32x4 w4[Q], m4[Q], v4[Q];
-#pragma unroll
-        for (int u = 0; u < Q; ++u) {
-            qi[u] = (static_cast<int64_t>(blockIdx.x) * Q + u) * TPB + threadIdx.x;
-            if (qi[u] < nquad) {
-                const int64_t e0 = qi[u] * kQuad;
-                load_rows<GDT, NDP>(rows[u], grads + e0, ld);
-                w4[u] = load16(W + e0);
-                m4[u] = load16(M + e0);
-                v4[u] = load16(V + e0);
-            }
-        }
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
+    if (q < nquad) {
+        const int64_t e0 = q * kQuad;
+        Rows<GDT, NDP> rows;
+        load_rows<GDT, NDP>(rows, grads + e0, ld);
+        const f32x4 w4 = load16(W + e0), m4 = load16(M + e0), v4 = load16(V + e0);
         loads_issued();
-#pragma unroll
-        for (int u = 0; u < Q; ++u) {
-            if (qi[u] < nquad) {
-                const int64_t e0 = qi[u] * kQuad;
-                step_quad_finish<GDT, WDT, NDP, OVF, SSQ>(rows[u], w4[u], m4[u], v4[u],
-                                                          grads + e0, ld, n_dp, e0, W, M, V,
-                                                          out, c, bad, ss);
-            }
-        }
+        step_quad_finish<GDT, WDT, NDP, OVF, SSQ>(rows, w4, m4, v4, grads + e0, ld, n_dp, e0, W,
+                                                  M, V, out, c, bad, ss);
     }
-    flags_epilogue<TPB, OVF, SSQ>(bad, ss, ovf, ssq);
+    flags_epilogue<TPB, OVF, SSQ>(bad, ss, ovf, part);
 }
 
 // element-per-thread variant for unaligned buffers and ragged tails
@@ -228,7 +196,7 @@ step_scalar_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t 
                    int64_t len,
                    float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
                    uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
-                   double *__restrict__ ssq) {
+                   double *__restrict__ part) {
     bool bad = false;
     double ss = 0.0;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
@@ -246,7 +214,7 @@ step_scalar_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t 
         V[j] = v;
         out[j] = narrow1<WDT>(w);
     }
-    flags_epilogue<kBlock, OVF, SSQ>(bad, ss, ovf, ssq);
+    flags_epilogue<kBlock, OVF, SSQ>(bad, ss, ovf, part);
 }
 
 // ---------------------------------------------------------------------------
@@ -273,51 +241,26 @@ __device__ __forceinline__ void reduce_quad_finish(Rows<GDT, NDP> &rows, f32x4 p
     store16(acc + e0, f32x4{a[0], a[1], a[2], a[3]});
 }
 
-template <int TPB, int Q, int GDT, int NDP, bool ACC, bool OVF, bool SSQ>
+template <int TPB, int GDT, int NDP, bool ACC, bool OVF, bool SSQ>
 __global__ void __launch_bounds__(TPB)
 reduce_quad_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld, int n,
                    int64_t nquad,
                    float *__restrict__ acc, uint32_t *__restrict__ ovf,
-                   double *__restrict__ ssq) {
+                   double *__restrict__ part) {
     bool bad = false;
     double ss = 0.0;
-    if constexpr (Q == 1) {
-        const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
-        if (q < nquad) {
-            const int64_t e0 = q * kQuad;
-            Rows<GDT, NDP> rows;
-            load_rows<GDT, NDP>(rows, grads + e0, ld);
-            f32x4 prev = {};
-            if constexpr (ACC) prev = load16(acc + e0);
-            loads_issued();
-            reduce_quad_finish<GDT, NDP, ACC, OVF, SSQ>(rows, prev, grads + e0, ld, n, e0, acc,
-                                                        bad, ss);
-        }
-    } else {
-        int64_t qi[Q];
-        Rows<GDT, NDP> rows[Q];
-        f32x4 prev[Q];
-#pragma unroll
-        for (int u = 0; u < Q; ++u) {
-            qi[u] = (static_cast<int64_t>(blockIdx.x) * Q + u) * TPB + threadIdx.x;
-            prev[u] = f32x4{};
-            if (qi[u] < nquad) {
-                const int64_t e0 = qi[u] * kQuad;
-                load_rows<GDT, NDP>(rows[u], grads + e0, ld);
-                if constexpr (ACC) prev[u] = load16(acc + e0);
-            }
-        }
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
+    if (q < nquad) {
+        const int64_t e0 = q * kQuad;
+        Rows<GDT, NDP> rows;
+        load_rows<GDT, NDP>(rows, grads + e0, ld);
+        f32x4 prev = {};
+        if constexpr (ACC) prev = load16(acc + e0);
         loads_issued();
-#pragma unroll
-        for (int u = 0; u < Q; ++u) {
-            if (qi[u] < nquad) {
-                const int64_t e0 = qi[u] * kQuad;
-                reduce_quad_finish<GDT, NDP, ACC, OVF, SSQ>(rows[u], prev[u], grads + e0, ld, n,
-                                                            e0, acc, bad, ss);
-            }
-        }
+        reduce_quad_finish<GDT, NDP, ACC, OVF, SSQ>(rows, prev, grads + e0, ld, n, e0, acc, bad,
+                                                    ss);
     }
-    flags_epilogue<TPB, OVF, SSQ>(bad, ss, ovf, ssq);
+    flags_epilogue<TPB, OVF, SSQ>(bad, ss, ovf, part);
 }
 
 template <int GDT, bool ACC, bool OVF, bool SSQ>
@@ -325,7 +268,7 @@ __global__ void __launch_bounds__(kBlock)
 reduce_scalar_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld, int n,
                      int64_t len,
                      float *__restrict__ acc, uint32_t *__restrict__ ovf,
-                     double *__restrict__ ssq) {
+                     double *__restrict__ part) {
     bool bad = false;
     double ss = 0.0;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
@@ -338,7 +281,7 @@ reduce_scalar_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_
         if constexpr (SSQ) ss += static_cast<double>(a) * static_cast<double>(a);
         acc[j] = a;
     }
-    flags_epilogue<kBlock, OVF, SSQ>(bad, ss, ovf, ssq);
+    flags_epilogue<kBlock, OVF, SSQ>(bad, ss, ovf, part);
 }
 
 // ---------------------------------------------------------------------------
@@ -540,28 +483,100 @@ bool rows_ok(int n_rows, int64_t ld, int64_t len) {
     return true;
 }
 
+// the workspace of a call that sums squares: given, 8-byte aligned, large enough
+bool workspace_ok(const void *ws, int64_t bytes, int64_t len) {
+    return ws && aligned8(ws) && bytes >= zero_sumsq_workspace_bytes(len);
+}
+
+// partials the quad launches and the element kernel of one call store:
+// one per one-wave workgroup of quads, one per element-kernel workgroup
+int64_t ssq_partial_count(int64_t nquad, int64_t rest) {
+    return (nquad + kWave - 1) / kWave + (rest > 0 ? scalar_grid(rest, true) : 0);
+}
+
+// Stage two of the sum: workgroup j adds partials [j * chunk, (j + 1) * chunk)
+// -- each thread a strided subset in index order, then a halving tree in
+// LDS -- into st2[j].  Fixed by count alone, so a call's sum is the same
+// bits every time.
+__global__ void __launch_bounds__(kBlock)
+ssq_stage2_kernel(const double *__restrict__ part, int64_t count, int64_t chunk,
+                  double *__restrict__ st2) {
+    __shared__ double s[kBlock];
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * chunk;
+    const int64_t hi = lo + chunk < count ? lo + chunk : count;
+    double t = 0.0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) t += part[i];
+    s[threadIdx.x] = t;
+    __syncthreads();
+#pragma unroll
+    for (int w = kBlock / 2; w > 0; w >>= 1) {
+        if (static_cast<int>(threadIdx.x) < w) s[threadIdx.x] += s[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) st2[blockIdx.x] = s[0];
+}
+
+// Stage three: the kSsqStage2 sums by a halving tree, added to the caller's
+// scalar with one atomic (calls on other streams may add to it as well).
+__global__ void __launch_bounds__(kSsqStage2)
+ssq_stage3_kernel(const double *__restrict__ st2, double *__restrict__ sumsq) {
+    __shared__ double s[kSsqStage2];
+    s[threadIdx.x] = st2[threadIdx.x];
+    __syncthreads();
+#pragma unroll
+    for (int w = kSsqStage2 / 2; w > 0; w >>= 1) {
+        if (static_cast<int>(threadIdx.x) < w) s[threadIdx.x] += s[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) unsafeAtomicAdd(sumsq, s[0]);
+}
+
 }  // namespace
+
+namespace zero_step {
+
+zero_status finish_sumsq(void *workspace, int64_t count, double *sumsq, hipStream_t st) {
+    static_assert(kSsqStage2 == kBlock, "stage two's sums are stage three's threads");
+    double *st2 = static_cast<double *>(workspace);
+    const int64_t chunk = (count + kSsqStage2 - 1) / kSsqStage2;
+    ssq_stage2_kernel<<<kSsqStage2, kBlock, 0, st>>>(ssq_partials(workspace), count,
+                                                     chunk > 0 ? chunk : 1, st2);
+    ssq_stage3_kernel<<<1, kSsqStage2, 0, st>>>(st2, sumsq);
+    return launch_status();
+}
+
+}  // namespace zero_step
+
+extern "C" int64_t zero_sumsq_workspace_bytes(int64_t len) {
+    if (len < 0 || len > kMaxLen) return -1;
+    return static_cast<int64_t>(sizeof(double)) * (kSsqStage2 + ssq_partials_cap(len));
+}
 
 // ===========================================================================
 
 extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int32_t n_contrib,
                                          int64_t ld, int64_t len, float *acc,
                                          int32_t accumulate, uint32_t *overflow,
-                                         double *sumsq, void *stream) {
+                                         double *sumsq, void *workspace,
+                                         int64_t workspace_bytes, void *stream) {
     if (!gdtype_ok(gdt) || !rows_ok(n_contrib, ld, len) || len > kMaxLen) return ZERO_EINVAL;
     if (len == 0) return ZERO_OK;
     if (!grads || !acc) return ZERO_EINVAL;
-    Span outs[3];
+    if (sumsq && !workspace_ok(workspace, workspace_bytes, len)) return ZERO_EINVAL;
+    Span outs[4];
     int n_out = 0;
     outs[n_out++] = span_of(acc, len, 4);
     if (overflow) outs[n_out++] = span_of(overflow, 1, 4);
     if (sumsq) outs[n_out++] = span_of(sumsq, 1, 8);
+    if (sumsq) outs[n_out++] = span_of(workspace, workspace_bytes, 1);
     if (any_alias(outs, n_out, grads, n_contrib, ld, len, gdtype_bytes(gdt))) return ZERO_EALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool vec = rows_vec_ok(grads, gdt, n_contrib, ld) && aligned16(acc);
     const int64_t nquad = vec ? len / kQuad : 0;
     const int64_t done = nquad * kQuad;
+    double *part = sumsq ? ssq_partials(workspace) : nullptr;
+    const int64_t n_qpart = (nquad + kWave - 1) / kWave;
     with_gdtype(gdt, [&](auto GD) {
         using E = typename GradT<GD.value>::elem;
         const E *g = static_cast<const E *>(grads);
@@ -569,29 +584,34 @@ extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int3
             with_bool(overflow != nullptr, [&](auto OV) {
                 with_bool(sumsq != nullptr, [&](auto SS) {
                     if (nquad > 0) {
-                        constexpr int tpb = SS.value ? kSsqBlock : kWave;
                         const size_t lds = residency_lds_bytes(
-                            SS.value ? kSsqWavesPerCU : kReduceWavesPerCU, tpb);
+                            SS.value ? kReduceSsqWavesPerCU : kReduceWavesPerCU, kWave);
                         with_ndp<GD.value>(n_contrib, [&](auto ND) {
-                            constexpr int q = SS.value ? ssq_quads(ND.value) : 1;
                             for_launches(nquad, [&](int64_t q0, int64_t nq) {
                                 const int64_t o = q0 * kQuad;
-                                reduce_quad_kernel<tpb, q, GD.value, ND.value, AC.value,
-                                                   OV.value, SS.value>
-                                    <<<grid_for(nq, tpb * q), tpb, lds, st>>>(
-                                        g + o, ld, n_contrib, nq, acc + o, overflow, sumsq);
+                                reduce_quad_kernel<kWave, GD.value, ND.value, AC.value, OV.value,
+                                                   SS.value>
+                                    <<<grid_for(nq, kWave), kWave, lds, st>>>(
+                                        g + o, ld, n_contrib, nq, acc + o, overflow,
+                                        SS.value ? part + q0 / kWave : nullptr);
                             });
                         });
                     }
                     if (len > done) {
                         reduce_scalar_kernel<GD.value, AC.value, OV.value, SS.value>
                             <<<scalar_grid(len - done, SS.value), kBlock, 0, st>>>(
-                                g + done, ld, n_contrib, len - done, acc + done, overflow, sumsq);
+                                g + done, ld, n_contrib, len - done, acc + done, overflow,
+                                SS.value ? part + n_qpart : nullptr);
                     }
                 });
             });
         });
     });
+    if (sumsq) {
+        const zero_status s1 = launch_status();
+        if (s1 != ZERO_OK) return s1;
+        return finish_sumsq(workspace, ssq_partial_count(nquad, len - done), sumsq, st);
+    }
     return launch_status();
 }
 
@@ -694,7 +714,8 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
                                        void *weight_full, zero_dtype wdt,
                                        const zero_layout *layout, int32_t rank,
                                        int64_t shard_off, const zero_adamw_hparams *hp,
-                                       uint32_t *overflow, double *sumsq, void *stream) {
+                                       uint32_t *overflow, double *sumsq, void *workspace,
+                                       int64_t workspace_bytes, void *stream) {
     if (!gdtype_ok(gdt) || !dtype_ok(wdt) || !layout_ok(layout) || !hparams_ok(hp))
         return ZERO_EINVAL;
     const int n_dp = layout->n_dp;
@@ -703,9 +724,10 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
     if (shard_off > layout->shard || len > layout->shard - shard_off) return ZERO_ERANGE;
     if (len == 0) return ZERO_OK;
     if (!grads || !master || !m || !v || !weight_full) return ZERO_EINVAL;
+    if (sumsq && !workspace_ok(workspace, workspace_bytes, len)) return ZERO_EINVAL;
     uint16_t *slot = static_cast<uint16_t *>(weight_full) +
                      static_cast<int64_t>(rank) * layout->shard + shard_off;
-    Span outs[6];
+    Span outs[7];
     int n_out = 0;
     outs[n_out++] = span_of(master, len, 4);
     outs[n_out++] = span_of(m, len, 4);
@@ -713,6 +735,7 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
     outs[n_out++] = span_of(slot, len, 2);
     if (overflow) outs[n_out++] = span_of(overflow, 1, 4);
     if (sumsq) outs[n_out++] = span_of(sumsq, 1, 8);
+    if (sumsq) outs[n_out++] = span_of(workspace, workspace_bytes, 1);
     if (any_alias(outs, n_out, grads, n_dp, ld, len, gdtype_bytes(gdt))) return ZERO_EALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -721,6 +744,8 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
                      aligned16(v) && aligned8(slot);
     const int64_t nquad = vec ? len / kQuad : 0;
     const int64_t done = nquad * kQuad;
+    double *part = sumsq ? ssq_partials(workspace) : nullptr;
+    const int64_t n_qpart = (nquad + kWave - 1) / kWave;
     with_gdtype(gdt, [&](auto GD) {
         using E = typename GradT<GD.value>::elem;
         const E *g = static_cast<const E *>(grads);
@@ -728,19 +753,16 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
             with_bool(overflow != nullptr, [&](auto OV) {
                 with_bool(sumsq != nullptr, [&](auto SS) {
                     if (nquad > 0) {
-                        constexpr int tpb = SS.value ? kSsqBlock : kWave;
                         with_ndp<GD.value>(n_dp, [&](auto ND) {
-                            constexpr int q = SS.value ? ssq_quads(ND.value) : 1;
                             const size_t lds = residency_lds_bytes(
-                                SS.value ? kSsqWavesPerCU : step_waves_per_cu(GD.value, ND.value),
-                                tpb);
+                                step_waves_per_cu(GD.value, ND.value, SS.value), kWave);
                             for_launches(nquad, [&](int64_t q0, int64_t nq) {
                                 const int64_t o = q0 * kQuad;
-                                step_quad_kernel<tpb, q, GD.value, WD.value, ND.value, OV.value,
+                                step_quad_kernel<kWave, GD.value, WD.value, ND.value, OV.value,
                                                  SS.value>
-                                    <<<grid_for(nq, tpb * q), tpb, lds, st>>>(
+                                    <<<grid_for(nq, kWave), kWave, lds, st>>>(
                                         g + o, ld, n_dp, nq, master + o, m + o, v + o, slot + o,
-                                        c, overflow, sumsq);
+                                        c, overflow, SS.value ? part + q0 / kWave : nullptr);
                             });
                         });
                     }
@@ -748,11 +770,17 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
                         step_scalar_kernel<GD.value, WD.value, OV.value, SS.value>
                             <<<scalar_grid(len - done, SS.value), kBlock, 0, st>>>(
                                 g + done, ld, n_dp, len - done, master + done, m + done,
-                                v + done, slot + done, c, overflow, sumsq);
+                                v + done, slot + done, c, overflow,
+                                SS.value ? part + n_qpart : nullptr);
                     }
                 });
             });
         });
     });
+    if (sumsq) {
+        const zero_status s1 = launch_status();
+        if (s1 != ZERO_OK) return s1;
+        return finish_sumsq(workspace, ssq_partial_count(nquad, len - done), sumsq, st);
+    }
     return launch_status();
 }
