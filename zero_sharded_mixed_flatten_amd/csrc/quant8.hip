@@ -48,8 +48,10 @@ constexpr int kRowBatchQ8 = 8;          // rows per batch when n_dp is not speci
 // divisions and square root, 8 dequantizations, the quantization) against
 // 33 bytes: it needs more waves than the 16-bit step to hide that work under
 // memory time.  Measured on the 7B shard (8 rows, random data), waves per
-// CU: 8 -> 66.8 %, 12 -> 76.4 %, 16 -> 78.4 %, 20 -> 76.7 %, 32 -> 75.0 %.
-constexpr int kQ8StepWavesPerCU = 16;   // residency cap of the fused 8-bit step
+// CU, with the whole-block body templated and wave-uniform bases: 12 ->
+// 80.0 %, 16 -> 79.4 %, 20 -> 79.3 % (with per-lane tests and 64-bit lane
+// addresses it was 12 -> 76.4 %, 16 -> 78.4 %, 32 -> 75.0 %).
+constexpr int kQ8StepWavesPerCU = 12;   // residency cap of the fused 8-bit step
 // Quantize and dequantize to fp32: Q blocks per wave, loads first.  Sweep on
 // the 7B shard (blocks per wave x waves per CU), quantize fp32 -> int8 +
 // scales: 1 x 32 -> 0.79 ms, 2 x 24 -> 0.67, 2 x 32 -> 0.63, 4 x 16 -> 0.68,
@@ -411,6 +413,87 @@ __device__ __forceinline__ void load_inputs(CodeRows<NDP> &r, float w[kQuad], fl
     }
 }
 
+// One block of the fused 8-bit step for a row count fixed at compile time.
+// FULL (the block lies wholly in the range) is a template parameter, so the
+// hot path carries no per-lane validity tests; the block's bases are
+// wave-uniform and each lane adds a 32-bit offset, which lets the loads and
+// stores take a scalar base address instead of per-lane 64-bit sums.
+template <int NDP, bool OVF, bool SSQ, bool FULL>
+__device__ __forceinline__ void step_q8_block(const int8_t *__restrict__ gq,
+                                              const float *__restrict__ gs, int64_t ld,
+                                              int64_t sld, int64_t len, int64_t b,
+                                              float *__restrict__ W, float *__restrict__ M,
+                                              float *__restrict__ V, int8_t *__restrict__ wq,
+                                              float *__restrict__ wsc, const Consts &c,
+                                              bool &bad, double &ss) {
+    const uint32_t lo = (threadIdx.x % kWave) * kQuad;  // the lane's first element in the block
+    const int64_t base = b * kB;
+    const int8_t *gqb = gq + base;
+    const float *gsb = gs + b;
+    float *Wb = W + base, *Mb = M + base, *Vb = V + base;
+    int8_t *wqb = wq + base;
+    int valid = kQuad;
+    if constexpr (!FULL) {
+        const int64_t e0 = base + lo;
+        valid = e0 + kQuad <= len ? kQuad : (e0 < len ? static_cast<int>(len - e0) : 0);
+    }
+    uint32_t cr[NDP];
+    float sr[NDP];
+    float w[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float m[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float v[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < NDP; ++k) {
+        cr[k] = FULL ? load_codes(gqb + k * ld + lo) : row_codes(gqb + k * ld + lo, false, valid);
+        sr[k] = gsb[k * sld];
+    }
+    if constexpr (FULL) {
+        const f32x4 w4 = load16(Wb + lo), m4 = load16(Mb + lo), v4 = load16(Vb + lo);
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e) {
+            w[e] = w4[e];
+            m[e] = m4[e];
+            v[e] = v4[e];
+        }
+    } else {
+        for (int e = 0; e < valid; ++e) {
+            w[e] = Wb[lo + e];
+            m[e] = Mb[lo + e];
+            v[e] = Vb[lo + e];
+        }
+    }
+    loads_issued();
+    float a[kQuad];
+    add_code_rows<NDP>(a, cr, sr, NDP, true);
+#pragma unroll
+    for (int e = 0; e < kQuad; ++e) {
+        if (FULL || e < valid) {
+            if constexpr (OVF) bad |= !__builtin_isfinite(a[e]);
+            const float g = a[e] * c.s;
+            if constexpr (SSQ) ss += static_cast<double>(g) * static_cast<double>(g);
+            adamw_element(g, w[e], m[e], v[e], c);
+        } else {
+            w[e] = 0.0f;  // outside the range: no part of the block's scale
+        }
+    }
+    const BlockScale bs = block_scale(w);
+    const uint32_t codes = quantize4(w, bs);
+    if (lo == 0) wsc[b] = bs.s;
+    if constexpr (FULL) {
+        store16(Wb + lo, f32x4{w[0], w[1], w[2], w[3]});
+        store16(Mb + lo, f32x4{m[0], m[1], m[2], m[3]});
+        store16(Vb + lo, f32x4{v[0], v[1], v[2], v[3]});
+        store_codes(wqb + lo, codes);
+    } else {
+        for (int e = 0; e < valid; ++e) {
+            Wb[lo + e] = w[e];
+            Mb[lo + e] = m[e];
+            Vb[lo + e] = v[e];
+            wqb[lo + e] = static_cast<int8_t>((codes >> (8 * e)) & 0xFFu);
+        }
+    }
+}
+
 template <int TPB, int NDP, bool OVF, bool SSQ>
 __global__ void __launch_bounds__(TPB)
 step_q8_kernel(const int8_t *__restrict__ gq, const float *__restrict__ gs, int64_t ld,
@@ -421,7 +504,16 @@ step_q8_kernel(const int8_t *__restrict__ gq, const float *__restrict__ gs, int6
     bool bad = false;
     double ss = 0.0;
     const int64_t b = wave_block<TPB>();
-    if (b < nblocks) {  // wave-uniform
+    if constexpr (NDP > 0) {
+        if (b < nblocks) {  // wave-uniform
+            if ((b + 1) * kB <= len)  // wave-uniform: the whole block in the range
+                step_q8_block<NDP, OVF, SSQ, true>(gq, gs, ld, sld, len, b, W, M, V, wq, wsc, c,
+                                                   bad, ss);
+            else
+                step_q8_block<NDP, OVF, SSQ, false>(gq, gs, ld, sld, len, b, W, M, V, wq, wsc, c,
+                                                    bad, ss);
+        }
+    } else if (b < nblocks) {  // any row count: rows in batches, as loaded
         const int lane = static_cast<int>(threadIdx.x) % kWave;
         const int64_t e0 = b * kB + lane * kQuad;
         const bool block_full = (b + 1) * kB <= len;  // wave-uniform
@@ -437,9 +529,7 @@ step_q8_kernel(const int8_t *__restrict__ gq, const float *__restrict__ gs, int6
             load_inputs<NDP, false>(r, w, m, v, gq, gs, ld, sld, b, e0, valid, W, M, V);
         }
         loads_issued();
-        if constexpr (NDP > 0) {
-            add_code_rows<NDP>(a, r.c, r.s, NDP, true);
-        } else {
+        {
             for (int k0 = 0; k0 < n_dp; k0 += kRowBatchQ8) {
                 const int cnt = n_dp - k0 < kRowBatchQ8 ? n_dp - k0 : kRowBatchQ8;
 #pragma unroll
