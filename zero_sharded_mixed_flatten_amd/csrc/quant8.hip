@@ -347,12 +347,6 @@ q8_dequantize_pair_kernel(const int8_t *__restrict__ q, const float *__restrict_
 // ---------------------------------------------------------------------------
 // fused step: dequantize + reduce -> scale -> AdamW -> quantize, one pass
 
-template <int NDP>
-struct CodeRows {
-    uint32_t c[NDP > 0 ? NDP : kRowBatchQ8];
-    float s[NDP > 0 ? NDP : kRowBatchQ8];
-};
-
 // a[e] += q_k[e] * s_k for the rows in r (first row assigns)
 template <int NR>
 __device__ __forceinline__ void add_code_rows(float a[kQuad], const uint32_t *c, const float *s,
@@ -377,25 +371,15 @@ __device__ __forceinline__ uint32_t row_codes(const int8_t *__restrict__ p, bool
     return c;
 }
 
-// One lane's inputs: NDP rows of codes (the batched path loads its rows
-// later) and the state.  FULL (wave-uniform: every quad of the block lies
-// in the range) takes straight-line vector loads; otherwise each lane loads
-// its valid elements one by one.
-template <int NDP, bool FULL>
-__device__ __forceinline__ void load_inputs(CodeRows<NDP> &r, float w[kQuad], float m[kQuad],
-                                            float v[kQuad], const int8_t *__restrict__ gq,
-                                            const float *__restrict__ gs, int64_t ld, int64_t sld,
-                                            int64_t b, int64_t e0, int valid,
-                                            const float *__restrict__ W,
-                                            const float *__restrict__ M,
-                                            const float *__restrict__ V) {
-    if constexpr (NDP > 0) {
-#pragma unroll
-        for (int k = 0; k < NDP; ++k) {
-            r.c[k] = FULL ? load_codes(gq + k * ld + e0) : row_codes(gq + k * ld + e0, false, valid);
-            r.s[k] = gs[k * sld + b];
-        }
-    }
+// One lane's state for the any-row-count path (its code rows are loaded in
+// batches later).  FULL (wave-uniform: every quad of the block lies in the
+// range) takes straight-line vector loads; otherwise each lane loads its
+// valid elements one by one.
+template <bool FULL>
+__device__ __forceinline__ void load_state(float w[kQuad], float m[kQuad], float v[kQuad],
+                                           int64_t e0, int valid, const float *__restrict__ W,
+                                           const float *__restrict__ M,
+                                           const float *__restrict__ V) {
     if constexpr (FULL) {
         const f32x4 w4 = load16(W + e0), m4 = load16(M + e0), v4 = load16(V + e0);
 #pragma unroll
@@ -522,25 +506,21 @@ step_q8_kernel(const int8_t *__restrict__ gq, const float *__restrict__ gs, int6
         float w[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
         float m[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
         float v[kQuad] = {0.0f, 0.0f, 0.0f, 0.0f};
-        CodeRows<NDP> r;
-        if (block_full) {
-            load_inputs<NDP, true>(r, w, m, v, gq, gs, ld, sld, b, e0, valid, W, M, V);
-        } else {
-            load_inputs<NDP, false>(r, w, m, v, gq, gs, ld, sld, b, e0, valid, W, M, V);
-        }
+        if (block_full) load_state<true>(w, m, v, e0, valid, W, M, V);
+        else load_state<false>(w, m, v, e0, valid, W, M, V);
         loads_issued();
-        {
-            for (int k0 = 0; k0 < n_dp; k0 += kRowBatchQ8) {
-                const int cnt = n_dp - k0 < kRowBatchQ8 ? n_dp - k0 : kRowBatchQ8;
+        uint32_t cr[kRowBatchQ8];
+        float sr[kRowBatchQ8];
+        for (int k0 = 0; k0 < n_dp; k0 += kRowBatchQ8) {
+            const int cnt = n_dp - k0 < kRowBatchQ8 ? n_dp - k0 : kRowBatchQ8;
 #pragma unroll
-                for (int k = 0; k < kRowBatchQ8; ++k) {
-                    if (k < cnt) {
-                        r.c[k] = row_codes(gq + (k0 + k) * ld + e0, valid == kQuad, valid);
-                        r.s[k] = gs[(k0 + k) * sld + b];
-                    }
+            for (int k = 0; k < kRowBatchQ8; ++k) {
+                if (k < cnt) {
+                    cr[k] = row_codes(gq + (k0 + k) * ld + e0, valid == kQuad, valid);
+                    sr[k] = gs[(k0 + k) * sld + b];
                 }
-                add_code_rows<kRowBatchQ8>(a, r.c, r.s, cnt, k0 == 0);
             }
+            add_code_rows<kRowBatchQ8>(a, cr, sr, cnt, k0 == 0);
         }
 #pragma unroll
         for (int e = 0; e < kQuad; ++e) {
