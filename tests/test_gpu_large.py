@@ -50,7 +50,8 @@ def _same_f32(a, b):
 def test_step_across_launches():
     """The fused step (n_dp = 1, bf16 row) over 2^31 + 4099 elements: the
     quad kernel in two launches, then a 3-element tail; step 1 plain, step 2
-    with the overflow flag and the sum of squares (the 512-thread variant)."""
+    with the overflow flag and the sum of squares (partials from both
+    launches and the tail, then the fixed-order finish)."""
     n = L + 4099
     print(f"\n[large] step n={n}", flush=True)
     lay, _ = zs.zero_flatten_layout([n], 1)

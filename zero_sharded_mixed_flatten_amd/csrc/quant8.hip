@@ -14,8 +14,8 @@
 // access -- the layout of the 16-bit step kernels with 4-byte code loads
 // (one contiguous 256-byte span per wave and row) and one scale per row and
 // block read through the scalar cache.  The fused step takes one block per
-// wave (16 per workgroup when a sum of squares is requested, for one atomic
-// per 4096 elements), quantize and dequantize to fp32 two consecutive blocks
+// one-wave workgroup (with a sum of squares, each wave stores its partial),
+// quantize and dequantize to fp32 two consecutive blocks
 // per wave, and dequantize to 16 bits a pair of blocks per wave at 8 codes
 // per lane, so that both its code loads and its 16-byte stores are
 // contiguous across the wave.
@@ -137,7 +137,7 @@ __device__ __forceinline__ void store_codes(int8_t *p, uint32_t x) {
 }
 
 // the block handled by this wave, made wave-uniform (scalar) for the scale
-// loads; a launch covers at most 2^30 blocks (kMaxLen / kB)
+// loads; a launch covers at most 2^23 blocks (kLaunchElems / kB)
 // Workgroups go round-robin over the 8 XCDs (each with its own L2), so the
 // 32 blocks whose scales share a 128-byte line run on all eight and each L2
 // fetches the line: the 7B step reads 1.06 x its algorithmic bytes.
