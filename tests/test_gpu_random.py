@@ -1,0 +1,134 @@
+"""Seeded random cases of the fused step and the reduce against the oracle,
+bitwise: row count, range length, row stride, rank, shard offset, gradient
+and weight formats, the flags, and -- by leading elements before each
+buffer -- the alignment of every pointer, so that calls mix the vector
+kernels, their ragged tails and the element kernels in ways the
+hand-picked cases do not.  The arithmetic is the sharded step of "ZeRO and
+FSDP" (A sharded Adam step); the bar is the same as everywhere: every
+element bit-identical, the sum of squares within its bound."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import zero_sharded_mixed_flatten_amd as zs
+from synth import BF16, F16, F32
+from synth.workloads import GradDraw
+from tests.gpu_util import check_16, check_f32, host_master, host_rows
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)
+ODT = {BF16: oracle.BF16, F16: oracle.FP16, F32: oracle.FP32}
+TDT = {zs.ZERO_BF16: torch.bfloat16, zs.ZERO_FP16: torch.float16}
+CANARY = 0x5A5A
+
+
+def _lead(a: np.ndarray, lead: int, tdt=None):
+    """Device copy of host array a starting `lead` elements into a fresh
+    buffer (so the pointer is off 16-byte alignment by lead * itemsize)."""
+    if a.dtype == np.uint16:
+        buf = np.zeros(a.size + lead, np.uint16)
+        buf[lead:] = a.reshape(-1)
+        return torch.from_numpy(buf.view(np.int16)).cuda().view(tdt)[lead:]
+    buf = np.zeros(a.size + lead, a.dtype)
+    buf[lead:] = a.reshape(-1)
+    return torch.from_numpy(buf).cuda()[lead:]
+
+
+def _host(t):
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.cpu().view(torch.int16).numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def _case(seed):
+    r = np.random.default_rng(seed)
+    n_dp = int(r.choice([1, 2, 3, 5, 8, 13, 64]))
+    shard = int(r.integers(1, 40_000 if n_dp == 64 else 200_000))
+    off = int(r.integers(0, shard)) if r.random() < 0.5 else 0
+    length = int(r.integers(0, shard - off + 1)) if r.random() < 0.3 else shard - off
+    pad = int(r.choice([0, 0, 4, 7, 64]))
+    kind = [BF16, F16, F32][int(r.integers(0, 3))]
+    wdt = [zs.ZERO_BF16, zs.ZERO_FP16][int(r.integers(0, 2))]
+    leads = [int(r.choice([0, 0, 1, 2, 3])) for _ in range(5)]   # grads, master, m, v, sums
+    return dict(n_dp=n_dp, shard=shard, off=off, length=length, ld=length + pad, kind=kind,
+                wdt=wdt, leads=leads, rank=int(r.integers(0, n_dp)),
+                ovf=bool(r.random() < 0.5), ssq=bool(r.random() < 0.5))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_step(seed):
+    c = _case(1000 + seed)
+    print(f"\n[random step] {c}", flush=True)
+    n_dp, S, off, L, ld = c["n_dp"], c["shard"], c["off"], c["length"], c["ld"]
+    lay, _ = zs.zero_flatten_layout([S * n_dp], n_dp)
+    assert lay.shard == S
+    draw = GradDraw(c["kind"], 1e-3, outlier_p=0.01, outlier_mul=100.0)
+    lo = c["rank"] * S + off
+    w = host_master(200 + seed, lo, L)
+    m = np.zeros(L, np.float32)
+    v = np.zeros(L, np.float32)
+    wout = np.full(lay.n_pad, CANARY, np.uint16)
+    g_lead, w_lead, m_lead, v_lead, _ = c["leads"]
+    dw, dm, dv = _lead(w, w_lead), _lead(m, m_lead), _lead(v, v_lead)
+    dwf = torch.from_numpy(wout.view(np.int16).copy()).cuda().view(TDT[c["wdt"]])
+    for t in (1, 2):
+        rows = host_rows(200 + seed, t, 0, n_dp, lo, L, draw) if L > 0 else \
+            np.zeros((n_dp, 0), np.float32 if c["kind"] == F32 else np.uint16)
+        slab = np.zeros((n_dp, ld), rows.dtype)
+        slab[:, :L] = rows
+        g = _lead(slab, g_lead, torch.bfloat16 if c["kind"] == BF16 else torch.float16)
+        hp = zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **HP)
+        d_ovf = torch.zeros(1, dtype=torch.int32, device="cuda") if c["ovf"] else None
+        d_ss = torch.zeros(1, dtype=torch.float64, device="cuda") if c["ssq"] else None
+        zs.zero_shard_step(g, ld, L, dw, dm, dv, dwf, lay, c["rank"], hp, shard_off=off,
+                           overflow=d_ovf, sumsq=d_ss)
+        o_ovf, o_ss = np.zeros(1, np.uint32), np.zeros(1)
+        slot = wout[lo:lo + L].copy()
+        if L > 0:
+            oracle.step(np.ascontiguousarray(slab.reshape(-1)), ODT[c["kind"]], n_dp, ld, L, w, m,
+                        v, slot, c["wdt"], t, grad_scale=1.0 / n_dp, overflow=o_ovf, sumsq=o_ss,
+                        **HP)
+        wout[lo:lo + L] = slot
+        torch.cuda.synchronize()
+        diff = check_f32(_host(dw), w, "master") + check_f32(_host(dm), m, "m")
+        diff += check_f32(_host(dv), v, "v")
+        got = _host(dwf)
+        diff += check_16(got[lo:lo + L], wout[lo:lo + L], c["wdt"], "weights")
+        assert diff == 0
+        assert np.array_equal(got[:lo], wout[:lo]) and np.array_equal(got[lo + L:], wout[lo + L:])
+        if c["ovf"]:
+            assert int(d_ovf.item()) == int(o_ovf[0])
+        if c["ssq"]:
+            assert abs(d_ss.item() - o_ss[0]) <= 1e-10 * o_ss[0]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_reduce(seed):
+    c = _case(2000 + seed)
+    n_dp, L, ld = c["n_dp"], c["length"], c["ld"]
+    acc_mode = seed % 2 == 1
+    print(f"\n[random reduce] {c} accumulate={acc_mode}", flush=True)
+    draw = GradDraw(c["kind"], 1e-3)
+    rows = host_rows(220 + seed, 1, 0, n_dp, 0, L, draw) if L > 0 else \
+        np.zeros((n_dp, 0), np.float32 if c["kind"] == F32 else np.uint16)
+    slab = np.zeros((n_dp, ld), rows.dtype)
+    slab[:, :L] = rows
+    g = _lead(slab, c["leads"][0], torch.bfloat16 if c["kind"] == BF16 else torch.float16)
+    acc = host_master(240 + seed, 0, L, sigma=1e-3) if acc_mode else np.zeros(L, np.float32)
+    dacc = _lead(acc, c["leads"][1])
+    d_ovf = torch.zeros(1, dtype=torch.int32, device="cuda") if c["ovf"] else None
+    d_ss = torch.zeros(1, dtype=torch.float64, device="cuda") if c["ssq"] else None
+    zs.zero_shard_reduce(g, n_dp, ld, L, dacc, accumulate=acc_mode, overflow=d_ovf, sumsq=d_ss)
+    o_ovf, o_ss = np.zeros(1, np.uint32), np.zeros(1)
+    if L > 0:
+        oracle.reduce(np.ascontiguousarray(slab.reshape(-1)), ODT[c["kind"]], n_dp, ld, L, acc,
+                      acc_mode, overflow=o_ovf, sumsq=o_ss)
+    torch.cuda.synchronize()
+    assert check_f32(_host(dacc), acc, "acc") == 0
+    if c["ovf"]:
+        assert int(d_ovf.item()) == int(o_ovf[0])
+    if c["ssq"] and L > 0:
+        assert abs(d_ss.item() - o_ss[0]) <= 1e-10 * o_ss[0]
