@@ -14,6 +14,7 @@ import oracle
 import synth
 import zero_sharded_mixed_flatten_amd as zs
 from synth import BF16, F16, F32
+from synth.synth_const import BUF_GRAD
 from synth.workloads import GradDraw
 from tests.gpu_util import check_16, check_f32, host_master, host_rows
 
@@ -131,4 +132,66 @@ def test_random_reduce(seed):
     if c["ovf"]:
         assert int(d_ovf.item()) == int(o_ovf[0])
     if c["ssq"] and L > 0:
+        assert abs(d_ss.item() - o_ss[0]) <= 1e-10 * o_ss[0]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_q8_step(seed):
+    """The fused 8-bit step within its stated requirements (shard and shard
+    offset multiples of 256, code rows 4-byte aligned, state 16-byte
+    aligned), everything else random: row count, range length and partial
+    last block, row and scale strides, rank, flags; codes from the oracle's
+    quantizer."""
+    r = np.random.default_rng(3000 + seed)
+    B = zs.ZERO_Q8_BLOCK
+    n_dp = int(r.choice([1, 2, 3, 8, 13, 64]))
+    S = B * int(r.integers(1, 60 if n_dp == 64 else 600))
+    off = B * int(r.integers(0, S // B)) if r.random() < 0.5 else 0
+    L = int(r.integers(1, S - off + 1)) if r.random() < 0.5 else S - off
+    ld = (L + 3) // 4 * 4 + 4 * int(r.integers(0, 20))   # a multiple of 4 (required)
+    nb = zs.q8_blocks(L)
+    sld = nb + int(r.integers(0, 5))
+    rank = int(r.integers(0, n_dp))
+    ovf, ssq = bool(r.random() < 0.5), bool(r.random() < 0.5)
+    q_lead = 4 * int(r.integers(0, 3))
+    print(f"\n[random q8] n_dp={n_dp} S={S} off={off} L={L} ld={ld} sld={sld} rank={rank} "
+          f"ovf={ovf} ssq={ssq} lead={q_lead}", flush=True)
+    lay, _ = zs.zero_flatten_layout([S * n_dp], n_dp, B)
+    assert lay.shard == S
+    gq = np.zeros((n_dp, ld), np.int8)
+    gs = np.zeros((n_dp, sld), np.float32)
+    for k in range(n_dp):
+        x = synth.fill_host(F32, 0, synth.tag(BUF_GRAD, 250, seed, 0, k), 0, L, 1e-3)
+        q, s = oracle.q8_quantize(x, oracle.FP32)
+        gq[k, :L], gs[k, :nb] = q, s
+    lo = rank * S + off
+    w = host_master(250, lo, L)
+    m, v = np.zeros(L, np.float32), np.zeros(L, np.float32)
+    o_wq = np.full(lay.n_pad, 0x33, np.int8)
+    o_ws = np.full(lay.n_pad // B, -3.0, np.float32)
+    dgq = _lead(gq, q_lead)
+    dgs = torch.from_numpy(gs.reshape(-1).copy()).cuda()
+    dw, dm, dv = (torch.from_numpy(a.copy()).cuda() for a in (w, m, v))
+    dwq = torch.from_numpy(o_wq.copy()).cuda()
+    dws = torch.from_numpy(o_ws.copy()).cuda()
+    d_ovf = torch.zeros(1, dtype=torch.int32, device="cuda") if ovf else None
+    d_ss = torch.zeros(1, dtype=torch.float64, device="cuda") if ssq else None
+    hp = zs.AdamWHParams(step=1, grad_scale=1.0 / n_dp, **HP)
+    zs.zero_shard_step_q8(dgq, dgs, ld, sld, L, dw, dm, dv, dwq, dws, lay, rank, hp,
+                          shard_off=off, overflow=d_ovf, sumsq=d_ss)
+    o_ovf, o_ss = np.zeros(1, np.uint32), np.zeros(1)
+    s_wq = o_wq[lo:lo + L].copy()
+    s_ws = o_ws[lo // B:lo // B + nb].copy()
+    oracle.step_q8(gq.reshape(-1), gs.reshape(-1), n_dp, ld, sld, L, w, m, v, s_wq, s_ws, 1,
+                   grad_scale=1.0 / n_dp, overflow=o_ovf, sumsq=o_ss, **HP)
+    o_wq[lo:lo + L] = s_wq
+    o_ws[lo // B:lo // B + nb] = s_ws
+    torch.cuda.synchronize()
+    assert check_f32(_host(dw), w, "master") + check_f32(_host(dm), m, "m") + \
+        check_f32(_host(dv), v, "v") == 0
+    assert np.array_equal(dwq.cpu().numpy(), o_wq)
+    assert np.array_equal(dws.cpu().numpy().view(np.uint32), o_ws.view(np.uint32))
+    if ovf:
+        assert int(d_ovf.item()) == int(o_ovf[0])
+    if ssq:
         assert abs(d_ss.item() - o_ss[0]) <= 1e-10 * o_ss[0]
