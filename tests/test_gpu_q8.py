@@ -194,3 +194,36 @@ def test_q8_step_full_size_sampled_blocks():
     assert _same_f32(V[dpos].cpu().numpy(), v)
     assert np.array_equal(wq[dpos + rank * S].cpu().numpy(), o_wq)
     assert _same_f32(wsc[dblk + rank * nb].cpu().numpy(), o_ws)
+
+
+def test_quantizer_cases_that_tell_the_readings_apart():
+    """Blocks in which rint(x * r) and rint(x / s) differ (found by search,
+    as in the oracle's pin): the device quantizer follows the oracle's
+    reading on every one, for fp32 and bf16 inputs."""
+    rng = np.random.default_rng(11)
+    blocks = []
+    for _ in range(400):
+        amax = np.float32(rng.uniform(0.5, 2.0))
+        s = amax / np.float32(127.0)
+        k = rng.integers(-126, 127, size=4096).astype(np.float32)
+        x = ((k + np.float32(0.5)) * s).astype(np.float32)
+        x = x + rng.integers(-2, 3, size=x.size).astype(np.float32) * np.spacing(x)
+        x = np.clip(x, -amax, amax).astype(np.float32)
+        hit = np.nonzero(np.rint(x * (np.float32(127.0) / amax)) != np.rint(x / s))[0]
+        if hit.size:
+            blk = np.zeros(B, np.float32)
+            blk[0] = amax
+            blk[1:1 + min(hit.size, B - 1)] = x[hit[:B - 1]]
+            blocks.append(blk)
+        if len(blocks) >= 64:
+            break
+    assert len(blocks) >= 16
+    xs = np.concatenate(blocks)
+    for kind, arr in ((F32, xs), (BF16, oracle.f32_to_bf16(xs))):
+        d = _dev(arr, kind)
+        q = torch.empty(xs.size, dtype=torch.int8, device="cuda")
+        sc = torch.empty(zs.q8_blocks(xs.size), device="cuda")
+        zs.zero_q8_quantize(d, q, sc)
+        oq, os_ = oracle.q8_quantize(arr, ODT[kind])
+        assert np.array_equal(q.cpu().numpy(), oq)
+        assert _same_f32(sc.cpu().numpy(), os_)

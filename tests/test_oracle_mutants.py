@@ -97,6 +97,9 @@ MUTANTS = [
     ("q8_codes_divided_by_the_reciprocal", "float r = rintf(grad_at(x, xdt, j) * inv);",
      "float r = rintf(grad_at(x, xdt, j) / inv);", PINS_Q8),
     ("q8_reciprocal_of_128", "float inv = 127.0f / amax;", "float inv = 128.0f / amax;", PINS_Q8),
+    # the other plausible reading: codes by division with the stored scale
+    ("q8_codes_by_division", "float r = rintf(grad_at(x, xdt, j) * inv);",
+     "float r = rintf(grad_at(x, xdt, j) / s);", PINS_Q8),
     ("q8_infinite_reciprocal_kept", "isinf(s) || isinf(inv)) {", "isinf(s)) {", PINS_Q8),
     ("q8_dequant_block_off_by_one", "return (float)q[j] * scales[j / ORA_Q8_BLOCK];",
      "return (float)q[j] * scales[(j + 1) / ORA_Q8_BLOCK];", PINS_Q8),

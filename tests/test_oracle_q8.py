@@ -140,3 +140,69 @@ def test_quantized_step_is_dequantize_step_quantize(n_dp):
     q3, s3 = oracle.q8_quantize(w2, oracle.FP32)
     assert np.array_equal(wq, q3) and np.array_equal(ws.view(np.uint32), s3.view(np.uint32))
     assert ss[0] == ss2[0]
+
+
+def _rne_f32(v):
+    """The binary32 value nearest the rational v, ties to even (normal
+    range), computed exactly with fractions -- no detour through double."""
+    from fractions import Fraction
+    v = Fraction(v)
+    if v == 0:
+        return Fraction(0)
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    unit = Fraction(2) ** (e - 23)            # the ulp of [2^e, 2^(e+1))
+    m = a / unit                              # in [2^23, 2^24)
+    lo = m.numerator // m.denominator
+    rem = m - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * lo * unit
+
+
+def _rint_even(v):
+    from fractions import Fraction
+    lo = v.numerator // v.denominator
+    rem = v - lo
+    return lo + 1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1) else lo
+
+
+def test_codes_are_formed_with_the_blocks_reciprocal():
+    """Pins the stated reading q = rint(x * r), r = fl(127 / absmax), against
+    the other plausible one, rint(x / s), s = fl(absmax / 127): blocks whose
+    elements round differently under the two are found by search, and the
+    expected code of each is derived in exact rational arithmetic with
+    explicit round-to-nearest-even to binary32 at each operation."""
+    from fractions import Fraction
+    rng = np.random.default_rng(7)
+    found = []
+    for _ in range(200):
+        amax = np.float32(rng.uniform(0.5, 2.0))
+        s = amax / np.float32(127.0)
+        k = rng.integers(-126, 127, size=4096).astype(np.float32)
+        x = ((k + np.float32(0.5)) * s).astype(np.float32)            # near half-integer codes
+        x = x + rng.integers(-2, 3, size=x.size).astype(np.float32) * np.spacing(x)
+        x = np.clip(x, -amax, amax).astype(np.float32)
+        by_r = np.rint(x * (np.float32(127.0) / amax))
+        by_s = np.rint(x / s)
+        hit = np.nonzero(by_r != by_s)[0]
+        if hit.size:
+            found.append((amax, x[hit[0]]))
+        if len(found) >= 6:
+            break
+    assert len(found) >= 6
+    for amax, xv in found:
+        blk = np.array([amax, xv], np.float32)
+        q, sc = oracle.q8_quantize(blk, oracle.FP32)
+        r = _rne_f32(Fraction(127) / Fraction(float(amax)))
+        want = _rint_even(_rne_f32(Fraction(float(xv)) * r))
+        s_ex = _rne_f32(Fraction(float(amax)) / Fraction(127))
+        other = _rint_even(_rne_f32(Fraction(float(xv)) / s_ex))
+        assert want != other                      # the case tells the readings apart
+        assert int(q[1]) == want and int(q[0]) == 127
+        assert Fraction(float(sc[0])) == s_ex     # the stored scale is absmax / 127
