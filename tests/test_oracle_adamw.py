@@ -281,3 +281,53 @@ def test_scalars_follow_the_stated_rounding():
     assert c["d"] == np.float32(1 - 1e-5)
     c10 = oracle.adamw_scalars(10, **HP)
     assert ulp_diff(np.float32(c10["bc1"]), np.float32(1 - 0.9 ** 10))[()] == 0
+
+
+@pytest.mark.parametrize("t,grad_scale", [(1, 0.125), (7, 1.0 / 3.0)])
+def test_each_operation_is_one_binary32_rounding(t, grad_scale):
+    """The oracle's update is the stated sequence of binary32 operations,
+    each rounded once to nearest-even (no contraction, no reassociation, no
+    reciprocal in place of a division): every element re-derived here in
+    exact rational arithmetic with one rounding per operation equals the
+    oracle's bits.  The constants are formed in double from the double
+    hyperparameters and rounded once (b1 = fl(beta1), c1 = fl(1 - beta1),
+    bc1 = fl(1 - beta1^t), d = fl(1 - lr * wd), s = fl(grad_scale)).  The
+    square root is the correctly rounded double sqrt rounded to binary32:
+    double has more than 2 * 24 + 2 bits, so that second rounding gives the
+    correctly rounded binary32 root (Figueroa, "When is double rounding
+    innocuous?", 1995)."""
+    import math
+    from fractions import Fraction as Fr
+    from tests.util import rne_f32
+    n = 400
+    rng = np.random.default_rng(100 + t)
+    acc = (rng.standard_normal(n) * 8e-3).astype(np.float32)
+    w = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = ((rng.standard_normal(n) * 1e-3) ** 2).astype(np.float32) + np.float32(1e-12)
+    hp = dict(HP)
+    f32 = lambda x: Fr(float(np.float32(x)))          # one rounding from double
+    b1, c1 = f32(hp["beta1"]), f32(1.0 - hp["beta1"])
+    b2, c2 = f32(hp["beta2"]), f32(1.0 - hp["beta2"])
+    bc1, bc2 = f32(1.0 - math.pow(hp["beta1"], t)), f32(1.0 - math.pow(hp["beta2"], t))
+    lr, eps = f32(hp["lr"]), f32(hp["eps"])
+    d, s = f32(1.0 - hp["lr"] * hp["weight_decay"]), f32(grad_scale)
+    R = rne_f32
+    want_w, want_m, want_v = [], [], []
+    for j in range(n):
+        g = R(Fr(float(acc[j])) * s)
+        mt = R(R(b1 * Fr(float(m[j]))) + R(c1 * g))
+        vt = R(R(b2 * Fr(float(v[j]))) + R(c2 * R(g * g)))
+        mhat, vhat = R(mt / bc1), R(vt / bc2)
+        root = Fr(float(np.float32(math.sqrt(float(vhat)))))
+        den = R(root + eps)
+        u = R(mhat / den)
+        wt = R(R(Fr(float(w[j])) * d) - R(lr * u))
+        want_w.append(float(wt))
+        want_m.append(float(mt))
+        want_v.append(float(vt))
+    wout = np.zeros(n, np.uint16)
+    oracle.adamw(acc, w, m, v, wout, oracle.BF16, n, t, grad_scale=grad_scale, **hp)
+    assert np.array_equal(w.view(np.uint32), np.array(want_w, np.float32).view(np.uint32))
+    assert np.array_equal(m.view(np.uint32), np.array(want_m, np.float32).view(np.uint32))
+    assert np.array_equal(v.view(np.uint32), np.array(want_v, np.float32).view(np.uint32))

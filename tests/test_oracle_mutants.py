@@ -33,6 +33,12 @@ MUTANTS = [
     ("no_bias_correction_m", "float mhat = mt / bc1;", "float mhat = mt;", PINS_MATH),
     ("no_bias_correction_v", "float vhat = vt / bc2;", "float vhat = vt;", PINS_MATH),
     ("eps_inside_sqrt", "float den = sqrtf(vhat) + eps;", "float den = sqrtf(vhat + eps);", PINS_MATH),
+    # last-bit changes: a reciprocal in place of a division, a contracted multiply-add
+    ("bias_correction_by_reciprocal", "float mhat = mt / bc1;", "float mhat = mt * (1.0f / bc1);",
+     PINS_MATH),
+    ("update_by_reciprocal", "float u = mhat / den;", "float u = mhat * (1.0f / den);", PINS_MATH),
+    ("m_update_fused", "float mt = b1 * *m + c1 * g;", "float mt = fmaf(b1, *m, c1 * g);",
+     PINS_MATH),
     ("no_weight_decay", "float wt = *w * d - lr * u;", "float wt = *w - lr * u;", PINS_MATH),
     ("update_sign", "float wt = *w * d - lr * u;", "float wt = *w * d + lr * u;", PINS_MATH),
     ("betas_swapped", "out10[1] = (float)beta1;", "out10[1] = (float)beta2;", PINS_MATH),

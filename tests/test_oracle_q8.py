@@ -13,6 +13,7 @@ import pytest
 import oracle
 import synth
 from synth import F32, tag
+from tests.util import rint_even, rne_f32
 
 U = 2.0 ** -24
 B = oracle.Q8_BLOCK
@@ -142,36 +143,6 @@ def test_quantized_step_is_dequantize_step_quantize(n_dp):
     assert ss[0] == ss2[0]
 
 
-def _rne_f32(v):
-    """The binary32 value nearest the rational v, ties to even (normal
-    range), computed exactly with fractions -- no detour through double."""
-    from fractions import Fraction
-    v = Fraction(v)
-    if v == 0:
-        return Fraction(0)
-    sign = -1 if v < 0 else 1
-    a = abs(v)
-    e = a.numerator.bit_length() - a.denominator.bit_length()
-    if Fraction(2) ** e > a:
-        e -= 1
-    while Fraction(2) ** (e + 1) <= a:
-        e += 1
-    unit = Fraction(2) ** (e - 23)            # the ulp of [2^e, 2^(e+1))
-    m = a / unit                              # in [2^23, 2^24)
-    lo = m.numerator // m.denominator
-    rem = m - lo
-    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
-        lo += 1
-    return sign * lo * unit
-
-
-def _rint_even(v):
-    from fractions import Fraction
-    lo = v.numerator // v.denominator
-    rem = v - lo
-    return lo + 1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1) else lo
-
-
 def test_codes_are_formed_with_the_blocks_reciprocal():
     """Pins the stated reading q = rint(x * r), r = fl(127 / absmax), against
     the other plausible one, rint(x / s), s = fl(absmax / 127): blocks whose
@@ -199,10 +170,10 @@ def test_codes_are_formed_with_the_blocks_reciprocal():
     for amax, xv in found:
         blk = np.array([amax, xv], np.float32)
         q, sc = oracle.q8_quantize(blk, oracle.FP32)
-        r = _rne_f32(Fraction(127) / Fraction(float(amax)))
-        want = _rint_even(_rne_f32(Fraction(float(xv)) * r))
-        s_ex = _rne_f32(Fraction(float(amax)) / Fraction(127))
-        other = _rint_even(_rne_f32(Fraction(float(xv)) / s_ex))
+        r = rne_f32(Fraction(127) / Fraction(float(amax)))
+        want = rint_even(rne_f32(Fraction(float(xv)) * r))
+        s_ex = rne_f32(Fraction(float(amax)) / Fraction(127))
+        other = rint_even(rne_f32(Fraction(float(xv)) / s_ex))
         assert want != other                      # the case tells the readings apart
         assert int(q[1]) == want and int(q[0]) == 127
         assert Fraction(float(sc[0])) == s_ex     # the stored scale is absmax / 127

@@ -40,3 +40,36 @@ def rel_err(gpu, ref):
     g = np.asarray(gpu, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     return np.abs(g - r) / np.maximum(np.abs(r), 2.0 ** -126)
+
+
+def rne_f32(v):
+    """The binary32 value nearest the rational v (a Fraction or anything it
+    converts), ties to even, normal range -- computed exactly, with no
+    detour through double."""
+    from fractions import Fraction
+    v = Fraction(v)
+    if v == 0:
+        return Fraction(0)
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    unit = Fraction(2) ** (e - 23)            # the ulp of [2^e, 2^(e+1))
+    m = a / unit                              # in [2^23, 2^24)
+    lo = m.numerator // m.denominator
+    rem = m - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * lo * unit
+
+
+def rint_even(v):
+    """The integer nearest the rational v, ties to even."""
+    from fractions import Fraction
+    v = Fraction(v)
+    lo = v.numerator // v.denominator
+    rem = v - lo
+    return lo + 1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1) else lo
