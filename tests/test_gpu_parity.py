@@ -303,3 +303,51 @@ def test_sum_of_squares_is_reproducible(n_dp, length, lead):
                   sumsq=o_rs)
     assert abs(sums[0][0] - o_ss[0]) <= 1e-10 * o_ss[0]
     assert abs(sums[0][1] - o_rs[0]) <= 1e-10 * o_rs[0]
+
+
+@pytest.mark.parametrize("wdt", [zs.ZERO_BF16, zs.ZERO_FP16])
+def test_subnormal_operands_are_kept(wdt):
+    """No flush to zero on either side: bf16 gradient rows half of them
+    subnormal, and master, m, v mixing subnormal and small normal binary32
+    values; an inexact gradient scale (1/3) makes products land in the
+    subnormal range too.  Fused step (vector path and tail) and reduce,
+    bitwise against the oracle."""
+    rng = np.random.default_rng(77)
+    n_dp, n = 3, 100_003
+    lay, _ = zs.zero_flatten_layout([n * n_dp], n_dp)
+
+    def bf16_mix(size):
+        h = rng.integers(0, 1 << 7, size=size).astype(np.uint16)         # subnormal bf16
+        normal = rng.random(size) < 0.5
+        h[normal] = (rng.integers(1, 20, size=int(normal.sum())) << 7 |
+                     rng.integers(0, 1 << 7, size=int(normal.sum()))).astype(np.uint16)
+        return h | (rng.integers(0, 2, size=size).astype(np.uint16) << 15)
+
+    def f32_mix(size, positive=False):
+        mant = rng.integers(1, 1 << 23, size=size).astype(np.uint32)
+        exp = np.where(rng.random(size) < 0.5, 0, rng.integers(1, 12, size=size)).astype(np.uint32)
+        sign = np.zeros(size, np.uint32) if positive else \
+            rng.integers(0, 2, size=size).astype(np.uint32) << 31
+        return (sign | exp << 23 | mant).view(np.float32)
+
+    rows = np.stack([bf16_mix(n) for _ in range(n_dp)])
+    w, m, v = f32_mix(n), f32_mix(n), f32_mix(n, positive=True)
+    assert np.count_nonzero((w.view(np.uint32) & 0x7F800000) == 0) > n // 4
+    dw, dm, dv = devf(w), devf(m), devf(v)
+    dwf = dev16(np.zeros(lay.n_pad, np.uint16), wdt)
+    g = dev16(rows, zs.ZERO_BF16)
+    hp = zs.AdamWHParams(step=2, grad_scale=1.0 / 3.0, **HP)
+    zs.zero_shard_step(g, n, n, dw, dm, dv, dwf, lay, 0, hp)
+    slot = np.zeros(n, np.uint16)
+    oracle.step(rows, oracle.BF16, n_dp, n, n, w, m, v, slot, wdt, 2, grad_scale=1.0 / 3.0, **HP)
+    torch.cuda.synchronize()
+    diff = check_f32(hostf(dw), w, "master") + check_f32(hostf(dm), m, "m")
+    diff += check_f32(hostf(dv), v, "v") + check_16(host16(dwf)[:n], slot, wdt, "weights")
+    assert diff == 0
+    acc = torch.empty(n, device="cuda")
+    zs.zero_shard_reduce(g, n_dp, n, n, acc)
+    o_acc = np.zeros(n, np.float32)
+    oracle.reduce(rows, oracle.BF16, n_dp, n, n, o_acc, False)
+    torch.cuda.synchronize()
+    assert check_f32(hostf(acc), o_acc, "acc") == 0
+    assert np.count_nonzero((o_acc.view(np.uint32) & 0x7F800000) == 0) > n // 20
