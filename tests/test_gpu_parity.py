@@ -204,14 +204,22 @@ def test_overflow_skips_the_step(where, mb, bits):
     assert _accum_case(8, length, 4, inject=(mb, 5, idx, bits), cfg=101) == 1
 
 
-def test_overflow_flag_of_fused_step_and_update_applied():
+@pytest.mark.parametrize("plant,idx", [
+    ({2: 0x7F80}, 1234),                 # +Inf
+    ({0: 0xFF80}, 4095),                 # -Inf at the last element (the tail of the launch)
+    ({3: 0x7FC1}, 7),                    # a NaN
+    ({1: 0x7F80, 2: 0xFF80}, 2048),      # +Inf + -Inf: NaN from finite-looking rows
+])
+def test_overflow_flag_of_fused_step_and_update_applied(plant, idx):
     """The fused step reports a non-finite reduced gradient (and, being one
-    pass, still applies the update, like the oracle)."""
+    pass, still applies the update, like the oracle): Inf and NaN propagate
+    through m, v, the master and the cast exactly as in the oracle."""
     draw = GradDraw(BF16, 1e-3)
-    n_dp, s = 4, 4096
-    lay, _ = zs.zero_flatten_layout([n_dp * s], n_dp, 8)
+    n_dp, s = 4, 4096 + 3                # a 3-element tail after the quads
+    lay, _ = zs.zero_flatten_layout([n_dp * s], n_dp)
     rows = host_rows(102, 1, 0, n_dp, s, s, draw)
-    rows[2, 1234] = 0x7F80  # +Inf
+    for k, bits in plant.items():
+        rows[k, idx] = bits
     w = host_master(102, s, s)
     m = np.zeros(s, np.float32)
     v = np.zeros(s, np.float32)
@@ -226,6 +234,8 @@ def test_overflow_flag_of_fused_step_and_update_applied():
     torch.cuda.synchronize()
     assert int(d_ovf.item()) == 1 == int(o_ovf[0])
     assert check_f32(hostf(dw), w, "master") + check_16(host16(dwf)[s:2 * s], slot, 0, "w") == 0
+    assert check_f32(hostf(dm), m, "m") + check_f32(hostf(dv), v, "v") == 0
+    assert not np.isfinite(w[idx]) and np.all(np.isfinite(np.delete(w, idx)))
 
 
 # ---------------------------------------------------------------------------
