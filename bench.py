@@ -526,7 +526,7 @@ def bench_codec(args):
             reps += 1
         dt = time.perf_counter() - t1
         line["cpu_baseline"] = {"value": reps * n / dt, "unit": "elements/s", "cores": 1,
-                                "kind": "oracle",
+                                "kind": "oracle", "host": host_description(),
                                 "sample": f"the first {n} elements of the shard, {reps} calls, "
                                           f"single-threaded C oracle ({dt:.1f} s)"}
     print(json.dumps(line), flush=True)
@@ -565,6 +565,7 @@ def cpu_baseline_copy(op, s8, n):
         what = f"the first {per_call} elements of shard 0 into the parameter tensors they cover"
     dt = time.perf_counter() - t0
     return {"value": reps * per_call / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "host": host_description(),
             "sample": f"{what} ({per_call} elements per call, {reps} calls, single-threaded C "
                       f"oracle, {dt:.1f} s)"}
 
@@ -600,6 +601,7 @@ def cpu_baseline(wl, S, rank, log2n, steps):
                            grad_scale=1.0 / wl.n_dp, **wl.hp)
         dt = time.perf_counter() - t0
         return {"value": n * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+                "host": host_description(),
                 "sample": f"first {n} parameters of rank {rank}'s shard, {wl.n_dp} 8-bit rows, "
                           f"{steps} optimizer steps, single-threaded C oracle ({dt:.1f} s)"}
     scale = np.array([wl.loss_scale], np.float32)
@@ -627,8 +629,23 @@ def cpu_baseline(wl, S, rank, log2n, steps):
                              skip=flag, **wl.hp)
     dt = time.perf_counter() - t0
     return {"value": n * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "host": host_description(),
             "sample": f"first {n} parameters of rank {rank}'s shard, {wl.n_dp} gradient rows, "
                       f"{steps} optimizer steps, single-threaded C oracle ({dt:.1f} s)"}
+
+
+def host_description():
+    """The host the CPU baseline ran on: CPU model and logical CPU count."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs"
 
 
 def host_threads():
@@ -682,6 +699,7 @@ def cpu_baseline_all_cores(wl, S, rank, log2n, steps):
         list(pool.map(run, range(threads)))
         dt = time.perf_counter() - t0
     return {"value": n * steps / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "host": host_description(),
             "sample": f"first {n} parameters of rank {rank}'s shard, {wl.n_dp} gradient rows, "
                       f"{steps} optimizer steps, the single-threaded C oracle on {threads} "
                       f"contiguous ranges in {threads} threads ({dt:.1f} s)"}
