@@ -1,0 +1,60 @@
+"""bench.py's host-side contract, on the CPU: one GPU only (more exits with
+a message and a non-zero status before touching a device), the CPU
+baselines' host description and thread count, and the all-core oracle
+baseline equal, element for element, to one whole-range oracle call."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from synth import BF16, F32  # noqa: E402
+from synth.synth_const import BUF_GRAD, BUF_MASTER  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_host_description_and_threads():
+    d = bench.host_description()
+    assert d.endswith(f"{os.cpu_count()} logical CPUs")
+    assert 1 <= bench.host_threads() <= 16
+
+
+def test_ranges_in_threads_equal_one_call():
+    """The all-core baseline cuts the sample into contiguous ranges, one
+    per thread; the oracle step is element-wise, so the ranges stepped in
+    threads must equal one whole-range call bit for bit."""
+    from concurrent.futures import ThreadPoolExecutor
+    n, n_dp, T = 50_003, 8, 5
+    hp = dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)
+    rows = np.stack([synth.fill_host(BF16, 0, synth.tag(BUF_GRAD, 2, 1, 0, k), 0, n, 1e-3)
+                     for k in range(n_dp)])
+    flat = rows.reshape(-1)
+    w0 = synth.fill_host(F32, 0, synth.tag(BUF_MASTER, 2), 0, n, 0.02)
+    state = [w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)]
+    ref = [w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)]
+    cuts = [n * i // T for i in range(T + 1)]
+
+    def run(i):
+        a, b = cuts[i], cuts[i + 1]
+        for t in (1, 2, 3):
+            oracle.step(flat[a:], oracle.BF16, n_dp, n, b - a, state[0][a:b], state[1][a:b],
+                        state[2][a:b], state[3][a:b], oracle.BF16, t, grad_scale=1.0 / n_dp, **hp)
+
+    with ThreadPoolExecutor(max_workers=T) as pool:
+        list(pool.map(run, range(T)))
+    for t in (1, 2, 3):
+        oracle.step(rows, oracle.BF16, n_dp, n, n, *ref, oracle.BF16, t, grad_scale=1.0 / n_dp, **hp)
+    for got, want in zip(state, ref):
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
