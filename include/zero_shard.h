@@ -424,7 +424,9 @@ ZERO_API zero_status zero_q8_quantize(const void *x, zero_dtype xdt, int64_t len
                                       float *scales, void *stream);
 
 /* y[j] = q[j] * scales[j / ZERO_Q8_BLOCK] in fp32, stored as ydt (BF16 and
- * FP16 rounded to nearest even).  Errors as for zero_q8_quantize. */
+ * FP16 rounded to nearest even).  Any alignment (16-byte y with 4-byte
+ * codes for FP32, 16-byte y with 8-byte codes for 16-bit values take the
+ * vector path).  Errors as for zero_q8_quantize. */
 ZERO_API zero_status zero_q8_dequantize(const int8_t *q, const float *scales, int64_t len,
                                         void *y, zero_dtype ydt, void *stream);
 
