@@ -285,8 +285,9 @@ def main():
         launch_bytes = 30 * S
     achieved = launch_bytes / (k_avg * 1e-3) / 1e9
     # the committed counter summaries cover the variant without the flags
+    # (for the stage-2 workloads: the timed AdamW launch)
     traffic = (committed_traffic(wl.name, Q8_SOURCE if q8 else KERNEL_SOURCE)
-               if micro == 1 and not args.flags else None)
+               if not args.flags else None)
 
     line = {
         "metric": "sharded AdamW step params/s and HBM GB/s (% of 8 TB/s), 7B n_dp=8 shard",
