@@ -38,7 +38,9 @@
  *    processes at most 2^38 elements (EINVAL beyond).
  *  - Element j of the processed range is independent of every other element:
  *    any range can be processed by one call or split over several calls
- *    (buckets) with identical results.
+ *    (buckets) with identical results -- except the optional sum of squares,
+ *    a reduction over the range, whose last bits depend on the split (for a
+ *    given split they are the same on every run).
  *  - Arithmetic is IEEE binary32 with round-to-nearest-even, no fused
  *    multiply-add, correctly rounded division and square root, and no
  *    flushing of denormals; the scalars are formed on the host in double
