@@ -52,6 +52,9 @@ def parse():
                    help="CPU baseline sample: 2^k parameters of the shard")
     p.add_argument("--cpu-steps", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--bucket-elems", type=int, default=0, metavar="B",
+                   help="single-launch 16-bit steps: issue the shard as consecutive buckets of B "
+                        "elements, one library call each (0: one call for the whole shard)")
     p.add_argument("--flags", action="store_true",
                    help="single-launch steps: also raise the overflow flag and sum the squares "
                         "of the scaled gradient (the shard's part of the global norm)")
@@ -208,6 +211,11 @@ def main():
             if q8:
                 zs.zero_shard_step_q8(slab, slab_s, S, nb, S, master, m, v, wfull, wfull_s, lay,
                                       rank, hp, stream=stream, **fl)
+            elif args.bucket_elems > 0:
+                for b0 in range(0, S, args.bucket_elems):
+                    b1 = min(S, b0 + args.bucket_elems)
+                    zs.zero_shard_step(slab[:, b0:], S, b1 - b0, master[b0:], m[b0:], v[b0:],
+                                       wfull, lay, rank, hp, shard_off=b0, stream=stream, **fl)
             else:
                 zs.zero_shard_step(slab, S, S, master, m, v, wfull, lay, rank, hp, stream=stream,
                                    **fl)
@@ -313,7 +321,11 @@ def main():
                    "micro_batches": micro, "bytes_per_param": bytes_per_param,
                    "controls": "clip 1.0 + dynamic loss scale" if wl.controls else None,
                    "flags": "overflow + sum of squares" if args.flags and micro == 1 else None,
-                   "launches_per_step": 1 if micro == 1 else micro + 1 + int(wl.controls)},
+                   "bucket_elems": args.bucket_elems if args.bucket_elems > 0 and micro == 1
+                   and not q8 else None,
+                   "launches_per_step": (-(-S // args.bucket_elems) if args.bucket_elems > 0
+                                         and not q8 else 1) if micro == 1
+                   else micro + 1 + int(wl.controls)},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "launch_ms_avg": k_avg, "launch_ms_min": min(kms),
