@@ -35,7 +35,9 @@
  *  - Arguments are validated on the host before anything is launched; on any
  *    error status nothing is launched and nothing is written.
  *  - Element counts and offsets are in elements, never bytes; one call
- *    processes at most 2^38 elements (EINVAL beyond).
+ *    processes at most 2^38 elements (EINVAL beyond), and a buffer or set of
+ *    rows it addresses spans at most 2^60 elements (EINVAL beyond: a layout's
+ *    N_pad, or (rows - 1) * ld + len for rows ld elements apart).
  *  - Element j of the processed range is independent of every other element:
  *    any range can be processed by one call or split over several calls
  *    (buckets) with identical results -- except the optional sum of squares,

@@ -160,6 +160,9 @@ def _step(grads=BASE, ld=1024, length=1024, master=BASE + (1 << 30), m=BASE + (2
     (dict(shard_off=1, length=1024), zs.ZERO_ERANGE),
     (dict(shard_off=-1), zs.ZERO_EINVAL),
     (dict(length=1025, ld=1025), zs.ZERO_ERANGE),
+    # rows spanning more than 2^60 elements: byte offsets would leave int64
+    (dict(ld=1 << 61), zs.ZERO_EINVAL),
+    (dict(ld=(1 << 60) // 3), zs.ZERO_EINVAL),
     (dict(m=BASE + (1 << 30) + 4092), zs.ZERO_EALIAS),       # m overlaps master's tail
     (dict(v=BASE + 2046), zs.ZERO_EALIAS),                    # v inside row 0
     (dict(master=BASE + 3 * 1024 * 2), zs.ZERO_EALIAS),       # master on the last row
@@ -183,6 +186,9 @@ def test_step_bad_layout_and_empty_range():
     lay = zs.zero_flatten_layout([4096], 4)[0]
     bad = zs.ZeroLayout(lay.n, lay.n_pad + 1, lay.shard, lay.align, lay.n_dp, 0)
     assert _step(lay=bad) == zs.ZERO_EINVAL
+    # a consistent layout whose buffer spans more than 2^60 elements
+    huge = zs.ZeroLayout(1 << 61, 1 << 61, 1 << 58, 1, 8, 0)
+    assert _step(lay=huge) == zs.ZERO_EINVAL
     # an empty range is a no-op that needs no buffers at all
     assert _step(length=0, grads=0, master=0, m=0, v=0, wfull=0) == zs.ZERO_OK
 
@@ -198,6 +204,8 @@ def test_reduce_and_adamw_reject_bad_arguments():
              None) == zs.ZERO_EINVAL
     assert R(P(BASE), 0, 2, 16, 16, P(BASE + 40), 0, None, None, None, 0,
              None) == zs.ZERO_EALIAS
+    assert R(P(BASE), 0, 2, 1 << 62, 16, P(BASE + 4096), 0, None, None, None, 0,
+             None) == zs.ZERO_EINVAL                                      # rows past 2^60
     assert R(P(BASE), 0, 2, 16, 16, P(BASE + 4096), 0, P(BASE + 4096 + 60), None,
              None, 0, None) == zs.ZERO_EALIAS
     assert R(None, 0, 2, 16, 0, None, 0, None, None, None, 0, None) == zs.ZERO_OK
@@ -383,6 +391,8 @@ def test_q8_entry_points_reject_bad_arguments():
     assert step(sld=15) == zs.ZERO_EINVAL                           # scale rows too short
     assert step(ld=4098) == zs.ZERO_EINVAL                          # row stride not % 4
     assert step(gq=BASE + 2) == zs.ZERO_EINVAL                      # codes misaligned
+    assert step(ld=1 << 60) == zs.ZERO_EINVAL                       # code rows past 2^60
+    assert step(sld=1 << 59) == zs.ZERO_EINVAL                      # scale rows past 2^60
     assert step(w=BASE + (2 << 28) + 4) == zs.ZERO_EINVAL           # master misaligned
     assert step(length=4096, off=256) == zs.ZERO_ERANGE
     odd = zs.zero_flatten_layout([8 * 4000], 8)[0]                  # shard 4000: not % 256

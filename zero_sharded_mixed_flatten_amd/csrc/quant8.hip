@@ -682,9 +682,7 @@ extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales
     if (layout->shard % kB != 0 || shard_off % kB != 0) return ZERO_EINVAL;
     const int64_t nb = blocks_of(len);
     if (n_dp > 1 && (ld % kQuad != 0 || sld < nb)) return ZERO_EINVAL;
-    if (n_dp > 1 && (static_cast<int64_t>(n_dp - 1) > (INT64_MAX - len) / (ld > 0 ? ld : 1) ||
-                     sld > INT64_MAX / n_dp))
-        return ZERO_EINVAL;
+    if (n_dp > 1 && (!rows_ok(n_dp, ld, len) || !rows_ok(n_dp, sld, nb))) return ZERO_EINVAL;
     if (shard_off > layout->shard || len > layout->shard - shard_off) return ZERO_ERANGE;
     if (len == 0) return ZERO_OK;
     if (!gq || !gscales || !master || !m || !v || !wq_full || !wscales_full) return ZERO_EINVAL;

@@ -29,6 +29,17 @@ constexpr int kQuad = 4;  // elements per lane
 // Ranges beyond kMaxLen elements (2^38, far beyond any HBM) are rejected.
 constexpr int64_t kMaxLen = int64_t(1) << 38;
 
+// A buffer or row slab may span at most kMaxSpan elements (2^60), so that the
+// byte offset of any element of up to 8 bytes fits in int64.
+constexpr int64_t kMaxSpan = INT64_MAX / 8;
+
+// n_rows rows of len elements, ld elements apart (n_rows >= 1, 0 <= len <=
+// ld), spanning (n_rows - 1) * ld + len <= kMaxSpan elements
+inline bool rows_ok(int64_t n_rows, int64_t ld, int64_t len) {
+    if (n_rows < 1 || len < 0 || ld < len || len > kMaxSpan) return false;
+    return ld == 0 || n_rows - 1 <= (kMaxSpan - len) / ld;
+}
+
 // A dispatch counts its grid in work-items in 32 bits, so one launch of a
 // one-shot kernel (a thread per quad or per block lane) covers at most
 // kLaunchElems elements and longer ranges go out as consecutive launches.
@@ -51,7 +62,7 @@ inline bool layout_ok(const zero_layout *l) {
     if (!l || l->n_dp < 1 || l->align < 1 || l->shard < 0 || l->n < 0) return false;
     if (l->shard % l->align != 0) return false;
     if (l->shard > 0 && l->n_dp > INT64_MAX / l->shard) return false;
-    return l->n_pad == l->shard * l->n_dp && l->n <= l->n_pad;
+    return l->n_pad == l->shard * l->n_dp && l->n <= l->n_pad && l->n_pad <= kMaxSpan;
 }
 
 inline bool hparams_ok(const zero_adamw_hparams *hp) {

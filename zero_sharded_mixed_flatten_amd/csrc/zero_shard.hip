@@ -476,13 +476,6 @@ void for_launches(int64_t nquad, F &&f) {
     for (int64_t q0 = 0; q0 < nquad; q0 += per) f(q0, nquad - q0 < per ? nquad - q0 : per);
 }
 
-// rows of the gradient slab all fit in int64 and do not wrap
-bool rows_ok(int n_rows, int64_t ld, int64_t len) {
-    if (n_rows < 1 || len < 0 || ld < len) return false;
-    if (ld > 0 && static_cast<int64_t>(n_rows - 1) > (INT64_MAX - len) / ld) return false;
-    return true;
-}
-
 // the workspace of a call that sums squares: given, 8-byte aligned, large enough
 bool workspace_ok(const void *ws, int64_t bytes, int64_t len) {
     return ws && aligned8(ws) && bytes >= zero_sumsq_workspace_bytes(len);
