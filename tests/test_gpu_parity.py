@@ -86,13 +86,14 @@ def _run_case(numels, n_dp, rank, steps, draw, cfg, wdt=zs.ZERO_BF16, align=1, l
 
 def test_tiny_workload_all_steps():
     """The tiny workload: 10,000 parameters, 4 ranks, shard 2,500, rank 1,
-    steps 1-3 (its slot at byte 5,000 is not 16-byte aligned: element path)."""
+    steps 1-3 (its slot at byte 5,000 is 8-byte aligned: the vector path)."""
     wl = workload(0)
     _run_case(wl.numels, wl.n_dp, wl.rank, wl.steps, wl.grad, cfg=0)
 
 
 @pytest.mark.parametrize("rank", [0, 2, 3])
 def test_tiny_workload_other_ranks(rank):
+    """Rank 3's slot starts at byte 7,500, not 8-byte aligned: the element path."""
     wl = workload(0)
     _run_case(wl.numels, wl.n_dp, rank, (1, 2), wl.grad, cfg=0)
 
