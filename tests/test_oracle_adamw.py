@@ -232,6 +232,30 @@ def test_fused_equals_reduce_then_adamw():
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
+@pytest.mark.parametrize("n", [1, 3, 8])
+def test_step_sum_of_squares_and_flag(n):
+    """The fused step's shard-wide reductions: the sum of squares is that of
+    the averaged gradient g = fl(a * s), a the left-to-right fp32 sum of the
+    rows (computed here with numpy), checked in float64; the overflow flag is
+    raised by a non-finite row element and only then."""
+    length = 3000
+    rows = _grads(n, length, 1, 58, BF16, thr=10486, mul=100.0)
+    x = oracle.bf16_to_f32(rows)
+    a = x[0].copy()
+    for k in range(1, n):
+        a = (a + x[k]).astype(np.float32)
+    g = (a * np.float32(1.0 / n)).astype(np.float32)
+    ss, flag = np.zeros(1), np.zeros(1, np.uint32)
+    oracle.step(rows, oracle.BF16, n, length, length, *_state(length, 58), oracle.BF16, 1,
+                grad_scale=1.0 / n, overflow=flag, sumsq=ss, **HP)
+    ref = np.sum(g.astype(np.float64) ** 2)
+    assert flag[0] == 0 and abs(ss[0] - ref) <= 1e-12 * ref
+    rows[n - 1, 1234] = 0xFF80  # -inf in the last row
+    oracle.step(rows, oracle.BF16, n, length, length, *_state(length, 58), oracle.BF16, 1,
+                grad_scale=1.0 / n, overflow=flag, **HP)
+    assert flag[0] == 1
+
+
 def test_skip_flag_leaves_state_untouched():
     length = 1000
     acc = np.ones(length, np.float32)

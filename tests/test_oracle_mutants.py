@@ -116,6 +116,35 @@ MUTANTS = [
      "else\n            memset(d, 1, (size_t)elem_bytes);", PINS_RESHARD),
     ("reshard_half_elements", "(const unsigned char *)src[r] + o * elem_bytes;",
      "(const unsigned char *)src[r] + o * 2;", PINS_RESHARD),
+    ("v_decay_uses_beta1", "float vt = b2 * *v + c2 * (g * g);", "float vt = b1 * *v + c2 * (g * g);",
+     PINS_MATH),
+    ("decay_after_update", "float wt = *w * d - lr * u;", "float wt = (*w - lr * u) * d;", PINS_MATH),
+    ("cast_from_old_master",
+     "        adamw_element(g, &w[j], &m[j], &v[j], c);\n        wout[j] = narrow(w[j], wdt);\n    }\n"
+     "    if (overflow",
+     "        wout[j] = narrow(w[j], wdt);\n        adamw_element(g, &w[j], &m[j], &v[j], c);\n    }\n"
+     "    if (overflow", PINS_MATH),
+    ("skip_ignored", "    if (skip && *skip) return;\n    float c[10];\n    ora_adamw_scalars(hp6, step, c);\n    for",
+     "    float c[10];\n    ora_adamw_scalars(hp6, step, c);\n    for", PINS_MATH),
+    ("sum_started_from_plus_zero",
+     "        float x = grad_at(grads, gdt, (int64_t)k * ld + j);\n        a = (k == 0) ? x : a + x;",
+     "        float x = grad_at(grads, gdt, (int64_t)k * ld + j);\n        a = a + x;", PINS_MATH),
+    ("reduce_sumsq_of_the_partial", "        acc[j] = r;\n        ss += (double)r * (double)r;",
+     "        acc[j] = r;\n        ss += (double)a * (double)a;", PINS_MATH),
+    ("step_sumsq_before_the_average",
+     "        ss += (double)g * (double)g;\n        adamw_element(g, &w[j], &m[j], &v[j], c);\n        wout[j]",
+     "        ss += (double)a * (double)a;\n        adamw_element(g, &w[j], &m[j], &v[j], c);\n        wout[j]",
+     PINS_MATH),
+    ("step_overflow_never_set",
+     "        if (nonfinite(a)) bad = 1;\n        float g = a * c[0];\n        ss += (double)g * (double)g;\n"
+     "        adamw_element(g, &w[j], &m[j], &v[j], c);\n        wout",
+     "        float g = a * c[0];\n        ss += (double)g * (double)g;\n"
+     "        adamw_element(g, &w[j], &m[j], &v[j], c);\n        wout", PINS_MATH),
+    ("scale_interval_off_by_one", "if (*good_steps >= interval) {", "if (*good_steps > interval) {",
+     PINS_CONTROL),
+    ("clip_norm_not_unscaled",
+     "    if (sumsq && max_norm > 0.0) clip = ora_clip_coef(*sumsq, c[0], max_norm);",
+     "    if (sumsq && max_norm > 0.0) clip = ora_clip_coef(*sumsq, 1.0f, max_norm);", PINS_CONTROL),
 ]
 
 

@@ -123,6 +123,28 @@ def test_overflow_flag_on_nonfinite_input(pos, bad):
     assert flag[0] == 1
 
 
+def test_sum_of_negative_zero_rows_keeps_the_sign():
+    """The sum starts from row 0 itself (not from +0), so rows of -0 add up
+    to -0 under round-to-nearest, and a single row comes back unchanged."""
+    rows = np.full((3, 16), 0x8000, np.uint16)  # bf16 -0
+    acc = np.zeros(16, np.float32)
+    oracle.reduce(rows, oracle.BF16, 3, 16, 16, acc, 0)
+    assert np.all(acc.view(np.uint32) == 0x80000000)
+
+
+def test_sumsq_is_that_of_the_accumulated_gradient():
+    """With accumulation, the sum of squares is over the accumulator after
+    the call (the gradient the update will use), not over the call's own
+    partial sum."""
+    n, length = 4, 3000
+    acc = np.zeros(length, dtype=np.float32)
+    oracle.reduce(_rows(n, length, cfg=99), oracle.BF16, n, length, length, acc, 0)
+    ss = np.zeros(1, dtype=np.float64)
+    oracle.reduce(_rows(n, length, cfg=100), oracle.BF16, n, length, length, acc, 1, sumsq=ss)
+    ref = np.sum(acc.astype(np.float64) ** 2)
+    assert abs(ss[0] - ref) <= 1e-12 * ref
+
+
 def test_sumsq_matches_float64():
     rows = _rows(8, 4096, cfg=98)
     acc = np.zeros(4096, dtype=np.float32)
