@@ -142,6 +142,17 @@ MUTANTS = [
      "        adamw_element(g, &w[j], &m[j], &v[j], c);\n        wout", PINS_MATH),
     ("scale_interval_off_by_one", "if (*good_steps >= interval) {", "if (*good_steps > interval) {",
      PINS_CONTROL),
+    ("q8_scale_rows_at_the_code_stride",
+     "float x = dequant(gq + (int64_t)k * ld, gs + (int64_t)k * sld, j);",
+     "float x = dequant(gq + (int64_t)k * ld, gs + (int64_t)k * (ld / ORA_Q8_BLOCK), j);", PINS_Q8),
+    ("q8_absmax_signed", "float a = fabsf(grad_at(x, xdt, j));", "float a = grad_at(x, xdt, j);", PINS_Q8),
+    ("gather_begin_ignored", "int32_t k = ora_flat_locate(flat_off, len, n_src, n, begin + j, &off);",
+     "int32_t k = ora_flat_locate(flat_off, len, n_src, n, j, &off);", PINS_RESHARD),
+    ("reshard_divides_by_the_new_shard", "int64_t r = flat / src_shard, o = flat % src_shard;",
+     "int64_t r = flat / dst_shard, o = flat % dst_shard;", PINS_RESHARD),
+    ("layout_offsets_shifted", "        if (offsets) offsets[i] = n;\n        n += numels[i];",
+     "        n += numels[i];\n        if (offsets) offsets[i] = n;", PINS_LAYOUT),
+    ("dim0_chunk_not_clamped", "        if (have > c) have = c;\n", "", PINS_DIM0),
     ("clip_norm_not_unscaled",
      "    if (sumsq && max_norm > 0.0) clip = ora_clip_coef(*sumsq, c[0], max_norm);",
      "    if (sumsq && max_norm > 0.0) clip = ora_clip_coef(*sumsq, 1.0f, max_norm);", PINS_CONTROL),

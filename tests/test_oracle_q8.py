@@ -114,15 +114,21 @@ def test_dequantize_16bit_is_the_rounded_fp32_value():
 
 
 @pytest.mark.parametrize("n_dp", [1, 3, 8])
-def test_quantized_step_is_dequantize_step_quantize(n_dp):
+@pytest.mark.parametrize("scale_pad", [0, 3])
+def test_quantized_step_is_dequantize_step_quantize(n_dp, scale_pad):
     """ora_step_q8 = dequantize each row to fp32, the fp32-row step (pinned
-    elsewhere), then quantize the new master -- bit for bit."""
+    elsewhere), then quantize the new master -- bit for bit.  With scale_pad
+    the scale rows are wider than the code rows need (sld > ld / B), their
+    padding a huge value that a wrong scale stride would pick up."""
     length, ld = 3 * B + 77, 4 * B
-    sld = ld // B
+    sld = ld // B + scale_pad
     rows = np.stack([_x(ld, 20 + k, 1e-3) for k in range(n_dp)])
     qs = [oracle.q8_quantize(rows[k], oracle.FP32) for k in range(n_dp)]
     gq = np.concatenate([q for q, _ in qs])
-    gs = np.concatenate([s for _, s in qs])
+    gs = np.full((n_dp, sld), 1e30, np.float32)
+    for k, (_, s) in enumerate(qs):
+        gs[k, :s.size] = s
+    gs = gs.reshape(-1)
     w0 = _x(length, 30, 0.02)
     hp = dict(lr=1e-3, weight_decay=0.1)
     w, m, v = w0.copy(), np.zeros(length, np.float32), np.zeros(length, np.float32)
