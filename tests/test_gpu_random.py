@@ -1,4 +1,5 @@
-"""Seeded random cases of the fused step and the reduce against the oracle,
+"""Seeded random cases of the fused step, the reduce, the 8-bit step and
+AdamW (with and without its controls) against the oracle,
 bitwise: row count, range length, row stride, rank, shard offset, gradient
 and weight formats, the flags, and -- by leading elements before each
 buffer -- the alignment of every pointer, so that calls mix the vector
@@ -195,3 +196,72 @@ def test_random_q8_step(seed):
         assert int(d_ovf.item()) == int(o_ovf[0])
     if ssq:
         assert abs(d_ss.item() - o_ss[0]) <= 1e-10 * o_ss[0]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_adamw(seed):
+    """AdamW from an fp32 gradient buffer -- the plain entry point, or the
+    one with controls in any mix (skip flag, clipping from a sum of squares
+    to a random norm, a device loss scale) -- on random ranges, shard
+    offsets and pointer alignments, non-zero moments, two steps, bitwise
+    against the oracle, canaries around the slot."""
+    c = _case(4000 + seed)
+    n_dp, S, off, L = c["n_dp"], c["shard"], c["off"], c["length"]
+    lay, _ = zs.zero_flatten_layout([S * n_dp], n_dp)
+    lo = c["rank"] * S + off
+    # the controls cycle with the seed so that each runs un-skipped: clipping
+    # that bites (seeds 1, 5; with a loss scale on 1), a loss scale alone (4),
+    # a sum too small to clip (7), controls all absent (8), a skipped step (2)
+    ex = seed % 3 != 0
+    skip_v = (None, 0, 1, 0)[seed % 4]
+    scale = (None, 1024.0, 65536.0)[(seed + 1) % 3] if ex else None
+    base = (None, 1e6, 1e2, 1e-6)[seed % 4] if ex else None
+    ssq_v = base * (scale or 1.0) ** 2 if base is not None else None
+    max_norm = (0.5, 1.0)[seed % 2] if ssq_v is not None else 0.0
+    print(f"\n[random adamw] {c} ex={ex} skip={skip_v} sumsq={ssq_v} max_norm={max_norm} "
+          f"loss_scale={scale}", flush=True)
+    gs = 1.0 / n_dp
+    if ssq_v is not None:
+        s = float(np.float32(gs / scale)) if scale else float(np.float32(gs))
+        bites = oracle.clip_coef(ssq_v, s, max_norm) < 1.0
+        assert bites if seed in (1, 5) else (not bites if seed == 7 else True)
+    acc = host_master(150 + seed, lo, L, sigma=1e-3 * (scale or 1.0))
+    w = host_master(160 + seed, lo, L)
+    m = host_master(170 + seed, lo, L, sigma=1e-4)
+    v = np.abs(host_master(180 + seed, lo, L, sigma=1e-8))
+    wout = np.full(lay.n_pad, CANARY, np.uint16)
+    leads = c["leads"]
+    dacc, dw, dm, dv = (_lead(a, k) for a, k in zip((acc, w, m, v), leads))
+    dwf = torch.from_numpy(wout.view(np.int16).copy()).cuda().view(TDT[c["wdt"]])
+    d_skip = (torch.tensor([skip_v], dtype=torch.int32, device="cuda")
+              if skip_v is not None else None)
+    d_ss = torch.tensor([ssq_v], dtype=torch.float64, device="cuda") if ssq_v is not None else None
+    d_ls = zs.new_loss_scale(scale) if scale is not None else None
+    o_skip = np.array([skip_v], np.uint32) if skip_v is not None else None
+    o_ss = np.array([ssq_v]) if ssq_v is not None else None
+    o_ls = np.array([scale], np.float32) if scale is not None else None
+    for t in (1, 2):
+        hp = zs.AdamWHParams(step=t, grad_scale=gs, **HP)
+        if ex:
+            zs.zero_shard_adamw_ex(dacc, dw, dm, dv, dwf, lay, c["rank"], hp, shard_off=off,
+                                   length=L, skip=d_skip, sumsq=d_ss, max_norm=max_norm,
+                                   loss_scale=d_ls)
+        else:
+            zs.zero_shard_adamw(dacc, dw, dm, dv, dwf, lay, c["rank"], hp, shard_off=off,
+                                length=L, skip=d_skip)
+        slot = wout[lo:lo + L].copy()
+        if L > 0:
+            if ex:
+                oracle.adamw_ex(acc, w, m, v, slot, c["wdt"], L, t, grad_scale=gs, skip=o_skip,
+                                sumsq=o_ss, max_norm=max_norm, loss_scale=o_ls, **HP)
+            else:
+                oracle.adamw(acc, w, m, v, slot, c["wdt"], L, t, grad_scale=gs, skip=o_skip, **HP)
+        wout[lo:lo + L] = slot
+        torch.cuda.synchronize()
+        diff = check_f32(_host(dw), w, "master") + check_f32(_host(dm), m, "m")
+        diff += check_f32(_host(dv), v, "v")
+        got = _host(dwf)
+        diff += check_16(got[lo:lo + L], wout[lo:lo + L], c["wdt"], "weights")
+        assert diff == 0
+        assert np.array_equal(got[:lo], wout[:lo]) and np.array_equal(got[lo + L:], wout[lo + L:])
+        assert np.array_equal(_host(dacc), acc)
