@@ -55,6 +55,10 @@ def parse():
     p.add_argument("--bucket-elems", type=int, default=0, metavar="B",
                    help="single-launch 16-bit steps: issue the shard as consecutive buckets of B "
                         "elements, one library call each (0: one call for the whole shard)")
+    p.add_argument("--graph", action="store_true",
+                   help="single-launch 16-bit steps: capture the step (all its buckets) once as "
+                        "a HIP graph that reads the step's constants from device memory, then "
+                        "per step copy that step's constants and replay the graph")
     p.add_argument("--flags", action="store_true",
                    help="single-launch steps: also raise the overflow flag and sum the squares "
                         "of the scaled gradient (the shard's part of the global norm)")
@@ -192,13 +196,60 @@ def main():
     if wl.controls:
         loss_scale = zs.new_loss_scale(wl.loss_scale, dev)
     stream = torch.cuda.current_stream(dev)
+    graph = None
+    if args.graph:
+        if micro != 1 or q8:
+            print("--graph applies to the single-launch 16-bit steps", file=sys.stderr)
+            sys.exit(2)
+        # every step's constants in pinned host memory up front (no buffer is
+        # rewritten while an earlier asynchronous copy may still read it), one
+        # device buffer the captured kernels read
+        host_consts = torch.empty((args.warmup + args.steps, 48), dtype=torch.uint8,
+                                  pin_memory=True)
+        for i in range(args.warmup + args.steps):
+            hpi = zs.AdamWHParams(step=i + 1, grad_scale=1.0 / n_dp, **hp_kw)
+            host_consts[i].copy_(torch.from_numpy(zs.zero_step_consts_make(hpi)))
+        consts = zs.new_step_consts(dev)
+        bucket = args.bucket_elems if args.bucket_elems > 0 else S
+        fl = dict(overflow=flag, sumsq=sumsq) if args.flags else {}
+        ws = (torch.empty(zs.zero_sumsq_workspace_bytes(bucket) // 8 + 1, dtype=torch.float64,
+                          device=dev) if args.flags else None)
+
+        def issue(st):
+            if args.flags:
+                flag.zero_()
+                sumsq.zero_()
+            for b0 in range(0, S, bucket):
+                b1 = min(S, b0 + bucket)
+                zs.zero_shard_step_dc(slab[:, b0:], S, b1 - b0, master[b0:], m[b0:], v[b0:],
+                                      wfull, lay, rank, consts, shard_off=b0, stream=st,
+                                      workspace=ws, **fl)
+
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                issue(side)
+        stream.wait_stream(side)
     torch.cuda.synchronize()
 
     # ---- one step of the hot path ------------------------------------------
     events = []
 
     def step(t, timed):
-        if micro == 1:
+        if graph is not None:
+            consts.copy_(host_consts[t - 1], non_blocking=True)
+            e0 = torch.cuda.Event(enable_timing=True) if timed else None
+            e1 = torch.cuda.Event(enable_timing=True) if timed else None
+            if timed:
+                e0.record(stream)
+            graph.replay()
+            if timed:
+                e1.record(stream)
+                events.append((e0, e1))
+        elif micro == 1:
             hp = zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **hp_kw)
             e0 = torch.cuda.Event(enable_timing=True) if timed else None
             e1 = torch.cuda.Event(enable_timing=True) if timed else None
@@ -277,6 +328,8 @@ def main():
     elif micro == 1:
         bytes_per_param = gbytes * n_dp + 26
         kernel = f"step_quad_kernel (fused reduce + AdamW + cast{with_flags})"
+        if args.graph:
+            kernel += ", one graph replay per step, constants read from device memory"
     else:
         # 4 B written by the first reduce, 2 n_dp + 8 by each later one,
         # 30 by the gated AdamW (acc 4 + state 12 read, state 12 + weight 2 written)
@@ -293,9 +346,10 @@ def main():
         launch_bytes = 30 * S
     achieved = launch_bytes / (k_avg * 1e-3) / 1e9
     # the committed counter summaries cover the variant without the flags
-    # (for the stage-2 workloads: the timed AdamW launch)
+    # whose constants are kernel arguments (for the stage-2 workloads: the
+    # timed AdamW launch)
     traffic = (committed_traffic(wl.name, Q8_SOURCE if q8 else KERNEL_SOURCE)
-               if not args.flags else None)
+               if not args.flags and not args.graph else None)
 
     line = {
         "metric": "sharded AdamW step params/s and HBM GB/s (% of 8 TB/s), 7B n_dp=8 shard",
@@ -323,6 +377,8 @@ def main():
                    "flags": "overflow + sum of squares" if args.flags and micro == 1 else None,
                    "bucket_elems": args.bucket_elems if args.bucket_elems > 0 and micro == 1
                    and not q8 else None,
+                   "graph": "one captured graph, step constants in device memory"
+                   if args.graph else None,
                    "launches_per_step": (-(-S // args.bucket_elems) if args.bucket_elems > 0
                                          and not q8 else 1) if micro == 1
                    else micro + 1 + int(wl.controls)},

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define ZERO_SHARD_ABI_VERSION 2
+#define ZERO_SHARD_ABI_VERSION 3
 
 /* every entry point is exported from the shared library */
 #if defined(__GNUC__) || defined(__clang__)
@@ -345,6 +345,57 @@ ZERO_API zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_t 
                             int64_t shard_off, const zero_adamw_hparams *hp,
                             uint32_t *overflow, double *sumsq, void *workspace,
                             int64_t workspace_bytes, void *stream);
+
+/* ---- step constants in device memory (one graph for every step) ----------
+ * A captured HIP graph replays the arguments it was captured with, so a
+ * graph of zero_shard_step or zero_shard_adamw_ex repeats the step number
+ * and learning rate of the step it captured.  The _dc variants read the
+ * update's constants from device memory when their kernels run instead:
+ * capture once, and before each replay write that step's constants into the
+ * device buffer (zero_step_consts_make on the host, then a copy).  The step
+ * number, a learning-rate schedule and every other hyperparameter may then
+ * change from replay to replay -- for instance t held back after a step
+ * the overflow flag skipped.  Given the constants of the same
+ * hyperparameters, results are bit-identical to the hp-taking call. */
+
+/* The update's constants as zero_adamw_hparams defines them: the ten fp32
+ * values, and grad_scale itself for a dynamic loss scale (s = fl(grad_scale
+ * / loss_scale) is formed from the double).  48 bytes, 8-byte aligned. */
+typedef struct zero_step_consts {
+    float s, b1, c1, b2, c2, bc1, bc2, lr, eps, d;
+    double grad_scale;
+} zero_step_consts;
+
+/* Forms the constants of hp (host memory in and out), by the same rule as
+ * the hp-taking entry points.  EINVAL: NULL hp or out, or hyperparameters
+ * those entry points reject. */
+ZERO_API zero_status zero_step_consts_make(const zero_adamw_hparams *hp,
+                                           zero_step_consts *out);
+
+/* zero_shard_step with its constants read from consts (device, 8-byte
+ * aligned, read when the kernels run; the values are used as they are, as
+ * the library cannot inspect device memory at call time).  Errors as for
+ * zero_shard_step, without the hyperparameter checks; EINVAL also for a NULL
+ * or unaligned consts, EALIAS when consts overlaps an output. */
+ZERO_API zero_status zero_shard_step_dc(const void *grads, zero_dtype gdt, int64_t ld,
+                                        int64_t len, float *master, float *m, float *v,
+                                        void *weight_full, zero_dtype wdt,
+                                        const zero_layout *layout, int32_t rank,
+                                        int64_t shard_off, const zero_step_consts *consts,
+                                        uint32_t *overflow, double *sumsq, void *workspace,
+                                        int64_t workspace_bytes, void *stream);
+
+/* zero_shard_adamw_ex with its constants read from consts (as for
+ * zero_shard_step_dc; with a loss scale, s = fl(consts->grad_scale /
+ * scale)).  Errors as for zero_shard_adamw_ex without the hyperparameter
+ * checks; EINVAL also for a NULL or unaligned consts, EALIAS when consts
+ * overlaps an output. */
+ZERO_API zero_status zero_shard_adamw_dc(const float *acc, float *master, float *m,
+                                         float *v, void *weight_full, zero_dtype wdt,
+                                         const zero_layout *layout, int32_t rank,
+                                         int64_t shard_off, int64_t len,
+                                         const zero_step_consts *consts,
+                                         const zero_step_control *ctl, void *stream);
 
 /* ---- moving flat ranges: flatten, unflatten, re-shard (device) -----------
  * A sharded checkpoint is tied to the layout it was written with; resuming

@@ -1,18 +1,22 @@
 """The library's calls under HIP graph capture: a launch-bound loop (a
 shard stepped in small buckets, "ZeRO and FSDP", A sharded Adam step) is
-captured once and replayed.  The step's constants (bias corrections of step
-t) are kernel arguments, so a graph replays the step it captured; each
-replay here starts from the same state, restored eagerly between replays,
-and must equal the eager result bit for bit -- weights, moments, the slot,
-the overflow flag and the (fixed-order) sum of squares."""
+captured once and replayed.  With the step's constants as kernel arguments
+a graph replays the step it captured: each replay starts from the same
+state, restored eagerly between replays, and must equal the eager result
+bit for bit -- weights, moments, the slot, the overflow flag and the
+(fixed-order) sum of squares.  With the constants in device memory (the _dc
+entry points) one graph serves a run of steps, each replay checked against
+the oracle's step, including a stage-2 step whose step number the host
+holds back after an overflow."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import zero_sharded_mixed_flatten_amd as zs
-from synth import BF16
+from synth import BF16, F16
 from synth.workloads import GradDraw
-from tests.gpu_util import dev16, devf, host_master, host_rows
+from tests.gpu_util import dev16, devf, host16, host_master, host_rows, hostf
 
 pytestmark = pytest.mark.gpu
 
@@ -76,3 +80,140 @@ def test_bucketed_step_replays_in_a_graph():
                 a, b = a.view(torch.int16), b.view(torch.int16)
             assert torch.equal(a, b), f"replay {replay}: {name} differs from the eager step"
     assert int(ref[4].item()) == 0 and float(ref[5].item()) > 0.0
+
+
+def test_one_graph_serves_every_step():
+    """With the constants in device memory (zero_shard_step_dc) one captured
+    graph serves a run of steps: before each replay the next step's
+    constants (step t, a halving learning rate) and gradients are written
+    into the buffers the graph reads, and every replay must equal the
+    oracle's step t bit for bit."""
+    n_dp, rank, S = 4, 1, 100_000
+    buckets = [(0, 25_000), (25_000, 50_003), (50_003, 75_000), (75_000, S)]
+    lay, _ = zs.zero_flatten_layout([S * n_dp], n_dp)
+    draw = GradDraw(BF16, 1e-3)
+    w = host_master(251, rank * S, S)
+    m, v = np.zeros(S, np.float32), np.zeros(S, np.float32)
+    wout = np.zeros(lay.n_pad, np.uint16)
+    g = dev16(host_rows(251, 1, 0, n_dp, rank * S, S, draw), zs.ZERO_BF16)
+    W, M, V = devf(w), devf(m), devf(v)
+    wf = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ss = torch.zeros(1, dtype=torch.float64, device="cuda")
+    ws = torch.empty(zs.zero_sumsq_workspace_bytes(S) // 8 + 1, dtype=torch.float64,
+                     device="cuda")
+    consts = zs.new_step_consts()
+
+    def step(stream):
+        flag.zero_()
+        ss.zero_()
+        for b0, b1 in buckets:
+            zs.zero_shard_step_dc(g.view(n_dp, S)[:, b0:], S, b1 - b0, W[b0:], M[b0:], V[b0:], wf,
+                                  lay, rank, consts, shard_off=b0, overflow=flag, sumsq=ss,
+                                  workspace=ws, stream=stream)
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    # capture ran nothing: the state is still the initial one
+    assert np.array_equal(hostf(W).view(np.uint32), w.view(np.uint32))
+    for t in (1, 2, 3, 4):
+        lr = 1e-4 / 2 ** (t - 1)
+        hp = zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **dict(HP, lr=lr))
+        rows = host_rows(251, t, 0, n_dp, rank * S, S, draw)
+        g.copy_(dev16(rows, zs.ZERO_BF16))
+        consts.copy_(torch.from_numpy(zs.zero_step_consts_make(hp)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_ovf, o_ss = np.zeros(1, np.uint32), np.zeros(1)
+        slot = wout[rank * S:(rank + 1) * S].copy()
+        oracle.step(rows, oracle.BF16, n_dp, S, S, w, m, v, slot, oracle.BF16, t,
+                    grad_scale=1.0 / n_dp, overflow=o_ovf, sumsq=o_ss, **dict(HP, lr=lr))
+        wout[rank * S:(rank + 1) * S] = slot
+        for name, got, want in (("master", hostf(W), w), ("m", hostf(M), m), ("v", hostf(V), v)):
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"t={t}: {name}"
+        assert np.array_equal(host16(wf), wout), f"t={t}: weights"
+        assert int(flag.item()) == 0 and abs(ss.item() - o_ss[0]) <= 1e-10 * o_ss[0]
+
+
+def test_stage2_graph_holds_the_step_back_after_an_overflow():
+    """A stage-2 step -- two fp16 micro-batch reduces with the overflow
+    flag, AdamW with the device constants gated on the flag and scaled by
+    the device loss scale, the loss-scale update -- captured once and
+    replayed for six iterations.  The host reads the flag after each replay
+    and advances t only when the step was taken; an infinity injected in
+    iteration 2 must skip that step (state untouched, scale backed off) and
+    hold t back.  Every iteration equals the oracle's bit for bit."""
+    n_dp, rank, S, micro = 4, 2, 50_000, 2
+    lay, _ = zs.zero_flatten_layout([S * n_dp], n_dp)
+    draw = GradDraw(F16, 1e-3, scale=65536.0)
+    w = host_master(250, rank * S, S)
+    m, v = np.zeros(S, np.float32), np.zeros(S, np.float32)
+    wout = np.zeros(lay.n_pad, np.uint16)
+    gb = [dev16(host_rows(250, 1, mb, n_dp, rank * S, S, draw), zs.ZERO_FP16)
+          for mb in range(micro)]
+    acc = torch.zeros(S, dtype=torch.float32, device="cuda")
+    W, M, V = devf(w), devf(m), devf(v)
+    wf = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dls = zs.new_loss_scale(65536.0)
+    consts = zs.new_step_consts()
+    o_scale, o_good = np.array([65536.0], np.float32), np.zeros(1, np.int32)
+    o_acc = np.zeros(S, np.float32)
+
+    def step(stream):
+        flag.zero_()
+        for mb in range(micro):
+            zs.zero_shard_reduce(gb[mb], n_dp, S, S, acc, accumulate=mb > 0, overflow=flag,
+                                 stream=stream)
+        zs.zero_shard_adamw_dc(acc, W, M, V, wf, lay, rank, consts, skip=flag, loss_scale=dls,
+                               stream=stream)
+        zs.zero_loss_scale_update(dls, flag, 2.0, 0.5, 3, stream=stream)
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    t, taken = 1, []
+    for it in range(6):
+        rows = [host_rows(250, it + 1, mb, n_dp, rank * S, S, draw) for mb in range(micro)]
+        if it == 2:
+            rows[1][3, 777] = 0x7C00                  # fp16 +inf in the last micro-batch
+        for mb in range(micro):
+            gb[mb].copy_(dev16(rows[mb], zs.ZERO_FP16))
+        hp = zs.AdamWHParams(step=t, grad_scale=1.0 / (n_dp * micro), **HP)
+        consts.copy_(torch.from_numpy(zs.zero_step_consts_make(hp)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        skipped = int(flag.item()) != 0
+        # the oracle, the same iteration
+        o_flag = np.zeros(1, np.uint32)
+        for mb in range(micro):
+            oracle.reduce(rows[mb], oracle.FP16, n_dp, S, S, o_acc, int(mb > 0), overflow=o_flag)
+        slot = wout[rank * S:(rank + 1) * S].copy()
+        oracle.adamw_ex(o_acc, w, m, v, slot, oracle.BF16, S, t, grad_scale=1.0 / (n_dp * micro),
+                        skip=o_flag, loss_scale=o_scale.copy(), **HP)
+        wout[rank * S:(rank + 1) * S] = slot
+        oracle.loss_scale_update(o_scale, o_good, int(o_flag[0]), 2.0, 0.5, 3)
+        assert skipped == bool(o_flag[0]) == (it == 2), f"iteration {it}"
+        for name, got, want in (("master", hostf(W), w), ("m", hostf(M), m), ("v", hostf(V), v)):
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"it={it}: {name}"
+        assert np.array_equal(host16(wf), wout), f"it={it}: weights"
+        assert zs.read_loss_scale(dls) == (float(o_scale[0]), int(o_good[0])), f"it={it}"
+        taken.append(t)
+        if not skipped:
+            t += 1
+    assert taken == [1, 2, 3, 3, 4, 5]

@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 20, names
+    assert len(names) == 23, names
     lib = ctypes.CDLL(zs.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -260,6 +260,47 @@ def test_controls_reject_bad_arguments():
     assert A(*base, ctypes.byref(ctl), None) == zs.ZERO_EINVAL
     ctl = zs._StepControl(None, None, 0.0, P(BASE + (2 << 30) + 100).value)  # loss scale inside m
     assert A(*base, ctypes.byref(ctl), None) == zs.ZERO_EALIAS
+
+
+@pytest.mark.parametrize("step", [1, 2, 7, 1000])
+@pytest.mark.parametrize("grad_scale", [1.0 / 8, 1.0 / 3])
+def test_step_consts_equal_the_oracles(step, grad_scale):
+    """zero_step_consts_make forms the ten constants by the same rule as the
+    oracle (separate code, same stated rounding): equal bit for bit, with
+    grad_scale kept as the double it was given."""
+    hp = zs.AdamWHParams(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
+                         grad_scale=grad_scale, step=step)
+    got = zs.zero_step_consts_make(hp)
+    assert got.size == 48
+    d = oracle.adamw_scalars(step, lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8,
+                             weight_decay=0.1, grad_scale=grad_scale)
+    want = np.array([d[k] for k in ("s", "b1", "c1", "b2", "c2", "bc1", "bc2", "lr", "eps", "d")],
+                    np.float32)
+    assert np.array_equal(got[:40].view(np.uint32), want.view(np.uint32))
+    assert got[40:].view(np.float64)[0] == grad_scale
+    with pytest.raises(ValueError):
+        zs.zero_step_consts_make(zs.AdamWHParams(step=0))
+    assert L.zero_step_consts_make(ctypes.byref(_hp()), None) == zs.ZERO_EINVAL
+
+
+@cpu_only
+def test_device_consts_entry_points_reject_bad_arguments():
+    lay = zs.zero_flatten_layout([4096], 4)[0]
+    S = L.zero_shard_step_dc
+    args = [P(BASE), 0, 1024, 1024, P(BASE + (1 << 30)), P(BASE + (2 << 30)), P(BASE + (3 << 30)),
+            P(BASE + (4 << 30)), 0, ctypes.byref(lay), 1, 0]
+    tail = [None, None, None, 0, None]
+    assert S(*args, None, *tail) == zs.ZERO_EINVAL                        # no constants
+    assert S(*args, P(BASE + (5 << 30) + 4), *tail) == zs.ZERO_EINVAL     # not 8-byte aligned
+    assert S(*args, P(BASE + (1 << 30) + 64), *tail) == zs.ZERO_EALIAS    # inside master
+    assert S(*args, P(BASE + (4 << 30) + 2048 + 8), *tail) == zs.ZERO_EALIAS  # inside the slot
+    assert S(P(0), 0, 1024, 0, *args[4:], P(0), *tail) == zs.ZERO_EINVAL  # NULL even when empty
+    A = L.zero_shard_adamw_dc
+    base = [P(BASE), P(BASE + (1 << 30)), P(BASE + (2 << 30)), P(BASE + (3 << 30)),
+            P(BASE + (4 << 30)), 0, ctypes.byref(lay), 1, 0, 1024]
+    assert A(*base, None, None, None) == zs.ZERO_EINVAL
+    assert A(*base, P(BASE + (5 << 30) + 4), None, None) == zs.ZERO_EINVAL
+    assert A(*base, P(BASE + (3 << 30) + 400), None, None) == zs.ZERO_EALIAS  # inside v
 
 
 def _pc(*pieces):

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libzero_shard.so")
 ZERO_OK, ZERO_EINVAL, ZERO_EALIAS, ZERO_ERANGE, ZERO_EDEVICE = range(5)
 ZERO_BF16, ZERO_FP16, ZERO_FP32 = 0, 1, 2
 ZERO_Q8_BLOCK = 256
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class ZeroError(RuntimeError):
@@ -59,6 +59,13 @@ class _HParams(ctypes.Structure):
 class _StepControl(ctypes.Structure):
     _fields_ = [("skip", ctypes.c_void_p), ("sumsq", ctypes.c_void_p),
                 ("max_norm", ctypes.c_double), ("loss_scale", ctypes.c_void_p)]
+
+
+class ZeroStepConsts(ctypes.Structure):
+    """zero_step_consts: the update's ten fp32 constants and grad_scale."""
+    _fields_ = [(name, ctypes.c_float) for name in
+                ("s", "b1", "c1", "b2", "c2", "bc1", "bc2", "lr", "eps", "d")] + \
+               [("grad_scale", ctypes.c_double)]
 
 
 class _Piece(ctypes.Structure):
@@ -122,6 +129,14 @@ def _load():
     L.zero_shard_step.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, ctypes.c_int,
                                   lay_p, i32, i64, hp_p, vp, vp, vp, i64, vp]
     L.zero_shard_step.restype = ctypes.c_int
+    L.zero_step_consts_make.argtypes = [hp_p, ctypes.POINTER(ZeroStepConsts)]
+    L.zero_step_consts_make.restype = ctypes.c_int
+    L.zero_shard_step_dc.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, ctypes.c_int,
+                                     lay_p, i32, i64, vp, vp, vp, vp, i64, vp]
+    L.zero_shard_step_dc.restype = ctypes.c_int
+    L.zero_shard_adamw_dc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, lay_p, i32, i64, i64,
+                                      vp, ctypes.POINTER(_StepControl), vp]
+    L.zero_shard_adamw_dc.restype = ctypes.c_int
     piece_p = ctypes.POINTER(_Piece)
     L.zero_flat_gather.argtypes = [piece_p, i32, i64, i32, i64, i64, vp, vp]
     L.zero_flat_gather.restype = ctypes.c_int
@@ -427,6 +442,68 @@ def zero_shard_step(grads, ld: int, length: int, master, m, v, weight_full,
         ctypes.byref(hpc), _buf(overflow, "overflow", 1, torch.int32, d),
         _buf(sumsq, "sumsq", 1, torch.float64, d), ws, ws_bytes, _stream(stream, master)),
         "zero_shard_step")
+
+
+def zero_step_consts_make(hp: AdamWHParams) -> np.ndarray:
+    """The step's constants (a zero_step_consts, 48 bytes) as a uint8 array,
+    to be copied into a device buffer from new_step_consts() before the
+    _dc calls (or a graph of them) run."""
+    out = ZeroStepConsts()
+    hpc = hp._c()
+    _check(_lib.zero_step_consts_make(ctypes.byref(hpc), ctypes.byref(out)),
+           "zero_step_consts_make")
+    return np.frombuffer(bytes(out), dtype=np.uint8).copy()
+
+
+def new_step_consts(device="cuda"):
+    """A device buffer for one zero_step_consts (uint8[48])."""
+    import torch
+    return torch.zeros(ctypes.sizeof(ZeroStepConsts), dtype=torch.uint8, device=device)
+
+
+def _consts(consts, device):
+    import torch
+    return _buf(consts, "consts", ctypes.sizeof(ZeroStepConsts), torch.uint8, device)
+
+
+def zero_shard_step_dc(grads, ld: int, length: int, master, m, v, weight_full,
+                       layout: ZeroLayout, rank: int, consts, shard_off: int = 0,
+                       overflow=None, sumsq=None, stream=None, workspace=None):
+    """zero_shard_step with the constants read from the device buffer consts
+    (see zero_step_consts_make) when the kernels run."""
+    import torch
+    d = master.device
+    ws, ws_bytes = _workspace(sumsq, workspace, length, d)
+    _check(_lib.zero_shard_step_dc(
+        _rows(grads, "grads", layout.n_dp, ld, length, device=d),
+        _dtype_code(grads, "grads", True), ld, length,
+        _buf(master, "master", length, torch.float32), _buf(m, "m", length, torch.float32, d),
+        _buf(v, "v", length, torch.float32, d),
+        _buf(weight_full, "weight_full", _slot_end(layout, rank, shard_off, length), device=d),
+        _dtype_code(weight_full, "weight_full"), ctypes.byref(layout), rank, shard_off,
+        _consts(consts, d), _buf(overflow, "overflow", 1, torch.int32, d),
+        _buf(sumsq, "sumsq", 1, torch.float64, d), ws, ws_bytes, _stream(stream, master)),
+        "zero_shard_step_dc")
+
+
+def zero_shard_adamw_dc(acc, master, m, v, weight_full, layout: ZeroLayout, rank: int, consts,
+                        shard_off: int = 0, length: Optional[int] = None, skip=None,
+                        sumsq=None, max_norm: float = 0.0, loss_scale=None, stream=None):
+    """zero_shard_adamw_ex with the constants read from the device buffer
+    consts when the kernels run."""
+    import torch
+    if length is None:
+        length = master.numel()
+    d = master.device
+    ctl = _StepControl(_buf(skip, "skip", 1, torch.int32, d),
+                       _buf(sumsq, "sumsq", 1, torch.float64, d), float(max_norm),
+                       _buf(loss_scale, "loss_scale", 2, torch.int32, d))
+    _check(_lib.zero_shard_adamw_dc(
+        _buf(acc, "acc", length, torch.float32, d), _buf(master, "master", length, torch.float32),
+        _buf(m, "m", length, torch.float32, d), _buf(v, "v", length, torch.float32, d),
+        _buf(weight_full, "weight_full", _slot_end(layout, rank, shard_off, length), device=d),
+        _dtype_code(weight_full, "weight_full"), ctypes.byref(layout), rank, shard_off, length,
+        _consts(consts, d), ctypes.byref(ctl), _stream(stream, master)), "zero_shard_adamw_dc")
 
 
 def _slot_end(layout: ZeroLayout, rank: int, shard_off: int, length: int) -> int:

@@ -92,6 +92,12 @@ inline Consts make_consts(const zero_adamw_hparams &hp) {
     return c;
 }
 
+// the fp32 constants of a zero_step_consts (a kernel reads it from device
+// memory when the step's constants are not kernel arguments)
+__host__ __device__ inline Consts consts_of(const zero_step_consts &d) {
+    return Consts{d.s, d.b1, d.c1, d.b2, d.c2, d.bc1, d.bc2, d.lr, d.eps, d.d};
+}
+
 // ---------------------------------------------------------------------------
 // 16-bit <-> fp32.  Widening is exact.  Narrowing uses gfx950's packed
 // converts (v_cvt_pk_bf16_f32, v_cvt_pk_f16_f32): round to nearest even.

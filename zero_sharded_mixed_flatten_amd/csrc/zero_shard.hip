@@ -166,14 +166,16 @@ __device__ __forceinline__ void step_quad_finish(Rows<GDT, NDP> &rows, f32x4 w4,
 
 // One quad per lane, one-wave workgroups (TPB == kWave): the rows and the
 // state of the quad are all loaded before the first add.  With SSQ the
-// wave's partial sum of squares goes to part[blockIdx.x].
-template <int TPB, int GDT, int WDT, int NDP, bool OVF, bool SSQ>
+// wave's partial sum of squares goes to part[blockIdx.x].  With DC the
+// constants come from dc (device memory) instead of c.
+template <int TPB, int GDT, int WDT, int NDP, bool OVF, bool SSQ, bool DC>
 __global__ void __launch_bounds__(TPB)
 step_quad_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld, int n_dp,
                  int64_t nquad,
                  float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
                  uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
-                 double *__restrict__ part) {
+                 double *__restrict__ part, const zero_step_consts *__restrict__ dc) {
+    if constexpr (DC) c = consts_of(*dc);
     bool bad = false;
     double ss = 0.0;
     const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
@@ -190,13 +192,14 @@ step_quad_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld
 }
 
 // element-per-thread variant for unaligned buffers and ragged tails
-template <int GDT, int WDT, bool OVF, bool SSQ>
+template <int GDT, int WDT, bool OVF, bool SSQ, bool DC>
 __global__ void __launch_bounds__(kBlock)
 step_scalar_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld, int n_dp,
                    int64_t len,
                    float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
                    uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
-                   double *__restrict__ part) {
+                   double *__restrict__ part, const zero_step_consts *__restrict__ dc) {
+    if constexpr (DC) c = consts_of(*dc);
     bool bad = false;
     double ss = 0.0;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
@@ -301,13 +304,18 @@ __device__ __forceinline__ float resolve_controls(const Control &k, Consts &c) {
     return clip;
 }
 
-template <int TPB, int WDT, bool SKIP, bool EXT>
+template <int TPB, int WDT, bool SKIP, bool EXT, bool DC>
 __global__ void __launch_bounds__(TPB)
 adamw_quad_kernel(const float *__restrict__ acc, float *__restrict__ W, float *__restrict__ M,
                   float *__restrict__ V, uint16_t *__restrict__ out, int64_t nquad, Consts c,
-                  const uint32_t *__restrict__ skip, Control ctl) {
+                  const uint32_t *__restrict__ skip, Control ctl,
+                  const zero_step_consts *__restrict__ dc) {
     if constexpr (SKIP) {
         if (*skip != 0u) return;
+    }
+    if constexpr (DC) {
+        c = consts_of(*dc);
+        ctl.grad_scale = dc->grad_scale;
     }
     float clip = 1.0f;
     if constexpr (EXT) clip = resolve_controls(ctl, c);
@@ -335,13 +343,18 @@ adamw_quad_kernel(const float *__restrict__ acc, float *__restrict__ W, float *_
     }
 }
 
-template <int WDT, bool SKIP, bool EXT>
+template <int WDT, bool SKIP, bool EXT, bool DC>
 __global__ void __launch_bounds__(kBlock)
 adamw_scalar_kernel(const float *__restrict__ acc, float *__restrict__ W, float *__restrict__ M,
                     float *__restrict__ V, uint16_t *__restrict__ out, int64_t len, Consts c,
-                    const uint32_t *__restrict__ skip, Control ctl) {
+                    const uint32_t *__restrict__ skip, Control ctl,
+                    const zero_step_consts *__restrict__ dc) {
     if constexpr (SKIP) {
         if (*skip != 0u) return;
+    }
+    if constexpr (DC) {
+        c = consts_of(*dc);
+        ctl.grad_scale = dc->grad_scale;
     }
     float clip = 1.0f;
     if constexpr (EXT) clip = resolve_controls(ctl, c);
@@ -610,11 +623,17 @@ extern "C" zero_status zero_shard_reduce(const void *grads, zero_dtype gdt, int3
 
 namespace {
 
+// the step's constants: hyperparameters on the host (hp), or constants in
+// device memory (dc, read by the kernels); exactly one of the two is given
+bool consts_arg_ok(const zero_adamw_hparams *hp, const zero_step_consts *dc) {
+    return dc ? aligned8(dc) : hparams_ok(hp);
+}
+
 zero_status adamw_impl(const float *acc, float *master, float *m, float *v, void *weight_full,
                        zero_dtype wdt, const zero_layout *layout, int32_t rank, int64_t shard_off,
-                       int64_t len, const zero_adamw_hparams *hp, const zero_step_control *ctl,
-                       void *stream) {
-    if (!dtype_ok(wdt) || !layout_ok(layout) || !hparams_ok(hp)) return ZERO_EINVAL;
+                       int64_t len, const zero_adamw_hparams *hp, const zero_step_consts *dc,
+                       const zero_step_control *ctl, void *stream) {
+    if (!dtype_ok(wdt) || !layout_ok(layout) || !consts_arg_ok(hp, dc)) return ZERO_EINVAL;
     if (rank < 0 || rank >= layout->n_dp || shard_off < 0 || len < 0 || len > kMaxLen)
         return ZERO_EINVAL;
     if (ctl && !std::isfinite(ctl->max_norm)) return ZERO_EINVAL;
@@ -627,19 +646,20 @@ zero_status adamw_impl(const float *acc, float *master, float *m, float *v, void
                           span_of(slot, len, 2)};
     // acc and the controls are read only, but no output may overlap them
     const uint32_t *skip = ctl ? ctl->skip : nullptr;
-    Span ins[4];
+    Span ins[5];
     int n_in = 0;
     ins[n_in++] = span_of(acc, len, 4);
+    if (dc) ins[n_in++] = span_of(dc, 1, sizeof(zero_step_consts));
     if (skip) ins[n_in++] = span_of(skip, 1, 4);
     if (ctl && ctl->sumsq) ins[n_in++] = span_of(ctl->sumsq, 1, 8);
     if (ctl && ctl->loss_scale) ins[n_in++] = span_of(ctl->loss_scale, 1, sizeof(zero_loss_scale));
     if (any_alias(outs, 4, nullptr, 0, 0, 0, 4, ins, n_in)) return ZERO_EALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const Consts c = make_consts(*hp);
+    const Consts c = dc ? Consts{} : make_consts(*hp);
     const bool ext = ctl && ((ctl->sumsq && ctl->max_norm > 0.0) || ctl->loss_scale);
     const Control k{ctl ? ctl->sumsq : nullptr, ctl ? ctl->max_norm : 0.0,
-                    ctl ? ctl->loss_scale : nullptr, hp->grad_scale};
+                    ctl ? ctl->loss_scale : nullptr, dc ? 0.0 : hp->grad_scale};
     const bool vec = aligned16(acc) && aligned16(master) && aligned16(m) && aligned16(v) &&
                      aligned8(slot);
     const int64_t nquad = vec ? len / kQuad : 0;
@@ -648,18 +668,20 @@ zero_status adamw_impl(const float *acc, float *master, float *m, float *v, void
     with_dtype(wdt, [&](auto WD) {
         with_bool(skip != nullptr, [&](auto SK) {
             with_bool(ext, [&](auto EX) {
-                for_launches(nquad, [&](int64_t q0, int64_t nq) {
-                    const int64_t o = q0 * kQuad;
-                    adamw_quad_kernel<kWave, WD.value, SK.value, EX.value>
-                        <<<grid_for(nq, kWave), kWave, lds, st>>>(acc + o, master + o, m + o,
-                                                                  v + o, slot + o, nq, c, skip, k);
+                with_bool(dc != nullptr, [&](auto DV) {
+                    for_launches(nquad, [&](int64_t q0, int64_t nq) {
+                        const int64_t o = q0 * kQuad;
+                        adamw_quad_kernel<kWave, WD.value, SK.value, EX.value, DV.value>
+                            <<<grid_for(nq, kWave), kWave, lds, st>>>(
+                                acc + o, master + o, m + o, v + o, slot + o, nq, c, skip, k, dc);
+                    });
+                    if (len > done) {
+                        adamw_scalar_kernel<WD.value, SK.value, EX.value, DV.value>
+                            <<<scalar_grid(len - done, false), kBlock, 0, st>>>(
+                                acc + done, master + done, m + done, v + done, slot + done,
+                                len - done, c, skip, k, dc);
+                    }
                 });
-                if (len > done) {
-                    adamw_scalar_kernel<WD.value, SK.value, EX.value>
-                        <<<scalar_grid(len - done, false), kBlock, 0, st>>>(
-                            acc + done, master + done, m + done, v + done, slot + done,
-                            len - done, c, skip, k);
-                }
             });
         });
     });
@@ -676,7 +698,7 @@ extern "C" zero_status zero_shard_adamw(const float *acc, float *master, float *
                                         void *stream) {
     const zero_step_control ctl{skip, nullptr, 0.0, nullptr};
     return adamw_impl(acc, master, m, v, weight_full, wdt, layout, rank, shard_off, len, hp,
-                      &ctl, stream);
+                      nullptr, &ctl, stream);
 }
 
 extern "C" zero_status zero_shard_adamw_ex(const float *acc, float *master, float *m, float *v,
@@ -685,8 +707,27 @@ extern "C" zero_status zero_shard_adamw_ex(const float *acc, float *master, floa
                                            int64_t shard_off, int64_t len,
                                            const zero_adamw_hparams *hp,
                                            const zero_step_control *ctl, void *stream) {
-    return adamw_impl(acc, master, m, v, weight_full, wdt, layout, rank, shard_off, len, hp, ctl,
-                      stream);
+    return adamw_impl(acc, master, m, v, weight_full, wdt, layout, rank, shard_off, len, hp,
+                      nullptr, ctl, stream);
+}
+
+extern "C" zero_status zero_shard_adamw_dc(const float *acc, float *master, float *m, float *v,
+                                           void *weight_full, zero_dtype wdt,
+                                           const zero_layout *layout, int32_t rank,
+                                           int64_t shard_off, int64_t len,
+                                           const zero_step_consts *consts,
+                                           const zero_step_control *ctl, void *stream) {
+    if (!consts) return ZERO_EINVAL;
+    return adamw_impl(acc, master, m, v, weight_full, wdt, layout, rank, shard_off, len, nullptr,
+                      consts, ctl, stream);
+}
+
+extern "C" zero_status zero_step_consts_make(const zero_adamw_hparams *hp, zero_step_consts *out) {
+    if (!out || !hparams_ok(hp)) return ZERO_EINVAL;
+    const Consts c = make_consts(*hp);
+    *out = zero_step_consts{c.s, c.b1, c.c1, c.b2, c.c2, c.bc1, c.bc2, c.lr, c.eps, c.d,
+                            hp->grad_scale};
+    return ZERO_OK;
 }
 
 extern "C" zero_status zero_loss_scale_update(zero_loss_scale *state, const uint32_t *overflow,
@@ -702,14 +743,15 @@ extern "C" zero_status zero_loss_scale_update(zero_loss_scale *state, const uint
     return launch_status();
 }
 
-extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_t ld,
-                                       int64_t len, float *master, float *m, float *v,
-                                       void *weight_full, zero_dtype wdt,
-                                       const zero_layout *layout, int32_t rank,
-                                       int64_t shard_off, const zero_adamw_hparams *hp,
-                                       uint32_t *overflow, double *sumsq, void *workspace,
-                                       int64_t workspace_bytes, void *stream) {
-    if (!gdtype_ok(gdt) || !dtype_ok(wdt) || !layout_ok(layout) || !hparams_ok(hp))
+namespace {
+
+zero_status step_impl(const void *grads, zero_dtype gdt, int64_t ld, int64_t len, float *master,
+                      float *m, float *v, void *weight_full, zero_dtype wdt,
+                      const zero_layout *layout, int32_t rank, int64_t shard_off,
+                      const zero_adamw_hparams *hp, const zero_step_consts *dc,
+                      uint32_t *overflow, double *sumsq, void *workspace,
+                      int64_t workspace_bytes, void *stream) {
+    if (!gdtype_ok(gdt) || !dtype_ok(wdt) || !layout_ok(layout) || !consts_arg_ok(hp, dc))
         return ZERO_EINVAL;
     const int n_dp = layout->n_dp;
     if (rank < 0 || rank >= n_dp || shard_off < 0 || !rows_ok(n_dp, ld, len) || len > kMaxLen)
@@ -729,10 +771,12 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
     if (overflow) outs[n_out++] = span_of(overflow, 1, 4);
     if (sumsq) outs[n_out++] = span_of(sumsq, 1, 8);
     if (sumsq) outs[n_out++] = span_of(workspace, workspace_bytes, 1);
-    if (any_alias(outs, n_out, grads, n_dp, ld, len, gdtype_bytes(gdt))) return ZERO_EALIAS;
+    const Span dspan = span_of(dc, dc ? 1 : 0, sizeof(zero_step_consts));
+    if (any_alias(outs, n_out, grads, n_dp, ld, len, gdtype_bytes(gdt), &dspan, dc ? 1 : 0))
+        return ZERO_EALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const Consts c = make_consts(*hp);
+    const Consts c = dc ? Consts{} : make_consts(*hp);
     const bool vec = rows_vec_ok(grads, gdt, n_dp, ld) && aligned16(master) && aligned16(m) &&
                      aligned16(v) && aligned8(slot);
     const int64_t nquad = vec ? len / kQuad : 0;
@@ -745,27 +789,30 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
         with_dtype(wdt, [&](auto WD) {
             with_bool(overflow != nullptr, [&](auto OV) {
                 with_bool(sumsq != nullptr, [&](auto SS) {
-                    if (nquad > 0) {
-                        with_ndp<GD.value>(n_dp, [&](auto ND) {
-                            const size_t lds = residency_lds_bytes(
-                                step_waves_per_cu(GD.value, ND.value, SS.value), kWave);
-                            for_launches(nquad, [&](int64_t q0, int64_t nq) {
-                                const int64_t o = q0 * kQuad;
-                                step_quad_kernel<kWave, GD.value, WD.value, ND.value, OV.value,
-                                                 SS.value>
-                                    <<<grid_for(nq, kWave), kWave, lds, st>>>(
-                                        g + o, ld, n_dp, nq, master + o, m + o, v + o, slot + o,
-                                        c, overflow, SS.value ? part + q0 / kWave : nullptr);
+                    with_bool(dc != nullptr, [&](auto DV) {
+                        if (nquad > 0) {
+                            with_ndp<GD.value>(n_dp, [&](auto ND) {
+                                const size_t lds = residency_lds_bytes(
+                                    step_waves_per_cu(GD.value, ND.value, SS.value), kWave);
+                                for_launches(nquad, [&](int64_t q0, int64_t nq) {
+                                    const int64_t o = q0 * kQuad;
+                                    step_quad_kernel<kWave, GD.value, WD.value, ND.value,
+                                                     OV.value, SS.value, DV.value>
+                                        <<<grid_for(nq, kWave), kWave, lds, st>>>(
+                                            g + o, ld, n_dp, nq, master + o, m + o, v + o,
+                                            slot + o, c, overflow,
+                                            SS.value ? part + q0 / kWave : nullptr, dc);
+                                });
                             });
-                        });
-                    }
-                    if (len > done) {
-                        step_scalar_kernel<GD.value, WD.value, OV.value, SS.value>
-                            <<<scalar_grid(len - done, SS.value), kBlock, 0, st>>>(
-                                g + done, ld, n_dp, len - done, master + done, m + done,
-                                v + done, slot + done, c, overflow,
-                                SS.value ? part + n_qpart : nullptr);
-                    }
+                        }
+                        if (len > done) {
+                            step_scalar_kernel<GD.value, WD.value, OV.value, SS.value, DV.value>
+                                <<<scalar_grid(len - done, SS.value), kBlock, 0, st>>>(
+                                    g + done, ld, n_dp, len - done, master + done, m + done,
+                                    v + done, slot + done, c, overflow,
+                                    SS.value ? part + n_qpart : nullptr, dc);
+                        }
+                    });
                 });
             });
         });
@@ -776,4 +823,29 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
         return finish_sumsq(workspace, ssq_partial_count(nquad, len - done), sumsq, st);
     }
     return launch_status();
+}
+
+}  // namespace
+
+extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_t ld,
+                                       int64_t len, float *master, float *m, float *v,
+                                       void *weight_full, zero_dtype wdt,
+                                       const zero_layout *layout, int32_t rank,
+                                       int64_t shard_off, const zero_adamw_hparams *hp,
+                                       uint32_t *overflow, double *sumsq, void *workspace,
+                                       int64_t workspace_bytes, void *stream) {
+    return step_impl(grads, gdt, ld, len, master, m, v, weight_full, wdt, layout, rank, shard_off,
+                     hp, nullptr, overflow, sumsq, workspace, workspace_bytes, stream);
+}
+
+extern "C" zero_status zero_shard_step_dc(const void *grads, zero_dtype gdt, int64_t ld,
+                                          int64_t len, float *master, float *m, float *v,
+                                          void *weight_full, zero_dtype wdt,
+                                          const zero_layout *layout, int32_t rank,
+                                          int64_t shard_off, const zero_step_consts *consts,
+                                          uint32_t *overflow, double *sumsq, void *workspace,
+                                          int64_t workspace_bytes, void *stream) {
+    if (!consts) return ZERO_EINVAL;
+    return step_impl(grads, gdt, ld, len, master, m, v, weight_full, wdt, layout, rank, shard_off,
+                     nullptr, consts, overflow, sumsq, workspace, workspace_bytes, stream);
 }
