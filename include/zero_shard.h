@@ -516,6 +516,18 @@ ZERO_API zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales, 
                                         uint32_t *overflow, double *sumsq, void *workspace,
                                         int64_t workspace_bytes, void *stream);
 
+/* zero_shard_step_q8 with its constants read from consts (device, 8-byte
+ * aligned; see zero_shard_step_dc).  Errors as for zero_shard_step_q8
+ * without the hyperparameter checks; EINVAL also for a NULL or unaligned
+ * consts, EALIAS when consts overlaps an output. */
+ZERO_API zero_status zero_shard_step_q8_dc(const int8_t *gq, const float *gscales, int64_t ld,
+                                           int64_t sld, int64_t len, float *master, float *m,
+                                           float *v, int8_t *wq_full, float *wscales_full,
+                                           const zero_layout *layout, int32_t rank,
+                                           int64_t shard_off, const zero_step_consts *consts,
+                                           uint32_t *overflow, double *sumsq, void *workspace,
+                                           int64_t workspace_bytes, void *stream);
+
 /* ---- accounting (host only) ----------------------------------------------
  * Model-state bytes per GPU at ZeRO stage 0..3 for n parameters on n_dp
  * ranks with 2-byte weights and gradients and k bytes of optimizer state

@@ -93,7 +93,10 @@ def _q8_rows(n_dp, ld, seed, cfg, t=1):
 
 @pytest.mark.parametrize("n_dp", [1, 3, 8, 64])
 @pytest.mark.parametrize("ragged", [False, True])
-def test_fused_q8_step_bitwise(n_dp, ragged):
+@pytest.mark.parametrize("dc", [False, True])
+def test_fused_q8_step_bitwise(n_dp, ragged, dc):
+    """dc: the constants from a device buffer (zero_shard_step_q8_dc),
+    written before each step -- the same results bit for bit."""
     shard = 64 * B if n_dp <= 8 else 16 * B
     lay, _ = zs.zero_flatten_layout([shard * n_dp], n_dp, B)
     S = lay.shard
@@ -116,9 +119,15 @@ def test_fused_q8_step_bitwise(n_dp, ragged):
         flag = torch.zeros(1, dtype=torch.int32, device="cuda")
         ss = torch.zeros(1, dtype=torch.float64, device="cuda")
         hp = zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **HP)
-        zs.zero_shard_step_q8(torch.from_numpy(gq.reshape(-1)).cuda(),
-                              torch.from_numpy(gs.reshape(-1)).cuda(), ld, sld, length, dw, dm, dv,
-                              wq, wsc, lay, rank, hp, overflow=flag, sumsq=ss)
+        dgq, dgs = torch.from_numpy(gq.reshape(-1)).cuda(), torch.from_numpy(gs.reshape(-1)).cuda()
+        if dc:
+            consts = zs.new_step_consts()
+            consts.copy_(torch.from_numpy(zs.zero_step_consts_make(hp)))
+            zs.zero_shard_step_q8_dc(dgq, dgs, ld, sld, length, dw, dm, dv, wq, wsc, lay, rank,
+                                     consts, overflow=flag, sumsq=ss)
+        else:
+            zs.zero_shard_step_q8(dgq, dgs, ld, sld, length, dw, dm, dv, wq, wsc, lay, rank, hp,
+                                  overflow=flag, sumsq=ss)
         o_flag = np.zeros(1, np.uint32)
         o_ss = np.zeros(1)
         oracle.step_q8(gq.reshape(-1), gs.reshape(-1), n_dp, ld, sld, length, w, m, v, o_wq, o_ws,

@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     lib = ctypes.CDLL(zs.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -301,6 +301,15 @@ def test_device_consts_entry_points_reject_bad_arguments():
     assert A(*base, None, None, None) == zs.ZERO_EINVAL
     assert A(*base, P(BASE + (5 << 30) + 4), None, None) == zs.ZERO_EINVAL
     assert A(*base, P(BASE + (3 << 30) + 400), None, None) == zs.ZERO_EALIAS  # inside v
+    lay8 = zs.zero_flatten_layout([8 * 4096], 8, 256)[0]
+    Q = L.zero_shard_step_q8_dc
+    q8 = [P(BASE), P(BASE + (1 << 28)), 4096, 16, 4096, P(BASE + (2 << 28)), P(BASE + (3 << 28)),
+          P(BASE + (4 << 28)), P(BASE + (5 << 28)), P(BASE + (6 << 28)), ctypes.byref(lay8), 1, 0]
+    qtail = [None, None, None, 0, None]
+    assert Q(*q8, None, *qtail) == zs.ZERO_EINVAL
+    assert Q(*q8, P(BASE + (7 << 28) + 4), *qtail) == zs.ZERO_EINVAL          # not 8-byte aligned
+    assert Q(*q8, P(BASE + (4 << 28) + 64), *qtail) == zs.ZERO_EALIAS         # inside v
+    assert Q(*q8, P(BASE + (6 << 28) + 16 * 4 + 8), *qtail) == zs.ZERO_EALIAS  # in the scale slot
 
 
 def _pc(*pieces):

@@ -151,6 +151,9 @@ def _load():
     L.zero_shard_step_q8.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, lay_p, i32, i64,
                                      hp_p, vp, vp, vp, i64, vp]
     L.zero_shard_step_q8.restype = ctypes.c_int
+    L.zero_shard_step_q8_dc.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, lay_p, i32,
+                                        i64, vp, vp, vp, vp, i64, vp]
+    L.zero_shard_step_q8_dc.restype = ctypes.c_int
     L.zero_model_state_bytes.argtypes = [dbl, dbl, i32, dbl, ctypes.POINTER(dbl)]
     L.zero_model_state_bytes.restype = ctypes.c_int
     L.zero_comm_bytes.argtypes = [dbl, dbl, i32, dbl, dbl, ctypes.POINTER(dbl)]
@@ -609,6 +612,29 @@ def zero_shard_step_q8(gq, gscales, ld: int, sld: int, length: int, master, m, v
         ctypes.byref(layout), rank, shard_off, ctypes.byref(hpc),
         _buf(overflow, "overflow", 1, torch.int32, d), _buf(sumsq, "sumsq", 1, torch.float64, d),
         ws, ws_bytes, _stream(stream, master)), "zero_shard_step_q8")
+
+
+def zero_shard_step_q8_dc(gq, gscales, ld: int, sld: int, length: int, master, m, v, wq_full,
+                          wscales_full, layout: ZeroLayout, rank: int, consts,
+                          shard_off: int = 0, overflow=None, sumsq=None, stream=None,
+                          workspace=None):
+    """zero_shard_step_q8 with the constants read from the device buffer
+    consts (see zero_step_consts_make) when the kernels run."""
+    import torch
+    d = master.device
+    ws, ws_bytes = _workspace(sumsq, workspace, length, d)
+    nb = q8_blocks(length)
+    end = _slot_end(layout, rank, shard_off, length)
+    _check(_lib.zero_shard_step_q8_dc(
+        _rows(gq, "gq", layout.n_dp, ld, length, torch.int8, d),
+        _rows(gscales, "gscales", layout.n_dp, sld, nb, torch.float32, d), ld, sld,
+        length, _buf(master, "master", length, torch.float32), _buf(m, "m", length, torch.float32, d),
+        _buf(v, "v", length, torch.float32, d), _buf(wq_full, "wq_full", end, torch.int8, d),
+        _buf(wscales_full, "wscales_full",
+             0 if length <= 0 else (end - length) // ZERO_Q8_BLOCK + nb, torch.float32, d),
+        ctypes.byref(layout), rank, shard_off, _consts(consts, d),
+        _buf(overflow, "overflow", 1, torch.int32, d), _buf(sumsq, "sumsq", 1, torch.float64, d),
+        ws, ws_bytes, _stream(stream, master)), "zero_shard_step_q8_dc")
 
 
 def zero_adam_step(grads, w_shards, m_shards, v_shards, t: int, lr: float = 1e-3,

@@ -478,13 +478,15 @@ __device__ __forceinline__ void step_q8_block(const int8_t *__restrict__ gq,
     }
 }
 
-template <int TPB, int NDP, bool OVF, bool SSQ>
+// With DC the constants come from dc (device memory) instead of c.
+template <int TPB, int NDP, bool OVF, bool SSQ, bool DC>
 __global__ void __launch_bounds__(TPB)
 step_q8_kernel(const int8_t *__restrict__ gq, const float *__restrict__ gs, int64_t ld,
                int64_t sld, int n_dp, int64_t len, int64_t nblocks, float *__restrict__ W,
                float *__restrict__ M, float *__restrict__ V, int8_t *__restrict__ wq,
                float *__restrict__ wsc, Consts c, uint32_t *__restrict__ ovf,
-               double *__restrict__ part) {
+               double *__restrict__ part, const zero_step_consts *__restrict__ dc) {
+    if constexpr (DC) c = consts_of(*dc);
     bool bad = false;
     double ss = 0.0;
     const int64_t b = wave_block<TPB>();
@@ -668,14 +670,15 @@ extern "C" zero_status zero_q8_dequantize(const int8_t *q, const float *scales, 
     return launch_status();
 }
 
-extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales, int64_t ld,
-                                          int64_t sld, int64_t len, float *master, float *m,
-                                          float *v, int8_t *wq_full, float *wscales_full,
-                                          const zero_layout *layout, int32_t rank,
-                                          int64_t shard_off, const zero_adamw_hparams *hp,
-                                          uint32_t *overflow, double *sumsq, void *workspace,
-                                          int64_t workspace_bytes, void *stream) {
-    if (!layout_ok(layout) || !hparams_ok(hp)) return ZERO_EINVAL;
+namespace {
+
+zero_status step_q8_impl(const int8_t *gq, const float *gscales, int64_t ld, int64_t sld,
+                         int64_t len, float *master, float *m, float *v, int8_t *wq_full,
+                         float *wscales_full, const zero_layout *layout, int32_t rank,
+                         int64_t shard_off, const zero_adamw_hparams *hp,
+                         const zero_step_consts *dc, uint32_t *overflow, double *sumsq,
+                         void *workspace, int64_t workspace_bytes, void *stream) {
+    if (!layout_ok(layout) || !(dc ? aligned8(dc) : hparams_ok(hp))) return ZERO_EINVAL;
     const int n_dp = layout->n_dp;
     if (rank < 0 || rank >= n_dp || shard_off < 0 || len < 0 || len > kMaxLen || ld < len)
         return ZERO_EINVAL;
@@ -707,6 +710,7 @@ extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales
     if (sumsq) outs[n_out++] = span_of(workspace, workspace_bytes, 1);
     if (spans_overlap(outs, n_out)) return ZERO_EALIAS;
     for (int i = 0; i < n_out; ++i) {
+        if (dc && overlap(outs[i], span_of(dc, 1, sizeof(zero_step_consts)))) return ZERO_EALIAS;
         for (int k = 0; k < n_dp; ++k) {
             if (overlap(outs[i], span_of(gq + static_cast<int64_t>(k) * ld, len, 1)) ||
                 overlap(outs[i], span_of(gscales + static_cast<int64_t>(k) * sld, nb, 4)))
@@ -715,25 +719,27 @@ extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales
     }
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const Consts c = make_consts(*hp);
+    const Consts c = dc ? Consts{} : make_consts(*hp);
     // with a sum of squares each wave (one block) stores its partial
     double *part = sumsq ? ssq_partials(workspace) : nullptr;
     with_bool(overflow != nullptr, [&](auto OV) {
         with_bool(sumsq != nullptr, [&](auto SS) {
-            const size_t lds = residency_lds_bytes(kQ8StepWavesPerCU, kWave);
-            auto go = [&](auto ND) {
-                for_launches(len, [&](int64_t o, int64_t n) {
-                    const int64_t ob = o / kB, nbn = blocks_of(n);
-                    step_q8_kernel<kWave, ND.value, OV.value, SS.value>
-                        <<<grid_waves(nbn, kWave), kWave, lds, st>>>(
-                            gq + o, gscales + ob, ld, sld, n_dp, n, nbn, master + o, m + o,
-                            v + o, wq + o, wsc + ob, c, overflow,
-                            SS.value ? part + ob : nullptr);
-                });
-            };
-            if (n_dp == 1) go(IntC<1>{});
-            else if (n_dp == 8) go(IntC<8>{});
-            else go(IntC<0>{});
+            with_bool(dc != nullptr, [&](auto DV) {
+                const size_t lds = residency_lds_bytes(kQ8StepWavesPerCU, kWave);
+                auto go = [&](auto ND) {
+                    for_launches(len, [&](int64_t o, int64_t n) {
+                        const int64_t ob = o / kB, nbn = blocks_of(n);
+                        step_q8_kernel<kWave, ND.value, OV.value, SS.value, DV.value>
+                            <<<grid_waves(nbn, kWave), kWave, lds, st>>>(
+                                gq + o, gscales + ob, ld, sld, n_dp, n, nbn, master + o, m + o,
+                                v + o, wq + o, wsc + ob, c, overflow,
+                                SS.value ? part + ob : nullptr, dc);
+                    });
+                };
+                if (n_dp == 1) go(IntC<1>{});
+                else if (n_dp == 8) go(IntC<8>{});
+                else go(IntC<0>{});
+            });
         });
     });
     if (sumsq) {
@@ -742,4 +748,32 @@ extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales
         return finish_sumsq(workspace, nb, sumsq, st);
     }
     return launch_status();
+}
+
+}  // namespace
+
+extern "C" zero_status zero_shard_step_q8(const int8_t *gq, const float *gscales, int64_t ld,
+                                          int64_t sld, int64_t len, float *master, float *m,
+                                          float *v, int8_t *wq_full, float *wscales_full,
+                                          const zero_layout *layout, int32_t rank,
+                                          int64_t shard_off, const zero_adamw_hparams *hp,
+                                          uint32_t *overflow, double *sumsq, void *workspace,
+                                          int64_t workspace_bytes, void *stream) {
+    return step_q8_impl(gq, gscales, ld, sld, len, master, m, v, wq_full, wscales_full, layout,
+                        rank, shard_off, hp, nullptr, overflow, sumsq, workspace,
+                        workspace_bytes, stream);
+}
+
+extern "C" zero_status zero_shard_step_q8_dc(const int8_t *gq, const float *gscales,
+                                             int64_t ld, int64_t sld, int64_t len,
+                                             float *master, float *m, float *v, int8_t *wq_full,
+                                             float *wscales_full, const zero_layout *layout,
+                                             int32_t rank, int64_t shard_off,
+                                             const zero_step_consts *consts, uint32_t *overflow,
+                                             double *sumsq, void *workspace,
+                                             int64_t workspace_bytes, void *stream) {
+    if (!consts) return ZERO_EINVAL;
+    return step_q8_impl(gq, gscales, ld, sld, len, master, m, v, wq_full, wscales_full, layout,
+                        rank, shard_off, nullptr, consts, overflow, sumsq, workspace,
+                        workspace_bytes, stream);
 }
