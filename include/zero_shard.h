@@ -33,7 +33,10 @@
  *    and runs asynchronously: a call returns once its kernels are launched.
  *    Buffers must stay valid until the stream has passed them.
  *  - Arguments are validated on the host before anything is launched; on any
- *    error status nothing is launched and nothing is written.
+ *    error status nothing is launched and nothing is written.  (Values held
+ *    in device memory -- flags, sums, a loss scale, the step constants of
+ *    the _dc variants -- are read when the kernels run and used as they
+ *    are.)
  *  - Element counts and offsets are in elements, never bytes; one call
  *    processes at most 2^38 elements (EINVAL beyond), and a buffer or set of
  *    rows it addresses spans at most 2^60 elements (EINVAL beyond: a layout's
@@ -46,7 +49,8 @@
  *  - Arithmetic is IEEE binary32 with round-to-nearest-even, no fused
  *    multiply-add, correctly rounded division and square root, and no
  *    flushing of denormals; the scalars are formed on the host in double
- *    and rounded once to fp32 (see zero_adamw_hparams).
+ *    and rounded once to fp32 (see zero_adamw_hparams; the _dc variants
+ *    read them from device memory, formed by zero_step_consts_make).
  */
 #ifndef ZERO_SHARD_H
 #define ZERO_SHARD_H
