@@ -12,8 +12,10 @@ import pytest
 import torch
 
 import oracle
+import synth
 import zero_sharded_mixed_flatten_amd as zs
 from synth import BF16
+from synth.synth_const import BUF_GRAD
 from synth.workloads import GradDraw
 from tests.gpu_util import check_16, check_f32, dev16, devf, host16, host_master, host_rows, hostf
 
@@ -72,3 +74,40 @@ def test_two_streams_add_into_one_sum_and_flag():
             assert abs(ss.item() - o_ss[0]) <= 1e-10 * o_ss[0]
         else:
             assert not np.isfinite(ss.item()) and not np.isfinite(o_ss[0])
+
+
+def test_binding_workspace_lives_on_the_calls_stream():
+    """A sum of squares asked for on a side stream without a workspace: the
+    binding's temporary workspace is freed when the call returns, so it
+    must belong to the call's stream.  Right after the call the current
+    stream takes blocks of the same size and fills them with NaN while the
+    side stream's step is still running; the step's sum must still equal
+    the reduce's sum of the same rows over 64 (s = 1/8 is a power of two,
+    and the order of both sums is fixed by the length alone)."""
+    n_dp, S = 8, 1 << 26
+    lay, _ = zs.zero_flatten_layout([S * n_dp], n_dp)
+    rows = torch.empty((n_dp, S), dtype=torch.bfloat16, device="cuda")
+    for k in range(n_dp):
+        synth.fill_device(rows[k], BF16, 0, synth.tag(BUF_GRAD, 254, 1, 0, k), 0, 1e-3)
+    acc = torch.empty(S, dtype=torch.float32, device="cuda")
+    ref = torch.zeros(1, dtype=torch.float64, device="cuda")
+    zs.zero_shard_reduce(rows, n_dp, S, S, acc, sumsq=ref)
+    del acc
+    W = torch.zeros(S, device="cuda")
+    M, V = torch.zeros(S, device="cuda"), torch.zeros(S, device="cuda")
+    wf = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device="cuda")
+    ss = torch.zeros(1, dtype=torch.float64, device="cuda")
+    ws_elems = (zs.zero_sumsq_workspace_bytes(S) + 7) // 8
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        ss.zero_()
+        torch.cuda.synchronize()
+        zs.zero_shard_step(rows, S, S, W, M, V, wf, lay, 0,
+                           zs.AdamWHParams(step=1, grad_scale=1.0 / n_dp, **HP), sumsq=ss,
+                           stream=side)
+        junk = [torch.empty(ws_elems, dtype=torch.float64, device="cuda").fill_(float("nan"))
+                for _ in range(4)]
+        torch.cuda.synchronize()
+        del junk
+        assert ss.item() == ref.item() / 64.0

@@ -255,15 +255,30 @@ def zero_sumsq_workspace_bytes(length: int) -> int:
     return n
 
 
-def _workspace(sumsq, workspace, length: int, device):
+def _torch_stream(stream, device):
+    """The call's stream as a torch stream: the current one for None, a
+    torch stream as given, a raw hipStream_t handle wrapped."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _workspace(sumsq, workspace, length: int, device, stream=None):
     """(pointer, bytes) of the sum's workspace: the caller's (checked for
-    size) or a new one; (NULL, 0) without a sum."""
+    size) or a new one; (NULL, 0) without a sum.  A new one is allocated on
+    the call's stream: it is freed when the call returns, and torch's
+    allocator reuses a block only in the order of the stream it was
+    allocated on, so the call's kernels finish with it first."""
     import torch
     if sumsq is None:
         return None, 0
     need = zero_sumsq_workspace_bytes(max(0, length))
     if workspace is None:
-        workspace = torch.empty((need + 7) // 8, dtype=torch.float64, device=device)
+        with torch.cuda.stream(_torch_stream(stream, device)):
+            workspace = torch.empty((need + 7) // 8, dtype=torch.float64, device=device)
     nbytes = workspace.numel() * workspace.element_size()
     if nbytes < need:
         raise ValueError(f"workspace: {need} bytes needed, the tensor holds {nbytes}")
@@ -271,10 +286,7 @@ def _workspace(sumsq, workspace, length: int, device):
 
 
 def _stream(stream, like):
-    import torch
-    if stream is None:
-        stream = torch.cuda.current_stream(like.device)
-    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+    return ctypes.c_void_p(_torch_stream(stream, like.device).cuda_stream)
 
 
 # ---------------------------------------------------------------------------
@@ -352,7 +364,7 @@ def zero_shard_reduce(grads, n_contrib: int, ld: int, length: int, acc,
     zero_sumsq_workspace_bytes(length) bytes is passed)."""
     import torch
     d = acc.device
-    ws, ws_bytes = _workspace(sumsq, workspace, length, d)
+    ws, ws_bytes = _workspace(sumsq, workspace, length, d, stream)
     _check(_lib.zero_shard_reduce(
         _rows(grads, "grads", n_contrib, ld, length, device=d),
         _dtype_code(grads, "grads", True), n_contrib, ld, length,
@@ -434,7 +446,7 @@ def zero_shard_step(grads, ld: int, length: int, master, m, v, weight_full,
     import torch
     hpc = hp._c()
     d = master.device
-    ws, ws_bytes = _workspace(sumsq, workspace, length, d)
+    ws, ws_bytes = _workspace(sumsq, workspace, length, d, stream)
     _check(_lib.zero_shard_step(
         _rows(grads, "grads", layout.n_dp, ld, length, device=d),
         _dtype_code(grads, "grads", True), ld, length,
@@ -476,7 +488,7 @@ def zero_shard_step_dc(grads, ld: int, length: int, master, m, v, weight_full,
     (see zero_step_consts_make) when the kernels run."""
     import torch
     d = master.device
-    ws, ws_bytes = _workspace(sumsq, workspace, length, d)
+    ws, ws_bytes = _workspace(sumsq, workspace, length, d, stream)
     _check(_lib.zero_shard_step_dc(
         _rows(grads, "grads", layout.n_dp, ld, length, device=d),
         _dtype_code(grads, "grads", True), ld, length,
@@ -599,7 +611,7 @@ def zero_shard_step_q8(gq, gscales, ld: int, sld: int, length: int, master, m, v
     import torch
     hpc = hp._c()
     d = master.device
-    ws, ws_bytes = _workspace(sumsq, workspace, length, d)
+    ws, ws_bytes = _workspace(sumsq, workspace, length, d, stream)
     nb = q8_blocks(length)
     end = _slot_end(layout, rank, shard_off, length)
     _check(_lib.zero_shard_step_q8(
@@ -622,7 +634,7 @@ def zero_shard_step_q8_dc(gq, gscales, ld: int, sld: int, length: int, master, m
     consts (see zero_step_consts_make) when the kernels run."""
     import torch
     d = master.device
-    ws, ws_bytes = _workspace(sumsq, workspace, length, d)
+    ws, ws_bytes = _workspace(sumsq, workspace, length, d, stream)
     nb = q8_blocks(length)
     end = _slot_end(layout, rank, shard_off, length)
     _check(_lib.zero_shard_step_q8_dc(
