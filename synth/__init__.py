@@ -98,6 +98,7 @@ def _gpu_lib():
     if _gpu is None:
         if not os.path.exists(LIB_GPU):
             raise ImportError(f"{LIB_GPU} is not built: run synth/build.py")
+        import torch  # noqa: F401  (its HIP runtime first: one runtime per process)
         L = ctypes.CDLL(LIB_GPU)
         vp = ctypes.c_void_p
         L.syn_gpu_fill.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,

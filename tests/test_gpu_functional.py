@@ -64,6 +64,37 @@ def test_functional_step_matches_oracle(n_dp, kind):
         ws, ms, vs = ws2, ms2, vs2
 
 
+def test_functional_step_on_a_side_stream():
+    """Given a stream, the functional step runs (and allocates) there: its
+    results equal the same step on the current stream bit for bit, with
+    the current stream allocating and overwriting memory meanwhile."""
+    n_dp, n = 4, 1_000_003
+    pieces = np.array_split(np.arange(n), n_dp)
+    w0 = synth.fill_host(F32, 0, tag(BUF_MASTER, 141), 0, n, 0.02)
+    g_host = np.stack([synth.fill_host(F32, 0, tag(BUF_GRAD, 141, 1, 0, k), 0, n, 1e-3)
+                       for k in range(n_dp)])
+    grads = [torch.from_numpy(g_host[k].copy()).cuda() for k in range(n_dp)]
+
+    def state():
+        return ([torch.from_numpy(w0[p].copy()).cuda() for p in pieces],
+                [torch.zeros(p.size, device="cuda") for p in pieces],
+                [torch.zeros(p.size, device="cuda") for p in pieces])
+
+    ref = zs.zero_adam_step(grads, *state(), 1, **HP)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    st = state()
+    side.wait_stream(torch.cuda.current_stream())
+    got = zs.zero_adam_step(grads, *st, 1, stream=side, **HP)
+    junk = [torch.empty(n, device="cuda").fill_(float("nan")) for _ in range(8)]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    del junk
+    for a_list, b_list in zip(ref, got):
+        for a, b in zip(a_list, b_list):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 def test_functional_step_more_ranks_than_elements():
     """n < n_dp: array_split leaves some ranks an empty piece."""
     n, n_dp = 5, 8

@@ -32,6 +32,24 @@ def test_library_exports_every_declared_symbol():
     assert lib.zero_abi_version() == zs.ABI_VERSION
 
 
+def test_one_hip_runtime_whatever_the_import_order():
+    """torch ships its own HIP runtime; the package must bind to it even
+    when imported before torch, or the process holds two runtimes and
+    torch's streams are not valid in the library's (launches fail).  A
+    fresh process imports the package first, then torch, and must map one
+    libamdhip64 only."""
+    import subprocess
+    import sys
+    code = ("import zero_sharded_mixed_flatten_amd, torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'amdhip64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    maps = eval(r.stdout.strip().splitlines()[-1])
+    assert len(maps) == 1, maps
+
+
 def test_status_strings():
     lib = ctypes.CDLL(zs.library_path())
     lib.zero_status_string.restype = ctypes.c_char_p

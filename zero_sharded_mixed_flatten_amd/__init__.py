@@ -97,6 +97,11 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                           "(hipcc --offload-arch=gfx950) first")
+    # torch ships its own HIP runtime.  Loaded first, it is the one this
+    # library binds to (same soname); loaded after this library it would be
+    # a second runtime in the process, and torch's streams would not be
+    # valid in this library's (its launches would fail).
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
     lay_p = ctypes.POINTER(ZeroLayout)
@@ -665,7 +670,10 @@ def zero_adam_step(grads, w_shards, m_shards, v_shards, t: int, lr: float = 1e-3
     times fl(1/n_dp)); Adam with bias correction from t = 1 (AdamW with
     weight_decay > 0).  Every step runs in the library's kernels: the flat
     copies build the gradient slab, clone the shards and gather the full
-    weights; the reduce and AdamW kernels update each rank's piece."""
+    weights; the reduce and AdamW kernels update each rank's piece.  Every
+    tensor it allocates -- the temporaries and the results -- belongs to the
+    call's stream, where all its work runs, so the temporaries freed on
+    return are reused only after that work."""
     import torch
     n_dp = len(grads)
     if n_dp < 1 or not (len(w_shards) == len(m_shards) == len(v_shards) == n_dp):
@@ -681,6 +689,16 @@ def zero_adam_step(grads, w_shards, m_shards, v_shards, t: int, lr: float = 1e-3
             if x.numel() != lens[r] or x.dtype != torch.float32:
                 raise ValueError(f"zero_adam_step: shard {r} must be fp32 of {lens[r]} elements")
     dev = grads[0].device
+    with torch.cuda.stream(_torch_stream(stream, dev)):
+        return _adam_step_on(grads, w_shards, m_shards, v_shards, t, lr, b1, b2, eps,
+                             weight_decay, n_dp, n, lens, starts, dev)
+
+
+def _adam_step_on(grads, w_shards, m_shards, v_shards, t, lr, b1, b2, eps, weight_decay, n_dp,
+                  n, lens, starts, dev):
+    """zero_adam_step's work, on the current stream."""
+    import torch
+    stream = None
     # the contributions as one [n_dp][n] slab (row k = rank k's gradient)
     slab = torch.empty(n_dp * n, dtype=grads[0].dtype, device=dev)
     zero_flat_gather([(g.reshape(-1), k * n) for k, g in enumerate(grads)], n_dp * n, 0, slab,
