@@ -389,6 +389,28 @@ ZERO_API zero_status zero_shard_step_dc(const void *grads, zero_dtype gdt, int64
                                         uint32_t *overflow, double *sumsq, void *workspace,
                                         int64_t workspace_bytes, void *stream);
 
+/* A step counter on the device, so that a replayed graph needs no host
+ * write at all between steps: the host fills a device table with the
+ * constants of steps 1..count (zero_step_consts_make for each), and the
+ * graph begins with zero_step_consts_select (consts = the row of step *t)
+ * and ends with zero_step_counter_advance (t = t + 1 unless the step was
+ * skipped), the step number staying put after an overflow exactly as
+ * zero_shard_adamw's skip leaves the state.
+ *   select:  one thread copies table[*t - 1] to *consts when 1 <= *t <=
+ *            count; any other *t writes constants that are all NaN (a step
+ *            run with them turns the state to NaN rather than reusing an
+ *            earlier step's constants).  consts, table: device, 8-byte
+ *            aligned; t: device int64.
+ *   advance: *t = *t + 1 unless skip is given and *skip != 0 (read when
+ *            the kernel runs).  t: device int64; skip: device uint32 or
+ *            NULL.
+ * EINVAL: a NULL required pointer, unaligned consts or table, count < 1.
+ * EALIAS: consts overlaps the table or t; t overlaps skip. */
+ZERO_API zero_status zero_step_consts_select(zero_step_consts *consts,
+                                             const zero_step_consts *table, int64_t count,
+                                             const int64_t *t, void *stream);
+ZERO_API zero_status zero_step_counter_advance(int64_t *t, const uint32_t *skip, void *stream);
+
 /* zero_shard_adamw_ex with its constants read from consts (as for
  * zero_shard_step_dc; with a loss scale, s = fl(consts->grad_scale /
  * scale)).  Errors as for zero_shard_adamw_ex without the hyperparameter

@@ -217,3 +217,93 @@ def test_stage2_graph_holds_the_step_back_after_an_overflow():
         if not skipped:
             t += 1
     assert taken == [1, 2, 3, 3, 4, 5]
+
+
+def test_stage2_graph_with_a_device_step_counter():
+    """The stage-2 graph with the step counter on the device: it begins by
+    selecting step t's constants from a table (steps 1..8) and ends by
+    advancing t unless the overflow flag skipped the step, so the host
+    writes neither constants nor t between replays -- only the next
+    micro-batches' gradients.  An infinity in iteration 2 must skip that
+    step and hold t at 3 for iteration 3; every iteration equals the
+    oracle's bit for bit, and the device counter ends at 6."""
+    n_dp, rank, S, micro = 4, 2, 50_000, 2
+    lay, _ = zs.zero_flatten_layout([S * n_dp], n_dp)
+    draw = GradDraw(F16, 1e-3, scale=65536.0)
+    w = host_master(249, rank * S, S)
+    m, v = np.zeros(S, np.float32), np.zeros(S, np.float32)
+    wout = np.zeros(lay.n_pad, np.uint16)
+    gb = [torch.zeros(n_dp * S, dtype=torch.float16, device="cuda") for _ in range(micro)]
+    acc = torch.zeros(S, dtype=torch.float32, device="cuda")
+    W, M, V = devf(w), devf(m), devf(v)
+    wf = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dls = zs.new_loss_scale(65536.0)
+    gs = 1.0 / (n_dp * micro)
+    table = zs.step_consts_table([zs.AdamWHParams(step=k, grad_scale=gs, **HP)
+                                  for k in range(1, 9)])
+    counter = zs.new_step_counter(1)
+    consts = zs.new_step_consts()
+    o_scale, o_good = np.array([65536.0], np.float32), np.zeros(1, np.int32)
+    o_acc = np.zeros(S, np.float32)
+
+    def step(stream):
+        zs.zero_step_consts_select(consts, table, counter, stream=stream)
+        flag.zero_()
+        for mb in range(micro):
+            zs.zero_shard_reduce(gb[mb], n_dp, S, S, acc, accumulate=mb > 0, overflow=flag,
+                                 stream=stream)
+        zs.zero_shard_adamw_dc(acc, W, M, V, wf, lay, rank, consts, skip=flag, loss_scale=dls,
+                               stream=stream)
+        zs.zero_loss_scale_update(dls, flag, 2.0, 0.5, 3, stream=stream)
+        zs.zero_step_counter_advance(counter, skip=flag, stream=stream)
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert int(counter.item()) == 1  # capture ran nothing
+    t = 1
+    for it in range(6):
+        rows = [host_rows(249, it + 1, mb, n_dp, rank * S, S, draw) for mb in range(micro)]
+        if it == 2:
+            rows[0][1, 4321] = 0x7C00                  # fp16 +inf in the first micro-batch
+        for mb in range(micro):
+            gb[mb].copy_(dev16(rows[mb], zs.ZERO_FP16).reshape(-1))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_flag = np.zeros(1, np.uint32)
+        for mb in range(micro):
+            oracle.reduce(rows[mb], oracle.FP16, n_dp, S, S, o_acc, int(mb > 0), overflow=o_flag)
+        slot = wout[rank * S:(rank + 1) * S].copy()
+        oracle.adamw_ex(o_acc, w, m, v, slot, oracle.BF16, S, t, grad_scale=gs, skip=o_flag,
+                        loss_scale=o_scale.copy(), **HP)
+        wout[rank * S:(rank + 1) * S] = slot
+        oracle.loss_scale_update(o_scale, o_good, int(o_flag[0]), 2.0, 0.5, 3)
+        if not o_flag[0]:
+            t += 1
+        assert bool(o_flag[0]) == (it == 2) and int(flag.item()) == int(o_flag[0])
+        assert int(counter.item()) == t, f"iteration {it}"
+        for name, got, want in (("master", hostf(W), w), ("m", hostf(M), m), ("v", hostf(V), v)):
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"it={it}: {name}"
+        assert np.array_equal(host16(wf), wout), f"it={it}: weights"
+        assert zs.read_loss_scale(dls) == (float(o_scale[0]), int(o_good[0])), f"it={it}"
+    assert t == 6
+
+
+def test_step_beyond_the_table_selects_nan_constants():
+    table = zs.step_consts_table([zs.AdamWHParams(step=k) for k in (1, 2)])
+    consts = zs.new_step_consts()
+    for k, want in ((1, 0), (2, 1), (0, None), (3, None), (-5, None)):
+        zs.zero_step_consts_select(consts, table, zs.new_step_counter(k))
+        got = consts.cpu().numpy()
+        if want is None:
+            assert np.all(np.isnan(got[:40].view(np.float32))) and np.isnan(got[40:].view(np.float64)[0])
+        else:
+            assert np.array_equal(got, table[want].cpu().numpy())

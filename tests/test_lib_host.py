@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     lib = ctypes.CDLL(zs.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -320,6 +320,17 @@ def test_device_consts_entry_points_reject_bad_arguments():
     assert A(*base, P(BASE + (5 << 30) + 4), None, None) == zs.ZERO_EINVAL
     assert A(*base, P(BASE + (3 << 30) + 400), None, None) == zs.ZERO_EALIAS  # inside v
     lay8 = zs.zero_flatten_layout([8 * 4096], 8, 256)[0]
+    C, V_ = L.zero_step_consts_select, L.zero_step_counter_advance
+    tab, cnt, ctr = P(BASE + (8 << 30)), 10, P(BASE + (9 << 30))
+    assert C(None, tab, cnt, ctr, None) == zs.ZERO_EINVAL
+    assert C(P(BASE + (7 << 30)), None, cnt, ctr, None) == zs.ZERO_EINVAL
+    assert C(P(BASE + (7 << 30)), tab, 0, ctr, None) == zs.ZERO_EINVAL          # empty table
+    assert C(P(BASE + (7 << 30)), tab, cnt, None, None) == zs.ZERO_EINVAL
+    assert C(P(BASE + (7 << 30) + 4), tab, cnt, ctr, None) == zs.ZERO_EINVAL    # unaligned
+    assert C(P(BASE + (8 << 30) + 96), tab, cnt, ctr, None) == zs.ZERO_EALIAS   # inside the table
+    assert C(P(BASE + (9 << 30) - 8), tab, cnt, ctr, None) == zs.ZERO_EALIAS    # over the counter
+    assert V_(None, None, None) == zs.ZERO_EINVAL
+    assert V_(ctr, P(BASE + (9 << 30) + 4), None) == zs.ZERO_EALIAS             # flag in counter
     Q = L.zero_shard_step_q8_dc
     q8 = [P(BASE), P(BASE + (1 << 28)), 4096, 16, 4096, P(BASE + (2 << 28)), P(BASE + (3 << 28)),
           P(BASE + (4 << 28)), P(BASE + (5 << 28)), P(BASE + (6 << 28)), ctypes.byref(lay8), 1, 0]

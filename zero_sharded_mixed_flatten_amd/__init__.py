@@ -142,6 +142,10 @@ def _load():
     L.zero_shard_adamw_dc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, lay_p, i32, i64, i64,
                                       vp, ctypes.POINTER(_StepControl), vp]
     L.zero_shard_adamw_dc.restype = ctypes.c_int
+    L.zero_step_consts_select.argtypes = [vp, vp, i64, vp, vp]
+    L.zero_step_consts_select.restype = ctypes.c_int
+    L.zero_step_counter_advance.argtypes = [vp, vp, vp]
+    L.zero_step_counter_advance.restype = ctypes.c_int
     piece_p = ctypes.POINTER(_Piece)
     L.zero_flat_gather.argtypes = [piece_p, i32, i64, i32, i64, i64, vp, vp]
     L.zero_flat_gather.restype = ctypes.c_int
@@ -479,6 +483,42 @@ def new_step_consts(device="cuda"):
     """A device buffer for one zero_step_consts (uint8[48])."""
     import torch
     return torch.zeros(ctypes.sizeof(ZeroStepConsts), dtype=torch.uint8, device=device)
+
+
+def step_consts_table(hps, device="cuda"):
+    """A device table of step constants, row k those of hps[k] (for the
+    device counter, row k serves step k + 1): uint8[len(hps)][48]."""
+    import torch
+    rows = np.stack([zero_step_consts_make(hp) for hp in hps])
+    return torch.from_numpy(rows).to(device)
+
+
+def new_step_counter(t: int = 1, device="cuda"):
+    """A device step counter (int64[1]) holding t."""
+    import torch
+    return torch.tensor([int(t)], dtype=torch.int64, device=device)
+
+
+def zero_step_consts_select(consts, table, t, stream=None):
+    """consts = table[*t - 1] on the device (all NaN when *t is outside the
+    table's rows)."""
+    import torch
+    d = consts.device
+    if table.dim() != 2 or table.shape[1] != ctypes.sizeof(ZeroStepConsts):
+        raise ValueError("zero_step_consts_select: table must be uint8[count][48]")
+    count = table.shape[0]
+    _check(_lib.zero_step_consts_select(
+        _consts(consts, d), _buf(table, "table", count * ctypes.sizeof(ZeroStepConsts),
+                                 torch.uint8, d), count,
+        _buf(t, "t", 1, torch.int64, d), _stream(stream, consts)), "zero_step_consts_select")
+
+
+def zero_step_counter_advance(t, skip=None, stream=None):
+    """*t += 1 on the device unless skip (int32 flag) is non-zero."""
+    import torch
+    _check(_lib.zero_step_counter_advance(
+        _buf(t, "t", 1, torch.int64), _buf(skip, "skip", 1, torch.int32, t.device),
+        _stream(stream, t)), "zero_step_counter_advance")
 
 
 def _consts(consts, device):

@@ -374,6 +374,27 @@ adamw_scalar_kernel(const float *__restrict__ acc, float *__restrict__ W, float 
     }
 }
 
+// The constants of step *t from a table of steps 1..count (one thread);
+// NaN constants for a step outside the table.
+__global__ void step_consts_select_kernel(zero_step_consts *__restrict__ out,
+                                          const zero_step_consts *__restrict__ table,
+                                          int64_t count, const int64_t *__restrict__ t) {
+    const int64_t k = *t;
+    if (k >= 1 && k <= count) {
+        *out = table[k - 1];
+    } else {
+        const float nan = __builtin_nanf("");
+        *out = zero_step_consts{nan, nan, nan, nan, nan, nan, nan, nan, nan, nan,
+                                __builtin_nan("")};
+    }
+}
+
+// t = t + 1 unless the step was skipped (one thread)
+__global__ void step_counter_advance_kernel(int64_t *__restrict__ t,
+                                            const uint32_t *__restrict__ skip) {
+    if (skip == nullptr || *skip == 0u) *t = *t + 1;
+}
+
 // One step of the dynamic loss scale (one thread).
 __global__ void loss_scale_kernel(zero_loss_scale *__restrict__ st,
                                   const uint32_t *__restrict__ overflow, double growth,
@@ -720,6 +741,28 @@ extern "C" zero_status zero_shard_adamw_dc(const float *acc, float *master, floa
     if (!consts) return ZERO_EINVAL;
     return adamw_impl(acc, master, m, v, weight_full, wdt, layout, rank, shard_off, len, nullptr,
                       consts, ctl, stream);
+}
+
+extern "C" zero_status zero_step_consts_select(zero_step_consts *consts,
+                                               const zero_step_consts *table, int64_t count,
+                                               const int64_t *t, void *stream) {
+    if (!consts || !table || !t || count < 1 || !aligned8(consts) || !aligned8(table))
+        return ZERO_EINVAL;
+    if (count > INT64_MAX / static_cast<int64_t>(sizeof(zero_step_consts))) return ZERO_EINVAL;
+    const Span out = span_of(consts, 1, sizeof(zero_step_consts));
+    if (overlap(out, span_of(table, count, sizeof(zero_step_consts))) ||
+        overlap(out, span_of(t, 1, sizeof(int64_t))))
+        return ZERO_EALIAS;
+    step_consts_select_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(consts, table, count,
+                                                                             t);
+    return launch_status();
+}
+
+extern "C" zero_status zero_step_counter_advance(int64_t *t, const uint32_t *skip, void *stream) {
+    if (!t) return ZERO_EINVAL;
+    if (skip && overlap(span_of(t, 1, sizeof(int64_t)), span_of(skip, 1, 4))) return ZERO_EALIAS;
+    step_counter_advance_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(t, skip);
+    return launch_status();
 }
 
 extern "C" zero_status zero_step_consts_make(const zero_adamw_hparams *hp, zero_step_consts *out) {
