@@ -307,3 +307,13 @@ def test_step_beyond_the_table_selects_nan_constants():
             assert np.all(np.isnan(got[:40].view(np.float32))) and np.isnan(got[40:].view(np.float64)[0])
         else:
             assert np.array_equal(got, table[want].cpu().numpy())
+
+
+def test_counter_advances_unless_skipped():
+    t = zs.new_step_counter(41)
+    zs.zero_step_counter_advance(t)                                    # no flag: advance
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zero_step_counter_advance(t, skip=flag)                         # flag clear: advance
+    flag.fill_(1)
+    zs.zero_step_counter_advance(t, skip=flag)                         # flag set: hold
+    assert int(t.item()) == 43
