@@ -400,11 +400,11 @@ ZERO_API zero_status zero_shard_step_dc(const void *grads, zero_dtype gdt, int64
  *            count; any other *t writes constants that are all NaN (a step
  *            run with them turns the state to NaN rather than reusing an
  *            earlier step's constants).  consts, table: device, 8-byte
- *            aligned; t: device int64.
+ *            aligned; t: device int64, 8-byte aligned.
  *   advance: *t = *t + 1 unless skip is given and *skip != 0 (read when
- *            the kernel runs).  t: device int64; skip: device uint32 or
- *            NULL.
- * EINVAL: a NULL required pointer, unaligned consts or table, count < 1.
+ *            the kernel runs).  t: device int64, 8-byte aligned; skip:
+ *            device uint32 or NULL.
+ * EINVAL: a NULL required pointer, unaligned consts, table or t, count < 1.
  * EALIAS: consts overlaps the table or t; t overlaps skip. */
 ZERO_API zero_status zero_step_consts_select(zero_step_consts *consts,
                                              const zero_step_consts *table, int64_t count,

@@ -329,7 +329,9 @@ def test_device_consts_entry_points_reject_bad_arguments():
     assert C(P(BASE + (7 << 30) + 4), tab, cnt, ctr, None) == zs.ZERO_EINVAL    # unaligned
     assert C(P(BASE + (8 << 30) + 96), tab, cnt, ctr, None) == zs.ZERO_EALIAS   # inside the table
     assert C(P(BASE + (9 << 30) - 8), tab, cnt, ctr, None) == zs.ZERO_EALIAS    # over the counter
+    assert C(P(BASE + (7 << 30)), tab, cnt, P(BASE + (9 << 30) + 4), None) == zs.ZERO_EINVAL
     assert V_(None, None, None) == zs.ZERO_EINVAL
+    assert V_(P(BASE + (9 << 30) + 4), None, None) == zs.ZERO_EINVAL           # unaligned counter
     assert V_(ctr, P(BASE + (9 << 30) + 4), None) == zs.ZERO_EALIAS             # flag in counter
     Q = L.zero_shard_step_q8_dc
     q8 = [P(BASE), P(BASE + (1 << 28)), 4096, 16, 4096, P(BASE + (2 << 28)), P(BASE + (3 << 28)),

@@ -746,7 +746,8 @@ extern "C" zero_status zero_shard_adamw_dc(const float *acc, float *master, floa
 extern "C" zero_status zero_step_consts_select(zero_step_consts *consts,
                                                const zero_step_consts *table, int64_t count,
                                                const int64_t *t, void *stream) {
-    if (!consts || !table || !t || count < 1 || !aligned8(consts) || !aligned8(table))
+    if (!consts || !table || !t || count < 1 || !aligned8(consts) || !aligned8(table) ||
+        !aligned8(t))
         return ZERO_EINVAL;
     if (count > INT64_MAX / static_cast<int64_t>(sizeof(zero_step_consts))) return ZERO_EINVAL;
     const Span out = span_of(consts, 1, sizeof(zero_step_consts));
@@ -759,7 +760,7 @@ extern "C" zero_status zero_step_consts_select(zero_step_consts *consts,
 }
 
 extern "C" zero_status zero_step_counter_advance(int64_t *t, const uint32_t *skip, void *stream) {
-    if (!t) return ZERO_EINVAL;
+    if (!t || !aligned8(t)) return ZERO_EINVAL;
     if (skip && overlap(span_of(t, 1, sizeof(int64_t)), span_of(skip, 1, 4))) return ZERO_EALIAS;
     step_counter_advance_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(t, skip);
     return launch_status();
