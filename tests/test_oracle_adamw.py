@@ -79,6 +79,65 @@ def test_matches_torch_adamw_single_rank(wd):
     assert np.array_equal(wout, ref16)
 
 
+@pytest.mark.parametrize("n_dp", [1, 3, 8])
+def test_matches_a_numpy_transcription_of_the_pages_sharded_step(n_dp):
+    """"ZeRO and FSDP", A sharded Adam step, written out in NumPy float32 from
+    its prose: the ranks' gradients averaged (summed over ranks in order,
+    divided by n_dp), Adam with bias correction from t = 1 on the whole
+    vector -- the pieces of numpy.array_split updated independently are
+    the same update.  The constants are formed as the stated reading does
+    (in double, rounded once; beta^t from the C library's pow through
+    Python) and the update grouped as documented, lr * (mhat / (sqrt(vhat)
+    + eps)).  Independent code, the same rounding at each operation: the
+    oracle's reduce and AdamW per piece (wd = 0, grad_scale = fl(1/n_dp))
+    must agree bit for bit wherever fl(1/n_dp) is exact (n_dp = 1, 8), and
+    for n_dp = 3 -- where dividing and multiplying by the rounded reciprocal
+    differ in the last bit -- within a few roundings."""
+    n, steps = 5003, 5
+    lr, b1, b2, eps = 1e-3, 0.9, 0.999, 1e-8
+    f32 = np.float32
+    w0 = _master(n, 59)
+    W, Mn, Vn = w0.copy(), np.zeros(n, f32), np.zeros(n, f32)
+    pieces = np.array_split(np.arange(n), n_dp)
+    ow = [w0[p].copy() for p in pieces]
+    om = [np.zeros(p.size, f32) for p in pieces]
+    ov = [np.zeros(p.size, f32) for p in pieces]
+    c1, c2 = f32(1.0 - b1), f32(1.0 - b2)
+    mag = np.zeros(n)  # running sum of |terms| that make up m (m itself may cancel)
+    for t in range(1, steps + 1):
+        bc1, bc2 = f32(1.0 - b1 ** t), f32(1.0 - b2 ** t)
+        rows = _grads(n_dp, n, t, 59)
+        x = oracle.bf16_to_f32(rows)
+        G = x[0].copy()
+        for k in range(1, n_dp):
+            G = (G + x[k]).astype(f32)
+        G = (G / f32(n_dp)).astype(f32)
+        mag = b1 * mag + (1 - b1) * np.abs(G.astype(np.float64))
+        Mn = (f32(b1) * Mn + c1 * G).astype(f32)
+        Vn = (f32(b2) * Vn + c2 * (G * G)).astype(f32)
+        mhat, vhat = (Mn / bc1).astype(f32), (Vn / bc2).astype(f32)
+        W = (W - f32(lr) * (mhat / (np.sqrt(vhat) + f32(eps)))).astype(f32)
+        for r, p in enumerate(pieces):
+            if p.size == 0:
+                continue
+            acc = np.zeros(p.size, f32)
+            oracle.reduce(np.ascontiguousarray(rows[:, p]), oracle.BF16, n_dp, p.size, p.size,
+                          acc, 0)
+            wo = np.zeros(p.size, np.uint16)
+            oracle.adamw(acc, ow[r], om[r], ov[r], wo, oracle.BF16, p.size, t, lr=lr, beta1=b1,
+                         beta2=b2, eps=eps, weight_decay=0.0, grad_scale=1.0 / n_dp)
+        w, m, v = np.concatenate(ow), np.concatenate(om), np.concatenate(ov)
+        if n_dp in (1, 8):
+            for a, b in ((w, W), (m, Mn), (v, Vn)):
+                assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"t={t}"
+        else:
+            # g differs by at most an ulp; m and v carry it (a few roundings
+            # per step), the update by a relative few ulps
+            assert np.all(np.abs(m - Mn) <= 8 * U * t * mag)
+            assert np.all(np.abs(v - Vn) <= 8 * U * t * np.abs(Vn) + 1e-30)
+            assert np.all(np.abs(w - W) <= t * (4 * U * np.abs(W) + lr * 1e-6))
+
+
 # ---------------------------------------------------------------------------
 # closed forms
 
