@@ -85,8 +85,14 @@ def test_random_step(seed):
         hp = zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **HP)
         d_ovf = torch.zeros(1, dtype=torch.int32, device="cuda") if c["ovf"] else None
         d_ss = torch.zeros(1, dtype=torch.float64, device="cuda") if c["ssq"] else None
-        zs.zero_shard_step(g, ld, L, dw, dm, dv, dwf, lay, c["rank"], hp, shard_off=off,
-                           overflow=d_ovf, sumsq=d_ss)
+        if seed % 2:  # odd seeds: the constants from a device buffer
+            consts = zs.new_step_consts()
+            consts.copy_(torch.from_numpy(zs.zero_step_consts_make(hp)))
+            zs.zero_shard_step_dc(g, ld, L, dw, dm, dv, dwf, lay, c["rank"], consts,
+                                  shard_off=off, overflow=d_ovf, sumsq=d_ss)
+        else:
+            zs.zero_shard_step(g, ld, L, dw, dm, dv, dwf, lay, c["rank"], hp, shard_off=off,
+                               overflow=d_ovf, sumsq=d_ss)
         o_ovf, o_ss = np.zeros(1, np.uint32), np.zeros(1)
         slot = wout[lo:lo + L].copy()
         if L > 0:
@@ -242,7 +248,13 @@ def test_random_adamw(seed):
     o_ls = np.array([scale], np.float32) if scale is not None else None
     for t in (1, 2):
         hp = zs.AdamWHParams(step=t, grad_scale=gs, **HP)
-        if ex:
+        if ex and seed % 2:  # odd seeds: the constants from a device buffer
+            consts = zs.new_step_consts()
+            consts.copy_(torch.from_numpy(zs.zero_step_consts_make(hp)))
+            zs.zero_shard_adamw_dc(dacc, dw, dm, dv, dwf, lay, c["rank"], consts, shard_off=off,
+                                   length=L, skip=d_skip, sumsq=d_ss, max_norm=max_norm,
+                                   loss_scale=d_ls)
+        elif ex:
             zs.zero_shard_adamw_ex(dacc, dw, dm, dv, dwf, lay, c["rank"], hp, shard_off=off,
                                    length=L, skip=d_skip, sumsq=d_ss, max_norm=max_norm,
                                    loss_scale=d_ls)
