@@ -105,3 +105,48 @@ def test_reshard_validation(n_src, src_shard, n, eb, dst_rank, dst_shard):
     if s in (zs.ZERO_OK, zs.ZERO_EDEVICE) and dst_shard > 0:
         assert n_src >= 1 and src_shard >= 0 and 0 <= n <= n_src * src_shard
         assert eb in (2, 4) and dst_rank >= 0 and dst_shard <= (1 << 38)
+
+
+@cpu_only
+@settings(max_examples=500, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(data=st.data())
+def test_q8_step_validation(data):
+    B = zs.ZERO_Q8_BLOCK
+    n_dp = data.draw(st.integers(1, 64))
+    shard = B * data.draw(st.integers(0, 4096))
+    lay = zs.ZeroLayout(shard * n_dp, shard * n_dp, shard, B, n_dp, 0)
+    rank = data.draw(st.integers(0, n_dp - 1))
+    shard_off = B * data.draw(st.integers(0, shard // B))
+    length = data.draw(st.integers(0, shard - shard_off))
+    nb = -(-length // B)
+    ld = length + 4 * data.draw(st.integers(0, 16)) + (4 - length % 4) % 4
+    sld = nb + data.draw(st.integers(0, 4))
+    field = data.draw(st.sampled_from(["none", "none", "ld", "sld", "length", "shard_off",
+                                       "rank", "shard"]))
+    extreme = data.draw(I64)
+    if field == "ld":
+        ld = extreme
+    elif field == "sld":
+        sld = extreme
+    elif field == "length":
+        length = extreme
+    elif field == "shard_off":
+        shard_off = extreme
+    elif field == "rank":
+        rank = max(-(1 << 31), min((1 << 31) - 1, extreme))
+    elif field == "shard":
+        lay.shard = extreme
+    hp = zs.AdamWHParams()._c()
+    s = L.zero_shard_step_q8(P(_spread(1)), P(_spread(2)), ld, sld, length, P(_spread(3)),
+                             P(_spread(4)), P(_spread(5)), P(_spread(6)), P(_spread(7)),
+                             ctypes.byref(lay), rank, shard_off, ctypes.byref(hp), None, None,
+                             None, 0, None)
+    assert s in STATUSES
+    event(f"status {s}")
+    if s in (zs.ZERO_OK, zs.ZERO_EDEVICE) and length > 0:
+        nbl = -(-length // B)
+        assert 0 < length <= (1 << 38) and ld >= length and 0 <= rank < n_dp
+        assert lay.shard % B == 0 and shard_off % B == 0 and shard_off + length <= lay.shard
+        if n_dp > 1:
+            assert ld % 4 == 0 and sld >= nbl
+            assert (n_dp - 1) * ld + length <= (1 << 60) and (n_dp - 1) * sld + nbl <= (1 << 60)
