@@ -150,3 +150,35 @@ def test_q8_step_validation(data):
         if n_dp > 1:
             assert ld % 4 == 0 and sld >= nbl
             assert (n_dp - 1) * ld + length <= (1 << 60) and (n_dp - 1) * sld + nbl <= (1 << 60)
+
+
+@cpu_only
+@settings(max_examples=400, deadline=None)
+@given(data=st.data())
+def test_flat_gather_validation(data):
+    """Pieces with random (sometimes overlapping, negative or huge) flat
+    ranges: a gather that gets through has pieces disjoint in flat index,
+    non-negative fields without index overflow, and a count within 2^38."""
+    k = data.draw(st.integers(0, 6))
+    raw = []
+    for i in range(k):
+        off = data.draw(st.one_of(st.integers(0, 5000), I64))
+        ln = data.draw(st.one_of(st.integers(0, 3000), I64))
+        raw.append((off, ln))
+    pieces = (zs._Piece * max(k, 1))()
+    for i, (off, ln) in enumerate(raw):
+        pieces[i] = zs._Piece(_spread(2 + i), off, ln)
+    n = data.draw(st.one_of(st.integers(0, 10000), I64))
+    begin = data.draw(st.one_of(st.integers(0, 10000), I64))
+    count = data.draw(st.one_of(st.integers(0, 10000), I64))
+    eb = data.draw(st.sampled_from([2, 4, 3, 0]))
+    s = L.zero_flat_gather(pieces, k, n, eb, begin, count, P(_spread(1)), None)
+    assert s in STATUSES
+    event(f"status {s}")
+    if s in (zs.ZERO_OK, zs.ZERO_EDEVICE):
+        assert eb in (2, 4) and n >= 0 and begin >= 0 and 0 <= count <= (1 << 38)
+        live = sorted((off, ln) for off, ln in raw if ln > 0)
+        for off, ln in live:
+            assert off >= 0 and ln <= ((1 << 63) - 1) // 4 and off + ln < (1 << 63)
+        for (o1, l1), (o2, _) in zip(live, live[1:]):
+            assert o1 + l1 <= o2
