@@ -317,3 +317,40 @@ def test_counter_advances_unless_skipped():
     flag.fill_(1)
     zs.zero_step_counter_advance(t, skip=flag)                         # flag set: hold
     assert int(t.item()) == 43
+
+
+def test_device_constants_keep_grad_scale_in_double():
+    """With a dynamic loss scale, s = fl(grad_scale / scale) is formed from
+    the double grad_scale: for grad_scale = 1/12 (not an fp32 value) the
+    device-constant AdamW must equal the hp-taking one bit for bit, which it
+    would not if it divided the fp32-rounded scale instead."""
+    S, gs, scale = 40_000, 1.0 / 12, 65535.0
+    # the two readings of s differ for these values (a power-of-two scale
+    # would not tell them apart: dividing by it commutes with rounding)
+    assert np.float32(gs / scale) != np.float32(float(np.float32(gs)) / scale)
+    lay, _ = zs.zero_flatten_layout([S], 1)
+    acc = devf(host_master(248, 0, S, sigma=1e-3 * scale))
+    outs = []
+    for dc in (False, True):
+        W, M, V = devf(host_master(247, 0, S)), torch.zeros(S, device="cuda"), torch.zeros(S, device="cuda")
+        wf = torch.zeros(S, dtype=torch.bfloat16, device="cuda")
+        ls = zs.new_loss_scale(scale)
+        for t in (1, 2):
+            hp = zs.AdamWHParams(step=t, grad_scale=gs, **HP)
+            if dc:
+                consts = zs.new_step_consts()
+                consts.copy_(torch.from_numpy(zs.zero_step_consts_make(hp)))
+                zs.zero_shard_adamw_dc(acc, W, M, V, wf, lay, 0, consts, loss_scale=ls)
+            else:
+                zs.zero_shard_adamw_ex(acc, W, M, V, wf, lay, 0, hp, loss_scale=ls)
+        torch.cuda.synchronize()
+        outs.append([hostf(W), hostf(M), hostf(V), host16(wf)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    # and the oracle agrees
+    w, m, v = host_master(247, 0, S), np.zeros(S, np.float32), np.zeros(S, np.float32)
+    wo = np.zeros(S, np.uint16)
+    for t in (1, 2):
+        oracle.adamw_ex(hostf(acc), w, m, v, wo, oracle.BF16, S, t, grad_scale=gs,
+                        loss_scale=np.array([scale], np.float32), **HP)
+    assert np.array_equal(outs[0][0].view(np.uint32), w.view(np.uint32))
