@@ -47,11 +47,10 @@ constexpr int kRowBatchQ8 = 8;          // rows per batch when n_dp is not speci
 // The fused 8-bit step carries ~125 VALU operations per element (AdamW's
 // divisions and square root, 8 dequantizations, the quantization) against
 // 33 bytes: it needs more waves than the 16-bit step to hide that work under
-// memory time.  Measured on the 7B shard (8 rows, random data), waves per
-// CU, with the whole-block body templated and wave-uniform bases: 12 ->
-// 80.0 %, 16 -> 79.4 %, 20 -> 79.3 % (with per-lane tests and 64-bit lane
-// addresses it was 12 -> 76.4 %, 16 -> 78.4 %, 32 -> 75.0 %).
-constexpr int kQ8StepWavesPerCU = 12;   // residency cap of the fused 8-bit step
+// memory time, but not too many.  Measured on the 7B shard (8 rows, random
+// data, one process, same buffers), waves per CU: 8 -> 4.81 ms, 9 -> 4.56,
+// 10 -> 4.41, 11 -> 4.45, 12 -> 4.53, 14 -> 4.56-4.57.
+constexpr int kQ8StepWavesPerCU = 10;   // residency cap of the fused 8-bit step
 // Quantize and dequantize to fp32: Q blocks per wave, loads first.  Sweep on
 // the 7B shard (blocks per wave x waves per CU), quantize fp32 -> int8 +
 // scales: 1 x 32 -> 0.79 ms, 2 x 24 -> 0.67, 2 x 32 -> 0.63, 4 x 16 -> 0.68,
