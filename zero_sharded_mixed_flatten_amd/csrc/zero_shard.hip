@@ -62,13 +62,13 @@ constexpr int kRowBatch = 8;    // rows loaded together when n_dp is not special
 // (79.6 % of 8 TB/s against 78.7 % at 7 and 76.9 % uncapped, random data).
 // The summing variants carry a double accumulation per element and store a
 // partial per wave; swept separately (7B shard; GPT-2-XL list for 1 row):
-// 1 row 10 -> 79.2 %, 12 -> 82.3 %, 14 -> 80.9 %; 8 rows 7 -> 77.8 %,
-// 8 -> 81.0 %, 10 -> 80.8 %; 64 rows 12 -> 72.6 %, 16 -> 72.4 %; 8 fp32
+// 1 row 10 -> 79.2 %, 12 -> 82.3 %, 14 -> 80.9 %; 8 rows 7 -> 77.2 %,
+// 8 -> 80.3 %, 9 -> 81.4-81.7 %, 10 -> 80.8 %; 64 rows 12 -> 72.6 %, 16 -> 72.4 %; 8 fp32
 // rows 5 -> 78.6 %, 6 -> 80.9 %, 7 -> 80.9 %; the accumulating fp16 reduce
 // 10 -> 82.2 %, 12 -> 83.9 %, 16 -> 80.9 %.
 constexpr int step_waves_per_cu(int gdt, int ndp, bool ssq = false) {
     if (gdt == ZERO_FP32) return ndp == 1 ? 10 : ssq ? 6 : 5;
-    if (ssq) return ndp == 1 || ndp == 64 ? 12 : 8;
+    if (ssq) return ndp == 1 || ndp == 64 ? 12 : 9;
     return ndp == 1 ? 10 : ndp == 64 ? 12 : 7;
 }
 constexpr int kReduceWavesPerCU = 10;
