@@ -477,14 +477,15 @@ void ora_q8_quantize(const void *x, int xdt, int64_t len, int8_t *q, float *scal
         int64_t hi = lo + ORA_Q8_BLOCK < len ? lo + ORA_Q8_BLOCK : len;
         float amax = block_absmax(x, xdt, lo, hi);
         float s = amax / 127.0f; /* the stored scale: value = code * s */
-        float inv = 127.0f / amax; /* codes: rint(x * inv) */
         scales[b] = s;
         for (int64_t j = lo; j < hi; ++j) {
-            if (s == 0.0f || isnan(s) || isinf(s) || isinf(inv)) {
+            if (s == 0.0f || isnan(s) || isinf(s)) {
                 q[j] = 0;
                 continue;
             }
-            float r = rintf(grad_at(x, xdt, j) * inv); /* ties to even */
+            /* the code is the value measured in units of the stored scale:
+             * one correctly rounded division, then ties to even */
+            float r = rintf(grad_at(x, xdt, j) / s);
             if (r > 127.0f) r = 127.0f;
             if (r < -127.0f) r = -127.0f;
             q[j] = (int8_t)r;

@@ -190,10 +190,11 @@ void ora_flat_scatter(const void *src, int64_t begin, int64_t count,
  * is pinned only to its own mathematical properties).
  * Blocks of ORA_Q8_BLOCK consecutive elements (the last one may be short);
  * for block i, in fp32: s_i = absmax_i / 127 (absmax over the block, NaN if
- * any element is NaN) and r_i = 127 / absmax_i; q_j = rint(x_j * r_i)
- * clamped to [-127, 127] with round-to-nearest-even; s_i == 0, s_i not
- * finite or r_i infinite (absmax below about 3.7e-37) gives q_j = 0 (so a
- * block with an Inf or NaN dequantizes to NaN).  Dequantized: q_j * s_i. */
+ * any element is NaN); q_j = rint(x_j / s_i), one correctly rounded
+ * division, then round-to-nearest-even to an integer, clamped to
+ * [-127, 127]; s_i == 0 (absmax at most 127 times half the smallest
+ * subnormal) or s_i not finite gives q_j = 0 (so a block with an Inf or NaN
+ * dequantizes to NaN).  Dequantized: q_j * s_i. */
 #define ORA_Q8_BLOCK 256
 void ora_q8_quantize(const void *x, int xdt, int64_t len, int8_t *q, float *scales);
 void ora_q8_dequantize(const int8_t *q, const float *scales, int64_t len, void *y,

@@ -98,15 +98,20 @@ MUTANTS = [
     ("fp32_rows_read_as_16bit", "if (gdt == ORA_FP32) return ((const float *)grads)[i];",
      "(void)0;", PINS_DIM0),
     ("q8_scale_128", "float s = amax / 127.0f;", "float s = amax / 128.0f;", PINS_Q8),
-    ("q8_ties_away", "float r = rintf(grad_at(x, xdt, j) * inv);",
-     "float r = roundf(grad_at(x, xdt, j) * inv);", PINS_Q8),
-    ("q8_codes_divided_by_the_reciprocal", "float r = rintf(grad_at(x, xdt, j) * inv);",
-     "float r = rintf(grad_at(x, xdt, j) / inv);", PINS_Q8),
-    ("q8_reciprocal_of_128", "float inv = 127.0f / amax;", "float inv = 128.0f / amax;", PINS_Q8),
-    # the other plausible reading: codes by division with the stored scale
-    ("q8_codes_by_division", "float r = rintf(grad_at(x, xdt, j) * inv);",
-     "float r = rintf(grad_at(x, xdt, j) / s);", PINS_Q8),
-    ("q8_infinite_reciprocal_kept", "isinf(s) || isinf(inv)) {", "isinf(s)) {", PINS_Q8),
+    ("q8_ties_away", "float r = rintf(grad_at(x, xdt, j) / s);",
+     "float r = roundf(grad_at(x, xdt, j) / s);", PINS_Q8),
+    ("q8_codes_times_the_scale", "float r = rintf(grad_at(x, xdt, j) / s);",
+     "float r = rintf(grad_at(x, xdt, j) * s);", PINS_Q8),
+    ("q8_codes_scaled_by_128", "float r = rintf(grad_at(x, xdt, j) / s);",
+     "float r = rintf(grad_at(x, xdt, j) * (128.0f / amax));", PINS_Q8),
+    # the other plausible reading: codes with the block's reciprocal 127 / absmax
+    ("q8_codes_by_the_reciprocal", "float r = rintf(grad_at(x, xdt, j) / s);",
+     "float r = rintf(grad_at(x, xdt, j) * (127.0f / amax));", PINS_Q8),
+    # the exact quotient rounded to a code, skipping its rounding to binary32
+    ("q8_codes_from_the_exact_quotient", "float r = rintf(grad_at(x, xdt, j) / s);",
+     "float r = (float)rint((double)grad_at(x, xdt, j) / (double)s);", PINS_Q8),
+    ("q8_zero_scale_codes", "if (s == 0.0f || isnan(s) || isinf(s)) {", "if (isnan(s) || isinf(s)) {",
+     PINS_Q8),
     ("q8_dequant_block_off_by_one", "return (float)q[j] * scales[j / ORA_Q8_BLOCK];",
      "return (float)q[j] * scales[(j + 1) / ORA_Q8_BLOCK];", PINS_Q8),
     ("q8_nan_not_sticky", "if (isnan(a) || a > m) m = a;", "if (a > m) m = a;", PINS_Q8),

@@ -5,8 +5,11 @@ reduce-scatter ("ZeRO and FSDP", FSDP section; "ZeRO: How DeepSpeed Made
 Trillion-Parameter Training Practical"; "ZeRO Optimizer, in depth",
 "Offload and ZeRO++") but define no quantizer.  PARITY UNPINNED against the
 pages: these tests pin the stated quantizer (symmetric, one fp32 scale per
-256-element block, s = absmax / 127, q = rint(x * (127 / absmax))) to its
-mathematical properties and to a hand-worked example."""
+256-element block, s = absmax / 127, q = rint(x / s): the value measured in
+units of the stored scale) to its mathematical properties and to
+hand-worked examples."""
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -25,13 +28,16 @@ def _x(n, seed, sigma=1.0):
 
 
 def test_hand_worked_block():
-    # absmax 1: s = fl(1/127), r = 127 exactly; 0.5 r = 63.5 -> 64 (tie to even),
-    # -0.25 r = -31.75 -> -32, 0.1 r = 12.7 -> 13, 0.0236 r = 2.997 -> 3
+    # absmax 1: s = fl(1/127) = 2113665 * 2^-28, a little below 1/127.
+    # 0.5 / s = 63.50000024 exactly, whose nearest binary32 is 63.5 (ulp
+    # 2^-18): the code is rint(63.5) = 64, a tie to even; -0.25 / s rounds to
+    # -31.75 -> -32, 0.1 / s to 12.7 -> 13, 0.0236 / s to 2.9972 -> 3
     x = np.array([1.0, 0.5, -0.25, 0.1, 0.0236, 0.0], np.float32)
     q, s = oracle.q8_quantize(x, oracle.FP32)
     assert s[0] == np.float32(1.0) / np.float32(127.0)
+    assert Fraction(float(s[0])) == Fraction(2113665, 2 ** 28)
     assert q.tolist() == [127, 64, -32, 13, 3, 0]
-    # absmax 127 makes s and r exactly 1: the codes are the values rounded,
+    # absmax 127 makes s exactly 1: the codes are the values rounded,
     # ties to the even code (62.5 -> 62, -0.5 -> 0, 2.5 -> 2, -3.5 -> -4)
     x = np.array([127.0, 62.5, -0.5, 1.5, 2.5, -3.5, -127.0], np.float32)
     q, s = oracle.q8_quantize(x, oracle.FP32)
@@ -84,17 +90,23 @@ def test_zero_and_nonfinite_blocks():
     assert np.all(y[:B] == 0) and np.all(np.isnan(y[B:3 * B])) and np.all(np.isfinite(y[3 * B:]))
 
 
-def test_blocks_too_small_for_a_finite_reciprocal_code_zero():
-    """r = 127 / absmax overflows below absmax ~ 3.7e-37: such a block codes
-    as zeros (its scale is still absmax / 127)."""
-    x = np.zeros(2 * B, np.float32)
-    x[:B] = np.float32(1e-38) * np.sign(_x(B, 11))      # r infinite
-    x[B:] = np.float32(1e-36) * np.sign(_x(B, 12))      # r finite
+def test_tiny_blocks_code_until_the_scale_underflows_to_zero():
+    """Codes need only a non-zero finite scale: a block of subnormal-range
+    magnitudes still codes (its scale a subnormal, the largest element
+    +-127), and only a block whose absmax / 127 rounds to zero (absmax at
+    most 63 times the smallest subnormal) codes as zeros."""
+    tiny = np.float32(2.0 ** -149)
+    x = np.zeros(3 * B, np.float32)
+    x[:B] = np.float32(1e-38) * np.sign(_x(B, 11))       # s subnormal
+    x[B:2 * B] = np.float32(64) * tiny * np.sign(_x(B, 12))   # s = the smallest subnormal
+    x[2 * B:] = np.float32(63) * tiny * np.sign(_x(B, 13))    # s = 0
     q, s = oracle.q8_quantize(x, oracle.FP32)
-    with np.errstate(over="ignore"):
-        assert np.isinf(np.float32(127.0) / np.float32(1e-38))
-    assert s[0] == np.float32(1e-38) / np.float32(127.0) and not q[:B].any()
-    assert np.abs(q[B:]).max() == 127
+    assert 0 < s[0] < np.float32(2.0 ** -126) and np.abs(q[:B]).max() == 127
+    assert s[1] == tiny
+    # 64 * 2^-149 / 2^-149 = 64: the block's codes are +-64, not +-127,
+    # because the scale itself is rounded (64/127 of a subnormal step)
+    assert np.abs(q[B:2 * B]).max() == 64
+    assert s[2] == 0 and not q[2 * B:].any()
 
 
 def test_bf16_input_equals_its_fp32_widening():
@@ -149,20 +161,17 @@ def test_quantized_step_is_dequantize_step_quantize(n_dp, scale_pad):
     assert ss[0] == ss2[0]
 
 
-def test_codes_are_formed_with_the_blocks_reciprocal():
-    """Pins the stated reading q = rint(x * r), r = fl(127 / absmax), against
-    the other plausible one, rint(x / s), s = fl(absmax / 127): blocks whose
-    elements round differently under the two are found by search, and the
-    expected code of each is derived in exact rational arithmetic with
-    explicit round-to-nearest-even to binary32 at each operation."""
-    from fractions import Fraction
-    rng = np.random.default_rng(7)
+def _search_blocks_telling_the_readings_apart(seed, want=8):
+    """(absmax, x) pairs whose code differs between rint(x / s) and
+    rint(x * (127 / absmax)): elements within a few ulps of half-integer
+    codes, the only place where the two can disagree."""
+    rng = np.random.default_rng(seed)
     found = []
-    for _ in range(200):
+    for _ in range(400):
         amax = np.float32(rng.uniform(0.5, 2.0))
         s = amax / np.float32(127.0)
         k = rng.integers(-126, 127, size=4096).astype(np.float32)
-        x = ((k + np.float32(0.5)) * s).astype(np.float32)            # near half-integer codes
+        x = ((k + np.float32(0.5)) * s).astype(np.float32)
         x = x + rng.integers(-2, 3, size=x.size).astype(np.float32) * np.spacing(x)
         x = np.clip(x, -amax, amax).astype(np.float32)
         by_r = np.rint(x * (np.float32(127.0) / amax))
@@ -170,16 +179,58 @@ def test_codes_are_formed_with_the_blocks_reciprocal():
         hit = np.nonzero(by_r != by_s)[0]
         if hit.size:
             found.append((amax, x[hit[0]]))
-        if len(found) >= 6:
+        if len(found) >= want:
             break
+    return found
+
+
+def test_codes_are_the_value_divided_by_the_stored_scale():
+    """Pins q = rint(fl(x / s)), s = fl(absmax / 127), against the other
+    plausible form, rint(fl(x * fl(127 / absmax))): blocks whose elements
+    round differently under the two are found by search, and the expected
+    code of each is derived in exact rational arithmetic with explicit
+    round-to-nearest-even to binary32 at each operation."""
+    found = _search_blocks_telling_the_readings_apart(7)
     assert len(found) >= 6
     for amax, xv in found:
         blk = np.array([amax, xv], np.float32)
         q, sc = oracle.q8_quantize(blk, oracle.FP32)
-        r = rne_f32(Fraction(127) / Fraction(float(amax)))
-        want = rint_even(rne_f32(Fraction(float(xv)) * r))
         s_ex = rne_f32(Fraction(float(amax)) / Fraction(127))
-        other = rint_even(rne_f32(Fraction(float(xv)) / s_ex))
+        want = rint_even(rne_f32(Fraction(float(xv)) / s_ex))
+        r = rne_f32(Fraction(127) / Fraction(float(amax)))
+        other = rint_even(rne_f32(Fraction(float(xv)) * r))
         assert want != other                      # the case tells the readings apart
         assert int(q[1]) == want and int(q[0]) == 127
         assert Fraction(float(sc[0])) == s_ex     # the stored scale is absmax / 127
+
+
+def test_the_quotient_is_rounded_to_binary32_before_the_code():
+    """The code rounds the binary32 quotient, not the exact one: where the
+    exact x / s lies less than half an ulp from a half-integer k + 1/2, the
+    binary32 quotient is k + 1/2 itself, a tie that goes to the even code,
+    while the exact quotient would round to its nearer side.  Cases where
+    the two differ are found by search over scales; each is derived in exact
+    rational arithmetic."""
+    rng = np.random.default_rng(11)
+    cases = 0
+    for _ in range(20000):
+        amax = np.float32(rng.uniform(0.5, 2.0))
+        s = amax / np.float32(127.0)
+        k = int(rng.integers(0, 126))
+        x = np.float32((k + 0.5) * float(s))
+        if not x <= amax:
+            continue
+        exact = Fraction(float(x)) / Fraction(float(s))
+        rounded = rne_f32(exact)
+        if rounded != Fraction(2 * k + 1, 2) or exact == rounded:
+            continue
+        nearest = int(exact + Fraction(1, 2))     # exact > 0, not a tie
+        want = rint_even(rounded)
+        if nearest == want:
+            continue                              # both roundings agree here
+        q, _ = oracle.q8_quantize(np.array([amax, x], np.float32), oracle.FP32)
+        assert int(q[1]) == want
+        cases += 1
+        if cases >= 4:
+            break
+    assert cases >= 4
