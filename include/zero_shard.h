@@ -488,11 +488,11 @@ ZERO_API zero_status zero_reshard(const void *const *src_shards, int32_t n_src,
  * quantizer; this library uses the plain symmetric blockwise one:
  *   a vector of len elements is cut into blocks of ZERO_Q8_BLOCK (the last
  *   one may be short); block i has one fp32 scale s_i = absmax_i / 127
- *   (absmax NaN if the block holds a NaN) and codes q_j = rint(x_j * r_i)
- *   with r_i = 127 / absmax_i in fp32, clamped to [-127, 127], ties to even
- *   (q_j = 0 when s_i is 0, Inf or NaN or r_i is infinite, so a non-finite
- *   block dequantizes to NaN and one with absmax below ~3.7e-37 to zeros);
- *   the value is q_j * s_i.
+ *   (absmax NaN if the block holds a NaN) and codes q_j = rint(x_j / s_i):
+ *   the quotient correctly rounded to fp32, then rounded to an integer with
+ *   ties to even, clamped to [-127, 127] (q_j = 0 when s_i is 0, Inf or
+ *   NaN, so a non-finite block dequantizes to NaN, and one whose absmax / 127
+ *   rounds to zero to zeros); the value is q_j * s_i.
  * Codes: int8[len]; scales: float[ceil(len / ZERO_Q8_BLOCK)]. */
 #define ZERO_Q8_BLOCK 256
 

@@ -207,8 +207,8 @@ def test_q8_step_full_size_sampled_blocks():
 
 def test_quantizer_cases_that_tell_the_readings_apart():
     """Blocks in which rint(x * r) and rint(x / s) differ (found by search,
-    as in the oracle's pin): the device quantizer follows the oracle's
-    reading on every one, for fp32 and bf16 inputs."""
+    as in the oracle's pin): the device quantizer gives the oracle's codes,
+    those of the division, on every one, for fp32 and bf16 inputs."""
     rng = np.random.default_rng(11)
     blocks = []
     for _ in range(400):
@@ -236,3 +236,66 @@ def test_quantizer_cases_that_tell_the_readings_apart():
         oq, os_ = oracle.q8_quantize(arr, ODT[kind])
         assert np.array_equal(q.cpu().numpy(), oq)
         assert _same_f32(sc.cpu().numpy(), os_)
+
+
+def _boundary_blocks():
+    """Blocks crowded at the code boundaries: for many block scales (random,
+    exact powers of two, subnormal), every half-integer boundary's
+    neighbourhood in ulps, each block opening with its absmax."""
+    from tests.test_q8_code_rule import _scales, neighbourhoods
+    tiny = np.float32(2.0 ** -149)
+    scales = list(_scales(5, 24)) + [np.float32(127.0), np.float32(1.0),
+                                      np.float32(1e-38), np.float32(64) * tiny,
+                                      np.float32(63) * tiny, np.float32(2.0 ** -126)]
+    out = []
+    for amax in scales:
+        x = neighbourhoods(amax, 24)
+        n = -(-x.size // (B - 1))
+        blk = np.full((n, B), amax, np.float32)
+        flat = np.full(n * (B - 1), amax, np.float32)
+        flat[:x.size] = x
+        blk[:, 1:] = flat.reshape(n, B - 1)
+        out.append(blk.reshape(-1))
+    return np.concatenate(out)
+
+
+def test_codes_at_every_boundary_through_the_quantizer_and_the_step():
+    """The device's codes equal rint(fl(x / s)) at every code boundary of 30
+    block scales, dense in ulps (the same neighbourhoods as the CPU check of
+    the shortcut rule): through zero_q8_quantize, and through the fused
+    8-bit step's quantization of the new master (lr = 0 and no decay leave
+    the master as it was, so the step quantizes exactly these values)."""
+    xs = _boundary_blocks()
+    n = xs.size
+    print(f"\n[q8 boundaries] {n} elements", flush=True)
+    oq, os_ = oracle.q8_quantize(xs, oracle.FP32)
+    d = _dev(xs, F32)
+    q = torch.empty(n, dtype=torch.int8, device="cuda")
+    sc = torch.empty(zs.q8_blocks(n), device="cuda")
+    zs.zero_q8_quantize(d, q, sc)
+    got = q.cpu().numpy()
+    assert np.array_equal(got, oq), np.nonzero(got != oq)[0][:8]
+    assert _same_f32(sc.cpu().numpy(), os_)
+    # the step: one row of zero codes, the master the boundary blocks
+    lay, _ = zs.zero_flatten_layout([n], 1, B)
+    gq = torch.zeros(n, dtype=torch.int8, device="cuda")
+    gs = torch.ones(zs.q8_blocks(n), device="cuda")
+    W = d.clone()
+    M = torch.zeros(n, device="cuda")
+    V = torch.zeros(n, device="cuda")
+    wq = torch.zeros(lay.n_pad, dtype=torch.int8, device="cuda")
+    wsc = torch.zeros(lay.n_pad // B, device="cuda")
+    hp = dict(HP, lr=0.0, weight_decay=0.0)
+    zs.zero_shard_step_q8(gq, gs, n, zs.q8_blocks(n), n, W, M, V, wq, wsc, lay, 0,
+                          zs.AdamWHParams(step=1, grad_scale=1.0, **hp))
+    w, m, v = xs.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    o_wq = np.zeros(n, np.int8)
+    o_ws = np.zeros(zs.q8_blocks(n), np.float32)
+    oracle.step_q8(np.zeros(n, np.int8), np.ones(zs.q8_blocks(n), np.float32), 1, n,
+                   zs.q8_blocks(n), n, w, m, v, o_wq, o_ws, 1, grad_scale=1.0, **hp)
+    assert np.array_equal(w.view(np.uint32), xs.view(np.uint32))   # the master kept
+    assert np.array_equal(o_wq, oq)
+    got = wq.cpu().numpy()[:n]
+    assert np.array_equal(got, o_wq), np.nonzero(got != o_wq)[0][:8]
+    assert _same_f32(wsc.cpu().numpy()[:zs.q8_blocks(n)], o_ws)
+    assert _same_f32(W.cpu().numpy(), w)

@@ -4,8 +4,9 @@
 // reduce-scatter ("ZeRO and FSDP", FSDP section; "ZeRO Optimizer, in depth",
 // "Offload and ZeRO++").  The pages give no quantizer; the one here is the
 // plain symmetric blockwise int8 quantizer, one fp32 scale per block of 256
-// elements (s = absmax / 127 stored, codes q = rint(x * r) with the block's
-// reciprocal r = 127 / absmax, ties to even).
+// elements: s = absmax / 127 stored, codes q = rint(x / s), the value in
+// units of the stored scale with the quotient rounded to binary32 and then
+// to an integer, ties to even.
 //
 // A block is exactly one wave's quad layout: 64 lanes x 4 consecutive
 // elements, so a block's absmax is one wave reduction (DPP within each row
@@ -20,10 +21,11 @@
 // per lane, so that both its code loads and its 16-byte stores are
 // contiguous across the wave.
 //
-// Arithmetic matches the oracle's definition operation for operation:
-// correctly rounded fp32 divisions for absmax / 127 and 127 / absmax, one
-// rounded product x * r, v_rndne_f32 for the rounding, and q * s rounded
-// once to fp32.
+// Arithmetic gives the oracle's results bit for bit: a correctly rounded
+// fp32 division for absmax / 127, codes equal to rint(fl(x / s)) (formed
+// with the block's reciprocal where that provably gives the same integer,
+// by the division itself elsewhere; see quantize4), v_rndne_f32 for the
+// rounding, and q * s rounded once to fp32.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -96,8 +98,8 @@ __device__ __forceinline__ float wave_nanmax(float m) {
 }
 
 // A block's scale s = absmax / 127 (stored; value = code * s) and the
-// reciprocal r = 127 / absmax the codes are formed with, from the four
-// values of each lane (invalid ones 0).  Two divisions per lane per block.
+// reciprocal r = 127 / absmax, from the four values of each lane (invalid
+// ones 0).  Two divisions per lane per block.
 struct BlockScale {
     float s, r;
 };
@@ -110,16 +112,47 @@ __device__ __forceinline__ BlockScale block_scale(const float x[kQuad]) {
     return BlockScale{amax / 127.0f, 127.0f / amax};
 }
 
-// four codes rint(x * r), byte e = element e; all zero when s is zero or not
-// finite or r is infinite (absmax below what a code can carry)
+// Codes are rint(fl(x / s)); all zero when s is zero or not finite.
+//
+// A correctly rounded division per element is ~11 VALU instructions; the
+// product y = fl(x * r) is one, and it decides the code except within a
+// hair of a half-integer.  When s is normal (s >= 2^-126), r and 1/s differ
+// by at most the two roundings of s and r, so y = (x / s)(1 + t) with
+// |t| < 3.0000002 * 2^-24 (or an absolute error below 2^-150 where x * r is
+// subnormal), and |x / s| <= absmax / s < 127.0000076: |y - x / s| < 2.28e-5.
+// The binary32 quotient fl(x / s) lies within 2^-18 (half its ulp below 128)
+// of x / s.  So when y is more than 2^-14 = 6.1e-5 from every half-integer,
+// x / s and fl(x / s) lie strictly inside the same interval between
+// half-integers as y, and rint(y) = rint(fl(x / s)).  Only lanes whose y is
+// within 2^-14 of a half-integer (about 1 element in 8,000) -- and every
+// element of a block whose s is subnormal, where r no longer tracks 1/s --
+// take the division.  y - rint(y) is exact (the two are within 1/2 of each
+// other, below 2^23), so the test itself does not round.  The division sits
+// behind one wave-uniform branch per block (about 3 % of 256-element blocks
+// hold such an element), so the other blocks carry no per-element branch.
 __device__ __forceinline__ uint32_t quantize4(const float x[kQuad], BlockScale bs) {
-    if (!(bs.s > 0.0f) || __builtin_isinf(bs.s) || __builtin_isinf(bs.r)) return 0u;
+    if (!(bs.s > 0.0f) || __builtin_isinf(bs.s)) return 0u;
+    float r[kQuad];
+    bool near[kQuad];
+    bool any = bs.s < 0x1p-126f;  // wave-uniform: a subnormal scale divides everywhere
+#pragma unroll
+    for (int e = 0; e < kQuad; ++e) {
+        const float y = x[e] * bs.r;
+        r[e] = __builtin_rintf(y);
+        near[e] = any || fabsf(y - r[e]) >= 0.5f - 0x1p-14f;
+    }
+    if (__any(near[0] || near[1] || near[2] || near[3])) {  // wave-uniform
+#pragma unroll
+        for (int e = 0; e < kQuad; ++e) {
+            const float d = __builtin_rintf(x[e] / bs.s);
+            r[e] = near[e] ? d : r[e];
+        }
+    }
     uint32_t packed = 0u;
 #pragma unroll
     for (int e = 0; e < kQuad; ++e) {
-        float r = __builtin_rintf(x[e] * bs.r);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        packed |= (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu) << (8 * e);
+        const float c = fminf(fmaxf(r[e], -127.0f), 127.0f);
+        packed |= (static_cast<uint32_t>(static_cast<int32_t>(c)) & 0xFFu) << (8 * e);
     }
     return packed;
 }
