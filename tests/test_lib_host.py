@@ -128,12 +128,26 @@ def test_accounting_matches_oracle_and_pages():
 # rejected on the host before any launch, so it is exercised with made-up
 # addresses -- and therefore only where no GPU is visible.
 
+HIP_ERROR_NO_DEVICE = 100
+
+
 def _no_gpu():
+    """True only when no GPU can be reached; any doubt counts as a GPU.
+    No GPU device node (/dev/kfd, /dev/dri), the HIP runtime that the
+    library binds to (the process's libamdhip64, loaded with torch) reports
+    no device, and torch sees none."""
+    if os.path.exists("/dev/kfd") or os.path.exists("/dev/dri"):
+        return False
     try:
         import torch
-        return torch.cuda.device_count() == 0
+        if torch.cuda.device_count() != 0:
+            return False
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        n = ctypes.c_int(-1)
+        rc = hip.hipGetDeviceCount(ctypes.byref(n))
+        return rc == HIP_ERROR_NO_DEVICE or (rc == 0 and n.value == 0)
     except Exception:
-        return True
+        return False
 
 
 cpu_only = pytest.mark.skipif(not _no_gpu(), reason="uses made-up device addresses")
