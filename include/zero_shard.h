@@ -350,6 +350,31 @@ ZERO_API zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_t 
                             uint32_t *overflow, double *sumsq, void *workspace,
                             int64_t workspace_bytes, void *stream);
 
+/* ---- the fused step without a workspace ------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ * zero_shard_step with its sum of squares' workspace held by the library: a
+ * static device array of zero_sumsq_workspace_bytes(ZERO_NOALLOC_MAX_LEN) =
+ * 16,812,032 bytes, one copy on each GPU the call runs on, kept until the
+ * process ends.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its results equal zero_shard_step's with a
+ * workspace bit for bit, the sum of squares included.
+ *   len: at most ZERO_NOALLOC_MAX_LEN when sumsq != NULL (EINVAL beyond:
+ *        issue longer ranges as several calls, shard_off advancing; each
+ *        adds its part to *sumsq).  Without sumsq there is no limit.
+ * The array is shared by every call on one GPU: calls that sum squares and
+ * may run at the same time on one GPU (other streams, other threads) race
+ * on it and give wrong sums; issue them on one stream.  The first call on a
+ * GPU looks up the array's device address; EDEVICE if that fails.
+ * Other arguments and errors as for zero_shard_step. */
+#define ZERO_NOALLOC_MAX_LEN (1LL << 29)
+ZERO_API zero_status zero_shard_step_noalloc(const void *grads, zero_dtype gdt, int64_t ld,
+                                             int64_t len, float *master, float *m, float *v,
+                                             void *weight_full, zero_dtype wdt,
+                                             const zero_layout *layout, int32_t rank,
+                                             int64_t shard_off, const zero_adamw_hparams *hp,
+                                             uint32_t *overflow, double *sumsq, void *stream);
+
 /* ---- step constants in device memory (one graph for every step) ----------
  * A captured HIP graph replays the arguments it was captured with, so a
  * graph of zero_shard_step or zero_shard_adamw_ex repeats the step number

@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     lib = ctypes.CDLL(zs.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -502,3 +502,24 @@ def test_q8_entry_points_reject_bad_arguments():
                 wk_bytes=wkb - 1) == zs.ZERO_EINVAL                  # workspace too small
     assert step(ssq=BASE + (7 << 28), wk=BASE + (4 << 28),
                 wk_bytes=wkb) == zs.ZERO_EALIAS                      # workspace over v
+
+
+@cpu_only
+def test_noalloc_step_rejects_before_any_launch():
+    """zero_shard_step_noalloc: with a sum of squares, a range longer than
+    the library's scratch covers is refused; other arguments are checked as
+    zero_shard_step checks them."""
+    lay = zs.zero_flatten_layout([4096], 4)[0]
+    big = (1 << 29) + 4
+
+    def call(length=1024, ld=1024, rank=1, ssq=None):
+        return L.zero_shard_step_noalloc(P(BASE), 0, ld, length, P(BASE + (1 << 30)),
+                                         P(BASE + (2 << 30)), P(BASE + (3 << 30)),
+                                         P(BASE + (4 << 30)), 0, ctypes.byref(lay), rank, 0,
+                                         ctypes.byref(_hp()), None, P(ssq) if ssq else None,
+                                         None)
+    assert zs.ZERO_NOALLOC_MAX_LEN == 1 << 29
+    assert call(length=big, ld=big, ssq=BASE + (6 << 30)) == zs.ZERO_EINVAL
+    assert call(rank=4) == zs.ZERO_EINVAL
+    assert call(ld=1000) == zs.ZERO_EINVAL
+    assert call(length=1025, ld=1025) == zs.ZERO_ERANGE

@@ -134,6 +134,9 @@ def _load():
     L.zero_shard_step.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, ctypes.c_int,
                                   lay_p, i32, i64, hp_p, vp, vp, vp, i64, vp]
     L.zero_shard_step.restype = ctypes.c_int
+    L.zero_shard_step_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp,
+                                          ctypes.c_int, lay_p, i32, i64, hp_p, vp, vp, vp]
+    L.zero_shard_step_noalloc.restype = ctypes.c_int
     L.zero_step_consts_make.argtypes = [hp_p, ctypes.POINTER(ZeroStepConsts)]
     L.zero_step_consts_make.restype = ctypes.c_int
     L.zero_shard_step_dc.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, ctypes.c_int,
@@ -466,6 +469,36 @@ def zero_shard_step(grads, ld: int, length: int, master, m, v, weight_full,
         ctypes.byref(hpc), _buf(overflow, "overflow", 1, torch.int32, d),
         _buf(sumsq, "sumsq", 1, torch.float64, d), ws, ws_bytes, _stream(stream, master)),
         "zero_shard_step")
+
+
+ZERO_NOALLOC_MAX_LEN = 1 << 29
+
+
+def zero_shard_step_noalloc(grads, ld: int, length: int, master, m, v, weight_full,
+                            layout: ZeroLayout, rank: int, hp: AdamWHParams, shard_off: int = 0,
+                            overflow=None, sumsq=None, stream=None):
+    """zero_shard_step for callers that cannot allocate: the sum of squares
+    goes through the library's own device scratch (no workspace argument,
+    nothing allocated, here or in the library).  With sumsq, length is at
+    most ZERO_NOALLOC_MAX_LEN; calls that sum squares on one GPU must not
+    run concurrently (they share the scratch)."""
+    import torch
+    if sumsq is not None and length > ZERO_NOALLOC_MAX_LEN:
+        raise ZeroValueError(ZERO_EINVAL, f"zero_shard_step_noalloc: length {length} is above "
+                             f"ZERO_NOALLOC_MAX_LEN = {ZERO_NOALLOC_MAX_LEN} with a sum of "
+                             "squares; split the range into several calls")
+    hpc = hp._c()
+    d = master.device
+    _check(_lib.zero_shard_step_noalloc(
+        _rows(grads, "grads", layout.n_dp, ld, length, device=d),
+        _dtype_code(grads, "grads", True), ld, length,
+        _buf(master, "master", length, torch.float32), _buf(m, "m", length, torch.float32, d),
+        _buf(v, "v", length, torch.float32, d),
+        _buf(weight_full, "weight_full", _slot_end(layout, rank, shard_off, length), device=d),
+        _dtype_code(weight_full, "weight_full"), ctypes.byref(layout), rank, shard_off,
+        ctypes.byref(hpc), _buf(overflow, "overflow", 1, torch.int32, d),
+        _buf(sumsq, "sumsq", 1, torch.float64, d), _stream(stream, master)),
+        "zero_shard_step_noalloc")
 
 
 def zero_step_consts_make(hp: AdamWHParams) -> np.ndarray:

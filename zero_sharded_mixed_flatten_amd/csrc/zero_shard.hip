@@ -36,8 +36,10 @@
 // rounded fp32 division and square root, and keeps denormals.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "host_common.h"
@@ -880,6 +882,75 @@ extern "C" zero_status zero_shard_step(const void *grads, zero_dtype gdt, int64_
                                        int64_t workspace_bytes, void *stream) {
     return step_impl(grads, gdt, ld, len, master, m, v, weight_full, wdt, layout, rank, shard_off,
                      hp, nullptr, overflow, sumsq, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The step for callers that cannot allocate: the sum of squares' workspace
+// is a library-held device array, one copy per GPU, kept until the process
+// ends.  It holds the per-workgroup partials and the stage-two sums of one
+// call of up to ZERO_NOALLOC_MAX_LEN elements; every call writes the
+// partials it later reads, so nothing in it needs clearing between calls.
+
+namespace {
+
+constexpr int64_t kScratchDoubles = kSsqStage2 + (ZERO_NOALLOC_MAX_LEN + 255) / 256 + kSsqScalarBlocks;
+static_assert(static_cast<int64_t>(sizeof(double)) * kScratchDoubles ==
+                  8 * (256 + (ZERO_NOALLOC_MAX_LEN + 255) / 256 + 4096),
+              "the scratch holds exactly zero_sumsq_workspace_bytes(ZERO_NOALLOC_MAX_LEN)");
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) double scratch[kScratchDoubles];
+
+namespace {
+
+// The device address of the scratch array on the stream's GPU, looked up
+// once per device with that device current.  (In host code `scratch` names
+// a host-side stand-in, never passed to a kernel or a copy.)  nullptr when
+// the runtime cannot tell the device or the address.
+void *scratch_on(hipStream_t st) {
+    int dev = -1;
+    if (st ? hipStreamGetDevice(st, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+        return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void *q = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
+    if (e != hipSuccess || q == nullptr) return nullptr;
+    g_scratch[dev].store(q, std::memory_order_release);
+    return q;
+}
+
+}  // namespace
+
+extern "C" zero_status zero_shard_step_noalloc(const void *grads, zero_dtype gdt, int64_t ld,
+                                               int64_t len, float *master, float *m, float *v,
+                                               void *weight_full, zero_dtype wdt,
+                                               const zero_layout *layout, int32_t rank,
+                                               int64_t shard_off, const zero_adamw_hparams *hp,
+                                               uint32_t *overflow, double *sumsq,
+                                               void *stream) {
+    if (!sumsq)
+        return step_impl(grads, gdt, ld, len, master, m, v, weight_full, wdt, layout, rank,
+                         shard_off, hp, nullptr, overflow, nullptr, nullptr, 0, stream);
+    if (len > ZERO_NOALLOC_MAX_LEN) return ZERO_EINVAL;
+    void *ws = scratch_on(static_cast<hipStream_t>(stream));
+    if (!ws) return ZERO_EDEVICE;
+    return step_impl(grads, gdt, ld, len, master, m, v, weight_full, wdt, layout, rank, shard_off,
+                     hp, nullptr, overflow, sumsq, ws,
+                     static_cast<int64_t>(sizeof(double)) * kScratchDoubles, stream);
 }
 
 extern "C" zero_status zero_shard_step_dc(const void *grads, zero_dtype gdt, int64_t ld,
