@@ -52,6 +52,9 @@ def parse():
                    help="CPU baseline sample: 2^k parameters of the shard")
     p.add_argument("--cpu-steps", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="time only the chosen workload (the plain default line also times "
+                        "configurations 1, 3 and 4, the same-mix ceiling and the vendor copy)")
     p.add_argument("--bucket-elems", type=int, default=0, metavar="B",
                    help="single-launch 16-bit steps: issue the shard as consecutive buckets of B "
                         "elements, one library call each (0: one call for the whole shard)")
@@ -113,25 +116,83 @@ def committed_traffic(workload_name, source=KERNEL_SOURCE):
         return None
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the sharded step is emulated with all n_dp "
-              "ranks' gradient rows in one GPU's HBM, and no multi-GPU path is built. "
-              "Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+STEP_CAPS = {1: 10, 8: 7, 64: 12}   # the fused 16-bit step's residency caps (waves per CU)
+CEILING_CAPS = (5, 6, 7, 8, 10, 12, 16)
 
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy, args.steps)
-        return
-    if args.op in ("quantize", "dequantize"):
-        bench_codec(args)
-        return
-    if args.op != "step":
-        bench_copies(args)
-        return
 
-    import numpy as np
+def _stream_mix():
+    """libstream_mix.so: the same-mix ceiling kernel (calibration/)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "calibration", "libstream_mix.so"))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.stream_mix.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, i32, vp]
+    lib.stream_mix.restype = ctypes.c_int
+    return lib
+
+
+def time_ceiling(slab, n_dp, S, master, m, v, slot, stream, caps, reps=10):
+    """The same-mix ceiling on the step's own buffers: every byte the fused
+    16-bit step moves, with its launch shape, and no arithmetic (the state
+    is stored back as loaded).  Average kernel ms per cap (HIP events on the
+    stream it runs on)."""
+    import ctypes
+
+    import torch
+    lib = _stream_mix()
+    out = {}
+    for cap in caps:
+        def call():
+            rc = lib.stream_mix(slab.data_ptr(), n_dp, S, S, master.data_ptr(), m.data_ptr(),
+                                v.data_ptr(), slot.data_ptr(), cap,
+                                ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError("stream_mix refused its arguments")
+        for _ in range(3):
+            call()
+        ev = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        out[cap] = statistics.fmean(a.elapsed_time(b) for a, b in ev)
+    return out
+
+
+def time_vendor_copy(nbytes, reps=10):
+    """torch's device-to-device copy_ (HIP's own copy kernel) of nbytes:
+    nbytes read and nbytes written per launch."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dst.copy_(src)
+    ev = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = statistics.fmean(a.elapsed_time(b) for a, b in ev)
+    del src, dst
+    torch.cuda.empty_cache()
+    gbps = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "torch copy_ (device to device)", "bytes_read_per_launch": nbytes,
+            "bytes_written_per_launch": nbytes, "launch_ms_avg": ms, "achieved": gbps,
+            "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS}
+
+
+def time_step_workload(config, steps, warmup, flags=False, bucket_elems=0, use_graph=False,
+                       ceiling_caps=()):
+    """Draw workload `config`'s inputs into HBM, run `warmup` untimed and
+    `steps` timed steps of the hot path, and return the timings.  With
+    ceiling_caps (single-launch 16-bit steps of 1, 8 or 64 rows), the
+    same-mix ceiling is timed on the same buffers afterwards."""
     import torch
 
     import synth
@@ -140,12 +201,8 @@ def main():
     from synth.synth_const import BUF_GRAD, BUF_MASTER
     from synth.workloads import workload
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    wl = workload(args.config)
+    wl = workload(config)
     q8 = wl.comm == "q8"
     if wl.layout == "dim0":
         lay, _, _ = zs.zero_dim0_layout(wl.shapes, wl.n_dp)
@@ -161,10 +218,11 @@ def main():
     hp_kw = dict(wl.hp)
 
     # ---- inputs, resident in HBM -------------------------------------------
+    nb = S // zs.ZERO_Q8_BLOCK
+    slab_s = wfull_s = None
     if q8:
         # what each sender puts on the wire: its fp32 gradient for this shard,
         # quantized (before the timed region)
-        nb = S // zs.ZERO_Q8_BLOCK
         slab = torch.empty((n_dp, S), dtype=torch.int8, device=dev)
         slab_s = torch.empty((n_dp, nb), dtype=torch.float32, device=dev)
         tmp = torch.empty(S, dtype=torch.float32, device=dev)
@@ -190,33 +248,33 @@ def main():
     else:
         wfull = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device=dev)
     acc = torch.empty(S, dtype=torch.float32, device=dev) if micro > 1 else None
-    flag = torch.zeros(1, dtype=torch.int32, device=dev) if micro > 1 or args.flags else None
-    if wl.controls or args.flags:
+    flag = torch.zeros(1, dtype=torch.int32, device=dev) if micro > 1 or flags else None
+    sumsq = loss_scale = None
+    if wl.controls or flags:
         sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
     if wl.controls:
         loss_scale = zs.new_loss_scale(wl.loss_scale, dev)
     stream = torch.cuda.current_stream(dev)
     graph = None
-    if args.graph:
+    if use_graph:
         if micro != 1 or q8:
             print("--graph applies to the single-launch 16-bit steps", file=sys.stderr)
             sys.exit(2)
         # every step's constants in pinned host memory up front (no buffer is
         # rewritten while an earlier asynchronous copy may still read it), one
         # device buffer the captured kernels read
-        host_consts = torch.empty((args.warmup + args.steps, 48), dtype=torch.uint8,
-                                  pin_memory=True)
-        for i in range(args.warmup + args.steps):
+        host_consts = torch.empty((warmup + steps, 48), dtype=torch.uint8, pin_memory=True)
+        for i in range(warmup + steps):
             hpi = zs.AdamWHParams(step=i + 1, grad_scale=1.0 / n_dp, **hp_kw)
             host_consts[i].copy_(torch.from_numpy(zs.zero_step_consts_make(hpi)))
         consts = zs.new_step_consts(dev)
-        bucket = args.bucket_elems if args.bucket_elems > 0 else S
-        fl = dict(overflow=flag, sumsq=sumsq) if args.flags else {}
+        bucket = bucket_elems if bucket_elems > 0 else S
+        fl = dict(overflow=flag, sumsq=sumsq) if flags else {}
         ws = (torch.empty(zs.zero_sumsq_workspace_bytes(bucket) // 8 + 1, dtype=torch.float64,
-                          device=dev) if args.flags else None)
+                          device=dev) if flags else None)
 
         def issue(st):
-            if args.flags:
+            if flags:
                 flag.zero_()
                 sumsq.zero_()
             for b0 in range(0, S, bucket):
@@ -253,8 +311,8 @@ def main():
             hp = zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **hp_kw)
             e0 = torch.cuda.Event(enable_timing=True) if timed else None
             e1 = torch.cuda.Event(enable_timing=True) if timed else None
-            fl = dict(overflow=flag, sumsq=sumsq) if args.flags else {}
-            if args.flags:  # caller-zeroed, outside the timed launch
+            fl = dict(overflow=flag, sumsq=sumsq) if flags else {}
+            if flags:  # caller-zeroed, outside the timed launch
                 flag.zero_()
                 sumsq.zero_()
             if timed:
@@ -262,9 +320,9 @@ def main():
             if q8:
                 zs.zero_shard_step_q8(slab, slab_s, S, nb, S, master, m, v, wfull, wfull_s, lay,
                                       rank, hp, stream=stream, **fl)
-            elif args.bucket_elems > 0:
-                for b0 in range(0, S, args.bucket_elems):
-                    b1 = min(S, b0 + args.bucket_elems)
+            elif bucket_elems > 0:
+                for b0 in range(0, S, bucket_elems):
+                    b1 = min(S, b0 + bucket_elems)
                     zs.zero_shard_step(slab[:, b0:], S, b1 - b0, master[b0:], m[b0:], v[b0:],
                                        wfull, lay, rank, hp, shard_off=b0, stream=stream, **fl)
             else:
@@ -309,26 +367,25 @@ def main():
                 zs.zero_loss_scale_update(loss_scale, flag, 2.0, 0.5, 2000, stream=stream)
 
     t = 0
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         t += 1
         step(t, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         t += 1
         step(t, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ms_per_step = wall * 1e3 / args.steps
-    with_flags = " with the overflow flag and the sum of squares" if args.flags else ""
+    with_flags = " with the overflow flag and the sum of squares" if flags else ""
     if q8:
         bytes_per_param = n_dp * (1 + 4 / zs.ZERO_Q8_BLOCK) + 12 + 12 + 1 + 4 / zs.ZERO_Q8_BLOCK
         kernel = f"step_q8_kernel (fused dequantize + reduce + AdamW + quantize{with_flags})"
     elif micro == 1:
         bytes_per_param = gbytes * n_dp + 26
         kernel = f"step_quad_kernel (fused reduce + AdamW + cast{with_flags})"
-        if args.graph:
+        if use_graph:
             kernel += ", one graph replay per step, constants read from device memory"
     else:
         # 4 B written by the first reduce, 2 n_dp + 8 by each later one,
@@ -337,20 +394,113 @@ def main():
         kernel = ("adamw_quad_kernel (gated AdamW with clipping and dynamic loss scale + cast; "
                   "timed launch)" if wl.controls else
                   "adamw_quad_kernel (gated AdamW + cast; timed launch)")
-    step_bytes = bytes_per_param * S
     kms = [a.elapsed_time(b) for a, b in events]
+    r = dict(wl=wl, lay=lay, S=S, n_dp=n_dp, rank=rank, q8=q8, gdt=gdt, micro=micro,
+             steps=steps, warmup=warmup, wall=wall, kms=kms, kernel=kernel,
+             bytes_per_param=bytes_per_param, step_bytes=bytes_per_param * S,
+             launch_bytes=bytes_per_param * S if micro == 1 else 30 * S, ceiling=None)
+    if (ceiling_caps and micro == 1 and not q8 and gdt == zs.ZERO_BF16
+            and n_dp in STEP_CAPS):
+        r["ceiling"] = time_ceiling(slab, n_dp, S, master, m, v, wfull[rank * S:], stream,
+                                    ceiling_caps)
+    del slab, master, m, v, wfull, acc, slab_s, wfull_s
+    torch.cuda.empty_cache()
+    return r
+
+
+def roofline_of(r, traffic):
+    kms = r["kms"]
     k_avg = statistics.fmean(kms)
-    if micro == 1:
-        launch_bytes = step_bytes
-    else:
-        launch_bytes = 30 * S
-    achieved = launch_bytes / (k_avg * 1e-3) / 1e9
+    achieved = r["launch_bytes"] / (k_avg * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": r["kernel"], "achieved": achieved,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic, "launch_ms_avg": k_avg, "launch_ms_min": min(kms),
+            "launch_ms_median": statistics.median(kms),
+            "algorithmic_bytes_per_launch": r["launch_bytes"]}
+
+
+def ceiling_of(r):
+    """The same-mix ceiling at the step's own residency cap and the best cap,
+    and the step's kernel time as a fraction of the former."""
+    c = r["ceiling"]
+    if not c:
+        return None, None
+    own = STEP_CAPS[r["n_dp"]]
+    best = min(c, key=c.get)
+    k_avg = statistics.fmean(r["kms"])
+    gb = lambda ms: r["launch_bytes"] / (ms * 1e-3) / 1e9
+    return ({"kernel": "stream_mix (the step's bytes, launch shape and access, no arithmetic)",
+             "waves_per_cu": own, "launch_ms_avg": c[own], "achieved": gb(c[own]),
+             "unit": "GB/s", "frac": gb(c[own]) / HBM_PEAK_GBPS,
+             "best_waves_per_cu": best, "best_launch_ms_avg": c[best],
+             "best_frac": gb(c[best]) / HBM_PEAK_GBPS,
+             "sweep_ms": {str(k): v for k, v in sorted(c.items())}},
+            c[own] / k_avg)
+
+
+def summary_of(r):
+    """One workload's figures for the default line's other_configs."""
+    rl = roofline_of(r, committed_traffic(r["wl"].name, Q8_SOURCE if r["q8"] else KERNEL_SOURCE))
+    out = {"shard": r["S"], "n_dp": r["n_dp"], "rank": r["rank"],
+           "bytes_per_param": r["bytes_per_param"], "steps": r["steps"],
+           "warmup": r["warmup"], "ms_per_step": r["wall"] * 1e3 / r["steps"],
+           "params_per_s": r["S"] * r["steps"] / r["wall"],
+           "hbm_gbps": r["step_bytes"] * r["steps"] / r["wall"] / 1e9,
+           "hbm_frac": r["step_bytes"] * r["steps"] / r["wall"] / 1e9 / HBM_PEAK_GBPS,
+           "kernel": rl["kernel"], "kernel_ms_avg": rl["launch_ms_avg"],
+           "kernel_gbps": rl["achieved"], "kernel_frac": rl["frac"],
+           "algorithmic_bytes_per_launch": rl["algorithmic_bytes_per_launch"],
+           "traffic": rl["traffic"]}
+    if r["micro"] > 1:
+        out["launches_per_step"] = r["micro"] + 1 + int(r["wl"].controls)
+        out["kernel_bytes_per_param"] = 30
+    ceil, frac = ceiling_of(r)
+    if ceil:
+        out["ceiling"] = ceil
+        out["frac_of_ceiling"] = frac
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the sharded step is emulated with all n_dp "
+              "ranks' gradient rows in one GPU's HBM, and no multi-GPU path is built. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, args.steps)
+        return
+    if args.op in ("quantize", "dequantize"):
+        bench_codec(args)
+        return
+    if args.op != "step":
+        bench_copies(args)
+        return
+
+    import torch
+
+    import zero_sharded_mixed_flatten_amd as zs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    # the plain default line also times the other workloads, the same-mix
+    # ceiling and the vendor copy
+    plain = not (args.flags or args.graph or args.bucket_elems > 0 or args.no_extra)
+    r = time_step_workload(args.config, args.steps, args.warmup, flags=args.flags,
+                           bucket_elems=args.bucket_elems, use_graph=args.graph,
+                           ceiling_caps=CEILING_CAPS if plain else ())
+    wl, lay, S, n_dp, q8, micro = r["wl"], r["lay"], r["S"], r["n_dp"], r["q8"], r["micro"]
+    wall, gdt = r["wall"], r["gdt"]
     # the committed counter summaries cover the variant without the flags
     # whose constants are kernel arguments (for the stage-2 workloads: the
     # timed AdamW launch)
     traffic = (committed_traffic(wl.name, Q8_SOURCE if q8 else KERNEL_SOURCE)
                if not args.flags and not args.graph else None)
-
     line = {
         "metric": "sharded AdamW step params/s and HBM GB/s (% of 8 TB/s), 7B n_dp=8 shard",
         "value": S * args.steps / wall,
@@ -358,21 +508,21 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": wall * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "hbm_gbps": step_bytes / wall * args.steps / 1e9,
-        "hbm_frac": step_bytes / wall * args.steps / 1e9 / HBM_PEAK_GBPS,
-        "config": {"workload": wl.name, "n_params": lay.n, "n_dp": n_dp, "rank": rank,
+        "hbm_gbps": r["step_bytes"] / wall * args.steps / 1e9,
+        "hbm_frac": r["step_bytes"] / wall * args.steps / 1e9 / HBM_PEAK_GBPS,
+        "config": {"workload": wl.name, "n_params": lay.n, "n_dp": n_dp, "rank": r["rank"],
                    "shard": S, "layout": wl.layout,
                    "grad_dtype": "int8 blocks of 256 + fp32 scale" if q8 else
                    {zs.ZERO_BF16: "bf16", zs.ZERO_FP16: "fp16", zs.ZERO_FP32: "fp32"}[gdt],
                    "state_dtype": "fp32",
                    "weight_dtype": "int8 blocks of 256 + fp32 scale" if q8 else "bf16",
-                   "micro_batches": micro, "bytes_per_param": bytes_per_param,
+                   "micro_batches": micro, "bytes_per_param": r["bytes_per_param"],
                    "controls": "clip 1.0 + dynamic loss scale" if wl.controls else None,
                    "flags": "overflow + sum of squares" if args.flags and micro == 1 else None,
                    "bucket_elems": args.bucket_elems if args.bucket_elems > 0 and micro == 1
@@ -382,24 +532,30 @@ def main():
                    "launches_per_step": (-(-S // args.bucket_elems) if args.bucket_elems > 0
                                          and not q8 else 1) if micro == 1
                    else micro + 1 + int(wl.controls)},
-        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic, "launch_ms_avg": k_avg, "launch_ms_min": min(kms),
-                     "launch_ms_median": statistics.median(kms),
-                     "algorithmic_bytes_per_launch": launch_bytes},
+        "roofline": roofline_of(r, traffic),
         "cpu_baseline": None,
     }
+    ceil, frac = ceiling_of(r)
+    if ceil:
+        line["ceiling"] = ceil
+        line["frac_of_ceiling"] = frac
+    if plain:
+        line["vendor_copy"] = time_vendor_copy(4 << 30)
+        if args.config == 2:
+            others = {}
+            for c in (1, 3, 4):
+                o = time_step_workload(c, min(args.steps, 10), min(args.warmup, 3),
+                                       ceiling_caps=CEILING_CAPS)
+                others[o["wl"].name] = summary_of(o)
+            line["other_configs"] = others
 
     # ---- the oracle on the host: a reported baseline, never the target ------
     if not args.no_cpu_baseline:
-        del slab, master, m, v, wfull, acc
-        if q8:
-            del slab_s, wfull_s
-        torch.cuda.empty_cache()
-        line["cpu_baseline"] = cpu_baseline(wl, S, rank, args.cpu_sample_log2, args.cpu_steps)
+        line["cpu_baseline"] = cpu_baseline(wl, S, r["rank"], args.cpu_sample_log2,
+                                            args.cpu_steps)
         if micro == 1 and not q8:
             line["cpu_baseline_all_cores"] = cpu_baseline_all_cores(
-                wl, S, rank, args.cpu_sample_log2, 8 * args.cpu_steps)
+                wl, S, r["rank"], args.cpu_sample_log2, 8 * args.cpu_steps)
 
     print(json.dumps(line), flush=True)
 
