@@ -1,0 +1,201 @@
+"""Every element of a full-size shard against the oracle ("ZeRO and FSDP",
+"A sharded Adam step": rank r's whole shard after the step).
+
+The GPU runs a workload's whole trajectory over the whole shard, in the
+launch configuration the benchmark times.  Then the shard is compared chunk
+by chunk: for each chunk the oracle replays the same steps on its elements,
+on all host cores (the update is element-wise, so each thread takes one
+contiguous range of the chunk and the result equals one whole-range call),
+and every element of master, m, v and the rank's weight slot must be bit
+for bit the oracle's.
+
+Inputs come from the shared seeded generator (synth, which holds none of
+the method's arithmetic): the master is drawn on the host; each step's
+gradient rows for a chunk are drawn on the device by the generator's device
+build, which draws bit-identical values to its host build
+(tests/test_gpu_synth.py), and copied to the host for the oracle -- drawing
+the 6.7e10 gradient values of a trajectory on the host would take minutes.
+
+Workloads: the Llama-shaped 7B list over n_dp = 8, rank 1 (842,301,952
+elements, t = 1..10, the benchmark's workload) and over n_dp = 64, rank 1
+(105,287,744 elements, 9 warm-up steps and t = 10); the GPT-2-XL-shaped list
+at n_dp = 1 (1,557,611,200 elements, 5 warm-up steps and t = 6); and the 7B
+stage-2 accumulation (fp16 rows x 65536, 4 micro-batches reduced into the
+fp32 accumulator, AdamW gated on the overflow flag), whose accumulator is
+compared too."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import zero_sharded_mixed_flatten_amd as zs
+from synth import F32
+from synth.synth_const import BUF_GRAD, BUF_MASTER
+from synth.workloads import workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _threads():
+    return synth.host_threads()
+
+
+def _oracle_steps(rows_of, ts, w, m, v, out, n_dp, wl):
+    """The oracle's steps ts on one chunk (w, m, v, out in place); rows_of(t)
+    gives step t's rows as one flat uint16 array of n_dp * chunk elements."""
+    n = w.size
+    T = _threads()
+    cuts = [n * i // T for i in range(T + 1)]
+    with ThreadPoolExecutor(max_workers=T) as pool:
+        for t in ts:
+            flat = rows_of(t)
+
+            def run(i, flat=flat, t=t):
+                a, b = cuts[i], cuts[i + 1]
+                oracle.step(flat[a:], oracle.BF16, n_dp, n, b - a, w[a:b], m[a:b], v[a:b],
+                            out[a:b], oracle.BF16, t, grad_scale=1.0 / n_dp, **wl.hp)
+            list(pool.map(run, range(T)))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cid,chunk_log2", [(2, 26), (3, 23), (1, 27)])
+def test_every_element_of_the_full_shard(cid, chunk_log2):
+    wl = workload(cid)
+    lay, _ = zs.zero_flatten_layout(wl.numels, wl.n_dp)
+    S, n_dp, rank = lay.shard, wl.n_dp, wl.rank
+    ts = tuple(range(1, wl.warmup_steps + 1)) + wl.steps
+    d = wl.grad
+    print(f"\n[full shard] config {cid} rank {rank} S={S} n_dp={n_dp} steps={ts}", flush=True)
+    dev = torch.device("cuda")
+    slab = torch.empty((n_dp, S), dtype=torch.bfloat16, device=dev)
+    W = torch.empty(S, dtype=torch.float32, device=dev)
+    synth.fill_device(W, F32, wl.seed, synth.tag(BUF_MASTER, cid), rank * S, wl.master_sigma)
+    M = torch.zeros(S, dtype=torch.float32, device=dev)
+    V = torch.zeros(S, dtype=torch.float32, device=dev)
+    wf = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device=dev)
+    for t in ts:
+        for k in range(n_dp):
+            synth.fill_device(slab[k], d.kind, wl.seed, synth.tag(BUF_GRAD, cid, t, 0, k),
+                              rank * S, d.eff_sigma, d.thr, d.outlier_mul)
+        zs.zero_shard_step(slab, S, S, W, M, V, wf, lay, rank,
+                           zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **wl.hp))
+    torch.cuda.synchronize()
+    del slab
+    torch.cuda.empty_cache()
+
+    C = 1 << chunk_log2
+    rows_d = torch.empty((n_dp, C), dtype=torch.bfloat16, device=dev)
+    rows_h = torch.empty((n_dp, C), dtype=torch.int16, pin_memory=True)
+    slot = wf.view(torch.int16)[rank * S:(rank + 1) * S]
+    compared = 0
+    for c0 in range(0, S, C):
+        n = min(C, S - c0)
+        start = rank * S + c0
+
+        def rows_of(t, n=n, start=start):
+            for k in range(n_dp):
+                synth.fill_device(rows_d[k, :n], d.kind, wl.seed,
+                                  synth.tag(BUF_GRAD, cid, t, 0, k), start, d.eff_sigma, d.thr,
+                                  d.outlier_mul)
+            rows_h[:, :n].copy_(rows_d.view(torch.int16)[:, :n])
+            return np.ascontiguousarray(rows_h[:, :n].numpy()).view(np.uint16).reshape(-1)
+
+        w = synth.fill_host(F32, wl.seed, synth.tag(BUF_MASTER, cid), start, n, wl.master_sigma)
+        m = np.zeros(n, np.float32)
+        v = np.zeros(n, np.float32)
+        out = np.zeros(n, np.uint16)
+        _oracle_steps(rows_of, ts, w, m, v, out, n_dp, wl)
+        for name, got, want in (("master", W[c0:c0 + n], w), ("m", M[c0:c0 + n], m),
+                                ("v", V[c0:c0 + n], v)):
+            g = got.cpu().numpy()
+            bad = np.count_nonzero(g.view(np.uint32) != want.view(np.uint32))
+            assert bad == 0, f"{name}: {bad} of {n} elements at shard offset {c0} differ"
+        g = slot[c0:c0 + n].cpu().numpy().view(np.uint16)
+        bad = np.count_nonzero(g != out)
+        assert bad == 0, f"weights: {bad} of {n} elements at shard offset {c0} differ"
+        compared += n
+        print(f"[full shard] config {cid}: {compared} of {S} elements bit-identical", flush=True)
+    assert compared == S
+
+
+@pytest.mark.timeout(900)
+def test_every_element_of_the_accumulated_full_shard():
+    wl = workload(4)
+    lay, _ = zs.zero_flatten_layout(wl.numels, wl.n_dp)
+    S, n_dp, rank, micro = lay.shard, wl.n_dp, wl.rank, wl.micro_batches
+    d = wl.grad
+    scale = 1.0 / (n_dp * wl.loss_scale * micro)
+    print(f"\n[full shard] config 4 rank {rank} S={S} n_dp={n_dp} micro={micro}", flush=True)
+    dev = torch.device("cuda")
+    slab = torch.empty((n_dp, S), dtype=torch.float16, device=dev)
+    acc = torch.empty(S, dtype=torch.float32, device=dev)
+    W = torch.empty(S, dtype=torch.float32, device=dev)
+    synth.fill_device(W, F32, wl.seed, synth.tag(BUF_MASTER, 4), rank * S, wl.master_sigma)
+    M = torch.zeros(S, dtype=torch.float32, device=dev)
+    V = torch.zeros(S, dtype=torch.float32, device=dev)
+    wf = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    for mb in range(micro):
+        for k in range(n_dp):
+            synth.fill_device(slab[k], d.kind, wl.seed, synth.tag(BUF_GRAD, 4, 1, mb, k),
+                              rank * S, d.eff_sigma, d.thr, d.outlier_mul)
+        zs.zero_shard_reduce(slab, n_dp, S, S, acc, accumulate=mb > 0, overflow=flag)
+    zs.zero_shard_adamw(acc, W, M, V, wf, lay, rank,
+                        zs.AdamWHParams(step=1, grad_scale=scale, **wl.hp), skip=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    del slab
+    torch.cuda.empty_cache()
+
+    C = 1 << 26
+    rows_d = torch.empty((n_dp, C), dtype=torch.float16, device=dev)
+    rows_h = torch.empty((n_dp, C), dtype=torch.int16, pin_memory=True)
+    slot = wf.view(torch.int16)[rank * S:(rank + 1) * S]
+    T = _threads()
+    compared = 0
+    with ThreadPoolExecutor(max_workers=T) as pool:
+        for c0 in range(0, S, C):
+            n = min(C, S - c0)
+            start = rank * S + c0
+            cuts = [n * i // T for i in range(T + 1)]
+            a = np.zeros(n, np.float32)
+            o_flag = np.zeros((T, 1), np.uint32)
+            for mb in range(micro):
+                for k in range(n_dp):
+                    synth.fill_device(rows_d[k, :n], d.kind, wl.seed,
+                                      synth.tag(BUF_GRAD, 4, 1, mb, k), start, d.eff_sigma,
+                                      d.thr, d.outlier_mul)
+                rows_h[:, :n].copy_(rows_d.view(torch.int16)[:, :n])
+                flat = np.ascontiguousarray(rows_h[:, :n].numpy()).view(np.uint16).reshape(-1)
+
+                def red(i, flat=flat, mb=mb):
+                    lo, hi = cuts[i], cuts[i + 1]
+                    oracle.reduce(flat[lo:], oracle.FP16, n_dp, n, hi - lo, a[lo:hi], mb > 0,
+                                  overflow=o_flag[i])
+                list(pool.map(red, range(T)))
+            assert not o_flag.any()
+            w = synth.fill_host(F32, wl.seed, synth.tag(BUF_MASTER, 4), start, n,
+                                wl.master_sigma)
+            m = np.zeros(n, np.float32)
+            v = np.zeros(n, np.float32)
+            out = np.zeros(n, np.uint16)
+
+            def upd(i):
+                lo, hi = cuts[i], cuts[i + 1]
+                oracle.adamw(a[lo:hi], w[lo:hi], m[lo:hi], v[lo:hi], out[lo:hi], oracle.BF16,
+                             hi - lo, 1, grad_scale=scale, skip=o_flag[i], **wl.hp)
+            list(pool.map(upd, range(T)))
+            for name, got, want in (("acc", acc[c0:c0 + n], a), ("master", W[c0:c0 + n], w),
+                                    ("m", M[c0:c0 + n], m), ("v", V[c0:c0 + n], v)):
+                g = got.cpu().numpy()
+                bad = np.count_nonzero(g.view(np.uint32) != want.view(np.uint32))
+                assert bad == 0, f"{name}: {bad} of {n} elements at shard offset {c0} differ"
+            g = slot[c0:c0 + n].cpu().numpy().view(np.uint16)
+            bad = np.count_nonzero(g != out)
+            assert bad == 0, f"weights: {bad} of {n} elements at shard offset {c0} differ"
+            compared += n
+            print(f"[full shard] config 4: {compared} of {S} elements bit-identical", flush=True)
+    assert compared == S
