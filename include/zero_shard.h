@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define ZERO_SHARD_ABI_VERSION 3
+#define ZERO_SHARD_ABI_VERSION 4
 
 /* every entry point is exported from the shared library */
 #if defined(__GNUC__) || defined(__clang__)
@@ -165,6 +165,16 @@ ZERO_API zero_status zero_shard_segments(const zero_layout *layout,
                                 const int64_t *numels, int64_t n_tensors,
                                 int32_t rank, zero_segment *out, int64_t cap,
                                 int64_t *count);
+
+/* The pieces of the functional sharded step ("ZeRO and FSDP", "A sharded
+ * Adam step"): rank r of n_dp holds elements [starts[r], starts[r] +
+ * lens[r]) of a vector of n, cut as numpy.array_split cuts it -- the first
+ * (n mod n_dp) pieces one element longer than the others, no padding.  (When
+ * n_dp divides n these are the equal shards of zero_flatten_layout.)
+ * starts, lens: host arrays of n_dp elements, written.  Host only.
+ * EINVAL: n < 0, n_dp < 1, NULL starts or lens (nothing written). */
+ZERO_API zero_status zero_array_split_layout(int64_t n, int32_t n_dp, int64_t *starts,
+                                             int64_t *lens);
 
 /* ---- per-parameter dim-0 sharding (host only) ------------------------------
  * "ZeRO and FSDP", FSDP section: FSDP2 keeps every parameter as a tensor
@@ -422,10 +432,14 @@ ZERO_API zero_status zero_shard_step_dc(const void *grads, zero_dtype gdt, int64
  * skipped), the step number staying put after an overflow exactly as
  * zero_shard_adamw's skip leaves the state.
  *   select:  one thread copies table[*t - 1] to *consts when 1 <= *t <=
- *            count; any other *t writes constants that are all NaN (a step
- *            run with them turns the state to NaN rather than reusing an
- *            earlier step's constants).  consts, table: device, 8-byte
- *            aligned; t: device int64, 8-byte aligned.
+ *            count; any other *t writes constants that are all NaN.  Every
+ *            _dc entry point holds a step whose constants have a NaN s: it
+ *            writes no state, weight, code or scale (a partial sum of
+ *            squares of zero), and raises *overflow when given one, so a
+ *            counter run past its table neither reuses an earlier step's
+ *            constants nor damages the state, and advance with that flag as
+ *            skip keeps the counter where it is.  consts, table: device,
+ *            8-byte aligned; t: device int64, 8-byte aligned.
  *   advance: *t = *t + 1 unless skip is given and *skip != 0 (read when
  *            the kernel runs).  t: device int64, 8-byte aligned; skip:
  *            device uint32 or NULL.

@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     lib = ctypes.CDLL(zs.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -523,3 +523,30 @@ def test_noalloc_step_rejects_before_any_launch():
     assert call(rank=4) == zs.ZERO_EINVAL
     assert call(ld=1000) == zs.ZERO_EINVAL
     assert call(length=1025, ld=1025) == zs.ZERO_ERANGE
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_array_split_layout_matches_numpy_and_the_oracle(seed):
+    """zero_array_split_layout cuts as numpy.array_split (a library routine)
+    cuts; the oracle's piece starts agree, also far beyond 2^32 elements."""
+    rng = np.random.default_rng(seed)
+    cases = [(0, 1), (0, 5), (3, 8), (7, 7), (10_000, 4), (10_001, 4)]
+    cases += [(int(rng.integers(0, 50_000)), int(rng.integers(1, 130))) for _ in range(60)]
+    for n, n_dp in cases:
+        starts, lens = zs.zero_array_split_layout(n, n_dp)
+        pieces = np.array_split(np.arange(n), n_dp)
+        assert lens.tolist() == [p.size for p in pieces]
+        assert starts.tolist() == [int(p[0]) if p.size else int(s) for p, s in zip(pieces, starts)]
+        assert np.array_equal(np.concatenate([np.arange(s, s + l) for s, l in zip(starts, lens)]
+                                             + [np.zeros(0, np.int64)]), np.arange(n))
+    for n, n_dp in [(6_738_415_616, 8), ((1 << 40) + 12_345, 64), (1_557_611_200, 3)]:
+        starts, lens = zs.zero_array_split_layout(n, n_dp)
+        assert starts.tolist() == [oracle.array_split_start(n, n_dp, r) for r in range(n_dp)]
+        assert int(lens.sum()) == n and starts[-1] + lens[-1] == n
+
+
+def test_array_split_layout_rejects_invalid():
+    for n, n_dp in [(-1, 4), (10, 0), (10, -3)]:
+        with pytest.raises(zs.ZeroValueError):
+            zs.zero_array_split_layout(n, n_dp)
+    assert L.zero_array_split_layout(10, 4, None, None) == zs.ZERO_EINVAL

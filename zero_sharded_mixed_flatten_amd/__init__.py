@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libzero_shard.so")
 ZERO_OK, ZERO_EINVAL, ZERO_EALIAS, ZERO_ERANGE, ZERO_EDEVICE = range(5)
 ZERO_BF16, ZERO_FP16, ZERO_FP32 = 0, 1, 2
 ZERO_Q8_BLOCK = 256
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class ZeroError(RuntimeError):
@@ -114,6 +114,8 @@ def _load():
     L.zero_flatten_layout.restype = ctypes.c_int
     L.zero_shard_segments.argtypes = [lay_p, vp, i64, i32, vp, i64, ctypes.POINTER(i64)]
     L.zero_shard_segments.restype = ctypes.c_int
+    L.zero_array_split_layout.argtypes = [i64, i32, vp, vp]
+    L.zero_array_split_layout.restype = ctypes.c_int
     L.zero_dim0_layout.argtypes = [vp, vp, i64, i32, i64, vp, vp, lay_p]
     L.zero_dim0_layout.restype = ctypes.c_int
     L.zero_dim0_segments.argtypes = [lay_p, vp, vp, i64, i32, vp, i64, ctypes.POINTER(i64)]
@@ -303,6 +305,16 @@ def _stream(stream, like):
 
 # ---------------------------------------------------------------------------
 # entry points
+
+
+def zero_array_split_layout(n: int, n_dp: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(starts, lens) of the n_dp pieces numpy.array_split cuts n elements into."""
+    starts = np.zeros(max(n_dp, 0), dtype=np.int64)
+    lens = np.zeros(max(n_dp, 0), dtype=np.int64)
+    _check(_lib.zero_array_split_layout(int(n), int(n_dp), starts.ctypes.data_as(ctypes.c_void_p),
+                                        lens.ctypes.data_as(ctypes.c_void_p)),
+           "zero_array_split_layout")
+    return starts, lens
 
 
 def zero_flatten_layout(numels: Sequence[int], n_dp: int, align: int = 1
@@ -754,9 +766,7 @@ def zero_adam_step(grads, w_shards, m_shards, v_shards, t: int, lr: float = 1e-3
     n = grads[0].numel()
     if any(g.numel() != n or g.dtype != grads[0].dtype for g in grads):
         raise ValueError("zero_adam_step: every rank's gradient is one vector of n elements")
-    base, extra = divmod(n, n_dp)
-    lens = [base + (1 if r < extra else 0) for r in range(n_dp)]   # numpy.array_split
-    starts = [sum(lens[:r]) for r in range(n_dp)]
+    starts, lens = (a.tolist() for a in zero_array_split_layout(n, n_dp))
     for shards in (w_shards, m_shards, v_shards):
         for r, x in enumerate(shards):
             if x.numel() != lens[r] or x.dtype != torch.float32:

@@ -139,6 +139,22 @@ bool dim0_sizes(const int64_t *rows, const int64_t *cols, int64_t n_tensors, int
 
 }  // namespace
 
+// "ZeRO and FSDP", "A sharded Adam step": the exercise cuts the flat vector
+// with numpy.array_split -- n / n_dp elements per rank, the first n mod n_dp
+// ranks one more, contiguous and in rank order.
+extern "C" zero_status zero_array_split_layout(int64_t n, int32_t n_dp, int64_t *starts,
+                                               int64_t *lens) {
+    if (n < 0 || n_dp < 1 || !starts || !lens) return ZERO_EINVAL;
+    const int64_t each = n / n_dp, extra = n % n_dp;
+    int64_t at = 0;
+    for (int32_t r = 0; r < n_dp; ++r) {
+        starts[r] = at;
+        lens[r] = each + (r < extra ? 1 : 0);
+        at += lens[r];
+    }
+    return ZERO_OK;
+}
+
 extern "C" zero_status zero_dim0_layout(const int64_t *rows, const int64_t *cols,
                                         int64_t n_tensors, int32_t n_dp, int64_t align,
                                         int64_t *packed_off, int64_t *chunk_rows,
