@@ -309,6 +309,62 @@ def test_step_beyond_the_table_selects_nan_constants():
             assert np.array_equal(got, table[want].cpu().numpy())
 
 
+def test_steps_past_the_table_are_held():
+    """A counter past its table selects NaN constants; every device-constant
+    entry point then holds the step: master, m, v, the weight slot, the
+    8-bit codes and scales keep every bit, the overflow flag goes up, the
+    sum of squares gets nothing, and the counter, advanced with that flag
+    as skip, stays where it is.  A shard with a ragged tail, so that the
+    element kernels hold too."""
+    n_dp, rank, S = 4, 1, 50_003
+    lay, _ = zs.zero_flatten_layout([S * n_dp], n_dp)
+    table = zs.step_consts_table([zs.AdamWHParams(step=k, grad_scale=1.0 / n_dp, **HP)
+                                  for k in (1, 2)])
+    consts = zs.new_step_consts()
+    t = zs.new_step_counter(3)
+    zs.zero_step_consts_select(consts, table, t)
+    rows = dev16(host_rows(201, 1, 0, n_dp, 0, S, GradDraw(BF16, 1e-3)), 0).view(n_dp, S)
+    W0 = devf(host_master(202, 0, S))
+    M0 = devf(host_master(203, 0, S, sigma=1e-4))
+    V0 = devf(np.abs(host_master(204, 0, S, sigma=1e-6)))
+    W, M, V = W0.clone(), M0.clone(), V0.clone()
+    wf = torch.full((lay.n_pad,), -2.0, dtype=torch.bfloat16, device="cuda")
+    wf0 = wf.clone()
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ss = torch.zeros(1, dtype=torch.float64, device="cuda")
+    zs.zero_shard_step_dc(rows, S, S, W, M, V, wf, lay, rank, consts, overflow=flag, sumsq=ss)
+    acc = devf(host_master(205, 0, S, sigma=1e-3))
+    zs.zero_shard_adamw_dc(acc, W, M, V, wf, lay, rank, consts)
+    zs.zero_step_counter_advance(t, skip=flag)
+    torch.cuda.synchronize()
+    for got, want in ((W, W0), (M, M0), (V, V0), (wf, wf0)):
+        assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else
+                           got.view(torch.int32),
+                           want.view(torch.int16) if want.dtype == torch.bfloat16 else
+                           want.view(torch.int32))
+    assert int(flag.item()) == 1 and ss.item() == 0.0 and int(t.item()) == 3
+    # the 8-bit step
+    B = zs.ZERO_Q8_BLOCK
+    Sq = 40 * B + 77
+    layq, _ = zs.zero_flatten_layout([Sq * n_dp], n_dp, B)
+    Sq = layq.shard
+    x = devf(host_master(206, 0, n_dp * Sq, sigma=1e-3))
+    gq = torch.empty(n_dp * Sq, dtype=torch.int8, device="cuda")
+    gs = torch.empty(zs.q8_blocks(n_dp * Sq), device="cuda")
+    zs.zero_q8_quantize(x, gq, gs)
+    Wq0 = devf(host_master(207, 0, Sq))
+    Wq, Mq, Vq = Wq0.clone(), torch.zeros(Sq, device="cuda"), torch.zeros(Sq, device="cuda")
+    wq = torch.full((layq.n_pad,), 5, dtype=torch.int8, device="cuda")
+    wsc = torch.full((layq.n_pad // B,), 0.25, device="cuda")
+    flag.zero_()
+    zs.zero_shard_step_q8_dc(gq, gs, Sq, Sq // B, Sq, Wq, Mq, Vq, wq, wsc, layq, rank, consts,
+                             overflow=flag)
+    torch.cuda.synchronize()
+    assert torch.equal(Wq.view(torch.int32), Wq0.view(torch.int32))
+    assert not Mq.any() and not Vq.any()
+    assert bool((wq == 5).all()) and bool((wsc == 0.25).all()) and int(flag.item()) == 1
+
+
 def test_counter_advances_unless_skipped():
     t = zs.new_step_counter(41)
     zs.zero_step_counter_advance(t)                                    # no flag: advance

@@ -518,10 +518,14 @@ step_q8_kernel(const int8_t *__restrict__ gq, const float *__restrict__ gs, int6
                float *__restrict__ M, float *__restrict__ V, int8_t *__restrict__ wq,
                float *__restrict__ wsc, Consts c, uint32_t *__restrict__ ovf,
                double *__restrict__ part, const zero_step_consts *__restrict__ dc) {
-    if constexpr (DC) c = consts_of(*dc);
-    bool bad = false;
+    bool held = false;
+    if constexpr (DC) {
+        c = consts_of(*dc);
+        held = step_held(c);
+    }
+    bool bad = held;
     double ss = 0.0;
-    const int64_t b = wave_block<TPB>();
+    const int64_t b = held ? nblocks : wave_block<TPB>();  // a held step touches no block
     if constexpr (NDP > 0) {
         if (b < nblocks) {  // wave-uniform
             if ((b + 1) * kB <= len)  // wave-uniform: the whole block in the range

@@ -98,6 +98,13 @@ __host__ __device__ inline Consts consts_of(const zero_step_consts &d) {
     return Consts{d.s, d.b1, d.c1, d.b2, d.c2, d.bc1, d.bc2, d.lr, d.eps, d.d};
 }
 
+// Device constants whose gradient scale is not a number (what a step
+// counter past its table selects) hold the step: the kernel writes no
+// state, no weight and no partial sum of squares beyond a zero, and raises
+// the overflow flag when it has one, so that the state survives and the
+// caller can tell the step was not taken.
+__host__ __device__ inline bool step_held(const Consts &c) { return c.s != c.s; }
+
 // ---------------------------------------------------------------------------
 // 16-bit <-> fp32.  Widening is exact.  Narrowing uses gfx950's packed
 // converts (v_cvt_pk_bf16_f32, v_cvt_pk_f16_f32): round to nearest even.

@@ -177,11 +177,15 @@ step_quad_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t ld
                  float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
                  uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
                  double *__restrict__ part, const zero_step_consts *__restrict__ dc) {
-    if constexpr (DC) c = consts_of(*dc);
-    bool bad = false;
+    bool held = false;
+    if constexpr (DC) {
+        c = consts_of(*dc);
+        held = step_held(c);
+    }
+    bool bad = held;
     double ss = 0.0;
     const int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x;
-    if (q < nquad) {
+    if (q < nquad && !held) {
         const int64_t e0 = q * kQuad;
         Rows<GDT, NDP> rows;
         load_rows<GDT, NDP>(rows, grads + e0, ld);
@@ -201,11 +205,15 @@ step_scalar_kernel(const typename GradT<GDT>::elem *__restrict__ grads, int64_t 
                    float *__restrict__ W, float *__restrict__ M, float *__restrict__ V,
                    uint16_t *__restrict__ out, Consts c, uint32_t *__restrict__ ovf,
                    double *__restrict__ part, const zero_step_consts *__restrict__ dc) {
-    if constexpr (DC) c = consts_of(*dc);
-    bool bad = false;
+    bool held = false;
+    if constexpr (DC) {
+        c = consts_of(*dc);
+        held = step_held(c);
+    }
+    bool bad = held;
     double ss = 0.0;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < len;
+    for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < len && !held;
          j += stride) {
         float a = widen1<GDT>(grads[j]);
         for (int k = 1; k < n_dp; ++k) a = a + widen1<GDT>(grads[static_cast<int64_t>(k) * ld + j]);
@@ -317,6 +325,7 @@ adamw_quad_kernel(const float *__restrict__ acc, float *__restrict__ W, float *_
     }
     if constexpr (DC) {
         c = consts_of(*dc);
+        if (step_held(c)) return;
         ctl.grad_scale = dc->grad_scale;
     }
     float clip = 1.0f;
@@ -356,6 +365,7 @@ adamw_scalar_kernel(const float *__restrict__ acc, float *__restrict__ W, float 
     }
     if constexpr (DC) {
         c = consts_of(*dc);
+        if (step_held(c)) return;
         ctl.grad_scale = dc->grad_scale;
     }
     float clip = 1.0f;
@@ -377,7 +387,8 @@ adamw_scalar_kernel(const float *__restrict__ acc, float *__restrict__ W, float 
 }
 
 // The constants of step *t from a table of steps 1..count (one thread);
-// NaN constants for a step outside the table.
+// NaN constants for a step outside the table, which every device-constant
+// kernel holds (step_held): it writes nothing.
 __global__ void step_consts_select_kernel(zero_step_consts *__restrict__ out,
                                           const zero_step_consts *__restrict__ table,
                                           int64_t count, const int64_t *__restrict__ t) {
