@@ -39,7 +39,11 @@
 #include "oracle_zero.h"
 
 #include <math.h>
+#include <stdint.h>
 #include <string.h>
+
+/* ceil(a / b) for a >= 0, b >= 1, without forming a + b - 1 */
+static int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
 
 /* ------------------------------------------------------------------------ */
 /* Layout.  "ZeRO and FSDP", "The idea, one stage at a time": one flat vector
@@ -52,12 +56,14 @@ int ora_flatten_layout(const int64_t *numels, int64_t n_tensors, int32_t n_dp,
     if (n_tensors > 0 && numels == 0) return -1;
     int64_t n = 0;
     for (int64_t i = 0; i < n_tensors; ++i) {
-        if (numels[i] < 0) return -1;
+        if (numels[i] < 0 || numels[i] > INT64_MAX - n) return -1; /* N fits int64 */
         if (offsets) offsets[i] = n;
         n += numels[i];
     }
+    if (align > INT64_MAX / n_dp) return -1;
     int64_t unit = (int64_t)n_dp * align;
-    int64_t units = (n + unit - 1) / unit;
+    int64_t units = ceil_div(n, unit);
+    if (units > INT64_MAX / unit) return -1; /* N_pad fits int64 */
     int64_t shard = units * align;
     out3[0] = n;
     out3[1] = shard * n_dp;
@@ -104,14 +110,11 @@ int64_t ora_shard_segments(const int64_t *numels, int64_t n_tensors,
     return count;
 }
 
-/* "A sharded Adam step": the shards are the pieces of numpy.array_split,
- * whose first (n mod parts) pieces are one element longer. */
 /* Per-parameter dim-0 sharding.  "ZeRO and FSDP", FSDP section: each
  * parameter sharded along its first dimension, a unit's shards packed into
  * one buffer per collective.  The cut is torch.chunk's: ceil(rows / n_dp)
  * rows per rank, the last ranks possibly short or empty (padded). */
 
-static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int ora_dim0_layout(const int64_t *rows, const int64_t *cols, int64_t n_tensors,
                     int32_t n_dp, int64_t align, int64_t *packed_off,
@@ -122,11 +125,16 @@ int ora_dim0_layout(const int64_t *rows, const int64_t *cols, int64_t n_tensors,
     for (int64_t i = 0; i < n_tensors; ++i) {
         if (rows[i] < 0 || cols[i] < 0) return -1;
         int64_t c = ceil_div(rows[i], n_dp);
+        /* every size fits int64: the tensor, the flat total, the packed total */
+        if (cols[i] > 0 && (rows[i] > INT64_MAX / cols[i] ||
+                            rows[i] * cols[i] > INT64_MAX - n ||
+                            c * cols[i] > INT64_MAX - p)) return -1;
         if (packed_off) packed_off[i] = p;
         if (chunk_rows) chunk_rows[i] = c;
         p += c * cols[i];
         n += rows[i] * cols[i];
     }
+    if (ceil_div(p, align) > INT64_MAX / align) return -1;
     out2[0] = n;
     out2[1] = ceil_div(p, align) * align;
     return 0;
@@ -178,6 +186,8 @@ int64_t ora_dim0_segments(const int64_t *rows, const int64_t *cols,
     return count;
 }
 
+/* "A sharded Adam step": the shards are the pieces of numpy.array_split,
+ * whose first (n mod parts) pieces are one element longer. */
 int64_t ora_array_split_start(int64_t n, int64_t parts, int64_t i) {
     int64_t each = n / parts, extra = n % parts;
     return i * each + (i < extra ? i : extra);

@@ -116,3 +116,21 @@ def test_invalid_layout_rejected(args):
 def test_empty_vector():
     assert oracle.flatten_layout([], 4)[1:] == (0, 0, 0)
     assert oracle.shard_segments([], 4, 3) == []
+
+
+def test_sizes_beyond_int64_are_rejected():
+    """A layout whose N or N_pad would not fit int64 is rejected rather than
+    wrapped; the largest that fit come out exact."""
+    big = (1 << 63) - 1
+    for nums, n_dp, align in [([big, 1], 1, 1), ([big // 2, big // 2 + 2], 1, 1),
+                              ([big - 5], 4, 8), ([1], 1 << 30, big // 4)]:
+        with pytest.raises(ValueError):
+            oracle.flatten_layout(nums, n_dp, align)
+    _, n, n_pad, s = oracle.flatten_layout([big], 1, 1)
+    assert n == n_pad == s == big
+    _, n, n_pad, s = oracle.flatten_layout([1 << 62], 2, 1 << 40)
+    assert (n, n_pad, s) == (1 << 62, 1 << 62, 1 << 61)
+    with pytest.raises(ValueError):
+        oracle.dim0_layout([(big, 2)], 8)
+    with pytest.raises(ValueError):
+        oracle.dim0_layout([(1 << 40, 1 << 22), (1 << 40, 1 << 22)], 8)

@@ -59,7 +59,7 @@ MUTANTS = [
     ("bf16_ties_away", "(lo == 0x8000u && (hi & 1u))", "(lo == 0x8000u)", PINS_CONVERT),
     ("f16_widen_bias", "((e + 112u) << 23)", "((e + 111u) << 23)", PINS_CONVERT),
     ("f16_subnormal_shift", "shift = -e - 1;", "shift = -e;", PINS_CONVERT),
-    ("layout_floor", "int64_t units = (n + unit - 1) / unit;", "int64_t units = n / unit;", PINS_LAYOUT),
+    ("layout_floor", "int64_t units = ceil_div(n, unit);", "int64_t units = n / unit;", PINS_LAYOUT),
     ("segment_offset", "quads[4 * count + 1] = s - a;\n                quads[4 * count + 2] = s - lo;",
      "quads[4 * count + 1] = s - a;\n                quads[4 * count + 2] = s - lo + 1;", PINS_LAYOUT),
     ("padding_segment_dropped", "    if (hi > s) {\n        if (count < cap) {\n            quads[4 * count + 0] = -1;",
@@ -89,8 +89,8 @@ MUTANTS = [
      PINS_RESHARD),
     ("dim0_chunk_floor", "int64_t c = ceil_div(rows[i], n_dp);\n        int64_t first",
      "int64_t c = rows[i] / n_dp;\n        int64_t first", PINS_DIM0),
-    ("dim0_layout_chunk_floor", "int64_t c = ceil_div(rows[i], n_dp);\n        if (packed_off)",
-     "int64_t c = rows[i] / n_dp;\n        if (packed_off)", PINS_DIM0),
+    ("dim0_layout_chunk_floor", "int64_t c = ceil_div(rows[i], n_dp);\n        /* every size",
+     "int64_t c = rows[i] / n_dp;\n        /* every size", PINS_DIM0),
     ("dim0_row_offset_not_scaled", "quads[4 * count + 1] = first * cols[i];",
      "quads[4 * count + 1] = first;", PINS_DIM0),
     ("dim0_padding_dropped", "if (have < c && cols[i] > 0) {", "if (0) {", PINS_DIM0),
