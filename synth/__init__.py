@@ -11,7 +11,9 @@ import numpy as np
 from .synth_const import F32, BF16, F16, TABLE_SIZE, outlier_threshold, tag  # noqa: F401
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_CPU = os.path.join(HERE, "libsynth.so")
+# SYNTH_LIB selects another build of synth_cpu.c (the sanitizer tests load
+# an AddressSanitizer/UBSan build this way)
+LIB_CPU = os.environ.get("SYNTH_LIB") or os.path.join(HERE, "libsynth.so")
 LIB_GPU = os.path.join(HERE, "libsynth_gpu.so")
 
 _cpu = None
