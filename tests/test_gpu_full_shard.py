@@ -22,7 +22,11 @@ elements, t = 1..10, the benchmark's workload) and over n_dp = 64, rank 1
 at n_dp = 1 (1,557,611,200 elements, 5 warm-up steps and t = 6); and the 7B
 stage-2 accumulation (fp16 rows x 65536, 4 micro-batches reduced into the
 fp32 accumulator, AdamW gated on the overflow flag), whose accumulator is
-compared too."""
+compared too; the 7B list in the per-parameter dim-0 layout with fp32
+gradient rows (842,301,952 packed elements, t = 1..3); and the 8-bit path
+(fp32 draws quantized to int8 blocks on the device, the fused 8-bit step
+at t = 1, 2: every code and scale of the last step's rows, of the weight
+slot and every element of the state)."""
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -198,4 +202,160 @@ def test_every_element_of_the_accumulated_full_shard():
             assert bad == 0, f"weights: {bad} of {n} elements at shard offset {c0} differ"
             compared += n
             print(f"[full shard] config 4: {compared} of {S} elements bit-identical", flush=True)
+    assert compared == S
+
+
+@pytest.mark.timeout(900)
+def test_every_element_of_the_dim0_fp32_row_shard():
+    wl = workload(5)
+    lay, _, _ = zs.zero_dim0_layout(wl.shapes, wl.n_dp)
+    S, n_dp, rank = lay.shard, wl.n_dp, wl.rank
+    d = wl.grad
+    print(f"\n[full shard] config 5 rank {rank} S={S} n_dp={n_dp} steps={wl.steps}", flush=True)
+    dev = torch.device("cuda")
+    slab = torch.empty((n_dp, S), dtype=torch.float32, device=dev)
+    W = torch.empty(S, dtype=torch.float32, device=dev)
+    synth.fill_device(W, F32, wl.seed, synth.tag(BUF_MASTER, 5), rank * S, wl.master_sigma)
+    M = torch.zeros(S, dtype=torch.float32, device=dev)
+    V = torch.zeros(S, dtype=torch.float32, device=dev)
+    wf = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device=dev)
+    for t in wl.steps:
+        for k in range(n_dp):
+            synth.fill_device(slab[k], F32, wl.seed, synth.tag(BUF_GRAD, 5, t, 0, k), rank * S,
+                              d.eff_sigma, d.thr, d.outlier_mul)
+        zs.zero_shard_step(slab, S, S, W, M, V, wf, lay, rank,
+                           zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **wl.hp))
+    torch.cuda.synchronize()
+    del slab
+    torch.cuda.empty_cache()
+
+    C = 1 << 25
+    rows_d = torch.empty((n_dp, C), dtype=torch.float32, device=dev)
+    rows_h = torch.empty((n_dp, C), dtype=torch.float32, pin_memory=True)
+    slot = wf.view(torch.int16)[rank * S:(rank + 1) * S]
+    T = _threads()
+    compared = 0
+    with ThreadPoolExecutor(max_workers=T) as pool:
+        for c0 in range(0, S, C):
+            n = min(C, S - c0)
+            start = rank * S + c0
+            cuts = [n * i // T for i in range(T + 1)]
+            w = synth.fill_host(F32, wl.seed, synth.tag(BUF_MASTER, 5), start, n,
+                                wl.master_sigma)
+            m = np.zeros(n, np.float32)
+            v = np.zeros(n, np.float32)
+            out = np.zeros(n, np.uint16)
+            for t in wl.steps:
+                for k in range(n_dp):
+                    synth.fill_device(rows_d[k, :n], F32, wl.seed, synth.tag(BUF_GRAD, 5, t, 0, k),
+                                      start, d.eff_sigma, d.thr, d.outlier_mul)
+                rows_h[:, :n].copy_(rows_d[:, :n])
+                flat = np.ascontiguousarray(rows_h[:, :n].numpy()).reshape(-1)
+
+                def run(i, flat=flat, t=t):
+                    lo, hi = cuts[i], cuts[i + 1]
+                    oracle.step(flat[lo:], oracle.FP32, n_dp, n, hi - lo, w[lo:hi], m[lo:hi],
+                                v[lo:hi], out[lo:hi], oracle.BF16, t, grad_scale=1.0 / n_dp,
+                                **wl.hp)
+                list(pool.map(run, range(T)))
+            for name, got, want in (("master", W[c0:c0 + n], w), ("m", M[c0:c0 + n], m),
+                                    ("v", V[c0:c0 + n], v)):
+                g = got.cpu().numpy()
+                bad = np.count_nonzero(g.view(np.uint32) != want.view(np.uint32))
+                assert bad == 0, f"{name}: {bad} of {n} elements at shard offset {c0} differ"
+            g = slot[c0:c0 + n].cpu().numpy().view(np.uint16)
+            bad = np.count_nonzero(g != out)
+            assert bad == 0, f"weights: {bad} of {n} elements at shard offset {c0} differ"
+            compared += n
+            print(f"[full shard] config 5: {compared} of {S} elements bit-identical", flush=True)
+    assert compared == S
+
+
+def _same_f32(a, b):
+    """bitwise, NaN matching NaN"""
+    na, nb = np.isnan(a), np.isnan(b)
+    return np.array_equal(na, nb) and np.array_equal(a[~na].view(np.uint32), b[~nb].view(np.uint32))
+
+
+@pytest.mark.timeout(900)
+def test_every_element_of_the_8bit_shard():
+    B = zs.ZERO_Q8_BLOCK
+    wl = workload(6)
+    lay, _ = zs.zero_flatten_layout(wl.numels, wl.n_dp, B)
+    S, n_dp, rank = lay.shard, wl.n_dp, wl.rank
+    nb = S // B
+    d = wl.grad
+    print(f"\n[full shard] config 6 rank {rank} S={S} n_dp={n_dp} steps={wl.steps}", flush=True)
+    dev = torch.device("cuda")
+    rows_q = torch.empty((n_dp, S), dtype=torch.int8, device=dev)
+    rows_s = torch.empty((n_dp, nb), dtype=torch.float32, device=dev)
+    tmp = torch.empty(S, dtype=torch.float32, device=dev)
+    W = torch.empty(S, dtype=torch.float32, device=dev)
+    synth.fill_device(W, F32, wl.seed, synth.tag(BUF_MASTER, 6), rank * S, wl.master_sigma)
+    M = torch.zeros(S, dtype=torch.float32, device=dev)
+    V = torch.zeros(S, dtype=torch.float32, device=dev)
+    wq = torch.zeros(lay.n_pad, dtype=torch.int8, device=dev)
+    wsc = torch.zeros(lay.n_pad // B, dtype=torch.float32, device=dev)
+    for t in wl.steps:
+        for k in range(n_dp):
+            synth.fill_device(tmp, F32, wl.seed, synth.tag(BUF_GRAD, 6, t, 0, k), rank * S,
+                              d.eff_sigma, d.thr, d.outlier_mul)
+            zs.zero_q8_quantize(tmp, rows_q[k], rows_s[k])
+        zs.zero_shard_step_q8(rows_q, rows_s, S, nb, S, W, M, V, wq, wsc, lay, rank,
+                              zs.AdamWHParams(step=t, grad_scale=1.0 / n_dp, **wl.hp))
+    torch.cuda.synchronize()
+    del tmp
+    torch.cuda.empty_cache()
+
+    C = 1 << 25                                   # a whole number of blocks
+    rows_d = torch.empty((n_dp, C), dtype=torch.float32, device=dev)
+    rows_h = torch.empty((n_dp, C), dtype=torch.float32, pin_memory=True)
+    T = _threads()
+    compared = 0
+    last = wl.steps[-1]
+    with ThreadPoolExecutor(max_workers=T) as pool:
+        for c0 in range(0, S, C):
+            n = min(C, S - c0)
+            nbk = n // B
+            start = rank * S + c0
+            blk_cuts = [nbk * i // T for i in range(T + 1)]
+            w = synth.fill_host(F32, wl.seed, synth.tag(BUF_MASTER, 6), start, n,
+                                wl.master_sigma)
+            m = np.zeros(n, np.float32)
+            v = np.zeros(n, np.float32)
+            o_wq = np.zeros(n, np.int8)
+            o_ws = np.zeros(nbk, np.float32)
+            for t in wl.steps:
+                for k in range(n_dp):
+                    synth.fill_device(rows_d[k, :n], F32, wl.seed, synth.tag(BUF_GRAD, 6, t, 0, k),
+                                      start, d.eff_sigma, d.thr, d.outlier_mul)
+                rows_h[:, :n].copy_(rows_d[:, :n])
+                x = np.ascontiguousarray(rows_h[:, :n].numpy())
+                qs = list(pool.map(lambda k: oracle.q8_quantize(x[k], oracle.FP32), range(n_dp)))
+                gq = np.concatenate([q for q, _ in qs])
+                gs = np.concatenate([s_ for _, s_ in qs])
+                if t == last:  # the device quantizer: every code and scale of the step's rows
+                    for k in range(n_dp):
+                        assert np.array_equal(rows_q[k, c0:c0 + n].cpu().numpy(), qs[k][0]), \
+                            f"codes of row {k} at shard offset {c0}"
+                        assert _same_f32(rows_s[k, c0 // B:c0 // B + nbk].cpu().numpy(), qs[k][1]), \
+                            f"scales of row {k} at shard offset {c0}"
+
+                def run(i, gq=gq, gs=gs, t=t):
+                    b0, b1 = blk_cuts[i], blk_cuts[i + 1]
+                    lo, hi = b0 * B, b1 * B
+                    oracle.step_q8(gq[lo:], gs[b0:], n_dp, n, nbk, hi - lo, w[lo:hi], m[lo:hi],
+                                   v[lo:hi], o_wq[lo:hi], o_ws[b0:b1], t, grad_scale=1.0 / n_dp,
+                                   **wl.hp)
+                list(pool.map(run, range(T)))
+            for name, got, want in (("master", W[c0:c0 + n], w), ("m", M[c0:c0 + n], m),
+                                    ("v", V[c0:c0 + n], v)):
+                g = got.cpu().numpy()
+                bad = np.count_nonzero(g.view(np.uint32) != want.view(np.uint32))
+                assert bad == 0, f"{name}: {bad} of {n} elements at shard offset {c0} differ"
+            lo = rank * S + c0
+            assert np.array_equal(wq[lo:lo + n].cpu().numpy(), o_wq), f"weight codes at {c0}"
+            assert _same_f32(wsc[lo // B:lo // B + nbk].cpu().numpy(), o_ws), f"weight scales at {c0}"
+            compared += n
+            print(f"[full shard] config 6: {compared} of {S} elements bit-identical", flush=True)
     assert compared == S
