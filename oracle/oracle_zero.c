@@ -27,8 +27,11 @@
  *    pinned to the quantizer's own properties: codes in [-127, 127], the
  *    block's largest magnitude coded +-127, the rounding bound s/2, exact
  *    invariance under power-of-two scaling and sign flips, zero and
- *    non-finite blocks; ora_step_q8 equal to dequantize + the fp32-row step
- *    + quantize.
+ *    non-finite blocks, subnormal scales, hand-worked blocks and blocks
+ *    found by search where rint(x / s) differs from rint(x * 127 / absmax)
+ *    or from rounding the exact quotient (derived in exact rational
+ *    arithmetic); ora_step_q8 equal to dequantize + the fp32-row step +
+ *    quantize.
  *  - ora_reshard / ora_flat_*: slicing and concatenation of the flat vector
  *    in numpy, agreement of the two independent forms (equal shards against
  *    general pieces), round trips n_dp -> n_dp' -> n_dp, scatter after

@@ -58,3 +58,21 @@ def test_ranges_in_threads_equal_one_call():
         oracle.step(rows, oracle.BF16, n_dp, n, n, *ref, oracle.BF16, t, grad_scale=1.0 / n_dp, **hp)
     for got, want in zip(state, ref):
         assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+
+
+def test_roofline_and_ceiling_figures():
+    """The bench line's kernel figures from given event times: achieved GB/s
+    is the algorithmic bytes per launch over the average launch time, the
+    ceiling is read at the step's own residency cap, and frac_of_ceiling is
+    the ceiling's time over the step's."""
+    S, n_dp = 1_000_000, 8
+    r = dict(kms=[2.0, 2.0, 2.0], launch_bytes=42 * S, kernel="k", n_dp=n_dp,
+             ceiling={5: 2.2, 7: 1.9, 10: 1.8})
+    rl = bench.roofline_of(r, None)
+    assert rl["launch_ms_avg"] == 2.0 and rl["achieved"] == 42 * S / 2e-3 / 1e9
+    assert rl["frac"] == rl["achieved"] / bench.HBM_PEAK_GBPS
+    ceil, frac = bench.ceiling_of(r)
+    assert ceil["waves_per_cu"] == bench.STEP_CAPS[n_dp] == 7
+    assert ceil["launch_ms_avg"] == 1.9 and frac == 1.9 / 2.0
+    assert ceil["best_waves_per_cu"] == 10 and ceil["best_launch_ms_avg"] == 1.8
+    assert bench.ceiling_of(dict(r, ceiling=None)) == (None, None)
