@@ -50,7 +50,8 @@ def parse():
                         "7 configuration 4 with clipping and a dynamic loss scale")
     p.add_argument("--cpu-sample-log2", type=int, default=25,
                    help="CPU baseline sample: 2^k parameters of the shard")
-    p.add_argument("--cpu-steps", type=int, default=8)
+    p.add_argument("--cpu-steps", type=int, default=12,
+                   help="CPU baseline: optimizer steps over the sample (about 12 s single-threaded)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true",
                    help="time only the chosen workload (the plain default line also times "
