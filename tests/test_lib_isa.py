@@ -18,7 +18,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "zero_sharded_mixed_flatten_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["zero_shard.hip", "quant8.hip", "flat_copy.hip"]
+SOURCES = [os.path.join(CSRC, f) for f in ("zero_shard.hip", "quant8.hip", "flat_copy.hip")] + \
+    [os.path.join(ROOT, "calibration", "stream_mix.hip")]
 
 FORBIDDEN = [r"\bv_fma_mix", r"\bv_mad_mix", r"\bv_pk_fma_f32", r"\bv_pk_mul_f32",
              r"\bv_pk_add_f32"]
@@ -29,7 +30,7 @@ SCALAR_WRITES = [r"\bs_store", r"\bs_buffer_store", r"\bs_scratch_store", r"\bs_
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("src", SOURCES)
+@pytest.mark.parametrize("src", SOURCES, ids=os.path.basename)
 def test_no_rounding_changing_instructions(src):
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
@@ -38,7 +39,7 @@ def test_no_rounding_changing_instructions(src):
                         "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang",
                         "-packed-fp32-ops", "--offload-device-only", "-S",
                         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-                        os.path.join(CSRC, src), "-o", out],
+                        src, "-o", out],
                        check=True, capture_output=True)
         asm = open(out).read()
     kernels = len(re.findall(r"^\s*\.amdhsa_kernel\b", asm, flags=re.M))
