@@ -22,7 +22,8 @@ elements, t = 1..10, the benchmark's workload) and over n_dp = 64, rank 1
 at n_dp = 1 (1,557,611,200 elements, 5 warm-up steps and t = 6); and the 7B
 stage-2 accumulation (fp16 rows x 65536, 4 micro-batches reduced into the
 fp32 accumulator, AdamW gated on the overflow flag), whose accumulator is
-compared too; the 7B list in the per-parameter dim-0 layout with fp32
+compared too, alone and with global-norm clipping and the device-resident
+loss scale; the 7B list in the per-parameter dim-0 layout with fp32
 gradient rows (842,301,952 packed elements, t = 1..3); and the 8-bit path
 (fp32 draws quantized to int8 blocks on the device, the fused 8-bit step
 at t = 1, 2: every code and scale of the last step's rows, of the weight
@@ -126,29 +127,50 @@ def test_every_element_of_the_full_shard(cid, chunk_log2):
 
 
 @pytest.mark.timeout(900)
-def test_every_element_of_the_accumulated_full_shard():
-    wl = workload(4)
+@pytest.mark.parametrize("cid", [4, 7])
+def test_every_element_of_the_accumulated_full_shard(cid):
+    """Stage 2: 4 fp16 micro-batches reduced into the fp32 accumulator, then
+    AdamW gated on the overflow flag; with cid 7 also the sum of squares on
+    the last reduce, global-norm clipping (to a norm it must clip to) and
+    the device-resident loss scale.  The oracle is given the device's sum of
+    squares (its order differs by design); that sum is checked against the
+    oracle's own within 1e-10."""
+    wl = workload(cid)
     lay, _ = zs.zero_flatten_layout(wl.numels, wl.n_dp)
     S, n_dp, rank, micro = lay.shard, wl.n_dp, wl.rank, wl.micro_batches
     d = wl.grad
+    ctl = wl.controls
     scale = 1.0 / (n_dp * wl.loss_scale * micro)
-    print(f"\n[full shard] config 4 rank {rank} S={S} n_dp={n_dp} micro={micro}", flush=True)
+    print(f"\n[full shard] config {cid} rank {rank} S={S} n_dp={n_dp} micro={micro}", flush=True)
     dev = torch.device("cuda")
     slab = torch.empty((n_dp, S), dtype=torch.float16, device=dev)
     acc = torch.empty(S, dtype=torch.float32, device=dev)
     W = torch.empty(S, dtype=torch.float32, device=dev)
-    synth.fill_device(W, F32, wl.seed, synth.tag(BUF_MASTER, 4), rank * S, wl.master_sigma)
+    synth.fill_device(W, F32, wl.seed, synth.tag(BUF_MASTER, cid), rank * S, wl.master_sigma)
     M = torch.zeros(S, dtype=torch.float32, device=dev)
     V = torch.zeros(S, dtype=torch.float32, device=dev)
     wf = torch.zeros(lay.n_pad, dtype=torch.bfloat16, device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    ss = torch.zeros(1, dtype=torch.float64, device=dev)
     for mb in range(micro):
         for k in range(n_dp):
-            synth.fill_device(slab[k], d.kind, wl.seed, synth.tag(BUF_GRAD, 4, 1, mb, k),
+            synth.fill_device(slab[k], d.kind, wl.seed, synth.tag(BUF_GRAD, cid, 1, mb, k),
                               rank * S, d.eff_sigma, d.thr, d.outlier_mul)
-        zs.zero_shard_reduce(slab, n_dp, S, S, acc, accumulate=mb > 0, overflow=flag)
-    zs.zero_shard_adamw(acc, W, M, V, wf, lay, rank,
-                        zs.AdamWHParams(step=1, grad_scale=scale, **wl.hp), skip=flag)
+        zs.zero_shard_reduce(slab, n_dp, S, S, acc, accumulate=mb > 0, overflow=flag,
+                             sumsq=ss if ctl and mb == micro - 1 else None)
+    if ctl:
+        dls = zs.new_loss_scale(wl.loss_scale)
+        torch.cuda.synchronize()
+        d_ss = float(ss.item())
+        s_ = 1.0 / (n_dp * micro) / wl.loss_scale
+        max_norm = 0.5 * (d_ss ** 0.5) * s_
+        assert oracle.clip_coef(d_ss, np.float32(s_), max_norm) < 1.0
+        zs.zero_shard_adamw_ex(acc, W, M, V, wf, lay, rank,
+                               zs.AdamWHParams(step=1, grad_scale=1.0 / (n_dp * micro), **wl.hp),
+                               skip=flag, sumsq=ss, max_norm=max_norm, loss_scale=dls)
+    else:
+        zs.zero_shard_adamw(acc, W, M, V, wf, lay, rank,
+                            zs.AdamWHParams(step=1, grad_scale=scale, **wl.hp), skip=flag)
     torch.cuda.synchronize()
     assert int(flag.item()) == 0
     del slab
@@ -160,6 +182,7 @@ def test_every_element_of_the_accumulated_full_shard():
     slot = wf.view(torch.int16)[rank * S:(rank + 1) * S]
     T = _threads()
     compared = 0
+    o_ss_total = 0.0
     with ThreadPoolExecutor(max_workers=T) as pool:
         for c0 in range(0, S, C):
             n = min(C, S - c0)
@@ -167,21 +190,24 @@ def test_every_element_of_the_accumulated_full_shard():
             cuts = [n * i // T for i in range(T + 1)]
             a = np.zeros(n, np.float32)
             o_flag = np.zeros((T, 1), np.uint32)
+            o_ss = np.zeros((T, 1), np.float64)
             for mb in range(micro):
                 for k in range(n_dp):
                     synth.fill_device(rows_d[k, :n], d.kind, wl.seed,
-                                      synth.tag(BUF_GRAD, 4, 1, mb, k), start, d.eff_sigma,
+                                      synth.tag(BUF_GRAD, cid, 1, mb, k), start, d.eff_sigma,
                                       d.thr, d.outlier_mul)
                 rows_h[:, :n].copy_(rows_d.view(torch.int16)[:, :n])
                 flat = np.ascontiguousarray(rows_h[:, :n].numpy()).view(np.uint16).reshape(-1)
+                last = mb == micro - 1
 
-                def red(i, flat=flat, mb=mb):
+                def red(i, flat=flat, mb=mb, last=last):
                     lo, hi = cuts[i], cuts[i + 1]
                     oracle.reduce(flat[lo:], oracle.FP16, n_dp, n, hi - lo, a[lo:hi], mb > 0,
-                                  overflow=o_flag[i])
+                                  overflow=o_flag[i], sumsq=o_ss[i] if ctl and last else None)
                 list(pool.map(red, range(T)))
             assert not o_flag.any()
-            w = synth.fill_host(F32, wl.seed, synth.tag(BUF_MASTER, 4), start, n,
+            o_ss_total += float(o_ss.sum())
+            w = synth.fill_host(F32, wl.seed, synth.tag(BUF_MASTER, cid), start, n,
                                 wl.master_sigma)
             m = np.zeros(n, np.float32)
             v = np.zeros(n, np.float32)
@@ -189,8 +215,15 @@ def test_every_element_of_the_accumulated_full_shard():
 
             def upd(i):
                 lo, hi = cuts[i], cuts[i + 1]
-                oracle.adamw(a[lo:hi], w[lo:hi], m[lo:hi], v[lo:hi], out[lo:hi], oracle.BF16,
-                             hi - lo, 1, grad_scale=scale, skip=o_flag[i], **wl.hp)
+                if ctl:
+                    oracle.adamw_ex(a[lo:hi], w[lo:hi], m[lo:hi], v[lo:hi], out[lo:hi],
+                                    oracle.BF16, hi - lo, 1, grad_scale=1.0 / (n_dp * micro),
+                                    skip=o_flag[i], sumsq=np.array([d_ss]), max_norm=max_norm,
+                                    loss_scale=np.array([wl.loss_scale], np.float32), **wl.hp)
+                else:
+                    oracle.adamw(a[lo:hi], w[lo:hi], m[lo:hi], v[lo:hi], out[lo:hi],
+                                 oracle.BF16, hi - lo, 1, grad_scale=scale, skip=o_flag[i],
+                                 **wl.hp)
             list(pool.map(upd, range(T)))
             for name, got, want in (("acc", acc[c0:c0 + n], a), ("master", W[c0:c0 + n], w),
                                     ("m", M[c0:c0 + n], m), ("v", V[c0:c0 + n], v)):
@@ -201,8 +234,10 @@ def test_every_element_of_the_accumulated_full_shard():
             bad = np.count_nonzero(g != out)
             assert bad == 0, f"weights: {bad} of {n} elements at shard offset {c0} differ"
             compared += n
-            print(f"[full shard] config 4: {compared} of {S} elements bit-identical", flush=True)
+            print(f"[full shard] config {cid}: {compared} of {S} elements bit-identical", flush=True)
     assert compared == S
+    if ctl:
+        assert abs(d_ss - o_ss_total) <= 1e-10 * o_ss_total
 
 
 @pytest.mark.timeout(900)
