@@ -227,6 +227,51 @@ def test_full_size_reshard_8_to_16_sampled():
     torch.cuda.empty_cache()
 
 
+def test_full_size_conversions_every_element():
+    """The 7B fp32 master in 8 old shards of 842M elements: re-sharded to new
+    rank 5 of 16 and to new rank 11 of 12 (ending in padding), and
+    consolidated into the model's 291 parameter tensors (one scatter per
+    old shard).  A conversion moves each element of the flat vector, so the
+    expected value of every element is the seeded stream's draw at its flat
+    index (zero past N); it is drawn on the device by the generator's device
+    build (bit-identical to its host build, tests/test_gpu_synth.py) and
+    every element is compared bit for bit."""
+    l8 = _llama_layout(8)
+    n, s8 = l8.n, l8.shard
+    tg = tag(5, 73)
+    old = []
+    for r in range(8):
+        t = torch.empty(s8, device="cuda")
+        synth.fill_device(t, F32, 7, tg, r * s8, 0.02)
+        old.append(t)
+    for n_new, rank in ((16, 5), (12, 11)):
+        s_new = _llama_layout(n_new).shard
+        print(f"\n[full] re-shard 8 -> {n_new}, rank {rank}, {s_new} elements", flush=True)
+        out = torch.empty(s_new, device="cuda")
+        zs.zero_reshard(old, n, rank, out)
+        want = torch.zeros(s_new, device="cuda")
+        lo = rank * s_new
+        live = min(s_new, n - lo)
+        synth.fill_device(want[:live], F32, 7, tg, lo, 0.02)
+        assert torch.equal(out.view(torch.int32), want.view(torch.int32)), f"8 -> {n_new}"
+        assert live < s_new or n_new == 16
+        del out, want
+    numels = llama7b_numels()
+    _, offs = zs.zero_flatten_layout(numels, 8, 8)
+    tensors = [torch.empty(k, device="cuda") for k in numels]
+    pieces = list(zip(tensors, [int(o) for o in offs]))
+    for r in range(8):
+        zs.zero_flat_scatter(old[r], r * s8, pieces)
+    del old
+    torch.cuda.empty_cache()
+    print(f"[full] consolidation into {len(numels)} tensors", flush=True)
+    want = torch.empty(max(numels), device="cuda")
+    for t, o in pieces:
+        k = t.numel()
+        synth.fill_device(want[:k], F32, 7, tg, o, 0.02)
+        assert torch.equal(t.view(torch.int32), want[:k].view(torch.int32)), f"tensor at {o}"
+
+
 def test_resume_on_another_gpu_count_keeps_the_trajectory():
     """3 steps on 4 ranks, the state (fp32 master, m, v and the bf16 weight
     buffer) converted on the device to 3 ranks, 3 more steps: bit-identical
