@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -94,13 +95,43 @@ def calibrate_copy(mib, steps):
                       "bytes_written_per_launch": n, "launches": steps}), flush=True)
 
 
+def kernel_files(source=KERNEL_SOURCE):
+    """The kernel source and every local header it includes, directly or
+    through another header (quoted includes, looked up beside the source and
+    in include/), sorted by path relative to the repository."""
+    seen, todo = set(), [os.path.abspath(source)]
+    dirs = [os.path.dirname(os.path.abspath(source)), os.path.join(ROOT, "include")]
+    while todo:
+        f = todo.pop()
+        if f in seen:
+            continue
+        seen.add(f)
+        for line in open(f, encoding="utf-8"):
+            m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+            if m:
+                for d in dirs:
+                    h = os.path.join(d, m.group(1))
+                    if os.path.exists(h):
+                        todo.append(os.path.abspath(h))
+                        break
+    return sorted(os.path.relpath(f, ROOT) for f in seen)
+
+
 def source_digest(source=KERNEL_SOURCE):
-    return hashlib.sha256(open(source, "rb").read()).hexdigest()
+    """sha256 over the names and contents of kernel_files(source): a change
+    to the kernel or to any header it includes changes the digest."""
+    h = hashlib.sha256()
+    for rel in kernel_files(source):
+        data = open(os.path.join(ROOT, rel), "rb").read()
+        h.update(f"{rel}\0{len(data)}\0".encode())
+        h.update(data)
+    return h.hexdigest()
 
 
 def committed_traffic(workload_name, source=KERNEL_SOURCE):
     """Counter-measured HBM bytes per launch of the dominant kernel, from the
-    committed counter summary -- only if it was taken on this kernel source."""
+    committed counter summary -- only if it was taken on this kernel source
+    and these headers (source_digest)."""
     path = os.path.join(COUNTERS_DIR, f"{workload_name}.counters.txt")
     if not os.path.exists(path):
         return None
@@ -109,7 +140,7 @@ def committed_traffic(workload_name, source=KERNEL_SOURCE):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != source_digest(source):
+    if kv.get("kernel_sources_sha256") != source_digest(source):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])

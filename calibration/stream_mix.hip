@@ -5,7 +5,10 @@
 // slot out: 2 n_dp + 26 bytes per element.  mix_kernel moves exactly those
 // bytes with the step's launch shape -- one quad (4 elements) per lane,
 // one-wave workgroups, one-shot grid, every load issued before any store,
-// non-temporal access, the same residency cap -- and does no arithmetic:
+// the same cache policies (non-temporal loads; non-temporal stores at
+// device scope, with the two wait states a store of more than 64 bits of
+// data needs before its registers are reused), the same residency cap --
+// and does no arithmetic:
 // the state is stored back as loaded and the slot gets the XOR of the
 // rows' bits.  Its time is the ceiling of that access pattern on this GPU,
 // against which the step's own time is reported.
@@ -18,6 +21,14 @@ namespace {
 constexpr int kWave = 64;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store16(float *p, f32x4 x) {
+    asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" : : "v"(p), "v"(x)
+                 : "memory");
+}
+__device__ __forceinline__ void store8(uint16_t *p, u32x2 x) {
+    asm volatile("global_store_dwordx2 %0, %1, off nt sc1" : : "v"(p), "v"(x) : "memory");
+}
 
 template <int NDP>
 __global__ void __launch_bounds__(kWave)
@@ -42,10 +53,10 @@ mix_kernel(const uint16_t *__restrict__ rows, int64_t ld, int64_t nquad, float *
     u32x2 x = r[0];
 #pragma unroll
     for (int k = 1; k < NDP; ++k) x ^= r[k];
-    __builtin_nontemporal_store(w2, reinterpret_cast<f32x4 *>(W + e0));
-    __builtin_nontemporal_store(m2, reinterpret_cast<f32x4 *>(M + e0));
-    __builtin_nontemporal_store(v2, reinterpret_cast<f32x4 *>(V + e0));
-    __builtin_nontemporal_store(x, reinterpret_cast<u32x2 *>(out + e0));
+    store16(W + e0, w2);
+    store16(M + e0, m2);
+    store16(V + e0, v2);
+    store8(out + e0, x);
 }
 
 // dynamic LDS (otherwise unused) that leaves room for about waves_per_cu

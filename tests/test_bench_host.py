@@ -76,3 +76,26 @@ def test_roofline_and_ceiling_figures():
     assert ceil["launch_ms_avg"] == 1.9 and frac == 1.9 / 2.0
     assert ceil["best_waves_per_cu"] == 10 and ceil["best_launch_ms_avg"] == 1.8
     assert bench.ceiling_of(dict(r, ceiling=None)) == (None, None)
+
+
+def test_traffic_digest_covers_the_included_headers(tmp_path, monkeypatch):
+    """A committed counter summary is used only while the kernel it measured
+    is unchanged: the digest covers the kernel source and every header it
+    includes, so an edit to a shared header also retires the summary."""
+    csrc = "zero_sharded_mixed_flatten_amd/csrc/"
+    assert bench.kernel_files(bench.KERNEL_SOURCE) == sorted(
+        ["include/zero_shard.h", csrc + "host_common.h", csrc + "step_common.h",
+         csrc + "zero_shard.hip"])
+    assert csrc + "step_common.h" in bench.kernel_files(bench.Q8_SOURCE)
+    assert csrc + "step_common.h" not in bench.kernel_files(bench.COPY_SOURCE)
+    # a copy of the tree's sources with one header changed by one byte
+    for rel in bench.kernel_files(bench.KERNEL_SOURCE):
+        dst = tmp_path / rel
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        dst.write_bytes(open(os.path.join(bench.ROOT, rel), "rb").read())
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    src = str(tmp_path / csrc / "zero_shard.hip")
+    before = bench.source_digest(src)
+    hdr = tmp_path / csrc / "step_common.h"
+    hdr.write_bytes(hdr.read_bytes() + b"\n")
+    assert bench.source_digest(src) != before

@@ -1,7 +1,9 @@
 """bench.py's same-mix ceiling kernel issues exactly the memory
 instructions of the fused step it stands for (CPU): compiled for gfx950,
 each instance (1, 8, 64 rows) holds n_dp 8-byte row loads, three 16-byte
-state loads, three 16-byte state stores and one 8-byte slot store.  The
+state loads, three 16-byte state stores and one 8-byte slot store, with the
+step's cache policies (non-temporal loads, non-temporal device-scope
+stores).  The
 state goes back unchanged, so its stores cannot be told from no stores by
 the data; a compiler that treated them as no-ops (it once did, and the
 kernel then reported 160 % of peak) is caught here."""
@@ -46,6 +48,8 @@ def test_ceiling_kernel_keeps_every_load_and_store():
                "global_store_dwordx4": "st16", "global_store_dwordx2": "st8"}.get(op)
         if key:
             seen[cur][key] += 1
+            pol = set(t[1:])
+            assert ({"nt", "sc1"} <= pol) if key.startswith("st") else ("nt" in pol), line
     assert sorted(seen) == [1, 8, 64]
     for n_dp, c in seen.items():
         assert c == {"ld8": n_dp, "ld16": 3, "st16": 3, "st8": 1}, (n_dp, c)

@@ -7,7 +7,12 @@ for this hardware).  Plain v_fma_f32 is not listed: the correctly rounded
 division and square root sequences use it internally; contraction of the
 source's own multiply-adds is off in the build and the bitwise GPU tests
 would show it.  The same scan requires that no kernel writes through the
-scalar data cache: every store the compiler emits is a vector store."""
+scalar data cache: every store the compiler emits is a vector store.  And a
+store written out in inline assembly with more than 64 bits of data must
+itself provide the two wait states this chip needs before its data
+registers may be overwritten (the compiler adds them after its own stores
+only)."""
+import functools
 import os
 import re
 import subprocess
@@ -29,9 +34,8 @@ SCALAR_WRITES = [r"\bs_store", r"\bs_buffer_store", r"\bs_scratch_store", r"\bs_
                  r"\bs_buffer_atomic", r"\bs_dcache_wb", r"\bs_dcache_discard"]
 
 
-@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("src", SOURCES, ids=os.path.basename)
-def test_no_rounding_changing_instructions(src):
+@functools.lru_cache(maxsize=None)
+def _asm(src):
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
         # the library's own flags (build.py), device code only, as assembly
@@ -41,9 +45,50 @@ def test_no_rounding_changing_instructions(src):
                         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
                         src, "-o", out],
                        check=True, capture_output=True)
-        asm = open(out).read()
+        return open(out).read()
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("src", SOURCES, ids=os.path.basename)
+def test_no_rounding_changing_instructions(src):
+    asm = _asm(src)
     kernels = len(re.findall(r"^\s*\.amdhsa_kernel\b", asm, flags=re.M))
     assert kernels > 0
     for pat in FORBIDDEN + SCALAR_WRITES:
         hits = re.findall(pat + r"[^\n]*", asm)
         assert not hits, f"{src}: {len(hits)} x {hits[0]}"
+
+
+WIDE_STORE = re.compile(r"^\s*(global|buffer|flat)_store_dwordx[34]\b")
+NOP = re.compile(r"^\s*s_nop\s+(\d+)")
+
+
+def _inline_asm_blocks(asm):
+    """the instruction lines of every inline-assembly block"""
+    blocks, cur = [], None
+    for line in asm.splitlines():
+        if ";;#ASMSTART" in line:
+            cur = []
+        elif ";;#ASMEND" in line:
+            blocks.append(cur)
+            cur = None
+        elif cur is not None and line.strip() and not line.strip().startswith(";"):
+            cur.append(line)
+    return blocks
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("src", SOURCES, ids=os.path.basename)
+def test_wide_inline_stores_carry_their_wait_states(src):
+    blocks = _inline_asm_blocks(_asm(src))
+    wide = 0
+    for b in blocks:
+        for i, line in enumerate(b):
+            if WIDE_STORE.match(line):
+                wide += 1
+                nxt = b[i + 1] if i + 1 < len(b) else ""
+                m = NOP.match(nxt)
+                assert m and int(m.group(1)) >= 1, \
+                    f"{os.path.basename(src)}: {line.strip()!r} followed by {nxt.strip()!r}"
+    if os.path.basename(src) == "zero_shard.hip":
+        assert wide > 0  # the fused step's state stores are written out

@@ -73,8 +73,12 @@ __device__ __forceinline__ u32x4 load_nt(const unsigned char *p) {
 __device__ __forceinline__ u32x4 load_plain(const unsigned char *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
+// non-temporal at device scope (nt sc1), as the step's streaming stores;
+// written out, so it carries the two wait states a store of more than 64
+// bits of data needs before its registers may be overwritten
 __device__ __forceinline__ void store_nt(unsigned char *p, u32x4 x) {
-    __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(p));
+    asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" : : "v"(p), "v"(x)
+                 : "memory");
 }
 
 // bytes [P, P + 16) of the 32 bytes lo:hi (little-endian)

@@ -41,8 +41,6 @@ namespace {
 using namespace zero_host;
 using namespace zero_step;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kB = ZERO_Q8_BLOCK;
 static_assert(kB == kWave * kQuad, "a quantization block is one wave of quads");
 constexpr int kRowBatchQ8 = 8;          // rows per batch when n_dp is not specialised
@@ -164,9 +162,7 @@ __device__ __forceinline__ float code(uint32_t packed, int e) {
 __device__ __forceinline__ uint32_t load_codes(const int8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
 }
-__device__ __forceinline__ void store_codes(int8_t *p, uint32_t x) {
-    __builtin_nontemporal_store(x, reinterpret_cast<uint32_t *>(p));
-}
+__device__ __forceinline__ void store_codes(int8_t *p, uint32_t x) { store4(p, x); }
 
 // the block handled by this wave, made wave-uniform (scalar) for the scale
 // loads; a launch covers at most 2^23 blocks (kLaunchElems / kB)
@@ -365,7 +361,7 @@ q8_dequantize_pair_kernel(const int8_t *__restrict__ q, const float *__restrict_
         }
         const u32x4 o{narrow2<YDT>(v[0], v[1]), narrow2<YDT>(v[2], v[3]),
                       narrow2<YDT>(v[4], v[5]), narrow2<YDT>(v[6], v[7])};
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(y + e0));
+        store16(y + e0, o);
         return;
     }
     // the range's last wave, or unaligned buffers: element by element
