@@ -41,8 +41,9 @@ COUNTERS_DIR = os.path.join(ROOT, "profiles")
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=200,
+                   help="timed steps (default 200: about a second of GPU time on the 7B shard)")
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", type=int, default=2,
                    help="workload: 1 GPT-2-XL n_dp=1, 2 7B n_dp=8 (default), "
                         "3 7B n_dp=64, 4 7B n_dp=8 fp16 with 4 micro-batches, "
