@@ -1,0 +1,54 @@
+"""bench.py's default line on the GPU: one JSON line with the keys the
+measurement contract names (the workload, params/s, the roofline of the
+dominant kernel with its counter traffic, the same-mix ceiling, the vendor
+copy and the other workloads), from a short run in a child process."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_default_line_carries_the_contract_keys():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()  # the child needs about 40 GB of HBM
+    print("\n[bench line] bench.py --steps 5 --warmup 2 --no-cpu-baseline", flush=True)
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "5",
+                        "--warmup", "2", "--no-cpu-baseline"],
+                       capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert p.returncode == 0, p.stderr[-2000:]
+    lines = [l for l in p.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, p.stdout[-2000:]
+    d = json.loads(lines[0])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+              "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+              "roofline", "cpu_baseline"):
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 2
+    assert d["higher_is_better"] is True and d["vs_baseline"] is None
+    assert d["cpu_baseline"] is None
+    assert d["config"]["workload"] == "llama7b_ndp8_shard"
+    assert d["config"]["shard"] == 842_301_952 and d["config"]["n_dp"] == 8
+    S = d["config"]["shard"]
+    assert abs(d["value"] - S / (d["ms_per_step"] * 1e-3)) <= 1e-6 * d["value"]
+    rl = d["roofline"]
+    assert rl["bound"] == "hbm" and rl["peak"] == 8000.0 and rl["unit"] == "GB/s"
+    assert rl["algorithmic_bytes_per_launch"] == 42 * S
+    assert abs(rl["achieved"] - 42 * S / (rl["launch_ms_avg"] * 1e-3) / 1e9) <= 1e-6 * rl["achieved"]
+    assert abs(rl["frac"] - rl["achieved"] / 8000.0) <= 1e-9
+    assert 0.5 < rl["frac"] < 1.0
+    # counter bytes from the committed summary when its sources match the tree
+    assert rl["traffic"] is None or abs(rl["traffic"] / (42 * S) - 1) < 0.01
+    assert d["ceiling"]["waves_per_cu"] == 7 and 0.9 < d["frac_of_ceiling"] < 1.1
+    assert 0.3 < d["vendor_copy"]["frac"] < 1.0
+    others = d["other_configs"]
+    assert sorted(others) == ["gpt2xl_ndp1", "llama7b_ndp64_shard", "llama7b_ndp8_fp16_accum4"]
+    for name, o in others.items():
+        assert "error" not in o, (name, o)
+        assert 0.5 < o["kernel_frac"] < 1.0 and o["params_per_s"] > 0, name
