@@ -1,8 +1,8 @@
-"""The usage example in the README runs as printed: its first Python block
-is executed on the GPU, then the weight slot it wrote is checked against the
-round-to-nearest-even bf16 cast of the master it updated, and the buffer
-outside the slot against the zeros it started from."""
+"""The usage example in README.md runs as written (small shapes, three
+steps) and does what its comments say: the weights' slot holds the bf16
+cast of the updated master, nothing else in the buffer is touched."""
 import os
+import re
 
 import pytest
 import torch
@@ -12,20 +12,17 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _example() -> str:
-    text = open(os.path.join(ROOT, "README.md")).read()
-    start = text.index("```python\n") + len("```python\n")
-    return text[start:text.index("```", start)]
-
-
 def test_readme_example_runs():
+    text = open(os.path.join(ROOT, "README.md"), encoding="utf-8").read()
+    blocks = re.findall(r"```python\n(.*?)```", text, flags=re.S)
+    assert len(blocks) == 1
     ns = {}
-    exec(compile(_example(), "README example", "exec"), ns)
-    lay, rank, S = ns["lay"], ns["rank"], ns["S"]
-    master, m, v, weights = ns["master"], ns["m"], ns["v"], ns["weights"]
-    assert S == 16016 and lay.n_pad == 4 * S
-    assert torch.isfinite(master).all() and (v >= 0).all() and (m != 0).any()
-    slot = weights[rank * S:(rank + 1) * S]
-    assert torch.equal(slot.view(torch.int16), master.to(torch.bfloat16).view(torch.int16))
-    outside = torch.cat([weights[:rank * S], weights[(rank + 1) * S:]])
-    assert torch.equal(outside.view(torch.int16), torch.zeros_like(outside.view(torch.int16)))
+    exec(compile(blocks[0], "README.md", "exec"), ns)
+    zs, lay, rank, S = ns["zs"], ns["lay"], ns["rank"], ns["S"]
+    master, weights = ns["master"], ns["weights"]
+    assert lay.n == 1000 * 64 + 64 and lay.n_dp == 4 and S * 4 == lay.n_pad
+    w = weights.float().cpu()
+    want = master.to(torch.bfloat16).float().cpu()
+    assert torch.equal(w[rank * S:(rank + 1) * S], want)
+    assert torch.count_nonzero(w[:rank * S]) == 0 and torch.count_nonzero(w[(rank + 1) * S:]) == 0
+    assert int(ns["t"]) == 3 and isinstance(zs.AdamWHParams(step=1), zs.AdamWHParams)
