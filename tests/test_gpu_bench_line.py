@@ -42,7 +42,8 @@ def test_default_line_carries_the_contract_keys():
     assert rl["algorithmic_bytes_per_launch"] == 42 * S
     assert abs(rl["achieved"] - 42 * S / (rl["launch_ms_avg"] * 1e-3) / 1e9) <= 1e-6 * rl["achieved"]
     assert abs(rl["frac"] - rl["achieved"] / 8000.0) <= 1e-9
-    assert 0.5 < rl["frac"] < 1.0
+    # a regression guard with room for the box-to-box spread (measured 0.81-0.84)
+    assert 0.75 < rl["frac"] < 1.0
     # counter bytes from the committed summary when its sources match the tree
     assert rl["traffic"] is None or abs(rl["traffic"] / (42 * S) - 1) < 0.01
     assert d["ceiling"]["waves_per_cu"] == 7 and 0.9 < d["frac_of_ceiling"] < 1.1
@@ -51,4 +52,5 @@ def test_default_line_carries_the_contract_keys():
     assert sorted(others) == ["gpt2xl_ndp1", "llama7b_ndp64_shard", "llama7b_ndp8_fp16_accum4"]
     for name, o in others.items():
         assert "error" not in o, (name, o)
-        assert 0.5 < o["kernel_frac"] < 1.0 and o["params_per_s"] > 0, name
+        # measured 0.71-0.85 across the three workloads and boxes
+        assert 0.65 < o["kernel_frac"] < 1.0 and o["params_per_s"] > 0, name
