@@ -18,9 +18,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_default_line_carries_the_contract_keys():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()  # the child needs about 40 GB of HBM
-    print("\n[bench line] bench.py --steps 5 --warmup 2 --no-cpu-baseline", flush=True)
-    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "5",
-                        "--warmup", "2", "--no-cpu-baseline"],
+    print("\n[bench line] bench.py --steps 20 --warmup 5 --no-cpu-baseline", flush=True)
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "20",
+                        "--warmup", "5", "--no-cpu-baseline"],
                        capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert p.returncode == 0, p.stderr[-2000:]
     lines = [l for l in p.stdout.splitlines() if l.startswith("{")]
@@ -30,7 +30,7 @@ def test_default_line_carries_the_contract_keys():
               "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
               "roofline", "cpu_baseline"):
         assert k in d, k
-    assert d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 2
+    assert d["n_gpus"] == 1 and d["steps"] == 20 and d["warmup"] == 5
     assert d["higher_is_better"] is True and d["vs_baseline"] is None
     assert d["cpu_baseline"] is None
     assert d["config"]["workload"] == "llama7b_ndp8_shard"
@@ -42,8 +42,9 @@ def test_default_line_carries_the_contract_keys():
     assert rl["algorithmic_bytes_per_launch"] == 42 * S
     assert abs(rl["achieved"] - 42 * S / (rl["launch_ms_avg"] * 1e-3) / 1e9) <= 1e-6 * rl["achieved"]
     assert abs(rl["frac"] - rl["achieved"] / 8000.0) <= 1e-9
-    # a regression guard with room for the box-to-box spread (measured 0.81-0.84)
-    assert 0.75 < rl["frac"] < 1.0
+    print(f"[bench line] kernel {rl['launch_ms_avg']:.3f} ms, {rl['frac']:.4f} of 8 TB/s", flush=True)
+    # a loose regression guard, far below the box-to-box spread (0.81-0.84 measured)
+    assert 0.7 < rl["frac"] < 1.0
     # counter bytes from the committed summary when its sources match the tree
     assert rl["traffic"] is None or abs(rl["traffic"] / (42 * S) - 1) < 0.01
     assert d["ceiling"]["waves_per_cu"] == 7 and 0.9 < d["frac_of_ceiling"] < 1.1
@@ -53,4 +54,4 @@ def test_default_line_carries_the_contract_keys():
     for name, o in others.items():
         assert "error" not in o, (name, o)
         # measured 0.71-0.85 across the three workloads and boxes
-        assert 0.65 < o["kernel_frac"] < 1.0 and o["params_per_s"] > 0, name
+        assert 0.6 < o["kernel_frac"] < 1.0 and o["params_per_s"] > 0, name
